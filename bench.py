@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse matmul training step on one MI355X.
+
+A step is one pass of the whole per-batch path over one batch of synthetic input:
+fprop (y = x.W), bprop (dx = dy.W^T) and updat (dW over the present blocks), each
+one launch of libbsmm through its C ABI on the current HIP stream.  The layout
+compile and the one-time table upload happen before timing; identity_init is timed
+once on its own and reported beside the step.
+
+Workload (default): hidden 4096, block 32, minibatch 64, a Bernoulli(0.5) 128x128
+block layout (the usage example of the kiteco/blocksparse README), bf16 storage
+with fp32 accumulation, feature_axis 1, seed 1001.  Inputs are seeded synthetic data
+(synth.workload_problem); there is no dataset.
+
+Timing: W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize().
+To keep the timed passes reading HBM rather than the 256 MiB Infinity Cache, the
+step cycles through several copies of its buffers (at least --rotate-mib MiB in
+total); the same step on one buffer set is reported as "warm".  Kernel durations
+come from the dispatches' own timestamps (hipExtLaunchKernelGGL start/stop events
+via bsmm_profile_begin/end) over the timed region.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense, per dtype
+DT_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+PASSES = ("fprop", "bprop", "updat")
+KERNEL_NAME = {"fprop": "mm_kernel (fprop)", "bprop": "mm_kernel (bprop)", "updat": "updat_kernel"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="hidden4096_b32_n64")
+    ap.add_argument("--dtype", default=None, help="storage dtype (default: bf16 if the workload has it)")
+    ap.add_argument("--extra-dtypes", default="f32", help="comma list of further dtypes to time (reported aside)")
+    ap.add_argument("--rotate-mib", type=float, default=1024.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
+    return ap.parse_args()
+
+
+def pass_cost(P, dtype):
+    """FLOPs and algorithmic HBM bytes of one launch of each pass."""
+    b, N, G, nnz = P.block, P.N, 1, P.nnz
+    s = DT_BYTES[dtype]
+    C, K = P.R * b, P.S * b
+    flops = 2.0 * N * b * b * nnz
+    x, y, w = N * C * s, N * K * s, nnz * b * b * s
+    dw = nnz * b * b * 4
+    return {
+        "fprop": (flops, x + y + w),
+        "bprop": (flops, y + x + w),
+        "updat": (flops * G, G * (x + y) + dw),
+    }
+
+
+def roof(flops, nbytes, dtype):
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    return ("mfma", t_mfma) if t_mfma >= t_hbm else ("hbm", t_hbm)
+
+
+def traffic_record(kernel_key, workload, dtype):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if its kernel
+    source still matches; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}_{workload}_{dtype}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = open(os.path.join(ROOT, "block_sparse_matrix_amd", "csrc", "kernels.hip"), "rb").read()
+    if kv.get("kernels_hip_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(P, dtype, target_s):
+    """The oracle, untouched, on the host cores: whole passes of the same workload,
+    repeated until about target_s seconds have elapsed."""
+    import oracle
+    import synth
+    bits = synth.to_bits
+    L, b, fa, N = P.layout, P.block, P.fa, P.N
+    x, dy, w = bits(P.xs[0]), bits(P.dys[0]), bits(P.w)
+    flops_step = 3 * 2.0 * N * b * b * P.nnz
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fprop(L, b, fa, x, w, N, dtype)
+        oracle.bprop(L, b, fa, dy, w, N, dtype)
+        oracle.updat(L, b, fa, [x], [dy], N, dtype)
+        done += 1
+        flops += flops_step
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} full steps (fprop+bprop+updat) of the same workload and seed, "
+                      f"{dt:.1f} s on the host, fp64 accumulation"}
+
+
+def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
+    import torch
+    import block_sparse_matrix_amd as bs
+    import synth
+
+    t0 = time.perf_counter()
+    P = synth.workload_problem(name, dtype)
+    m = bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
+    t_layout = time.perf_counter() - t0   # includes input generation
+    h, N = m.handle, P.N
+    dev = torch.device("cuda", 0)
+    x0 = P.xs[0].to(dev)
+    dy0 = P.dys[0].to(dev)
+    w0 = P.w.to(dev)
+    set_bytes = (x0.numel() + dy0.numel() + w0.numel()) * x0.element_size() * 2 + w0.numel() * 4
+    R = max(1, int(np.ceil(rotate_mib * 2**20 / set_bytes)))
+    sets = []
+    for _ in range(R):
+        sets.append(dict(x=x0.clone(), dy=dy0.clone(), w=w0.clone(),
+                         y=torch.empty(m.o_shape(N), dtype=x0.dtype, device=dev),
+                         dx=torch.empty(m.i_shape(N), dtype=x0.dtype, device=dev),
+                         dw=torch.empty(m.w_shape, dtype=torch.float32, device=dev)))
+
+    def step(s):
+        bs.bsmm_fprop(h, s["x"], s["w"], s["y"], N)
+        bs.bsmm_bprop(h, s["dy"], s["w"], s["dx"], N)
+        bs.bsmm_updat(h, [s["x"]], [s["dy"]], s["dw"], N)
+
+    # identity_init, timed once on its own (after a warm-up launch)
+    wi = torch.empty(m.w_shape, dtype=x0.dtype, device=dev)
+    bs.bsmm_identity_init(h, wi)
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    bs.bsmm_identity_init(h, wi)
+    ident = bs.bsmm_profile_end()["identity"]
+
+    def timed(nsets):
+        for i in range(warmup):
+            step(sets[i % nsets])
+        torch.cuda.synchronize()
+        bs.bsmm_profile_begin()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(sets[i % nsets])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = bs.bsmm_profile_end()
+        return (t1 - t0) * 1e3 / steps, prof
+
+    ms_cold, prof_cold = timed(R)
+    ms_warm, prof_warm = timed(1)
+    cost = pass_cost(P, dtype)
+    per = {}
+    for p in PASSES:
+        flops, nbytes = cost[p]
+        tot, cnt = prof_cold[p]
+        us = tot / cnt * 1e3
+        bound, tstar = roof(flops, nbytes, dtype)
+        wt, wc = prof_warm[p]
+        per[p] = {"kernel_us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+                  "alg_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "alg_bytes": int(nbytes), "flops": int(flops),
+                  "bound": bound, "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 4),
+                  "warm_kernel_us": round(wt / wc * 1e3, 3)}
+    flops_step = sum(cost[p][0] for p in PASSES)
+    return dict(P=P, ms=ms_cold, ms_warm=ms_warm, per=per, flops_step=flops_step, R=R,
+                identity_us=ident[0] / max(ident[1], 1) * 1e3, prep_s=t_layout)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = synth.WORKLOADS[args.workload]
+    dtype = args.dtype or ("bf16" if "bf16" in wl.dtypes else wl.dtypes[0])
+    res = run_dtype(args, args.workload, dtype, args.rotate_mib, args.steps, args.warmup)
+    P, per = res["P"], res["per"]
+    dom = max(PASSES, key=lambda p: per[p]["kernel_us"])
+    d = per[dom]
+    if d["bound"] == "hbm":
+        achieved, peak, unit = d["alg_bytes"] / (d["kernel_us"] * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = d["flops"] / (d["kernel_us"] * 1e-6) / 1e12, MFMA_PEAK_TFLOPS[dtype], "TFLOP/s"
+    roofline = {"bound": d["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_record(dom, args.workload, dtype),
+                "kernel": KERNEL_NAME[dom], "kernel_us": d["kernel_us"],
+                "alg_bytes_per_launch": d["alg_bytes"], "flops_per_launch": d["flops"]}
+    value = res["flops_step"] / (res["ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "effective TFLOP/s (nonzero blocks) fprop/bprop/updat; % MFMA or HBM roofline",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "hidden": wl.hidden, "block": wl.block, "minibatch": P.N,
+                   "feature_axis": wl.fa, "layout": wl.layout_kind, "seed": wl.seed, "nnz": P.nnz,
+                   "passes": "fprop+bprop+updat", "buffer_sets_rotated": res["R"]},
+        "roofline": roofline,
+        "per_pass": per,
+        "warm_ms_per_step": round(res["ms_warm"], 5),
+        "identity_init_us": round(res["identity_us"], 3),
+    }
+    extras = {}
+    for xd in [t for t in args.extra_dtypes.split(",") if t and t in wl.dtypes and t != dtype]:
+        r = run_dtype(args, args.workload, xd, args.rotate_mib, args.steps, args.warmup)
+        extras[xd] = {"value": round(r["flops_step"] / (r["ms"] * 1e-3) / 1e12, 3), "ms_per_step": round(r["ms"], 5),
+                      "per_pass": r["per"]}
+    if extras:
+        out["other_dtypes"] = extras
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

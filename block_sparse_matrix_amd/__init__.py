@@ -1,0 +1,358 @@
+"""Block-sparse matrix multiply for AMD MI355X, over the C ABI of libbsmm.so.
+
+Python mirror of the BlocksparseMatMul interface in the kiteco/blocksparse README
+("API Documentation" › blocksparse.matmul): a layout of zeros and ones, a block size
+of 8, 16 or 32, the feature_axis choice of activation layout, the shape helpers,
+block_coord, identity_init, __call__ with dw_dtype, and the grouped weight gradient
+(group_param_grads becomes an explicit call, since PyTorch has no graph to rewrite).
+
+This module only marshals arguments: every arithmetic step runs in libbsmm's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no CPU
+path: tensors must live on a ROCm device, and a missing libbsmm.so raises.
+
+The raw C entry points are exposed under their C names (bsmm_create, bsmm_fprop,
+bsmm_bprop, bsmm_updat, bsmm_identity_init, ...) taking torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "BlocksparseMatMul", "BsmmError", "group_param_grads", "lib", "LIB_PATH",
+    "bsmm_create", "bsmm_destroy", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_identity_init",
+    "bsmm_w_shape", "bsmm_i_shape", "bsmm_o_shape", "bsmm_block_coord", "bsmm_workspace_size",
+    "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so")
+
+BSMM_OK = 0
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3}
+
+
+class BsmmError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbsmm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_matrix_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    P64 = ctypes.POINTER(i64)
+    sz = ctypes.c_size_t
+    sigs = {
+        "bsmm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, i32],
+        "bsmm_w_shape": [vp, P64],
+        "bsmm_i_shape": [vp, i64, P64],
+        "bsmm_o_shape": [vp, i64, P64],
+        "bsmm_block_coord": [vp, i64, P64, P64],
+        "bsmm_plan_info": [vp, P64],
+        "bsmm_workspace_size": [vp, i32, i64, i32, ctypes.POINTER(sz)],
+        "bsmm_fprop": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
+        "bsmm_bprop": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
+        "bsmm_updat": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
+        "bsmm_identity_init": [vp, vp, i32, vp],
+        "bsmm_debug_lut": [vp, i32, P64, i64, P64],
+        "bsmm_profile_begin": [],
+        "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.bsmm_destroy.argtypes = [vp]
+    L.bsmm_destroy.restype = None
+    L.bsmm_status_string.argtypes = [ctypes.c_int]
+    L.bsmm_status_string.restype = ctypes.c_char_p
+    L.bsmm_last_error.argtypes = []
+    L.bsmm_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str):
+    if status != BSMM_OK:
+        L = lib()
+        raise BsmmError(status, func, f"{L.bsmm_status_string(status).decode()}: {L.bsmm_last_error().decode()}")
+
+
+def _stream(t: Optional[torch.Tensor] = None):
+    dev = t.device if t is not None else torch.device("cuda", torch.cuda.current_device())
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a ROCm device tensor (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---- raw C entry points, same names -------------------------------------------------
+def bsmm_create(layout, block_size: int = 32, feature_axis: int = 1) -> ctypes.c_void_p:
+    L = np.ascontiguousarray(np.asarray(layout), dtype=np.uint8) if not isinstance(layout, np.ndarray) \
+        or layout.dtype != np.uint8 else np.ascontiguousarray(layout)
+    if L.ndim != 2:
+        raise ValueError("layout must be a 2-D array of zeros and ones")
+    h = ctypes.c_void_p()
+    _check(lib().bsmm_create(ctypes.byref(h), L.ctypes.data_as(ctypes.c_void_p), L.shape[0], L.shape[1],
+                             int(block_size), int(feature_axis)), "bsmm_create")
+    return h
+
+
+def bsmm_destroy(h) -> None:
+    lib().bsmm_destroy(h)
+
+
+def bsmm_w_shape(h):
+    out = (ctypes.c_int64 * 3)()
+    _check(lib().bsmm_w_shape(h, out), "bsmm_w_shape")
+    return tuple(out)
+
+
+def bsmm_i_shape(h, N: int):
+    out = (ctypes.c_int64 * 2)()
+    _check(lib().bsmm_i_shape(h, N, out), "bsmm_i_shape")
+    return tuple(out)
+
+
+def bsmm_o_shape(h, N: int):
+    out = (ctypes.c_int64 * 2)()
+    _check(lib().bsmm_o_shape(h, N, out), "bsmm_o_shape")
+    return tuple(out)
+
+
+def bsmm_block_coord(h, block: int):
+    c, k = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().bsmm_block_coord(h, block, ctypes.byref(c), ctypes.byref(k)), "bsmm_block_coord")
+    return int(c.value), int(k.value)
+
+
+def bsmm_plan_info(h):
+    out = (ctypes.c_int64 * 5)()
+    _check(lib().bsmm_plan_info(h, out), "bsmm_plan_info")
+    return dict(zip(("R", "S", "block_size", "feature_axis", "nnz"), tuple(out)))
+
+
+def bsmm_workspace_size(h, pass_: int, N: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().bsmm_workspace_size(h, pass_, N, DTYPE_CODE[dtype], ctypes.byref(out)), "bsmm_workspace_size")
+    return int(out.value)
+
+
+def bsmm_debug_lut(h, which: int) -> np.ndarray:
+    n = ctypes.c_int64()
+    _check(lib().bsmm_debug_lut(h, which, None, 0, ctypes.byref(n)), "bsmm_debug_lut")
+    out = np.zeros(max(n.value, 1), dtype=np.int64)
+    _check(lib().bsmm_debug_lut(h, which, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n.value,
+                                ctypes.byref(n)), "bsmm_debug_lut")
+    return out[:n.value]
+
+
+def _ws(h, pass_, N, dtype, device):
+    nbytes = bsmm_workspace_size(h, pass_, N, dtype)
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def bsmm_fprop(h, x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, N: int) -> None:
+    ws, nb = _ws(h, 0, N, x.dtype, x.device)
+    _check(lib().bsmm_fprop(h, _dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(y, "y"), N, DTYPE_CODE[x.dtype],
+                            _dev_ptr(ws, "ws"), nb, _stream(x)), "bsmm_fprop")
+
+
+def bsmm_bprop(h, dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, N: int) -> None:
+    ws, nb = _ws(h, 1, N, dy.dtype, dy.device)
+    _check(lib().bsmm_bprop(h, _dev_ptr(dy, "dy"), _dev_ptr(w, "w"), _dev_ptr(dx, "dx"), N,
+                            DTYPE_CODE[dy.dtype], _dev_ptr(ws, "ws"), nb, _stream(dy)), "bsmm_bprop")
+
+
+def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: torch.Tensor, N: int) -> None:
+    G = len(xs)
+    if G != len(dys):
+        raise ValueError("xs and dys differ in length")
+    xp = (ctypes.c_void_p * max(G, 1))(*[_dev_ptr(t, "xs[t]").value for t in xs])
+    dp = (ctypes.c_void_p * max(G, 1))(*[_dev_ptr(t, "dys[t]").value for t in dys])
+    dt = xs[0].dtype if G else dw.dtype
+    ws, nb = _ws(h, 2, N, dt, dw.device)
+    _check(lib().bsmm_updat(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[dt], DTYPE_CODE[dw.dtype],
+                            _dev_ptr(ws, "ws"), nb, _stream(dw)), "bsmm_updat")
+
+
+def bsmm_identity_init(h, w: torch.Tensor) -> None:
+    _check(lib().bsmm_identity_init(h, _dev_ptr(w, "w"), DTYPE_CODE[w.dtype], _stream(w)), "bsmm_identity_init")
+
+
+def bsmm_profile_begin() -> None:
+    _check(lib().bsmm_profile_begin(), "bsmm_profile_begin")
+
+
+def bsmm_profile_end():
+    """Returns {pass: (total_ms, count)} of the kernel times recorded since begin."""
+    ms = (ctypes.c_double * 4)()
+    cnt = (ctypes.c_int64 * 4)()
+    _check(lib().bsmm_profile_end(ms, cnt), "bsmm_profile_end")
+    return {name: (ms[i], int(cnt[i])) for name, i in PASS.items()}
+
+
+# ---- BlocksparseMatMul --------------------------------------------------------------
+class _Handle:
+    def __init__(self, h):
+        self.h = h
+
+    def __del__(self):
+        try:
+            if self.h:
+                lib().bsmm_destroy(self.h)
+        except Exception:
+            pass
+
+
+class _BsmmFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, bsmm, x, w, dw_dtype):
+        ctx.bsmm = bsmm
+        ctx.dw_dtype = dw_dtype
+        ctx.save_for_backward(x, w)
+        return bsmm.fprop(x, w)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w = ctx.saved_tensors
+        bsmm = ctx.bsmm
+        dy = dy.contiguous()
+        dx = bsmm.bprop(dy, w) if ctx.needs_input_grad[1] else None
+        dw = bsmm.updat([x], [dy], dw_dtype=ctx.dw_dtype).to(w.dtype) if ctx.needs_input_grad[2] else None
+        return None, dx, dw, None
+
+
+class BlocksparseMatMul:
+    """y = x . W for a block-sparse W (see include/bsmm.h for the exact conventions).
+
+    layout        2-D array of zeros and ones, shape (C/b, K/b); row = input block c.
+    block_size    8, 16 or 32.
+    feature_axis  1: activations (N, features); 0: (features, N).
+    """
+
+    def __init__(self, layout, block_size: int = 32, feature_axis: int = 1):
+        self.layout = np.ascontiguousarray(np.asarray(layout), dtype=np.uint8)
+        self.block_size = int(block_size)
+        self.feature_axis = int(feature_axis)
+        self._h = _Handle(bsmm_create(self.layout, self.block_size, self.feature_axis))
+        info = bsmm_plan_info(self._h.h)
+        self.R, self.S, self.nnz = info["R"], info["S"], info["nnz"]
+        self.C = self.R * self.block_size
+        self.K = self.S * self.block_size
+
+    @property
+    def handle(self):
+        return self._h.h
+
+    # shape helpers (N = minibatch)
+    @property
+    def w_shape(self):
+        return bsmm_w_shape(self.handle)
+
+    def i_shape(self, N: int):
+        return bsmm_i_shape(self.handle, N)
+
+    def o_shape(self, N: int):
+        return bsmm_o_shape(self.handle, N)
+
+    def block_coord(self, block: int):
+        return bsmm_block_coord(self.handle, block)
+
+    def _N(self, t: torch.Tensor, feats: int, what: str) -> int:
+        if t.dim() != 2:
+            raise ValueError(f"{what} must be 2-D")
+        if self.feature_axis == 1:
+            if t.shape[1] != feats:
+                raise ValueError(f"{what} has {t.shape[1]} features, expected {feats}")
+            return t.shape[0]
+        if t.shape[0] != feats:
+            raise ValueError(f"{what} has {t.shape[0]} features, expected {feats}")
+        return t.shape[1]
+
+    def _check_w(self, w: torch.Tensor, dtype):
+        if tuple(w.shape) != tuple(self.w_shape):
+            raise ValueError(f"w has shape {tuple(w.shape)}, expected {self.w_shape}")
+        if w.dtype != dtype:
+            raise ValueError("w and the activations must share a dtype")
+
+    def identity_init(self, gpu: bool = False, dtype=torch.float32, device=None):
+        """Identity on present diagonal blocks, zero elsewhere.  gpu=True runs the device
+        kernel and returns a device tensor; gpu=False returns the initial value as a host
+        numpy array built from the layout's block coordinates."""
+        if gpu:
+            device = device or torch.device("cuda", torch.cuda.current_device())
+            w = torch.empty(self.w_shape, dtype=dtype, device=device)
+            bsmm_identity_init(self.handle, w)
+            return w
+        b = self.block_size
+        w = np.zeros(self.w_shape, dtype=np.float32)
+        eye = np.eye(b, dtype=np.float32)
+        for t in range(self.nnz):
+            c, k = self.block_coord(t)
+            if c == k:
+                w[t] = eye
+        return w
+
+    def fprop(self, x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+        N = self._N(x, self.C, "x")
+        self._check_w(w, x.dtype)
+        y = torch.empty(self.o_shape(N), dtype=x.dtype, device=x.device)
+        bsmm_fprop(self.handle, x, w, y, N)
+        return y
+
+    def bprop(self, dy: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+        N = self._N(dy, self.K, "dy")
+        self._check_w(w, dy.dtype)
+        dx = torch.empty(self.i_shape(N), dtype=dy.dtype, device=dy.device)
+        bsmm_bprop(self.handle, dy, w, dx, N)
+        return dx
+
+    def updat(self, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw_dtype=torch.float32,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """dW summed over the given steps (1 to 8), written in dw_dtype."""
+        if not 1 <= len(xs) <= 8 or len(xs) != len(dys):
+            raise ValueError("updat takes 1 to 8 (x, dy) pairs")
+        N = self._N(xs[0], self.C, "x")
+        for x, dy in zip(xs, dys):
+            if self._N(x, self.C, "x") != N or self._N(dy, self.K, "dy") != N:
+                raise ValueError("every step must have the same minibatch")
+            if x.dtype != xs[0].dtype or dy.dtype != xs[0].dtype:
+                raise ValueError("all steps must share a dtype")
+        dw = out if out is not None else torch.empty(self.w_shape, dtype=dw_dtype, device=xs[0].device)
+        bsmm_updat(self.handle, xs, dys, dw, N)
+        return dw
+
+    def __call__(self, x: torch.Tensor, w: torch.Tensor, dw_dtype=torch.float32) -> torch.Tensor:
+        """y = x . W, differentiable in x and w (bprop and updat kernels)."""
+        return _BsmmFunction.apply(self, x, w, dw_dtype)
+
+
+def group_param_grads(bsmm: BlocksparseMatMul, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor],
+                      dw_dtype=torch.float32) -> torch.Tensor:
+    """One weight gradient for up to 8 steps that share W: the sum of the per-step dWs,
+    formed by a single grouped updat launch (fp32 accumulation)."""
+    return bsmm.updat(xs, dys, dw_dtype=dw_dtype)

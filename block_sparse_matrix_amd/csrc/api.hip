@@ -1,0 +1,401 @@
+// C ABI of libbsmm (declared and documented in include/bsmm.h): argument checks,
+// lazy per-device upload of the layout tables, and dispatch to the kernel launchers.
+// Every argument is validated before the first HIP call, so the error paths run
+// without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "bsmm_internal.h"
+#include "kernels.h"
+
+using namespace bsmm;
+
+namespace {
+
+thread_local std::string g_err;
+
+bsmm_status fail(bsmm_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+bsmm_status dev_fail(hipError_t e, const char* what) {
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return BSMM_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dt(int dt) { return dt == BSMM_F32 || dt == BSMM_BF16 || dt == BSMM_F16; }
+
+// ---- kernel timing (bsmm_profile_begin / bsmm_profile_end) ----
+struct ProfRec {
+    int pass;
+    hipEvent_t e0, e1;
+};
+struct Prof {
+    bool on = false;
+    std::vector<ProfRec> recs;
+    std::vector<hipEvent_t> pool;
+    ~Prof() {
+        for (auto e : pool) (void)hipEventDestroy(e);
+    }
+};
+thread_local Prof g_prof;
+
+hipEvent_t pool_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// ---- per-device tables ----
+template <typename V>
+size_t bytes_of(const V& v) {
+    return v.size() * sizeof(typename V::value_type);
+}
+
+bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> guard(h->mu);
+    auto it = h->dev.find(dev);
+    if (it != h->dev.end()) {
+        *out = &it->second;
+        return BSMM_OK;
+    }
+    const HostLut& L = h->lut;
+    const std::vector<int32_t>* parts[7] = {&L.coords, &L.colptr, &L.colent, &L.rowptr,
+                                            &L.rowent, &L.colorder, &L.roworder};
+    size_t off[7], total = 0;
+    for (int i = 0; i < 7; i++) {
+        off[i] = total;
+        total += (bytes_of(*parts[i]) + 255) & ~(size_t)255;
+    }
+    if (total == 0) total = 256;
+    std::vector<char> staging(total, 0);
+    for (int i = 0; i < 7; i++)
+        if (!parts[i]->empty()) std::memcpy(staging.data() + off[i], parts[i]->data(), bytes_of(*parts[i]));
+    void* base = nullptr;
+    e = hipMalloc(&base, total);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of layout tables failed")
+                                                         : dev_fail(e, "hipMalloc");
+    e = hipMemcpy(base, staging.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        return dev_fail(e, "hipMemcpy of layout tables");
+    }
+    DeviceLut d;
+    d.base = base;
+    const char* b = (const char*)base;
+    d.coords = (const int32_t*)(b + off[0]);
+    d.colptr = (const int32_t*)(b + off[1]);
+    d.colent = (const int32_t*)(b + off[2]);
+    d.rowptr = (const int32_t*)(b + off[3]);
+    d.rowent = (const int32_t*)(b + off[4]);
+    d.colorder = (const int32_t*)(b + off[5]);
+    d.roworder = (const int32_t*)(b + off[6]);
+    auto res = h->dev.emplace(dev, d);
+    *out = &res.first->second;
+    return BSMM_OK;
+}
+
+bsmm_status check_call(bsmm_handle h, int64_t N, int dt) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
+    if (N > INT32_MAX) return fail(BSMM_ERR_UNSUPPORTED, "N above 2^31-1");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
+    return BSMM_OK;
+}
+
+bsmm_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(BSMM_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (!aligned16(p)) return fail(BSMM_ERR_ALIGNMENT, std::string(name) + " is not 16-byte aligned");
+    return BSMM_OK;
+}
+
+bsmm_status run_mm(bsmm_handle h, const void* in, const void* w, void* out, int64_t N, bsmm_dtype dt,
+                   bool bprop) {
+    bsmm_status s = check_call(h, N, dt);
+    if (s != BSMM_OK) return s;
+    if (N == 0) return BSMM_OK;
+    const char* nin = bprop ? "dy" : "x";
+    const char* nout = bprop ? "dx" : "y";
+    if ((s = check_ptr(in, nin)) != BSMM_OK) return s;
+    if ((s = check_ptr(out, nout)) != BSMM_OK) return s;
+    const HostLut& L = h->lut;
+    if (L.nnz > 0 && (s = check_ptr(w, "w")) != BSMM_OK) return s;
+    return BSMM_OK;
+}
+
+}  // namespace
+
+namespace bsmm {
+void prof_events(int pass, void** start, void** stop) {
+    *start = *stop = nullptr;
+    if (!g_prof.on) return;
+    hipEvent_t e0 = pool_event(), e1 = pool_event();
+    if (!e0 || !e1) return;
+    g_prof.recs.push_back({pass, e0, e1});
+    *start = e0;
+    *stop = e1;
+}
+}  // namespace bsmm
+
+extern "C" {
+
+bsmm_status bsmm_create(bsmm_handle* out, const uint8_t* layout, int64_t R, int64_t S, int block_size,
+                        int feature_axis) {
+    if (!out) return fail(BSMM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsmm_plan* p = new (std::nothrow) bsmm_plan();
+    if (!p) return fail(BSMM_ERR_OOM, "out of host memory");
+    std::string err;
+    bool ok = false;
+    try {
+        ok = compile_layout(layout, R, S, block_size, feature_axis, p->lut, err);
+    } catch (const std::bad_alloc&) {
+        delete p;
+        return fail(BSMM_ERR_OOM, "out of host memory compiling the layout");
+    }
+    if (!ok) {
+        delete p;
+        return fail(BSMM_ERR_INVALID_ARG, err);
+    }
+    *out = p;
+    return BSMM_OK;
+}
+
+void bsmm_destroy(bsmm_handle h) {
+    if (!h) return;
+    int cur = -1;
+    bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto& kv : h->dev) {
+        if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.base);
+    }
+    if (have_cur && !h->dev.empty()) (void)hipSetDevice(cur);
+    delete h;
+}
+
+bsmm_status bsmm_w_shape(bsmm_handle h, int64_t out[3]) {
+    if (!h || !out) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    out[0] = h->lut.nnz;
+    out[1] = out[2] = h->lut.b;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_i_shape(bsmm_handle h, int64_t N, int64_t out[2]) {
+    if (!h || !out || N < 0) return fail(BSMM_ERR_INVALID_ARG, "NULL argument or N < 0");
+    const int64_t C = h->lut.R * h->lut.b;
+    out[0] = h->lut.fa ? N : C;
+    out[1] = h->lut.fa ? C : N;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_o_shape(bsmm_handle h, int64_t N, int64_t out[2]) {
+    if (!h || !out || N < 0) return fail(BSMM_ERR_INVALID_ARG, "NULL argument or N < 0");
+    const int64_t K = h->lut.S * h->lut.b;
+    out[0] = h->lut.fa ? N : K;
+    out[1] = h->lut.fa ? K : N;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_block_coord(bsmm_handle h, int64_t block, int64_t* c, int64_t* k) {
+    if (!h || !c || !k) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    if (block < 0 || block >= h->lut.nnz) return fail(BSMM_ERR_INVALID_ARG, "block id out of range");
+    *c = h->lut.coords[2 * block];
+    *k = h->lut.coords[2 * block + 1];
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_plan_info(bsmm_handle h, int64_t out[5]) {
+    if (!h || !out) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    out[0] = h->lut.R;
+    out[1] = h->lut.S;
+    out[2] = h->lut.b;
+    out[3] = h->lut.fa;
+    out[4] = h->lut.nnz;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype dt, size_t* bytes) {
+    if (!h || !bytes) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    if (pass < BSMM_PASS_FPROP || pass > BSMM_PASS_IDENTITY) return fail(BSMM_ERR_INVALID_ARG, "bad pass");
+    if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    *bytes = 0;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int64_t N, bsmm_dtype dt,
+                       void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    bsmm_status s = run_mm(h, x, w, y, N, dt, false);
+    if (s != BSMM_OK || N == 0) return s;
+    const DeviceLut* d = nullptr;
+    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    const HostLut& L = h->lut;
+    MMArgs a{};
+    a.in = x;
+    a.w = w;
+    a.out = y;
+    a.ptr = d->colptr;
+    a.ent = d->colent;
+    a.order = d->colorder;
+    a.N = N;
+    a.fin = (int32_t)(L.R * L.b);
+    a.fout = (int32_t)(L.S * L.b);
+    a.nout = (int32_t)L.S;
+    hipError_t e = launch_mm(a, dt, L.b, L.fa, false, stream, BSMM_PASS_FPROP);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "fprop launch");
+}
+
+bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, int64_t N, bsmm_dtype dt,
+                       void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    bsmm_status s = run_mm(h, dy, w, dx, N, dt, true);
+    if (s != BSMM_OK || N == 0) return s;
+    const DeviceLut* d = nullptr;
+    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    const HostLut& L = h->lut;
+    MMArgs a{};
+    a.in = dy;
+    a.w = w;
+    a.out = dx;
+    a.ptr = d->rowptr;
+    a.ent = d->rowent;
+    a.order = d->roworder;
+    a.N = N;
+    a.fin = (int32_t)(L.S * L.b);
+    a.fout = (int32_t)(L.R * L.b);
+    a.nout = (int32_t)L.R;
+    hipError_t e = launch_mm(a, dt, L.b, L.fa, true, stream, BSMM_PASS_BPROP);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "bprop launch");
+}
+
+bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
+                       int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    bsmm_status s = check_call(h, N, dt);
+    if (s != BSMM_OK) return s;
+    if (!valid_dt(dw_dt)) return fail(BSMM_ERR_INVALID_ARG, "dw dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
+    if (group < 1 || group > kMaxGroup) return fail(BSMM_ERR_INVALID_ARG, "group must be in [1, 8]");
+    const HostLut& L = h->lut;
+    if (L.nnz == 0) return BSMM_OK;
+    if ((s = check_ptr(dw, "dw")) != BSMM_OK) return s;
+    if (N > 0) {
+        if (!xs || !dys) return fail(BSMM_ERR_INVALID_ARG, "xs / dys is NULL");
+        for (int t = 0; t < group; t++) {
+            if ((s = check_ptr(xs[t], "xs[t]")) != BSMM_OK) return s;
+            if ((s = check_ptr(dys[t], "dys[t]")) != BSMM_OK) return s;
+        }
+    }
+    const DeviceLut* d = nullptr;
+    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    UpArgs a{};
+    for (int t = 0; t < group; t++) {
+        a.xs[t] = N > 0 ? xs[t] : nullptr;
+        a.dys[t] = N > 0 ? dys[t] : nullptr;
+    }
+    a.dw = dw;
+    a.coords = d->coords;
+    a.N = N;
+    a.C = (int32_t)(L.R * L.b);
+    a.K = (int32_t)(L.S * L.b);
+    a.nnz = (int32_t)L.nnz;
+    a.G = N > 0 ? group : 1;
+    a.dwdt = dw_dt;
+    hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "updat launch");
+}
+
+bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    const HostLut& L = h->lut;
+    if (L.nnz == 0) return BSMM_OK;
+    bsmm_status s = check_ptr(w, "w");
+    if (s != BSMM_OK) return s;
+    const DeviceLut* d = nullptr;
+    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    hipError_t e = launch_identity(w, d->coords, L.nnz, L.b, dt, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "identity_init launch");
+}
+
+const char* bsmm_status_string(bsmm_status s) {
+    switch (s) {
+    case BSMM_OK: return "BSMM_OK";
+    case BSMM_ERR_INVALID_ARG: return "BSMM_ERR_INVALID_ARG";
+    case BSMM_ERR_UNSUPPORTED: return "BSMM_ERR_UNSUPPORTED";
+    case BSMM_ERR_ALIGNMENT: return "BSMM_ERR_ALIGNMENT";
+    case BSMM_ERR_DEVICE: return "BSMM_ERR_DEVICE";
+    case BSMM_ERR_OOM: return "BSMM_ERR_OOM";
+    }
+    return "unknown bsmm_status";
+}
+
+const char* bsmm_last_error(void) { return g_err.c_str(); }
+
+bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len) {
+    if (!h || !len || cap < 0 || (cap > 0 && !out)) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
+    const HostLut& L = h->lut;
+    const std::vector<int32_t>* v = nullptr;
+    switch (which) {
+    case 0: v = &L.coords; break;
+    case 1: v = &L.colptr; break;
+    case 2: v = &L.colent; break;
+    case 3: v = &L.rowptr; break;
+    case 4: v = &L.rowent; break;
+    case 5: v = &L.colorder; break;
+    case 6: v = &L.roworder; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 6]");
+    }
+    *len = (int64_t)v->size();
+    const int64_t n = cap < *len ? cap : *len;
+    for (int64_t i = 0; i < n; i++) out[i] = (*v)[i];
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_profile_begin(void) {
+    g_prof.on = true;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_profile_end(double ms[4], int64_t count[4]) {
+    if (!g_prof.on) return fail(BSMM_ERR_INVALID_ARG, "profiling was not begun on this thread");
+    g_prof.on = false;
+    if (ms)
+        for (int i = 0; i < 4; i++) ms[i] = 0.0;
+    if (count)
+        for (int i = 0; i < 4; i++) count[i] = 0;
+    bsmm_status st = BSMM_OK;
+    for (auto& r : g_prof.recs) {
+        hipError_t e = hipEventSynchronize(r.e1);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.e0, r.e1);
+        if (e != hipSuccess && st == BSMM_OK) st = dev_fail(e, "profile event");
+        if (r.pass >= 0 && r.pass < 4) {
+            if (ms) ms[r.pass] += t;
+            if (count) count[r.pass] += 1;
+        }
+        g_prof.pool.push_back(r.e0);
+        g_prof.pool.push_back(r.e1);
+    }
+    g_prof.recs.clear();
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host-side layout compiler, the C ABI and the
+// kernel launchers of libbsmm.  Not installed; the public interface is include/bsmm.h.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "bsmm.h"
+
+namespace bsmm {
+
+// Host look-up tables compiled from a 0/1 block layout.
+//
+// Block ids number the layout's nonzeros in row-major order (the reading of
+// BlocksparseMatMul.w_shape / block_coord in the kiteco/blocksparse README, "API
+// Documentation" › blocksparse.matmul).  Every table below is derived from that
+// numbering:
+//   coords   (c, k) of each id, id order.
+//   colptr / colent   fprop lists: for output block k, entries (c, id) with L[c][k]=1,
+//                     ascending c.  colptr has S+1 offsets into colent (pairs).
+//   rowptr / rowent   bprop lists: for input block c, entries (k, id), ascending k.
+//   colorder / roworder  list indices by descending length (ties: ascending index);
+//                     kernels hand the longest lists out first for load balance.
+struct HostLut {
+    int64_t R = 0, S = 0, nnz = 0;
+    int b = 0, fa = 1;
+    std::vector<int32_t> coords;
+    std::vector<int32_t> colptr, colent;
+    std::vector<int32_t> rowptr, rowent;
+    std::vector<int32_t> colorder, roworder;
+    int32_t max_col = 0, max_row = 0;   // longest fprop / bprop list
+};
+
+// Builds every table above.  Pure host code: never touches HIP.  Returns false with a
+// message on invalid input (checked before anything is built).
+bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, HostLut& out,
+                    std::string& err);
+
+// Device copy of the tables: one allocation, the arrays laid out back to back.
+struct DeviceLut {
+    void* base = nullptr;
+    const int32_t* coords = nullptr;   // int2 per id
+    const int32_t* colptr = nullptr;
+    const int32_t* colent = nullptr;   // int2 per entry
+    const int32_t* rowptr = nullptr;
+    const int32_t* rowent = nullptr;
+    const int32_t* colorder = nullptr;
+    const int32_t* roworder = nullptr;
+};
+
+}  // namespace bsmm
+
+struct bsmm_plan {
+    bsmm::HostLut lut;
+    std::mutex mu;
+    std::map<int, bsmm::DeviceLut> dev;   // per HIP device ordinal
+};

@@ -1,0 +1,46 @@
+// Kernel argument blocks and host launchers (implemented in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace bsmm {
+
+// fprop / bprop: out[:, o-block] = sum over list(o) of in[:, blk-block] . Wop.
+struct MMArgs {
+    const void* in;        // x (fprop) or dy (bprop), storage dtype
+    const void* w;         // (nnz, b, b)
+    void* out;             // y (fprop) or dx (bprop)
+    const int32_t* ptr;    // nout+1 list offsets
+    const int32_t* ent;    // (blk, id) pairs
+    const int32_t* order;  // nout list indices, longest first
+    int64_t N;             // minibatch
+    int32_t fin, fout;     // feature counts of in and out
+    int32_t nout;          // number of lists (output blocks)
+    int32_t ntiles;        // minibatch tiles (set by the launcher)
+};
+
+constexpr int kMaxGroup = 8;
+
+struct UpArgs {
+    const void* xs[kMaxGroup];
+    const void* dys[kMaxGroup];
+    void* dw;
+    const int32_t* coords;  // (c, k) per id
+    int64_t N;
+    int32_t C, K;
+    int32_t nnz;
+    int32_t G;
+    int32_t dwdt;
+};
+
+hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);
+hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream);
+hipError_t launch_identity(void* w, const int32_t* coords, int64_t nnz, int b, int dt, void* stream);
+
+// Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
+// pair of HIP events to record around the next launch of `pass`; else sets both NULL.
+void prof_events(int pass, void** start, void** stop);
+
+}  // namespace bsmm

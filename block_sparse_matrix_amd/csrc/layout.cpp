@@ -1,0 +1,85 @@
+// Host-side layout compiler: turns a 0/1 block layout into the look-up tables the
+// kernels walk.  Pure C++ (no HIP calls), so it runs and is tested without a GPU.
+//
+// Layout semantics follow the kiteco/blocksparse README, "API Documentation" ›
+// blocksparse.matmul › BlocksparseMatMul: __init__ takes an R x S array of zeros and
+// ones and a block size of 8, 16 or 32; block_coord maps a block id to (c, k).  Ids
+// are the row-major rank of a nonzero.
+#include <algorithm>
+#include <numeric>
+
+#include "bsmm_internal.h"
+
+namespace bsmm {
+
+static std::vector<int32_t> order_by_length(const std::vector<int32_t>& ptr) {
+    const int32_t n = (int32_t)ptr.size() - 1;
+    std::vector<int32_t> ord(n);
+    std::iota(ord.begin(), ord.end(), 0);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+        return (ptr[a + 1] - ptr[a]) > (ptr[b + 1] - ptr[b]);
+    });
+    return ord;
+}
+
+bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, HostLut& out,
+                    std::string& err) {
+    if (!layout) { err = "layout is NULL"; return false; }
+    if (R < 1 || S < 1) { err = "layout must have at least one row and one column"; return false; }
+    if (b != 8 && b != 16 && b != 32) { err = "block_size must be 8, 16 or 32"; return false; }
+    if (fa != 0 && fa != 1) { err = "feature_axis must be 0 or 1"; return false; }
+    if (R * (int64_t)b > INT32_MAX || S * (int64_t)b > INT32_MAX) {
+        err = "feature dimension exceeds 2^31-1"; return false;
+    }
+    if (R * S > (int64_t)1 << 40) { err = "layout too large"; return false; }
+    int64_t nnz = 0;
+    for (int64_t t = 0; t < R * S; t++) {
+        if (layout[t] > 1) { err = "layout entries must be 0 or 1"; return false; }
+        nnz += layout[t];
+    }
+    if (nnz * (int64_t)b * b > INT32_MAX * (int64_t)64) { err = "too many blocks"; return false; }
+    if (nnz > INT32_MAX / 2) { err = "too many blocks"; return false; }
+
+    HostLut L;
+    L.R = R; L.S = S; L.b = b; L.fa = fa; L.nnz = nnz;
+    L.coords.resize(2 * nnz);
+    L.colptr.assign(S + 1, 0);
+    L.rowptr.assign(R + 1, 0);
+    // ids: row-major scan; count per column and row on the way
+    int32_t id = 0;
+    for (int64_t c = 0; c < R; c++)
+        for (int64_t k = 0; k < S; k++)
+            if (layout[c * S + k]) {
+                L.coords[2 * id] = (int32_t)c;
+                L.coords[2 * id + 1] = (int32_t)k;
+                L.colptr[k + 1]++;
+                L.rowptr[c + 1]++;
+                id++;
+            }
+    std::partial_sum(L.colptr.begin(), L.colptr.end(), L.colptr.begin());
+    std::partial_sum(L.rowptr.begin(), L.rowptr.end(), L.rowptr.begin());
+    // fprop lists (c ascending within each column) and bprop lists (k ascending within
+    // each row): a single pass in id order visits c ascending and, within a row, k
+    // ascending, so a counting sort keeps both orders.
+    L.colent.resize(2 * nnz);
+    L.rowent.resize(2 * nnz);
+    std::vector<int32_t> cfill(L.colptr.begin(), L.colptr.end() - 1);
+    std::vector<int32_t> rfill(L.rowptr.begin(), L.rowptr.end() - 1);
+    for (int32_t t = 0; t < (int32_t)nnz; t++) {
+        int32_t c = L.coords[2 * t], k = L.coords[2 * t + 1];
+        int32_t pc = cfill[k]++;
+        L.colent[2 * pc] = c;
+        L.colent[2 * pc + 1] = t;
+        int32_t pr = rfill[c]++;
+        L.rowent[2 * pr] = k;
+        L.rowent[2 * pr + 1] = t;
+    }
+    L.colorder = order_by_length(L.colptr);
+    L.roworder = order_by_length(L.rowptr);
+    for (int64_t k = 0; k < S; k++) L.max_col = std::max(L.max_col, L.colptr[k + 1] - L.colptr[k]);
+    for (int64_t c = 0; c < R; c++) L.max_row = std::max(L.max_row, L.rowptr[c + 1] - L.rowptr[c]);
+    out = std::move(L);
+    return true;
+}
+
+}  // namespace bsmm

@@ -1,0 +1,172 @@
+/*
+ * bsmm.h -- C ABI of libbsmm, a block-sparse matrix multiply for AMD MI355X (gfx950).
+ *
+ * The operation is the one the kiteco/blocksparse README documents under
+ * "API Documentation" › blocksparse.matmul › class BlocksparseMatMul:
+ *
+ *   layout  an R x S array of zeros and ones (BlocksparseMatMul.__init__, argument
+ *           "layout").  Row c indexes the b-wide input feature blocks, column k the
+ *           b-wide output feature blocks, so C = R*b inputs and K = S*b outputs.
+ *   b       the block size, 8, 16 or 32 (__init__, argument "block_size").
+ *   W       the weight, holding only the present blocks: shape (nnz, b, b)
+ *           (w_shape), block id t being the t-th nonzero of the layout in row-major
+ *           order (the (c,k) pair of an id is what block_coord returns).  Within a
+ *           block, W[t][i][j] couples input feature c*b+i to output feature k*b+j.
+ *   feature_axis  1: activations are (N, features), row-major; 0: (features, N)
+ *           (__init__, argument "feature_axis"; N is the minibatch, as in the shape
+ *           helpers i_shape(N) / o_shape(N)).
+ *
+ *   fprop   y  = x . W~        (BlocksparseMatMul.__call__)
+ *   bprop   dx = dy . W~^T     (the gradient of __call__ with respect to its input)
+ *   updat   dW[id(c,k)] = sum_t x_t[:, c-block]^T . dy_t[:, k-block], for present blocks
+ *           only (the weight gradient, with dw_dtype; the sum over up to 8 steps that
+ *           share W is what group_param_grads forms)
+ *   identity_init  W[id(c,k)] = I_b when c == k, else 0 (identity_init with gpu=True)
+ *
+ * where W~ is the C x K matrix that is W's blocks on the present (c,k) and zero
+ * elsewhere.  With feature_axis = 0 every activation is stored transposed; W's
+ * storage does not change.
+ *
+ * Conventions for every call below:
+ *   - Status codes are returned, never thrown; nothing aborts the process.  The
+ *     text of the last failure on the calling thread is bsmm_last_error().
+ *   - Device pointers are plain HIP device addresses (e.g. torch's data_ptr()).
+ *     The caller owns every device buffer.  Each must be 16-byte aligned and
+ *     dense in the layout stated; otherwise BSMM_ERR_ALIGNMENT / the result is
+ *     undefined.
+ *   - x, W, dy and their results share one storage dtype (BSMM_F32, BSMM_BF16,
+ *     BSMM_F16).  Products accumulate in fp32; results are rounded to the storage
+ *     dtype with round-to-nearest-even.
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  Kernels are
+ *     enqueued asynchronously; no call synchronizes the device.
+ *   - N = 0: fprop and bprop do nothing and return BSMM_OK; updat writes dW = 0 (the
+ *     empty sum).  Activation pointers may be NULL only when N = 0.
+ *   - A handle is immutable after bsmm_create; it may be used from several host
+ *     threads and streams at once.  Its look-up tables are copied to a device
+ *     the first time a kernel call runs on that device.
+ */
+#ifndef BSMM_H
+#define BSMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define BSMM_API __attribute__((visibility("default")))
+#else
+#define BSMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSMM_OK = 0,
+    BSMM_ERR_INVALID_ARG = 1,   /* a size, enum or pointer argument is out of range */
+    BSMM_ERR_UNSUPPORTED = 2,   /* a valid request this library does not implement */
+    BSMM_ERR_ALIGNMENT = 3,     /* a device pointer is not 16-byte aligned */
+    BSMM_ERR_DEVICE = 4,        /* a HIP runtime call failed */
+    BSMM_ERR_OOM = 5            /* host or device allocation failed */
+} bsmm_status;
+
+typedef enum { BSMM_F32 = 0, BSMM_BF16 = 1, BSMM_F16 = 2 } bsmm_dtype;
+
+typedef enum { BSMM_PASS_FPROP = 0, BSMM_PASS_BPROP = 1, BSMM_PASS_UPDAT = 2, BSMM_PASS_IDENTITY = 3 } bsmm_pass;
+
+typedef struct bsmm_plan* bsmm_handle;
+
+/* Compile a layout into a handle (BlocksparseMatMul.__init__).
+ *   layout        host array of R*S bytes, row-major, each 0 or 1; read during the call only.
+ *   R, S          layout rows (input blocks) and columns (output blocks), each >= 1.
+ *   block_size    8, 16 or 32.
+ *   feature_axis  0 or 1.
+ * An all-zero layout is valid (nnz = 0: outputs are zero).  Does not touch the GPU.
+ * Errors: BSMM_ERR_INVALID_ARG for a NULL out/layout, R or S < 1, R*b or S*b above
+ * 2^31-1, a block size outside {8,16,32}, feature_axis outside {0,1} or a layout
+ * byte outside {0,1}; BSMM_ERR_OOM.  *out is set to NULL on failure. */
+BSMM_API bsmm_status bsmm_create(bsmm_handle* out, const uint8_t* layout, int64_t R, int64_t S,
+                        int block_size, int feature_axis);
+
+/* Release a handle and its device tables.  NULL is ignored.  The caller must ensure
+ * no kernel that uses the handle is still queued. */
+BSMM_API void bsmm_destroy(bsmm_handle h);
+
+/* w_shape: out = {nnz, b, b}. */
+BSMM_API bsmm_status bsmm_w_shape(bsmm_handle h, int64_t out[3]);
+/* i_shape(N): {N, C} for feature_axis 1, {C, N} for 0.  N >= 0. */
+BSMM_API bsmm_status bsmm_i_shape(bsmm_handle h, int64_t N, int64_t out[2]);
+/* o_shape(N): {N, K} for feature_axis 1, {K, N} for 0.  N >= 0. */
+BSMM_API bsmm_status bsmm_o_shape(bsmm_handle h, int64_t N, int64_t out[2]);
+/* block_coord: the layout coordinates (c, k) of block id `block` (0 <= block < nnz). */
+BSMM_API bsmm_status bsmm_block_coord(bsmm_handle h, int64_t block, int64_t* c, int64_t* k);
+/* Layout description: out = {R, S, b, feature_axis, nnz}. */
+BSMM_API bsmm_status bsmm_plan_info(bsmm_handle h, int64_t out[5]);
+
+/* Bytes of device workspace a pass needs for minibatch N and dtype (0 today for every
+ * pass; the ws arguments below exist so that later kernels may use one).
+ * pass is a bsmm_pass value. */
+BSMM_API bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype dt, size_t* bytes);
+
+/* fprop: y = x . W~.
+ *   x  device, i_shape(N), dtype dt.    w  device, (nnz, b, b), dtype dt.
+ *   y  device, o_shape(N), dtype dt; fully overwritten (columns of output blocks with
+ *      no present block are written as zero).
+ *   ws, ws_bytes  device workspace of at least bsmm_workspace_size bytes (may be NULL
+ *      when that size is 0).
+ * x and y must not overlap. */
+BSMM_API bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int64_t N,
+                       bsmm_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* bprop: dx = dy . W~^T.
+ *   dy device, o_shape(N); w device, (nnz, b, b); dx device, i_shape(N), fully
+ *   overwritten.  All of dtype dt.  dy and dx must not overlap. */
+BSMM_API bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, int64_t N,
+                       bsmm_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* updat: dW[id] = sum over t < group of x_t[:, c-block]^T . dy_t[:, k-block], id = id(c,k).
+ *   xs, dys  host arrays of `group` device pointers (1 <= group <= 8), each x_t of
+ *            i_shape(N) and dy_t of o_shape(N), dtype dt; the host arrays are read
+ *            during the call only.
+ *   dw       device, (nnz, b, b), dtype dw_dt (BSMM_F32 is the default of the pages'
+ *            dw_dtype; BSMM_BF16 / BSMM_F16 round the fp32 sum with RNE).  Overwritten,
+ *            not accumulated into. */
+BSMM_API bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* dys, int group,
+                       void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* identity_init on the device: w (device, (nnz, b, b), dtype dt) is overwritten with
+ * I_b for every present diagonal block (c == k) and zero for the other blocks. */
+BSMM_API bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream);
+
+/* Static text for a status code. */
+BSMM_API const char* bsmm_status_string(bsmm_status s);
+/* Text of the last error raised on the calling thread ("" if none). */
+BSMM_API const char* bsmm_last_error(void);
+
+/* Layout compiler output, for inspection and tests (host only, no GPU needed).
+ *   which: 0 coords   (2*nnz:   c, k of every id, in id order)
+ *          1 colptr   (S+1:     fprop segment starts, one per output block k)
+ *          2 colent   (2*nnz:   fprop entries (c, id), ascending c within each k)
+ *          3 rowptr   (R+1:     bprop segment starts, one per input block c)
+ *          4 rowent   (2*nnz:   bprop entries (k, id), ascending k within each c)
+ *          5 colorder (S:       output blocks by descending entry count, ties ascending)
+ *          6 roworder (R:       input blocks by descending entry count, ties ascending)
+ * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
+ * length into *len. */
+BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);
+
+/* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
+ * every pass launched from the calling thread records HIP events around its kernels
+ * (hipExtLaunchKernelGGL start/stop events, i.e. the dispatch's own timestamps).
+ * bsmm_profile_end waits for those events and writes, per bsmm_pass index 0..3, the
+ * summed milliseconds and the number of passes recorded (arrays of 4).  Errors:
+ * BSMM_ERR_INVALID_ARG when not begun; BSMM_ERR_DEVICE. */
+BSMM_API bsmm_status bsmm_profile_begin(void);
+BSMM_API bsmm_status bsmm_profile_end(double ms[4], int64_t count[4]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSMM_H */

@@ -1,0 +1,132 @@
+"""libbsmm.so on the CPU: it loads, exports every declared symbol, and validates
+its arguments before any HIP call (so every error path runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_matrix_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, ALIGN = 1, 2, 3
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"BSMM_API\s+[\w\s\*]+?\b(bsmm_\w+)\s*\(", text))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert {"bsmm_create", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_identity_init"} <= names
+    L = bs.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+
+
+def _create(layout, b=8, fa=1):
+    L = np.ascontiguousarray(layout, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    st = bs.lib().bsmm_create(ctypes.byref(h), L.ctypes.data_as(ctypes.c_void_p), L.shape[0], L.shape[1], b, fa)
+    return st, h
+
+
+@pytest.mark.parametrize("layout,b,fa", [
+    (np.ones((2, 2)), 4, 1), (np.ones((2, 2)), 64, 1), (np.ones((2, 2)), 8, 2), (np.ones((2, 2)), 8, -1),
+    (np.array([[0, 2], [1, 1]]), 8, 1),
+])
+def test_create_rejects(layout, b, fa):
+    st, h = _create(layout, b, fa)
+    assert st == INVALID and not h.value
+    assert bs.lib().bsmm_last_error().decode()
+
+
+def test_create_rejects_null_and_empty():
+    h = ctypes.c_void_p()
+    assert bs.lib().bsmm_create(ctypes.byref(h), None, 2, 2, 8, 1) == INVALID
+    z = np.zeros(1, dtype=np.uint8)
+    assert bs.lib().bsmm_create(ctypes.byref(h), z.ctypes.data_as(ctypes.c_void_p), 0, 1, 8, 1) == INVALID
+    assert bs.lib().bsmm_create(None, z.ctypes.data_as(ctypes.c_void_p), 1, 1, 8, 1) == INVALID
+
+
+def test_all_zero_layout_is_valid():
+    m = bs.BlocksparseMatMul(np.zeros((3, 2)), block_size=16, feature_axis=0)
+    assert m.w_shape == (0, 16, 16)
+    assert m.i_shape(5) == (48, 5) and m.o_shape(5) == (32, 5)
+    with pytest.raises(bs.BsmmError):
+        m.block_coord(0)
+
+
+def test_shapes_and_block_coord():
+    rng = np.random.default_rng(0)
+    L = (rng.random((5, 7)) < 0.4).astype(np.uint8)
+    for fa in (0, 1):
+        m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
+        assert m.w_shape == (int(L.sum()), 32, 32)
+        assert m.i_shape(3) == ((3, 160) if fa else (160, 3))
+        assert m.o_shape(3) == ((3, 224) if fa else (224, 3))
+        for t, (c, k) in enumerate(zip(*np.nonzero(L))):
+            assert m.block_coord(t) == (c, k)
+    with pytest.raises(bs.BsmmError):
+        m.block_coord(int(L.sum()))
+    with pytest.raises(bs.BsmmError):
+        m.block_coord(-1)
+
+
+def test_call_validation_before_gpu():
+    L = bs.lib()
+    st, h = _create(np.ones((2, 3)), 8, 1)
+    assert st == 0
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+    odd = vp(0x10008)
+    try:
+        # bad dtype, negative N, NULL pointers, misalignment
+        assert L.bsmm_fprop(h, good, good, good, 4, 7, None, 0, None) == INVALID
+        assert L.bsmm_fprop(h, good, good, good, -1, 0, None, 0, None) == INVALID
+        assert L.bsmm_fprop(h, None, good, good, 4, 0, None, 0, None) == INVALID
+        assert L.bsmm_fprop(h, good, None, good, 4, 0, None, 0, None) == INVALID
+        assert L.bsmm_bprop(h, good, good, None, 4, 1, None, 0, None) == INVALID
+        assert L.bsmm_fprop(h, odd, good, good, 4, 0, None, 0, None) == ALIGN
+        assert L.bsmm_bprop(h, good, odd, good, 4, 2, None, 0, None) == ALIGN
+        assert L.bsmm_fprop(None, good, good, good, 4, 0, None, 0, None) == INVALID
+        assert L.bsmm_fprop(h, good, good, good, 1 << 40, 0, None, 0, None) == UNSUPPORTED
+        # N = 0 is a no-op for fprop / bprop, even with NULL pointers
+        assert L.bsmm_fprop(h, None, None, None, 0, 0, None, 0, None) == 0
+        assert L.bsmm_bprop(h, None, None, None, 0, 1, None, 0, None) == 0
+        arr = (vp * 8)(*([0x10000] * 8))
+        assert L.bsmm_updat(h, arr, arr, 0, good, 4, 0, 0, None, 0, None) == INVALID
+        assert L.bsmm_updat(h, arr, arr, 9, good, 4, 0, 0, None, 0, None) == INVALID
+        assert L.bsmm_updat(h, arr, arr, 1, good, 4, 0, 5, None, 0, None) == INVALID
+        assert L.bsmm_updat(h, arr, arr, 1, None, 4, 0, 0, None, 0, None) == INVALID
+        assert L.bsmm_updat(h, None, arr, 1, good, 4, 0, 0, None, 0, None) == INVALID
+        bad = (vp * 2)(0x10000, 0x10004)
+        assert L.bsmm_updat(h, bad, bad, 2, good, 4, 0, 0, None, 0, None) == ALIGN
+        assert L.bsmm_identity_init(h, None, 0, None) == INVALID
+        assert L.bsmm_identity_init(h, odd, 0, None) == ALIGN
+        assert L.bsmm_identity_init(h, good, 9, None) == INVALID
+        sz = ctypes.c_size_t(123)
+        assert L.bsmm_workspace_size(h, 0, 64, 0, ctypes.byref(sz)) == 0 and sz.value == 0
+        assert L.bsmm_workspace_size(h, 9, 64, 0, ctypes.byref(sz)) == INVALID
+        assert L.bsmm_last_error().decode()
+        for s in range(6):
+            assert L.bsmm_status_string(s).decode().startswith("BSMM_")
+        assert L.bsmm_profile_end(None, None) == INVALID
+    finally:
+        L.bsmm_destroy(h)
+    L.bsmm_destroy(None)
+
+
+def test_no_cpu_path():
+    import torch
+    m = bs.BlocksparseMatMul(np.ones((1, 1)), block_size=8)
+    x = torch.zeros(2, 8)
+    w = torch.zeros(1, 8, 8)
+    with pytest.raises(ValueError):
+        m.fprop(x, w)

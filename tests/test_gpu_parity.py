@@ -1,0 +1,182 @@
+"""HIP path against the CPU oracle, element by element (GPU; calls through the C ABI).
+
+Small random problems cover every (block size, feature_axis, dtype, pass) at sizes
+that span several tiles and end in a ragged minibatch tail; special cases cover
+identity_init (bit-exact), empty rows/columns, an all-zero layout, all-ones = dense,
+determinism, grouped weight gradients and low-precision dW."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_matrix_amd as bs
+import oracle
+import synth
+from gpu_util import TOL, TORCH_DT, assert_close, dev, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _prob(seed, R, S, b, N, fa, dtype, G=1, density=0.45):
+    rng = np.random.default_rng(seed)
+    L = (rng.random((R, S)) < density).astype(np.uint8)
+    L[0, :] = 0          # an empty input block row -> dx zero there
+    L[:, S - 1] = 0      # an empty output block column -> y zero there
+    L[1, 0] = 1
+    return synth.random_problem(rng, L, b, N, fa, dtype, G=G, w_std=0.1)
+
+
+def _run_all(P, dtype):
+    m = bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
+    w = dev(P.w)
+    xs = [dev(t) for t in P.xs]
+    dys = [dev(t) for t in P.dys]
+    y = m.fprop(xs[0], w)
+    dx = m.bprop(dys[0], w)
+    dw = m.updat(xs, dys)
+    torch.cuda.synchronize()
+    return y, dx, dw
+
+
+def _oracle_all(P, dtype):
+    bits = synth.to_bits
+    y = oracle.fprop(P.layout, P.block, P.fa, bits(P.xs[0]), bits(P.w), P.N, dtype)
+    dx = oracle.bprop(P.layout, P.block, P.fa, bits(P.dys[0]), bits(P.w), P.N, dtype)
+    dw = oracle.updat(P.layout, P.block, P.fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], P.N, dtype)
+    return y, dx, dw
+
+
+@pytest.mark.parametrize("N", [37, 200])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fa", [1, 0])
+@pytest.mark.parametrize("b", [32, 16, 8])
+def test_matrix(b, fa, dtype, N):
+    print(f"case b={b} fa={fa} dtype={dtype} N={N}", flush=True)
+    P = _prob(1000 * b + 10 * fa + N, 5, 7, b, N, fa, dtype)
+    y, dx, dw = _run_all(P, dtype)
+    ry, rdx, rdw = _oracle_all(P, dtype)
+    assert_close(y, ry, dtype, "fprop")
+    assert_close(dx, rdx, dtype, "bprop")
+    # dW is fp32: its only rounding is fp32 accumulation of exactly decoded products
+    assert_close(dw, rdw, "f32" if dtype == "f32" else dtype, "updat")
+    # structural zeros: empty column of the layout and empty row
+    Kb = P.block
+    ycols = y[:, -Kb:] if fa == 1 else y[-Kb:, :]
+    dxrows = dx[:, :Kb] if fa == 1 else dx[:Kb, :]
+    assert torch.count_nonzero(ycols) == 0 and torch.count_nonzero(dxrows) == 0
+
+
+@pytest.mark.parametrize("N", [1, 3, 63, 64, 65, 129])
+def test_ragged_minibatch(N):
+    for b, fa, dtype in [(32, 1, "bf16"), (16, 0, "f16"), (8, 0, "bf16"), (8, 1, "f32")]:
+        print(f"case N={N} b={b} fa={fa} dtype={dtype}", flush=True)
+        P = _prob(N * 7 + b, 4, 3, b, N, fa, dtype, G=2)
+        y, dx, dw = _run_all(P, dtype)
+        ry, rdx, rdw = _oracle_all(P, dtype)
+        assert_close(y, ry, dtype, "fprop")
+        assert_close(dx, rdx, dtype, "bprop")
+        assert_close(dw, rdw, dtype, "updat")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fa", [1, 0])
+@pytest.mark.parametrize("b", [32, 16, 8])
+def test_identity_init_bit_exact(b, fa, dtype):
+    print(f"case identity b={b} fa={fa} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(b + fa)
+    R = 6
+    L = ((rng.random((R, R)) < 0.4) | np.eye(R, dtype=bool)).astype(np.uint8)
+    m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=fa)
+    w = m.identity_init(gpu=True, dtype=TORCH_DT[dtype])
+    ref = oracle.identity(L, b)
+    assert np.array_equal(w.float().cpu().numpy(), ref.astype(np.float32))
+    host = m.identity_init(gpu=False)
+    assert np.array_equal(host, ref.astype(np.float32))
+    N = 77
+    x = dev(torch.randn(m.i_shape(N), generator=torch.Generator().manual_seed(1)).to(TORCH_DT[dtype]))
+    y = m.fprop(x, w)
+    dx = m.bprop(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x) and torch.equal(dx, x)
+
+
+def test_identity_partial_diagonal():
+    L = np.array([[1, 1, 0], [0, 0, 1], [1, 0, 1]], dtype=np.uint8)   # (1,1) absent
+    m = bs.BlocksparseMatMul(L, block_size=16, feature_axis=1)
+    w = m.identity_init(gpu=True, dtype=torch.bfloat16)
+    x = dev(torch.randn(20, 48).to(torch.bfloat16))
+    y = m.fprop(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :16], x[:, :16]) and torch.equal(y[:, 32:], x[:, 32:])
+    assert torch.count_nonzero(y[:, 16:32]) == 0
+
+
+@pytest.mark.parametrize("fa", [1, 0])
+def test_all_zero_layout(fa):
+    m = bs.BlocksparseMatMul(np.zeros((2, 3)), block_size=8, feature_axis=fa)
+    x = dev(torch.randn(m.i_shape(10)))
+    dy = dev(torch.randn(m.o_shape(10)))
+    w = torch.empty(m.w_shape, device="cuda")
+    y = torch.full(m.o_shape(10), 7.0, device="cuda")
+    dx = torch.full(m.i_shape(10), 7.0, device="cuda")
+    bs.bsmm_fprop(m.handle, x, w, y, 10)
+    bs.bsmm_bprop(m.handle, dy, w, dx, 10)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0 and torch.count_nonzero(dx) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_ones_layout_is_dense(dtype):
+    R, S, b, N = 4, 3, 32, 96
+    rng = np.random.default_rng(5)
+    P = synth.random_problem(rng, np.ones((R, S), np.uint8), b, N, 1, dtype, w_std=0.1)
+    y, dx, dw = _run_all(P, dtype)
+    Wd = P.w.double().reshape(R, S, b, b).permute(0, 2, 1, 3).reshape(R * b, S * b)
+    X, DY = P.xs[0].double(), P.dys[0].double()
+    assert_close(y, (X @ Wd).numpy(), dtype, "fprop")
+    assert_close(dx, (DY @ Wd.T).numpy(), dtype, "bprop")
+    full = (X.T @ DY).reshape(R, b, S, b).permute(0, 2, 1, 3).reshape(R * S, b, b)
+    assert_close(dw, full.numpy(), dtype, "updat")
+
+
+def test_deterministic():
+    for b, fa, dtype in [(32, 1, "bf16"), (16, 0, "f16"), (8, 0, "f32")]:
+        P = _prob(77 + b, 6, 6, b, 130, fa, dtype, G=3)
+        a = _run_all(P, dtype)
+        c = _run_all(P, dtype)
+        for u, v in zip(a, c):
+            iv = torch.int32 if u.dtype == torch.float32 else torch.int16
+            assert torch.equal(u.view(iv), v.view(iv))
+
+
+@pytest.mark.parametrize("G", [1, 2, 5, 8])
+def test_grouped_updat(G):
+    for b, fa, dtype in [(32, 1, "bf16"), (16, 0, "f16"), (8, 1, "f32")]:
+        P = _prob(G * 31 + b, 3, 4, b, 40, fa, dtype, G=G)
+        m = bs.BlocksparseMatMul(P.layout, block_size=b, feature_axis=fa)
+        dw = bs.group_param_grads(m, [dev(t) for t in P.xs], [dev(t) for t in P.dys])
+        ref = oracle.updat(P.layout, b, fa, [synth.to_bits(t) for t in P.xs],
+                           [synth.to_bits(t) for t in P.dys], P.N, dtype)
+        assert_close(dw, ref, dtype, f"grouped G={G}")
+
+
+@pytest.mark.parametrize("dw_dtype", ["bf16", "f16"])
+def test_low_precision_dw(dw_dtype):
+    P = _prob(3, 3, 3, 16, 50, 1, "bf16")
+    m = bs.BlocksparseMatMul(P.layout, block_size=16, feature_axis=1)
+    dw = m.updat([dev(P.xs[0])], [dev(P.dys[0])], dw_dtype=TORCH_DT[dw_dtype])
+    assert dw.dtype == TORCH_DT[dw_dtype]
+    ref = oracle.updat(P.layout, 16, 1, [synth.to_bits(P.xs[0])], [synth.to_bits(P.dys[0])], 50, "bf16")
+    assert_close(dw, ref, dw_dtype, "dW low precision")
+
+
+def test_autograd():
+    P = _prob(11, 4, 4, 32, 70, 1, "f32")
+    m = bs.BlocksparseMatMul(P.layout, block_size=32, feature_axis=1)
+    x = dev(P.xs[0]).requires_grad_()
+    w = dev(P.w).requires_grad_()
+    y = m(x, w)
+    y.backward(dev(P.dys[0]))
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    assert_close(x.grad, oracle.bprop(P.layout, 32, 1, bits(P.dys[0]), bits(P.w), 70), "f32", "dx")
+    assert_close(w.grad, oracle.updat(P.layout, 32, 1, [bits(P.xs[0])], [bits(P.dys[0])], 70), "f32", "dw")
