@@ -79,6 +79,18 @@ def roof(flops, nbytes, dtype):
     return ("mfma", t_mfma) if t_mfma >= t_hbm else ("hbm", t_hbm)
 
 
+def kernel_sources_sha256():
+    """Hash of the device sources (csrc/*.hip, csrc/*.h), to tell whether a stored
+    counter reading still describes the kernels that run."""
+    d = os.path.join(ROOT, "block_sparse_matrix_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(d)):
+        if fn.endswith((".hip", ".h")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(d, fn), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(kernel_key, workload, dtype):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if its kernel
     source still matches; else None."""
@@ -90,8 +102,7 @@ def traffic_record(kernel_key, workload, dtype):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = open(os.path.join(ROOT, "block_sparse_matrix_amd", "csrc", "kernels.hip"), "rb").read()
-    if kv.get("kernels_hip_sha256") != hashlib.sha256(src).hexdigest():
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

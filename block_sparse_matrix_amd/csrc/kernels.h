@@ -33,6 +33,7 @@ struct UpArgs {
     int32_t nnz;
     int32_t G;
     int32_t dwdt;
+    int32_t bpw;            // blocks per wave (set by the launcher)
 };
 
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);

@@ -1,0 +1,364 @@
+// fprop and bprop of the block-sparse product on gfx950.
+//
+//   fprop  y[:, k-block]  = sum over c with L[c][k]=1 of x[:, c-block]  . W[id(c,k)]
+//   bprop  dx[:, c-block] = sum over k with L[c][k]=1 of dy[:, k-block] . W[id(c,k)]^T
+// (kiteco/blocksparse README, "API Documentation" › blocksparse.matmul ›
+// BlocksparseMatMul.__call__ and its input gradient.)
+//
+// One kernel serves both: an output block o owns a list of entries (in-block, id)
+// (the layout column for fprop, the row for bprop); out[:, o] = sum over the list of
+// in[:, blk] . Wop with Wop[p][q] = W[id][p][q] (fprop) or W[id][q][p] (bprop).
+//
+// A workgroup (4 waves) computes an NT x b tile of one output block.  Waves split the
+// NT minibatch rows (WM) and/or the list (WK); WK partial tiles are added in wave
+// order through LDS, so results are bit-reproducible.  The contraction runs in steps
+// of 32 (16-bit) or 16 (fp32) values, i.e. 32/b entries per step for b < 32.  Each
+// wave keeps D steps of global loads in flight in a register ring.
+//
+// Operands reach the matrix cores in one of three ways:
+//   direct   the contraction index is contiguous in memory (activations with
+//            feature_axis 1, the weight in bprop): one 16-byte load per fragment.
+//   tr       the contraction index is the slow one (activations with feature_axis 0,
+//            the weight in fprop), 16-bit types: rows are loaded with 16-byte loads,
+//            stored to a wave-private LDS tile and read back with the transposing
+//            LDS read (frag_tr16).
+//   strided  the same case for fp32: four 4-byte loads per fragment (16 lanes read
+//            64 contiguous bytes per row).
+// The output tile is oriented so that each lane holds four consecutive outputs of
+// one row of the stored layout and writes them with one vector store.
+#include <cstdlib>
+
+#include "common.h"
+
+namespace bsmm {
+
+template <int DT, int B, int FA, bool TW, int MT, int WM, int WK, int D>
+struct MMCfg {
+    static constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;
+    static constexpr int QT = (B + 15) / 16;
+    static constexpr int NTW = 16 * MT, NT = NTW * WM;
+    static constexpr bool S16 = DT != BSMM_F32;
+    static constexpr bool W_TR = !TW && S16;
+    static constexpr bool X_TR = FA == 0 && S16;
+    static constexpr int WCH = B / 8;                        // 16-byte chunks per weight row
+    static constexpr int WR = W_TR ? (4 * B + 63) / 64 : QT;  // weight registers per lane and step
+    static constexpr int WPITCH = QT * 16 + 8;               // LDS row pitch, elements
+    static constexpr int XPITCH = NTW + 8;
+    static constexpr int WTILE = W_TR ? 32 * WPITCH : 0;     // elements per wave
+    static constexpr int XTILE = X_TR ? 32 * XPITCH : 0;
+    static constexpr int WAVES = WM * WK, THREADS = 64 * WAVES;
+    static constexpr int TILE_BYTES = WAVES * (WTILE + XTILE) * 2;
+    static constexpr int RED_BYTES = WK > 1 ? WAVES * MT * QT * 64 * 16 : 0;   // partial tiles
+    static constexpr int SMEM = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+};
+
+constexpr int LCAP = 1024;   // list entries staged in LDS at a time
+
+template <int WR, int XR> struct Slot {
+    u32x4 w[WR];
+    u32x4 x[XR];
+};
+
+template <int DT, int B, int FA, bool TW, int MT, int WM, int WK, int D>
+__global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
+    using Cfg = MMCfg<DT, B, FA, TW, MT, WM, WK, D>;
+    using T = typename Elt<DT>::T;
+    constexpr int VEC = Cfg::VEC, KS = Cfg::KS, QT = Cfg::QT, NT = Cfg::NT, NTW = Cfg::NTW;
+    constexpr int WR = Cfg::WR;
+    // wave-private transpose tiles during the walk; the WK partial tiles afterwards
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::SMEM > 0 ? Cfg::SMEM : 16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % WM, wk = wave / WM;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    int li, nt;
+    wg_decode(blockIdx.x, a.nout, a.ntiles, li, nt);
+    if (li < 0) return;   // the whole workgroup leaves together
+    const int o = a.order[li];
+    const int beg = a.ptr[o], len = a.ptr[o + 1] - beg;
+    const int64_t N = a.N;
+    const int64_t n0w = (int64_t)nt * NT + wm * NTW;
+    const T* __restrict__ in = (const T*)a.in;
+    const T* __restrict__ w = (const T*)a.w;
+    const int2* __restrict__ gent = reinterpret_cast<const int2*>(a.ent) + beg;
+    const bool xvec = (N % 8) == 0;
+    // The list is staged in LDS (chunks of LCAP entries) so that the weight and
+    // activation loads of the ring depend only on LDS reads, never on another global
+    // load: a dependent global load would make the wave wait for every load in flight.
+    __shared__ int2 lst[LCAP];
+    int clen = 0;   // entries of the current chunk
+
+    BSMM_LDS uint16_t* wt = (BSMM_LDS uint16_t*)smem + wave * (Cfg::WTILE + Cfg::XTILE);
+    BSMM_LDS uint16_t* xt = wt + Cfg::WTILE;
+    if constexpr (Cfg::W_TR && B == 8) {
+        // columns 8..15 of the weight tile stay zero (b = 8 uses half a 16-wide tile)
+        for (int i = lane; i < 32 * Cfg::WPITCH; i += 64) wt[i] = 0;
+    }
+
+    int csteps = 0;   // contraction steps of the current chunk
+    // Every load of a slot is issued unconditionally (out-of-range indices are clamped
+    // to a valid address and the value is masked to zero afterwards), so the number of
+    // loads in flight is the same on every path and the wave waits only for the slot
+    // it is about to use.
+    auto load_slot = [&](Slot<WR, MT>& sl, int s) {
+        const bool sv = s < csteps;   // wave-uniform
+        // ---- weight ----
+        if constexpr (Cfg::W_TR) {
+#pragma unroll
+            for (int i = 0; i < WR; i++) {
+                const int c0 = lane + 64 * i;
+                const bool cv = c0 < 4 * B;
+                const int c = cv ? c0 : 0;
+                const int r = c / Cfg::WCH, cc = c % Cfg::WCH;
+                const int kk = s * 32 + r, e0 = kk / B, p = kk % B;
+                const bool ok = sv && cv && e0 < clen;
+                const int id = lst[ok ? e0 : 0].y;
+                sl.w[i] = load_vec<DT>(or_zero(ok, w + (int64_t)id * B * B + p * B + cc * 8));
+            }
+        } else {
+            const int K0 = s * KS + g * VEC, e0 = K0 / B, p0 = K0 % B;
+            const bool ev = sv && e0 < clen;
+            const int id = lst[ev ? e0 : 0].y;
+#pragma unroll
+            for (int qt = 0; qt < QT; qt++) {
+                const int q = qt * 16 + r16;
+                const bool ok = ev && q < B;
+                if constexpr (TW)
+                    sl.w[qt] = load_vec<DT>(or_zero(ok, w + (int64_t)id * B * B + q * B + p0));
+                else
+                    sl.w[qt] = load_strided<DT>(or_zero(ok, w + (int64_t)id * B * B + p0 * B + q), ok ? B : 0, VEC);
+            }
+        }
+        // ---- activations ----
+        if constexpr (Cfg::X_TR) {
+#pragma unroll
+            for (int i = 0; i < MT; i++) {
+                const int c = lane + 64 * i;
+                const int r = c / (2 * MT), cc = c % (2 * MT);
+                const int kk = s * 32 + r, e0 = kk / B, p = kk % B;
+                const int64_t n = n0w + cc * 8;
+                const bool ok = sv && e0 < clen && n < N;
+                const int blk = lst[ok ? e0 : 0].x;
+                const T* row = in + ((int64_t)blk * B + p) * N + n;
+                if (xvec)
+                    sl.x[i] = load_vec<DT>(or_zero(ok, row));
+                else
+                    sl.x[i] = load_strided<DT>(row, 1, ok ? (int)(N - n < 8 ? N - n : 8) : 0);
+            }
+        } else {
+            const int K0 = s * KS + g * VEC, e0 = K0 / B, p0 = K0 % B;
+            const bool ev = sv && e0 < clen;
+            const int blk = lst[ev ? e0 : 0].x;
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const int64_t n = n0w + mt * 16 + r16;
+                const bool ok = ev && n < N;
+                if constexpr (FA == 1)
+                    sl.x[mt] = load_vec<DT>(or_zero(ok, in + n * a.fin + (int64_t)blk * B + p0));
+                else
+                    sl.x[mt] = load_strided<DT>(or_zero(ok, in + ((int64_t)blk * B + p0) * N + n), ok ? N : 0, VEC);
+            }
+        }
+    };
+
+    f32x4 acc[MT][QT];
+#pragma unroll
+    for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int j = 0; j < QT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_slot = [&](const Slot<WR, MT>& sl) {
+        if constexpr (Cfg::W_TR) {
+#pragma unroll
+            for (int i = 0; i < WR; i++) {
+                const int c = lane + 64 * i;
+                if (c < 4 * B) lds_store16(wt + (c / Cfg::WCH) * Cfg::WPITCH + (c % Cfg::WCH) * 8, sl.w[i]);
+            }
+        }
+        if constexpr (Cfg::X_TR) {
+#pragma unroll
+            for (int i = 0; i < MT; i++) {
+                const int c = lane + 64 * i;
+                lds_store16(xt + (c / (2 * MT)) * Cfg::XPITCH + (c % (2 * MT)) * 8, sl.x[i]);
+            }
+        }
+        wave_lds_order();
+        u32x4 wf[QT], xf[MT];
+#pragma unroll
+        for (int qt = 0; qt < QT; qt++) {
+            if constexpr (Cfg::W_TR)
+                wf[qt] = frag_tr16(wt, Cfg::WPITCH, 16 * qt, lane);
+            else
+                wf[qt] = sl.w[qt];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+            if constexpr (Cfg::X_TR)
+                xf[mt] = frag_tr16(xt, Cfg::XPITCH, 16 * mt, lane);
+            else
+                xf[mt] = sl.x[mt];
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int qt = 0; qt < QT; qt++) {
+                if constexpr (FA == 1)
+                    mma<DT>(acc[mt][qt], wf[qt], xf[mt]);   // D[q][n]
+                else
+                    mma<DT>(acc[mt][qt], xf[mt], wf[qt]);   // D[n][q]
+            }
+    };
+
+    for (int cbeg = 0; cbeg < len; cbeg += LCAP) {
+        clen = len - cbeg < LCAP ? len - cbeg : LCAP;
+        __syncthreads();   // the previous chunk is no longer read
+        for (int i = threadIdx.x; i < clen; i += Cfg::THREADS) lst[i] = gent[cbeg + i];
+        __syncthreads();
+        csteps = (clen * B + KS - 1) / KS;
+        const int mysteps = csteps > wk ? (csteps - wk + WK - 1) / WK : 0;
+        Slot<WR, MT> ring[D];
+#pragma unroll
+        for (int i = 0; i < D; i++) load_slot(ring[i], wk + WK * i);
+        // steps past the end compute on zeros; the trip count stays a multiple of D
+        for (int j = 0; j < mysteps; j += D) {
+#pragma unroll
+            for (int i = 0; i < D; i++) {
+                compute_slot(ring[i]);
+                load_slot(ring[i], wk + WK * (j + i + D));
+            }
+        }
+    }
+
+    const bool ovec = (N % 4) == 0;
+    // lane `l` of a wave holds, for tile (mt, qt), four consecutive outputs of one row of
+    // the stored layout; write them (vector store when aligned and in range)
+    auto store_tile = [&](int mt, int qt, int l, const f32x4& v4) {
+        const int lr16 = l & 15, lg = l >> 4;
+        if constexpr (FA == 1) {
+            const int64_t n = n0w + mt * 16 + lr16;   // out[n][q .. q+3]
+            const int q = qt * 16 + 4 * lg;
+            if (n < N && q < B) store4<DT>(a.out, n * a.fout + (int64_t)o * B + q, v4);
+        } else {
+            const int q = qt * 16 + lr16;              // out[q][n .. n+3]
+            const int64_t n = n0w + mt * 16 + 4 * lg;
+            if (q < B && n < N) {
+                const int64_t base = ((int64_t)o * B + q) * N + n;
+                if (ovec && n + 4 <= N) {
+                    store4<DT>(a.out, base, v4);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        if (n + v < N) store_elt(a.out, base + v, v4[v], DT);
+                }
+            }
+        }
+    };
+
+    if constexpr (WK > 1) {
+        // WK partial tiles: every wave parks its tile in LDS, then each wave adds up a
+        // share of the tile's elements over the WK partials in wave order.
+        __syncthreads();   // transpose tiles are dead; reuse the space
+        f32x4* red = reinterpret_cast<f32x4*>(smem);   // [wm][wk][tile][lane]
+        constexpr int TL = MT * QT * 64;
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+            for (int j = 0; j < QT; j++) red[(wm * WK + wk) * TL + (i * QT + j) * 64 + lane] = acc[i][j];
+        __syncthreads();
+        for (int sidx = wk * 64 + lane; sidx < TL; sidx += WK * 64) {
+            f32x4 sum = red[(wm * WK) * TL + sidx];
+#pragma unroll
+            for (int r = 1; r < WK; r++) sum += red[(wm * WK + r) * TL + sidx];
+            const int tile = sidx / 64;
+            store_tile(tile / QT, tile % QT, sidx % 64, sum);
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int qt = 0; qt < QT; qt++) store_tile(mt, qt, lane, acc[mt][qt]);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+static int mm_grid(int nlist, int ntiles) {
+    if (ntiles == 1) return nlist;
+    return ((nlist + 7) / 8) * 8 * ntiles;
+}
+
+template <int DT, int B, int FA, bool TW, int MT, int WM, int WK, int D>
+static hipError_t launch_cfg(MMArgs a, hipStream_t st, int pass) {
+    constexpr int NT = 16 * MT * WM;
+    a.ntiles = (int)((a.N + NT - 1) / NT);
+    const int64_t grid = (int64_t)mm_grid(a.nout, a.ntiles);
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    return launch(pass, mm_kernel<DT, B, FA, TW, MT, WM, WK, D>, dim3((unsigned)grid), dim3(64 * WM * WK), st, a);
+}
+
+// BSMM_MM_VARIANT=<n> (read once) forces one of the launch shapes below for A/B
+// measurements; every variant computes the same result.  0 or unset: automatic.
+static int mm_variant() {
+    static const int v = [] {
+        const char* e = getenv("BSMM_MM_VARIANT");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+template <int DT, int B, int FA, bool TW>
+static hipError_t launch_mm_t(const MMArgs& a, hipStream_t st, int pass) {
+    constexpr int DS = DT == BSMM_F32 ? 2 : 4;   // fp32 fragments take four loads each
+    switch (mm_variant()) {
+    case 1: return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
+    case 2: return launch_cfg<DT, B, FA, TW, 2, 1, 8, DS>(a, st, pass);
+    case 3: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
+    case 4: return launch_cfg<DT, B, FA, TW, 1, 1, 16, DS>(a, st, pass);
+    case 5: return launch_cfg<DT, B, FA, TW, 4, 1, 16, 2>(a, st, pass);
+    case 6: return launch_cfg<DT, B, FA, TW, 1, 1, 8, DS>(a, st, pass);
+    case 7: return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
+    case 8: return launch_cfg<DT, B, FA, TW, 2, 2, 4, DS>(a, st, pass);
+    case 9: return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
+    case 10: return launch_cfg<DT, B, FA, TW, 1, 4, 1, 4>(a, st, pass);
+    case 11: return launch_cfg<DT, B, FA, TW, 4, 4, 1, 2>(a, st, pass);
+    default: break;
+    }
+    // Small minibatch: the weight stream dominates and there are few output tiles, so
+    // 16 waves split each block list and every wave issues its whole share of loads at
+    // once (ring depth 4 covers a 64-entry list).
+    if (a.N <= 16) return launch_cfg<DT, B, FA, TW, 1, 1, 16, DS>(a, st, pass);
+    if (a.N <= 64) return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
+    // Otherwise 4 waves split 128 minibatch rows and each walks the whole list.
+    return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
+}
+
+template <int DT, bool TW>
+static hipError_t launch_mm_dt(const MMArgs& a, int b, int fa, hipStream_t st, int pass) {
+    switch (b * 2 + fa) {
+    case 16: return launch_mm_t<DT, 8, 0, TW>(a, st, pass);
+    case 17: return launch_mm_t<DT, 8, 1, TW>(a, st, pass);
+    case 32: return launch_mm_t<DT, 16, 0, TW>(a, st, pass);
+    case 33: return launch_mm_t<DT, 16, 1, TW>(a, st, pass);
+    case 64: return launch_mm_t<DT, 32, 0, TW>(a, st, pass);
+    case 65: return launch_mm_t<DT, 32, 1, TW>(a, st, pass);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass) {
+    hipStream_t st = (hipStream_t)stream;
+    if (a.nout == 0) return hipSuccess;
+    switch (dt * 2 + (transw ? 1 : 0)) {
+    case 0: return launch_mm_dt<BSMM_F32, false>(a, b, fa, st, pass);
+    case 1: return launch_mm_dt<BSMM_F32, true>(a, b, fa, st, pass);
+    case 2: return launch_mm_dt<BSMM_BF16, false>(a, b, fa, st, pass);
+    case 3: return launch_mm_dt<BSMM_BF16, true>(a, b, fa, st, pass);
+    case 4: return launch_mm_dt<BSMM_F16, false>(a, b, fa, st, pass);
+    case 5: return launch_mm_dt<BSMM_F16, true>(a, b, fa, st, pass);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bsmm
