@@ -12,12 +12,14 @@ block layout (the usage example of the kiteco/blocksparse README), bf16 storage
 with fp32 accumulation, feature_axis 1, seed 1001.  Inputs are seeded synthetic data
 (synth.workload_problem); there is no dataset.
 
-Timing: W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize().
-To keep the timed passes reading HBM rather than the 256 MiB Infinity Cache, the
-step cycles through several copies of its buffers (at least --rotate-mib MiB in
-total); the same step on one buffer set is reported as "warm".  Kernel durations
-come from the dispatches' own timestamps (hipExtLaunchKernelGGL start/stop events
-via bsmm_profile_begin/end) over the timed region.
+Timing: the step is captured once in a HIP graph that runs it on each of R copies of
+its buffers in turn (at least --rotate-mib MiB in total, so the timed passes read
+HBM rather than the 256 MiB Infinity Cache); after W warm-up steps the graph is
+replayed to run K steps, bracketed by torch.cuda.synchronize(): that is
+ms_per_step and value.  The same K steps are then launched eagerly with each
+kernel's dispatch timestamps recorded (hipExtLaunchKernelGGL start/stop events via
+bsmm_profile_begin/end, on the launch stream): per-pass kernel durations, the
+roofline fractions, and a "warm" duration on a single buffer set.
 
 Prints one JSON line (rank 0, N = 1).
 """
@@ -60,7 +62,7 @@ def parse():
 
 def pass_cost(P, dtype):
     """FLOPs and algorithmic HBM bytes of one launch of each pass."""
-    b, N, G, nnz = P.block, P.N, 1, P.nnz
+    b, N, G, nnz = P.block, P.N, len(P.xs), P.nnz
     s = DT_BYTES[dtype]
     C, K = P.R * b, P.S * b
     flops = 2.0 * N * b * b * nnz
@@ -156,49 +158,74 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     t0 = time.perf_counter()
     P = synth.workload_problem(name, dtype)
     m = bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
-    t_layout = time.perf_counter() - t0   # includes input generation
-    h, N = m.handle, P.N
+    t_prep = time.perf_counter() - t0   # input generation and layout compile
+    t0 = time.perf_counter()
+    bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
+    t_layout = time.perf_counter() - t0   # layout compile alone
+    h, N, G = m.handle, P.N, len(P.xs)
     dev = torch.device("cuda", 0)
-    x0 = P.xs[0].to(dev)
-    dy0 = P.dys[0].to(dev)
+    xs0 = [t.to(dev) for t in P.xs]
+    dys0 = [t.to(dev) for t in P.dys]
     w0 = P.w.to(dev)
-    set_bytes = (x0.numel() + dy0.numel() + w0.numel()) * x0.element_size() * 2 + w0.numel() * 4
-    R = max(1, int(np.ceil(rotate_mib * 2**20 / set_bytes)))
+    es = xs0[0].element_size()
+    set_bytes = (sum(t.numel() for t in xs0 + dys0) + w0.numel()) * es + (xs0[0].numel() + dys0[0].numel()) * es \
+        + w0.numel() * 4
+    R = max(1, min(64, int(np.ceil(rotate_mib * 2**20 / set_bytes))))
     sets = []
     for _ in range(R):
-        sets.append(dict(x=x0.clone(), dy=dy0.clone(), w=w0.clone(),
-                         y=torch.empty(m.o_shape(N), dtype=x0.dtype, device=dev),
-                         dx=torch.empty(m.i_shape(N), dtype=x0.dtype, device=dev),
+        sets.append(dict(xs=[t.clone() for t in xs0], dys=[t.clone() for t in dys0], w=w0.clone(),
+                         y=torch.empty(m.o_shape(N), dtype=w0.dtype, device=dev),
+                         dx=torch.empty(m.i_shape(N), dtype=w0.dtype, device=dev),
                          dw=torch.empty(m.w_shape, dtype=torch.float32, device=dev)))
 
     def step(s):
-        bs.bsmm_fprop(h, s["x"], s["w"], s["y"], N)
-        bs.bsmm_bprop(h, s["dy"], s["w"], s["dx"], N)
-        bs.bsmm_updat(h, [s["x"]], [s["dy"]], s["dw"], N)
+        bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
+        bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
+        bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
 
     # identity_init, timed once on its own (after a warm-up launch)
-    wi = torch.empty(m.w_shape, dtype=x0.dtype, device=dev)
+    wi = torch.empty(m.w_shape, dtype=w0.dtype, device=dev)
     bs.bsmm_identity_init(h, wi)
     torch.cuda.synchronize()
     bs.bsmm_profile_begin()
     bs.bsmm_identity_init(h, wi)
     ident = bs.bsmm_profile_end()["identity"]
 
-    def timed(nsets):
+    # Graph: one replay runs one step on each of the R buffer sets in turn.
+    for i in range(max(warmup, R)):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in sets:
+            step(s)
+    reps = max(1, steps // R)
+    nsteps = reps * R
+    for _ in range(max(1, warmup // R)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / nsteps
+
+    # Eager launches with each kernel's dispatch timestamps recorded (HIP events on the
+    # launch stream): the per-kernel durations behind the roofline figures.
+    def eager(nsets):
         for i in range(warmup):
             step(sets[i % nsets])
         torch.cuda.synchronize()
         bs.bsmm_profile_begin()
         t0 = time.perf_counter()
-        for i in range(steps):
+        for i in range(nsteps):
             step(sets[i % nsets])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        prof = bs.bsmm_profile_end()
-        return (t1 - t0) * 1e3 / steps, prof
+        return (t1 - t0) * 1e3 / nsteps, bs.bsmm_profile_end()
 
-    ms_cold, prof_cold = timed(R)
-    ms_warm, prof_warm = timed(1)
+    ms_eager, prof_cold = eager(R)
+    _, prof_warm = eager(1)
     cost = pass_cost(P, dtype)
     per = {}
     for p in PASSES:
@@ -212,8 +239,8 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
                   "bound": bound, "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 4),
                   "warm_kernel_us": round(wt / wc * 1e3, 3)}
     flops_step = sum(cost[p][0] for p in PASSES)
-    return dict(P=P, ms=ms_cold, ms_warm=ms_warm, per=per, flops_step=flops_step, R=R,
-                identity_us=ident[0] / max(ident[1], 1) * 1e3, prep_s=t_layout)
+    return dict(P=P, ms=ms_graph, ms_eager=ms_eager, per=per, flops_step=flops_step, R=R, steps=nsteps,
+                identity_us=ident[0] / max(ident[1], 1) * 1e3, layout_ms=t_layout * 1e3, prep_s=t_prep)
 
 
 def main():
@@ -247,7 +274,7 @@ def main():
     value = res["flops_step"] / (res["ms"] * 1e-3) / 1e12
     out = {
         "metric": "effective TFLOP/s (nonzero blocks) fprop/bprop/updat; % MFMA or HBM roofline",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": res["steps"], "warmup": args.warmup,
         "ms_per_step": round(res["ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic",
         "config": {"workload": args.workload, "hidden": wl.hidden, "block": wl.block, "minibatch": P.N,
@@ -255,14 +282,17 @@ def main():
                    "passes": "fprop+bprop+updat", "buffer_sets_rotated": res["R"]},
         "roofline": roofline,
         "per_pass": per,
-        "warm_ms_per_step": round(res["ms_warm"], 5),
+        "timing": "ms_per_step: HIP-graph replay of the three launches per step over rotating buffer sets; "
+                  "per_pass.kernel_us: dispatch timestamps of eager launches",
+        "eager_ms_per_step": round(res["ms_eager"], 5),
         "identity_init_us": round(res["identity_us"], 3),
+        "layout_compile_ms": round(res["layout_ms"], 3),
     }
     extras = {}
     for xd in [t for t in args.extra_dtypes.split(",") if t and t in wl.dtypes and t != dtype]:
         r = run_dtype(args, args.workload, xd, args.rotate_mib, args.steps, args.warmup)
         extras[xd] = {"value": round(r["flops_step"] / (r["ms"] * 1e-3) / 1e12, 3), "ms_per_step": round(r["ms"], 5),
-                      "per_pass": r["per"]}
+                      "eager_ms_per_step": round(r["ms_eager"], 5), "per_pass": r["per"]}
     if extras:
         out["other_dtypes"] = extras
     if not args.no_cpu_baseline:

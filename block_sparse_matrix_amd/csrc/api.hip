@@ -75,16 +75,17 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         return BSMM_OK;
     }
     const HostLut& L = h->lut;
-    const std::vector<int32_t>* parts[7] = {&L.coords, &L.colptr, &L.colent, &L.rowptr,
-                                            &L.rowent, &L.colorder, &L.roworder};
-    size_t off[7], total = 0;
-    for (int i = 0; i < 7; i++) {
+    constexpr int NP = 9;
+    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,   &L.colent,  &L.rowptr, &L.rowent,
+                                             &L.colorder, &L.roworder, &L.colwork, &L.rowwork};
+    size_t off[NP], total = 0;
+    for (int i = 0; i < NP; i++) {
         off[i] = total;
         total += (bytes_of(*parts[i]) + 255) & ~(size_t)255;
     }
     if (total == 0) total = 256;
     std::vector<char> staging(total, 0);
-    for (int i = 0; i < 7; i++)
+    for (int i = 0; i < NP; i++)
         if (!parts[i]->empty()) std::memcpy(staging.data() + off[i], parts[i]->data(), bytes_of(*parts[i]));
     void* base = nullptr;
     e = hipMalloc(&base, total);
@@ -105,6 +106,8 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
     d.rowent = (const int32_t*)(b + off[4]);
     d.colorder = (const int32_t*)(b + off[5]);
     d.roworder = (const int32_t*)(b + off[6]);
+    d.colwork = (const int32_t*)(b + off[7]);
+    d.rowwork = (const int32_t*)(b + off[8]);
     auto res = h->dev.emplace(dev, d);
     *out = &res.first->second;
     return BSMM_OK;
@@ -135,8 +138,14 @@ bsmm_status run_mm(bsmm_handle h, const void* in, const void* w, void* out, int6
     if ((s = check_ptr(out, nout)) != BSMM_OK) return s;
     const HostLut& L = h->lut;
     if (L.nnz > 0 && (s = check_ptr(w, "w")) != BSMM_OK) return s;
+    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+    const uint64_t feats = (uint64_t)(bprop ? L.S : L.R) * L.b;
+    if ((uint64_t)N * feats * es > kMaxTensorBytes || (uint64_t)L.nnz * L.b * L.b * es > kMaxTensorBytes)
+        return fail(BSMM_ERR_UNSUPPORTED, "an operand exceeds 2 GiB (the kernels use 32-bit offsets)");
     return BSMM_OK;
 }
+
+uint32_t bytes32(uint64_t v) { return (uint32_t)v; }
 
 }  // namespace
 
@@ -250,13 +259,15 @@ bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int
     a.in = x;
     a.w = w;
     a.out = y;
-    a.ptr = d->colptr;
+    a.work = d->colwork;
     a.ent = d->colent;
-    a.order = d->colorder;
     a.N = N;
     a.fin = (int32_t)(L.R * L.b);
     a.fout = (int32_t)(L.S * L.b);
     a.nout = (int32_t)L.S;
+    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+    a.in_bytes = bytes32((uint64_t)N * a.fin * es);
+    a.w_bytes = bytes32((uint64_t)L.nnz * L.b * L.b * es);
     hipError_t e = launch_mm(a, dt, L.b, L.fa, false, stream, BSMM_PASS_FPROP);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "fprop launch");
 }
@@ -274,13 +285,15 @@ bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, i
     a.in = dy;
     a.w = w;
     a.out = dx;
-    a.ptr = d->rowptr;
+    a.work = d->rowwork;
     a.ent = d->rowent;
-    a.order = d->roworder;
     a.N = N;
     a.fin = (int32_t)(L.S * L.b);
     a.fout = (int32_t)(L.R * L.b);
     a.nout = (int32_t)L.R;
+    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+    a.in_bytes = bytes32((uint64_t)N * a.fin * es);
+    a.w_bytes = bytes32((uint64_t)L.nnz * L.b * L.b * es);
     hipError_t e = launch_mm(a, dt, L.b, L.fa, true, stream, BSMM_PASS_BPROP);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "bprop launch");
 }
@@ -303,6 +316,11 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
             if ((s = check_ptr(dys[t], "dys[t]")) != BSMM_OK) return s;
         }
     }
+    {
+        const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+        if ((uint64_t)N * L.R * L.b * es > kMaxTensorBytes || (uint64_t)N * L.S * L.b * es > kMaxTensorBytes)
+            return fail(BSMM_ERR_UNSUPPORTED, "an activation exceeds 2 GiB (the kernels use 32-bit offsets)");
+    }
     const DeviceLut* d = nullptr;
     if ((s = device_lut(h, &d)) != BSMM_OK) return s;
     UpArgs a{};
@@ -318,6 +336,9 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
     a.nnz = (int32_t)L.nnz;
     a.G = N > 0 ? group : 1;
     a.dwdt = dw_dt;
+    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+    a.x_bytes = (uint32_t)((uint64_t)N * a.C * es);
+    a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "updat launch");
 }
@@ -361,7 +382,9 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 4: v = &L.rowent; break;
     case 5: v = &L.colorder; break;
     case 6: v = &L.roworder; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 6]");
+    case 7: v = &L.colwork; break;
+    case 8: v = &L.rowwork; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 8]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

@@ -31,6 +31,9 @@ struct HostLut {
     std::vector<int32_t> colptr, colent;
     std::vector<int32_t> rowptr, rowent;
     std::vector<int32_t> colorder, roworder;
+    // Per list in processing order (colorder / roworder): (list, start, length, 0);
+    // one 16-byte scalar load gives a workgroup everything it needs to find its list.
+    std::vector<int32_t> colwork, rowwork;
     int32_t max_col = 0, max_row = 0;   // longest fprop / bprop list
 };
 
@@ -49,6 +52,8 @@ struct DeviceLut {
     const int32_t* rowent = nullptr;
     const int32_t* colorder = nullptr;
     const int32_t* roworder = nullptr;
+    const int32_t* colwork = nullptr;
+    const int32_t* rowwork = nullptr;
 };
 
 }  // namespace bsmm

@@ -137,12 +137,37 @@ __device__ __forceinline__ u32x4 frag_tr16(const BSMM_LDS uint16_t* tile, int pi
     const BSMM_LDS uint16_t* p0 = tile + (8 * g + (m >> 2)) * pitch + col0 + 4 * (m & 3);
     const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSMM_LDS i16x4*)p0);
     const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSMM_LDS i16x4*)(p0 + 4 * pitch));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
     u32x4 r;
-    r.x = (uint32_t)(uint16_t)a.x | ((uint32_t)(uint16_t)a.y << 16);
-    r.y = (uint32_t)(uint16_t)a.z | ((uint32_t)(uint16_t)a.w << 16);
-    r.z = (uint32_t)(uint16_t)b.x | ((uint32_t)(uint16_t)b.y << 16);
-    r.w = (uint32_t)(uint16_t)b.z | ((uint32_t)(uint16_t)b.w << 16);
+    r.x = ua.x;
+    r.y = ua.y;
+    r.z = ub.x;
+    r.w = ub.y;
     return r;
+}
+
+// Raw buffer loads: a scalar 128-bit descriptor (base, size in bytes) plus a 32-bit
+// per-lane offset and a 32-bit scalar offset.  On gfx950 every dword whose
+// voffset + soffset lies at or beyond the descriptor's size reads as zero without
+// touching memory (measured on the device), so a whole load is switched off with a
+// scalar offset of kOffOff and a lane with voffset kOffLane; both leave
+// voffset + soffset below 2^32 as long as sizes stay below 2^31 bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOffLane = 0x80000000u;
+constexpr uint32_t kOffOff = 0x7fffffffu;
+constexpr uint64_t kMaxBufferBytes = 0x7fff0000ull;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
 __device__ __forceinline__ void lds_store16(BSMM_LDS uint16_t* p, const u32x4& v) {

@@ -12,18 +12,23 @@ struct MMArgs {
     const void* in;        // x (fprop) or dy (bprop), storage dtype
     const void* w;         // (nnz, b, b)
     void* out;             // y (fprop) or dx (bprop)
-    const int32_t* ptr;    // nout+1 list offsets
+    const int32_t* work;   // per list, longest first: (output block, start, length, 0)
     const int32_t* ent;    // (blk, id) pairs
-    const int32_t* order;  // nout list indices, longest first
     int64_t N;             // minibatch
     int32_t fin, fout;     // feature counts of in and out
     int32_t nout;          // number of lists (output blocks)
     int32_t ntiles;        // minibatch tiles (set by the launcher)
+    uint32_t in_bytes;     // size of `in`, bytes (< 2^31)
+    uint32_t w_bytes;      // size of `w`, bytes (< 2^31)
 };
+
+// Largest tensor the kernels address with 32-bit buffer offsets.
+constexpr uint64_t kMaxTensorBytes = 0x7fff0000ull;
 
 constexpr int kMaxGroup = 8;
 
 struct UpArgs {
+    uint32_t x_bytes, dy_bytes;   // size of each x_t / dy_t, bytes (< 2^31)
     const void* xs[kMaxGroup];
     const void* dys[kMaxGroup];
     void* dw;

@@ -76,6 +76,19 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
     }
     L.colorder = order_by_length(L.colptr);
     L.roworder = order_by_length(L.rowptr);
+    auto work = [](const std::vector<int32_t>& order, const std::vector<int32_t>& ptr) {
+        std::vector<int32_t> w(4 * order.size());
+        for (size_t i = 0; i < order.size(); i++) {
+            const int32_t o = order[i];
+            w[4 * i] = o;
+            w[4 * i + 1] = ptr[o];
+            w[4 * i + 2] = ptr[o + 1] - ptr[o];
+            w[4 * i + 3] = 0;
+        }
+        return w;
+    };
+    L.colwork = work(L.colorder, L.colptr);
+    L.rowwork = work(L.roworder, L.rowptr);
     for (int64_t k = 0; k < S; k++) L.max_col = std::max(L.max_col, L.colptr[k + 1] - L.colptr[k]);
     for (int64_t c = 0; c < R; c++) L.max_row = std::max(L.max_row, L.rowptr[c + 1] - L.rowptr[c]);
     out = std::move(L);

@@ -63,10 +63,19 @@ template <int DT, int B, int FA, bool TW, int MT, int WM, int WK, int D>
 __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
     using Cfg = MMCfg<DT, B, FA, TW, MT, WM, WK, D>;
     using T = typename Elt<DT>::T;
+    constexpr int S = (int)sizeof(T);
     constexpr int VEC = Cfg::VEC, KS = Cfg::KS, QT = Cfg::QT, NT = Cfg::NT, NTW = Cfg::NTW;
     constexpr int WR = Cfg::WR;
+    // UNI: a contraction step never spans two list entries, so the entry of a step is
+    // the same for the whole wave and its addresses are scalar offsets.
+    constexpr bool UNI = B >= KS;
+    constexpr int EPS = UNI ? 1 : KS / B;   // entries per step
     // wave-private transpose tiles during the walk; the WK partial tiles afterwards
     __shared__ __attribute__((aligned(16))) char smem[Cfg::SMEM > 0 ? Cfg::SMEM : 16];
+    // The list is staged in LDS (chunks of LCAP entries): the ring's loads then depend
+    // on LDS reads only, never on another global load, which would make the wave wait
+    // for every load in flight.
+    __shared__ int2 lst[LCAP];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -76,19 +85,14 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
     int li, nt;
     wg_decode(blockIdx.x, a.nout, a.ntiles, li, nt);
     if (li < 0) return;   // the whole workgroup leaves together
-    const int o = a.order[li];
-    const int beg = a.ptr[o], len = a.ptr[o + 1] - beg;
-    const int64_t N = a.N;
-    const int64_t n0w = (int64_t)nt * NT + wm * NTW;
-    const T* __restrict__ in = (const T*)a.in;
-    const T* __restrict__ w = (const T*)a.w;
+    const int4 wi = reinterpret_cast<const int4*>(a.work)[li];   // (output block, start, length)
+    const int o = wi.x, beg = wi.y, len = wi.z;
+    const int N = (int)a.N;
+    const int n0w = nt * NT + wm * NTW;
     const int2* __restrict__ gent = reinterpret_cast<const int2*>(a.ent) + beg;
+    const rsrc_t rin = make_rsrc(a.in, a.in_bytes);
+    const rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const bool xvec = (N % 8) == 0;
-    // The list is staged in LDS (chunks of LCAP entries) so that the weight and
-    // activation loads of the ring depend only on LDS reads, never on another global
-    // load: a dependent global load would make the wave wait for every load in flight.
-    __shared__ int2 lst[LCAP];
-    int clen = 0;   // entries of the current chunk
 
     BSMM_LDS uint16_t* wt = (BSMM_LDS uint16_t*)smem + wave * (Cfg::WTILE + Cfg::XTILE);
     BSMM_LDS uint16_t* xt = wt + Cfg::WTILE;
@@ -97,68 +101,133 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
         for (int i = lane; i < 32 * Cfg::WPITCH; i += 64) wt[i] = 0;
     }
 
+    // ---- per-lane constants: byte offsets inside a weight block / activation tile and
+    // the lane's entry within a step (0 when UNI); kOffLane for lanes with no data ----
+    uint32_t wc[WR];
+    int wel[WR];
+#pragma unroll
+    for (int i = 0; i < WR; i++) {
+        if constexpr (Cfg::W_TR) {
+            const int c = lane + 64 * i;
+            const bool cv = c < 4 * B;
+            const int r = cv ? c / Cfg::WCH : 0, cc = c % Cfg::WCH;
+            wel[i] = UNI ? 0 : r / B;
+            const int p = UNI ? r : r % B;
+            wc[i] = cv ? (uint32_t)((p * B + cc * 8) * S) : kOffLane;
+        } else {
+            const int q = 16 * i + r16;
+            const int pl = UNI ? g * VEC : (g * VEC) % B;
+            wel[i] = UNI ? 0 : (g * VEC) / B;
+            wc[i] = q < B ? (uint32_t)((TW ? q * B + pl : pl * B + q) * S) : kOffLane;
+        }
+    }
+    uint32_t xc[MT];
+    int xel[MT], xn[MT];
+#pragma unroll
+    for (int i = 0; i < MT; i++) {
+        if constexpr (Cfg::X_TR) {
+            const int c = lane + 64 * i;
+            const int r = c / (2 * MT), cc = c % (2 * MT);
+            const int n = n0w + cc * 8;
+            xel[i] = UNI ? 0 : r / B;
+            const int p = UNI ? r : r % B;
+            xn[i] = n;
+            xc[i] = n < N ? (uint32_t)p * (uint32_t)N * S + (uint32_t)n * S : kOffLane;
+        } else {
+            const int n = n0w + 16 * i + r16;
+            const int pl = UNI ? g * VEC : (g * VEC) % B;
+            xel[i] = UNI ? 0 : (g * VEC) / B;
+            xn[i] = n;
+            if constexpr (FA == 1)
+                xc[i] = n < N ? ((uint32_t)n * a.fin + pl) * S : kOffLane;
+            else
+                xc[i] = n < N ? ((uint32_t)pl * N + n) * S : kOffLane;
+        }
+    }
+
+    int clen = 0;     // entries of the current chunk
     int csteps = 0;   // contraction steps of the current chunk
-    // Every load of a slot is issued unconditionally (out-of-range indices are clamped
-    // to a valid address and the value is masked to zero afterwards), so the number of
-    // loads in flight is the same on every path and the wave waits only for the slot
-    // it is about to use.
     auto load_slot = [&](Slot<WR, MT>& sl, int s) {
         const bool sv = s < csteps;   // wave-uniform
-        // ---- weight ----
-        if constexpr (Cfg::W_TR) {
+        const int eu = UNI ? (s * KS) / B : s * EPS;
+        const int pu = UNI ? (s * KS) % B : 0;
+        if constexpr (UNI) {
+            const bool ev = sv && eu < clen;
+            const int2 en = lst[ev ? eu : 0];
+            const int blk = __builtin_amdgcn_readfirstlane(en.x), id = __builtin_amdgcn_readfirstlane(en.y);
+            // ---- weight ----
+            const uint32_t ws = (uint32_t)id * (B * B * S) + (TW ? pu * S : (Cfg::W_TR ? 0 : pu * B * S));
 #pragma unroll
             for (int i = 0; i < WR; i++) {
-                const int c0 = lane + 64 * i;
-                const bool cv = c0 < 4 * B;
-                const int c = cv ? c0 : 0;
-                const int r = c / Cfg::WCH, cc = c % Cfg::WCH;
-                const int kk = s * 32 + r, e0 = kk / B, p = kk % B;
-                const bool ok = sv && cv && e0 < clen;
-                const int id = lst[ok ? e0 : 0].y;
-                sl.w[i] = load_vec<DT>(or_zero(ok, w + (int64_t)id * B * B + p * B + cc * 8));
-            }
-        } else {
-            const int K0 = s * KS + g * VEC, e0 = K0 / B, p0 = K0 % B;
-            const bool ev = sv && e0 < clen;
-            const int id = lst[ev ? e0 : 0].y;
+                if constexpr (Cfg::W_TR || TW) {
+                    sl.w[i] = bload128(rw, wc[i], ev ? ws : kOffOff);
+                } else {   // fp32, contraction index is the weight row
 #pragma unroll
-            for (int qt = 0; qt < QT; qt++) {
-                const int q = qt * 16 + r16;
-                const bool ok = ev && q < B;
-                if constexpr (TW)
-                    sl.w[qt] = load_vec<DT>(or_zero(ok, w + (int64_t)id * B * B + q * B + p0));
-                else
-                    sl.w[qt] = load_strided<DT>(or_zero(ok, w + (int64_t)id * B * B + p0 * B + q), ok ? B : 0, VEC);
+                    for (int v = 0; v < 4; v++) sl.w[i][v] = bload32(rw, wc[i] + v * B * S, ev ? ws : kOffOff);
+                }
             }
-        }
-        // ---- activations ----
-        if constexpr (Cfg::X_TR) {
+            // ---- activations ----
 #pragma unroll
             for (int i = 0; i < MT; i++) {
-                const int c = lane + 64 * i;
-                const int r = c / (2 * MT), cc = c % (2 * MT);
-                const int kk = s * 32 + r, e0 = kk / B, p = kk % B;
-                const int64_t n = n0w + cc * 8;
-                const bool ok = sv && e0 < clen && n < N;
-                const int blk = lst[ok ? e0 : 0].x;
-                const T* row = in + ((int64_t)blk * B + p) * N + n;
-                if (xvec)
-                    sl.x[i] = load_vec<DT>(or_zero(ok, row));
-                else
-                    sl.x[i] = load_strided<DT>(row, 1, ok ? (int)(N - n < 8 ? N - n : 8) : 0);
+                if constexpr (Cfg::X_TR) {
+                    const uint32_t xs = (uint32_t)blk * B * (uint32_t)N * S;
+                    if (xvec) {
+                        sl.x[i] = bload128(rin, xc[i], ev ? xs : kOffOff);
+                    } else {   // rows not 16-byte aligned: element loads, tail masked
+                        uint32_t h[8];
+#pragma unroll
+                        for (int v = 0; v < 8; v++)
+                            h[v] = bload16(rin, xn[i] + v < N ? xc[i] + v * S : kOffLane, ev ? xs : kOffOff);
+                        sl.x[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                        h[6] | (h[7] << 16)};
+                    }
+                } else if constexpr (FA == 1) {
+                    sl.x[i] = bload128(rin, xc[i], ev ? (uint32_t)(blk * B + pu) * S : kOffOff);
+                } else {   // fp32, feature-major activations: four rows per fragment
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        sl.x[i][v] = bload32(rin, xc[i], ev ? ((uint32_t)(blk * B + pu + v) * N) * S : kOffOff);
+                }
             }
         } else {
-            const int K0 = s * KS + g * VEC, e0 = K0 / B, p0 = K0 % B;
-            const bool ev = sv && e0 < clen;
-            const int blk = lst[ev ? e0 : 0].x;
+            // ---- weight: the entry differs between lane groups ----
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-                const int64_t n = n0w + mt * 16 + r16;
-                const bool ok = ev && n < N;
-                if constexpr (FA == 1)
-                    sl.x[mt] = load_vec<DT>(or_zero(ok, in + n * a.fin + (int64_t)blk * B + p0));
-                else
-                    sl.x[mt] = load_strided<DT>(or_zero(ok, in + ((int64_t)blk * B + p0) * N + n), ok ? N : 0, VEC);
+            for (int i = 0; i < WR; i++) {
+                const int e = eu + wel[i];
+                const bool ok = sv && e < clen;
+                const int id = lst[ok ? e : 0].y;
+                const uint32_t vo = ok ? wc[i] + (uint32_t)id * (B * B * S) : kOffLane;
+                if constexpr (Cfg::W_TR || TW) {
+                    sl.w[i] = bload128(rw, vo, 0);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; v++) sl.w[i][v] = bload32(rw, vo + v * B * S, 0);
+                }
+            }
+            // ---- activations ----
+#pragma unroll
+            for (int i = 0; i < MT; i++) {
+                const int e = eu + xel[i];
+                const bool ok = sv && e < clen;
+                const int blk = lst[ok ? e : 0].x;
+                if constexpr (Cfg::X_TR) {
+                    const uint32_t vo = ok ? xc[i] + (uint32_t)blk * B * (uint32_t)N * S : kOffLane;
+                    if (xvec) {
+                        sl.x[i] = bload128(rin, vo, 0);
+                    } else {
+                        uint32_t h[8];
+#pragma unroll
+                        for (int v = 0; v < 8; v++) h[v] = bload16(rin, xn[i] + v < N ? vo + v * S : kOffLane, 0);
+                        sl.x[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                        h[6] | (h[7] << 16)};
+                    }
+                } else if constexpr (FA == 1) {
+                    sl.x[i] = bload128(rin, ok ? xc[i] + (uint32_t)blk * B * S : kOffLane, 0);
+                } else {
+                    const uint32_t vo = ok ? xc[i] + (uint32_t)blk * B * (uint32_t)N * S : kOffLane;
+#pragma unroll
+                    for (int v = 0; v < 4; v++) sl.x[i][v] = bload32(rin, vo, (uint32_t)v * N * S);
+                }
             }
         }
     };
@@ -326,10 +395,10 @@ static hipError_t launch_mm_t(const MMArgs& a, hipStream_t st, int pass) {
     default: break;
     }
     // Small minibatch: the weight stream dominates and there are few output tiles, so
-    // 16 waves split each block list and every wave issues its whole share of loads at
-    // once (ring depth 4 covers a 64-entry list).
-    if (a.N <= 16) return launch_cfg<DT, B, FA, TW, 1, 1, 16, DS>(a, st, pass);
-    if (a.N <= 64) return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
+    // the 4 waves of a workgroup split each block list (measured fastest at N = 64 of
+    // the shapes above).
+    if (a.N <= 16) return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
+    if (a.N <= 64) return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
     // Otherwise 4 waves split 128 minibatch rows and each walks the whole list.
     return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
 }

@@ -23,6 +23,7 @@ namespace bsmm {
 template <int DT, int B, int FA, int D>
 __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
     using T = typename Elt<DT>::T;
+    constexpr int S = (int)sizeof(T);
     constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;
     constexpr int PT = (B + 15) / 16;
     constexpr bool TR = FA == 1 && DT != BSMM_F32;
@@ -35,8 +36,8 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, g = lane >> 4;
-    const int64_t N = a.N;
-    const int spt = (int)((N + KS - 1) / KS);
+    const int N = (int)a.N;
+    const int spt = (N + KS - 1) / KS;
     const int nsb = a.G * spt;   // steps per block
     const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * a.bpw;
     if (b0 >= a.nnz) return;   // no workgroup barrier in this kernel
@@ -57,59 +58,98 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
         for (int i = lane; i < 2 * TILE; i += 64) xt[i] = 0;
     }
 
+    // Per-lane byte offsets relative to the step's first row (minibatch-major) or to the
+    // block's first feature row (feature-major).  With minibatch-major activations a row
+    // past the minibatch lies past the end of the tensor, so it reads as zero by itself.
+    uint32_t xc[RR], dc[RR];
+#pragma unroll
+    for (int i = 0; i < RR; i++) {
+        if constexpr (TR) {
+            const int ch = lane + 64 * i;
+            const bool chv = ch < 4 * B;
+            const int r = chv ? ch / WCH : 0, cc = ch % WCH;
+            xc[i] = chv ? (uint32_t)(r * a.C + cc * 8) * S : kOffLane;
+            dc[i] = chv ? (uint32_t)(r * a.K + cc * 8) * S : kOffLane;
+        } else if constexpr (FA == 1) {   // fp32: rows 4g + v of the step
+            const int p = 16 * i + r16;
+            xc[i] = p < B ? (uint32_t)(4 * g * a.C + p) * S : kOffLane;
+            dc[i] = p < B ? (uint32_t)(4 * g * a.K + p) * S : kOffLane;
+        } else {
+            const int p = 16 * i + r16;
+            xc[i] = p < B ? ((uint32_t)p * N + g * VEC) * S : kOffLane;
+            dc[i] = xc[i];
+        }
+    }
+
     struct SlotU {
         u32x4 x[RR];
         u32x4 d[RR];
     };
 
-    // Loads are issued unconditionally (clamped address, value masked afterwards) so
-    // the count of loads in flight does not depend on the path taken.
     auto load_slot = [&](SlotU& sl, int it0) {
         const bool iv = it0 < items;   // wave-uniform
         const int it = iv ? it0 : 0;
         const int j = it / nsb, st = it % nsb;
         const int t = st / spt;
-        const int64_t nb = (int64_t)(st % spt) * KS;
+        const int nb = (st % spt) * KS;
         const int c = __builtin_amdgcn_readlane(cl, j), k = __builtin_amdgcn_readlane(kl, j);
-        const T* __restrict__ x = (const T*)a.xs[t];
-        const T* __restrict__ dy = (const T*)a.dys[t];
-        if constexpr (TR) {
+        const void* xp = a.xs[0];
+        const void* dp = a.dys[0];
 #pragma unroll
-            for (int ri = 0; ri < RR; ri++) {
-                const int ch0 = lane + 64 * ri;
-                const bool chv = ch0 < 4 * B;
-                const int ch = chv ? ch0 : 0;
-                const int r = ch / WCH, cc = ch % WCH;
-                const int64_t n = nb + r;
-                const bool ok = iv && chv && n < N;
-                sl.x[ri] = load_vec<DT>(or_zero(ok, x + n * a.C + (int64_t)c * B + cc * 8));
-                sl.d[ri] = load_vec<DT>(or_zero(ok, dy + n * a.K + (int64_t)k * B + cc * 8));
+        for (int u = 1; u < kMaxGroup; u++)
+            if (t == u) {
+                xp = a.xs[u];
+                dp = a.dys[u];
+            }
+        const rsrc_t rx = make_rsrc(xp, a.x_bytes), rd = make_rsrc(dp, a.dy_bytes);
+        if constexpr (TR) {
+            const uint32_t xs = iv ? (uint32_t)(nb * a.C + c * B) * S : kOffOff;
+            const uint32_t ds = iv ? (uint32_t)(nb * a.K + k * B) * S : kOffOff;
+#pragma unroll
+            for (int i = 0; i < RR; i++) {
+                sl.x[i] = bload128(rx, xc[i], xs);
+                sl.d[i] = bload128(rd, dc[i], ds);
             }
         } else if constexpr (FA == 1) {   // fp32, minibatch-major: four rows per fragment
-            const int64_t n = nb + 4 * g;
-            const int nval = iv ? (int)(N - n >= 4 ? 4 : (N - n > 0 ? N - n : 0)) : 0;
 #pragma unroll
-            for (int pt = 0; pt < PT; pt++) {
-                const int p = pt * 16 + r16;
-                const int nv = p < B ? nval : 0;
-                sl.x[pt] = load_strided<DT>(x + n * a.C + (int64_t)c * B + p, a.C, nv);
-                sl.d[pt] = load_strided<DT>(dy + n * a.K + (int64_t)k * B + p, a.K, nv);
-            }
-        } else {   // feature-major: contraction index contiguous
-            const int64_t n = nb + g * VEC;
+            for (int i = 0; i < RR; i++)
 #pragma unroll
-            for (int pt = 0; pt < PT; pt++) {
-                const int p = pt * 16 + r16;
-                const T* xp = x + ((int64_t)c * B + p) * N + n;
-                const T* dp = dy + ((int64_t)k * B + p) * N + n;
-                const bool ok = iv && p < B && n < N;
+                for (int v = 0; v < 4; v++) {
+                    sl.x[i][v] = bload32(rx, xc[i], iv ? (uint32_t)((nb + v) * a.C + c * B) * S : kOffOff);
+                    sl.d[i][v] = bload32(rd, dc[i], iv ? (uint32_t)((nb + v) * a.K + k * B) * S : kOffOff);
+                }
+        } else {   // feature-major: the contraction index is contiguous
+            const uint32_t xs = iv ? ((uint32_t)c * B * N + nb) * S : kOffOff;
+            const uint32_t ds = iv ? ((uint32_t)k * B * N + nb) * S : kOffOff;
+            const int nl = nb + g * VEC;   // the lane group's first minibatch row
+#pragma unroll
+            for (int i = 0; i < RR; i++) {
                 if (xvec) {
-                    sl.x[pt] = load_vec<DT>(or_zero(ok, xp));
-                    sl.d[pt] = load_vec<DT>(or_zero(ok, dp));
-                } else {
-                    const int nval = ok ? (int)(N - n >= VEC ? VEC : N - n) : 0;
-                    sl.x[pt] = load_strided<DT>(or_zero(ok, xp), 1, nval);
-                    sl.d[pt] = load_strided<DT>(or_zero(ok, dp), 1, nval);
+                    const bool ok = nl < N;
+                    sl.x[i] = bload128(rx, ok ? xc[i] : kOffLane, xs);
+                    sl.d[i] = bload128(rd, ok ? dc[i] : kOffLane, ds);
+                } else {   // rows not 16-byte aligned: element loads, tail masked
+                    uint32_t hx[VEC], hd[VEC];
+#pragma unroll
+                    for (int v = 0; v < VEC; v++) {
+                        const uint32_t vo = nl + v < N ? xc[i] + v * S : kOffLane;
+                        if constexpr (DT == BSMM_F32) {
+                            hx[v] = bload32(rx, vo, xs);
+                            hd[v] = bload32(rd, vo, ds);
+                        } else {
+                            hx[v] = bload16(rx, vo, xs);
+                            hd[v] = bload16(rd, vo, ds);
+                        }
+                    }
+                    if constexpr (DT == BSMM_F32) {
+                        sl.x[i] = u32x4{hx[0], hx[1], hx[2], hx[3]};
+                        sl.d[i] = u32x4{hd[0], hd[1], hd[2], hd[3]};
+                    } else {
+                        sl.x[i] = u32x4{hx[0] | (hx[1] << 16), hx[2] | (hx[3] << 16), hx[4] | (hx[5] << 16),
+                                        hx[6] | (hx[7] << 16)};
+                        sl.d[i] = u32x4{hd[0] | (hd[1] << 16), hd[2] | (hd[3] << 16), hd[4] | (hd[5] << 16),
+                                        hd[6] | (hd[7] << 16)};
+                    }
                 }
             }
         }

@@ -39,6 +39,8 @@
  *     dtype with round-to-nearest-even.
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Kernels are
  *     enqueued asynchronously; no call synchronizes the device.
+ *   - Every activation and weight tensor must be smaller than 2 GiB (the kernels use
+ *     32-bit offsets); larger ones are rejected with BSMM_ERR_UNSUPPORTED.
  *   - N = 0: fprop and bprop do nothing and return BSMM_OK; updat writes dW = 0 (the
  *     empty sum).  Activation pointers may be NULL only when N = 0.
  *   - A handle is immutable after bsmm_create; it may be used from several host
@@ -152,6 +154,8 @@ BSMM_API const char* bsmm_last_error(void);
  *          4 rowent   (2*nnz:   bprop entries (k, id), ascending k within each c)
  *          5 colorder (S:       output blocks by descending entry count, ties ascending)
  *          6 roworder (R:       input blocks by descending entry count, ties ascending)
+ *          7 colwork  (4*S:     per output block in colorder: (k, start, length, 0))
+ *          8 rowwork  (4*R:     per input block in roworder: (c, start, length, 0))
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);
