@@ -16,9 +16,11 @@ Timing: the step is captured once in a HIP graph that runs it on each of R copie
 its buffers in turn (at least --rotate-mib MiB in total, so the timed passes read
 HBM rather than the 256 MiB Infinity Cache); after W warm-up steps the graph is
 replayed to run K steps, bracketed by torch.cuda.synchronize(): that is
-ms_per_step and value.  The same K steps are then launched eagerly with each
+ms_per_step and value.  (--overlap runs bprop and updat, the independent halves of
+the backward pass, on two streams joined at the end of each step.)  The same K steps are then launched eagerly with each
 kernel's dispatch timestamps recorded (hipExtLaunchKernelGGL start/stop events via
-bsmm_profile_begin/end, on the launch stream): per-pass kernel durations, the
+bsmm_profile_begin/end, on the launch stream), each pass timed on its own over the
+rotating sets so that every launch starts cold: per-pass kernel durations, the
 roofline fractions, and a "warm" duration on a single buffer set.
 
 Prints one JSON line (rank 0, N = 1).
@@ -53,6 +55,9 @@ def parse():
     ap.add_argument("--dtype", default=None, help="storage dtype (default: bf16 if the workload has it)")
     ap.add_argument("--extra-dtypes", default="f32", help="comma list of further dtypes to time (reported aside)")
     ap.add_argument("--rotate-mib", type=float, default=1024.0)
+    ap.add_argument("--overlap", action="store_true",
+                    help="run bprop and updat concurrently on two streams in the timed graph "
+                         "(measured slower on MI355X: the two kernels compete rather than overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,6 +188,19 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
         bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
         bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
 
+    side = torch.cuda.Stream(device=dev)   # default priority
+
+    def step_overlap(s):
+        # dx and dW of a backward pass are independent: the weight-read-bound bprop and
+        # the gradient-write-bound updat run concurrently on two streams, joined per step
+        cur = torch.cuda.current_stream(dev)
+        bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
+        bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
+        cur.wait_stream(side)
+
     # identity_init, timed once on its own (after a warm-up launch)
     wi = torch.empty(m.w_shape, dtype=w0.dtype, device=dev)
     bs.bsmm_identity_init(h, wi)
@@ -198,7 +216,7 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for s in sets:
-            step(s)
+            (step_overlap if args.overlap else step)(s)
     reps = max(1, steps // R)
     nsteps = reps * R
     for _ in range(max(1, warmup // R)):
@@ -211,21 +229,40 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     ms_graph = (time.perf_counter() - t0) * 1e3 / nsteps
 
     # Eager launches with each kernel's dispatch timestamps recorded (HIP events on the
-    # launch stream): the per-kernel durations behind the roofline figures.
-    def eager(nsets):
-        for i in range(warmup):
-            step(sets[i % nsets])
-        torch.cuda.synchronize()
-        bs.bsmm_profile_begin()
-        t0 = time.perf_counter()
-        for i in range(nsteps):
-            step(sets[i % nsets])
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return (t1 - t0) * 1e3 / nsteps, bs.bsmm_profile_end()
+    # launch stream): the per-kernel durations behind the roofline figures.  Each pass
+    # is timed on its own over the rotating sets, so every launch starts from cold
+    # buffers (within a step, bprop would find W still cached by fprop).
+    def one(p, s):
+        if p == "fprop":
+            bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
+        elif p == "bprop":
+            bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
+        else:
+            bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
 
-    ms_eager, prof_cold = eager(R)
-    _, prof_warm = eager(1)
+    def eager(nsets):
+        prof = {}
+        for p in PASSES:
+            for i in range(warmup):
+                one(p, sets[i % nsets])
+            torch.cuda.synchronize()
+            bs.bsmm_profile_begin()
+            for i in range(nsteps):
+                one(p, sets[i % nsets])
+            torch.cuda.synchronize()
+            prof[p] = bs.bsmm_profile_end()[p]
+        return prof
+
+    for i in range(warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / nsteps
+    prof_cold = eager(R)
+    prof_warm = eager(1)
     cost = pass_cost(P, dtype)
     per = {}
     for p in PASSES:
@@ -282,8 +319,9 @@ def main():
                    "passes": "fprop+bprop+updat", "buffer_sets_rotated": res["R"]},
         "roofline": roofline,
         "per_pass": per,
-        "timing": "ms_per_step: HIP-graph replay of the three launches per step over rotating buffer sets; "
-                  "per_pass.kernel_us: dispatch timestamps of eager launches",
+        "timing": "ms_per_step: HIP-graph replay of the three launches per step over rotating buffer sets"
+                  + (" (bprop and updat on two streams, joined each step)" if args.overlap else "")
+                  + "; per_pass.kernel_us: dispatch timestamps of eager launches, one stream",
         "eager_ms_per_step": round(res["ms_eager"], 5),
         "identity_init_us": round(res["identity_us"], 3),
         "layout_compile_ms": round(res["layout_ms"], 3),

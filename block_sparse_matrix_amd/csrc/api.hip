@@ -75,9 +75,9 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         return BSMM_OK;
     }
     const HostLut& L = h->lut;
-    constexpr int NP = 9;
+    constexpr int NP = 10;
     const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,   &L.colent,  &L.rowptr, &L.rowent,
-                                             &L.colorder, &L.roworder, &L.colwork, &L.rowwork};
+                                             &L.colorder, &L.roworder, &L.colwork, &L.rowwork, &L.ugroups};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -108,6 +108,8 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
     d.roworder = (const int32_t*)(b + off[6]);
     d.colwork = (const int32_t*)(b + off[7]);
     d.rowwork = (const int32_t*)(b + off[8]);
+    d.ugroups = (const int32_t*)(b + off[9]);
+    d.nugroups = (int32_t)(L.ugroups.size() / 4);
     auto res = h->dev.emplace(dev, d);
     *out = &res.first->second;
     return BSMM_OK;
@@ -260,6 +262,7 @@ bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int
     a.w = w;
     a.out = y;
     a.work = d->colwork;
+    a.ptr = d->colptr;
     a.ent = d->colent;
     a.N = N;
     a.fin = (int32_t)(L.R * L.b);
@@ -286,6 +289,7 @@ bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, i
     a.w = w;
     a.out = dx;
     a.work = d->rowwork;
+    a.ptr = d->rowptr;
     a.ent = d->rowent;
     a.N = N;
     a.fin = (int32_t)(L.S * L.b);
@@ -338,6 +342,8 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
     a.dwdt = dw_dt;
     const uint64_t es = dt == BSMM_F32 ? 4 : 2;
     a.x_bytes = (uint32_t)((uint64_t)N * a.C * es);
+    a.groups = d->ugroups;
+    a.ngroups = d->nugroups;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "updat launch");
@@ -384,7 +390,8 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 6: v = &L.roworder; break;
     case 7: v = &L.colwork; break;
     case 8: v = &L.rowwork; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 8]");
+    case 9: v = &L.ugroups; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 9]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

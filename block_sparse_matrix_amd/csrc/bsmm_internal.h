@@ -34,6 +34,9 @@ struct HostLut {
     // Per list in processing order (colorder / roworder): (list, start, length, 0);
     // one 16-byte scalar load gives a workgroup everything it needs to find its list.
     std::vector<int32_t> colwork, rowwork;
+    // Weight-gradient groups: runs of up to 8 consecutive ids within one layout row,
+    // in id order: (first id, count, row, 0).
+    std::vector<int32_t> ugroups;
     int32_t max_col = 0, max_row = 0;   // longest fprop / bprop list
 };
 
@@ -54,6 +57,8 @@ struct DeviceLut {
     const int32_t* roworder = nullptr;
     const int32_t* colwork = nullptr;
     const int32_t* rowwork = nullptr;
+    const int32_t* ugroups = nullptr;
+    int32_t nugroups = 0;
 };
 
 }  // namespace bsmm

@@ -13,6 +13,7 @@ struct MMArgs {
     const void* w;         // (nnz, b, b)
     void* out;             // y (fprop) or dx (bprop)
     const int32_t* work;   // per list, longest first: (output block, start, length, 0)
+    const int32_t* ptr;    // nout+1 list offsets (natural order)
     const int32_t* ent;    // (blk, id) pairs
     int64_t N;             // minibatch
     int32_t fin, fout;     // feature counts of in and out
@@ -39,6 +40,8 @@ struct UpArgs {
     int32_t G;
     int32_t dwdt;
     int32_t bpw;            // blocks per wave (set by the launcher)
+    const int32_t* groups;  // row groups of <= 8 consecutive ids: (first id, count, row, 0)
+    int32_t ngroups;
 };
 
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);

@@ -89,6 +89,12 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
     };
     L.colwork = work(L.colorder, L.colptr);
     L.rowwork = work(L.roworder, L.rowptr);
+    for (int64_t c = 0; c < R; c++)
+        for (int32_t s = L.rowptr[c]; s < L.rowptr[c + 1]; s += 8) {
+            const int32_t n = std::min<int32_t>(8, L.rowptr[c + 1] - s);
+            // ids of row c are rowptr[c] .. rowptr[c+1]-1 (row-major numbering)
+            L.ugroups.insert(L.ugroups.end(), {s, n, (int32_t)c, 0});
+        }
     for (int64_t k = 0; k < S; k++) L.max_col = std::max(L.max_col, L.colptr[k + 1] - L.colptr[k]);
     for (int64_t c = 0; c < R; c++) L.max_row = std::max(L.max_row, L.rowptr[c + 1] - L.rowptr[c]);
     out = std::move(L);

@@ -353,6 +353,258 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// Large minibatch.  A workgroup (4 waves) computes a 64*MTW-row x b tile of one output
+// block; each wave owns 16*MTW rows and walks the whole list.  The list's weight blocks
+// are staged in LDS once (in chunks) and shared by the waves: block rows are stacked
+// in list order, so for fprop the stack is the K-major tile the transposing read
+// expects, and for bprop each row holds one q with p contiguous.  Only activations
+// stream from global memory, through a ring of D steps per wave.  Workgroups are
+// dealt so that each XCD works on one minibatch tile at a time, columns in natural
+// order: the activation rows of that tile stay in the XCD's L2 while every list that
+// uses them runs.
+constexpr int WSTACK_BYTES = 48 * 1024;
+
+template <int DT, int B, int FA, bool TW, int MTW, int D>
+struct MMLCfg {
+    static constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;
+    static constexpr int S = DT == BSMM_F32 ? 4 : 2;
+    static constexpr int QT = (B + 15) / 16;
+    static constexpr int NTW = 16 * MTW, NT = 4 * NTW;
+    static constexpr bool S16 = DT != BSMM_F32;
+    static constexpr bool X_TR = FA == 0 && S16;
+    static constexpr int EPS = B >= KS ? 1 : KS / B;          // entries per step
+    static constexpr int PW = (TW ? B : QT * 16) + 8;         // stack row pitch, elements
+    // entries per chunk: a multiple of EPS; stack rows padded to whole steps + one zero row
+    static constexpr int ECAP = ((WSTACK_BYTES / (PW * S) - KS - 1) / B) / EPS * EPS;
+    static constexpr int ROWS = ((ECAP * B + KS - 1) / KS) * KS;   // stack rows
+    static constexpr int ZROW = ROWS;                           // an all-zero row
+    static constexpr int STACK = (ROWS + 1) * PW;               // elements
+    static constexpr int XPITCH = NTW + 8;
+    static constexpr int XTILE = X_TR ? 32 * XPITCH : 0;        // elements per wave
+    static_assert(ECAP >= EPS, "stack too small");
+};
+
+template <int DT, int B, int FA, bool TW, int MTW, int D>
+__global__ __launch_bounds__(256) void mml_kernel(MMArgs a) {
+    using Cfg = MMLCfg<DT, B, FA, TW, MTW, D>;
+    using T = typename Elt<DT>::T;
+    constexpr int S = Cfg::S, VEC = Cfg::VEC, KS = Cfg::KS, QT = Cfg::QT, NT = Cfg::NT, NTW = Cfg::NTW;
+    constexpr int PW = Cfg::PW, ECAP = Cfg::ECAP;
+    constexpr bool UNI = B >= KS;
+    constexpr int EPS = Cfg::EPS;
+    constexpr int CH = 16 / S;   // elements per 16-byte chunk
+    __shared__ __attribute__((aligned(16))) T wst[Cfg::STACK];
+    __shared__ __attribute__((aligned(16))) uint16_t xtl[Cfg::X_TR ? 4 * Cfg::XTILE : 8];
+    __shared__ int2 lst[ECAP];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    // workgroup -> (list, minibatch tile)
+    int li, nt;
+    {
+        const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+        if (a.ntiles >= 8) {   // each XCD walks the lists of one tile at a time
+            li = slot % a.nout;
+            nt = (slot / a.nout) * 8 + xcd;
+            if (nt >= a.ntiles) return;
+        } else {
+            li = (slot / a.ntiles) * 8 + xcd;
+            nt = slot % a.ntiles;
+            if (li >= a.nout) return;
+        }
+    }
+    const int o = li;
+    const int beg = a.ptr[o], len = a.ptr[o + 1] - beg;
+    const int N = (int)a.N;
+    const int n0w = nt * NT + wave * NTW;
+    const int2* __restrict__ gent = reinterpret_cast<const int2*>(a.ent) + beg;
+    const rsrc_t rin = make_rsrc(a.in, a.in_bytes);
+    const rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const bool xvec = (N % 8) == 0;
+    BSMM_LDS uint16_t* xt = (BSMM_LDS uint16_t*)xtl + wave * Cfg::XTILE;
+    BSMM_LDS T* stk = (BSMM_LDS T*)wst;
+
+    // zero the stack once: padding columns, the zero row and rows past a short list
+    // are never written afterwards except by the staging of real block rows
+    for (int i = threadIdx.x; i < Cfg::STACK; i += 256) stk[i] = (T)0;
+
+    // ---- activation fragments: per-lane constants (as in mm_kernel) ----
+    uint32_t xc[MTW];
+    int xel[MTW], xn[MTW];
+#pragma unroll
+    for (int i = 0; i < MTW; i++) {
+        if constexpr (Cfg::X_TR) {
+            const int c = lane + 64 * i;
+            const int r = c / (2 * MTW), cc = c % (2 * MTW);
+            const int n = n0w + cc * 8;
+            xel[i] = UNI ? 0 : r / B;
+            const int p = UNI ? r : r % B;
+            xn[i] = n;
+            xc[i] = n < N ? (uint32_t)p * (uint32_t)N * S + (uint32_t)n * S : kOffLane;
+        } else {
+            const int n = n0w + 16 * i + r16;
+            const int pl = UNI ? g * VEC : (g * VEC) % B;
+            xel[i] = UNI ? 0 : (g * VEC) / B;
+            xn[i] = n;
+            if constexpr (FA == 1)
+                xc[i] = n < N ? ((uint32_t)n * a.fin + pl) * S : kOffLane;
+            else
+                xc[i] = n < N ? ((uint32_t)pl * N + n) * S : kOffLane;
+        }
+    }
+
+    int clen = 0, csteps = 0;
+    auto load_x = [&](u32x4* xr, int s) {
+        const bool sv = s < csteps;
+        const int eu = UNI ? (s * KS) / B : s * EPS;
+        const int pu = UNI ? (s * KS) % B : 0;
+#pragma unroll
+        for (int i = 0; i < MTW; i++) {
+            const int e = eu + xel[i];
+            const bool ok = sv && e < clen;
+            const int blk = UNI ? __builtin_amdgcn_readfirstlane(lst[ok ? e : 0].x) : lst[ok ? e : 0].x;
+            if constexpr (Cfg::X_TR) {
+                const uint32_t vo = ok ? xc[i] + (uint32_t)blk * B * (uint32_t)N * S : kOffLane;
+                if (xvec) {
+                    xr[i] = bload128(rin, vo, 0);
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int v = 0; v < 8; v++) h[v] = bload16(rin, xn[i] + v < N ? vo + v * S : kOffLane, 0);
+                    xr[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                }
+            } else if constexpr (FA == 1) {
+                xr[i] = bload128(rin, ok ? xc[i] : kOffLane, (uint32_t)(blk * B + pu) * S);
+            } else {
+                const uint32_t vo = ok ? xc[i] : kOffLane;
+#pragma unroll
+                for (int v = 0; v < 4; v++) xr[i][v] = bload32(rin, vo, ((uint32_t)(blk * B + pu + v) * N) * S);
+            }
+        }
+    };
+
+    f32x4 acc[MTW][QT];
+#pragma unroll
+    for (int i = 0; i < MTW; i++)
+#pragma unroll
+        for (int j = 0; j < QT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const u32x4* xr, int s) {
+        const int K0 = s * KS + g * VEC;   // this lane group's first contraction index
+        u32x4 wf[QT], xf[MTW];
+#pragma unroll
+        for (int qt = 0; qt < QT; qt++) {
+            const int q = 16 * qt + r16;
+            if constexpr (!TW && Cfg::S16) {
+                wf[qt] = frag_tr16((const BSMM_LDS uint16_t*)stk + s * KS * PW, PW, 16 * qt, lane);
+            } else if constexpr (!TW) {   // fp32: rows K0 + v, column q (zero columns past b)
+#pragma unroll
+                for (int v = 0; v < 4; v++) wf[qt][v] = __float_as_uint(stk[(K0 + v) * PW + q]);
+            } else {   // bprop: row e*B + q holds W[id][q][.]; p contiguous
+                const int e = K0 / B, p0 = K0 % B;
+                const int row = q < B ? e * B + q : Cfg::ZROW;
+                wf[qt] = *reinterpret_cast<const BSMM_LDS u32x4*>(stk + row * PW + (q < B ? p0 : 0));
+            }
+        }
+        if constexpr (Cfg::X_TR) {
+#pragma unroll
+            for (int i = 0; i < MTW; i++) {
+                const int c = lane + 64 * i;
+                lds_store16(xt + (c / (2 * MTW)) * Cfg::XPITCH + (c % (2 * MTW)) * 8, xr[i]);
+            }
+            wave_lds_order();
+#pragma unroll
+            for (int mt = 0; mt < MTW; mt++) xf[mt] = frag_tr16(xt, Cfg::XPITCH, 16 * mt, lane);
+            wave_lds_order();
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MTW; mt++) xf[mt] = xr[mt];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MTW; mt++)
+#pragma unroll
+            for (int qt = 0; qt < QT; qt++) {
+                if constexpr (FA == 1)
+                    mma<DT>(acc[mt][qt], wf[qt], xf[mt]);   // D[q][n]
+                else
+                    mma<DT>(acc[mt][qt], xf[mt], wf[qt]);   // D[n][q]
+            }
+    };
+
+    for (int cbeg = 0; cbeg < len; cbeg += ECAP) {
+        clen = len - cbeg < ECAP ? len - cbeg : ECAP;
+        csteps = (clen * B + KS - 1) / KS;
+        __syncthreads();   // previous chunk fully consumed (and the stack zeroed)
+        for (int i = threadIdx.x; i < clen; i += 256) lst[i] = gent[cbeg + i];
+        __syncthreads();
+        // stage the chunk's weight blocks: block e's row r -> stack row e*B + r
+        {
+            constexpr int CPB = B * B / CH;   // chunks per block
+            for (int t = threadIdx.x; t < clen * CPB; t += 256) {
+                const int e = t / CPB, rc = t % CPB;
+                const int r = rc / (B / CH), cc = rc % (B / CH);
+                const uint32_t off = (uint32_t)lst[e].y * (B * B * S) + (uint32_t)(r * B + cc * CH) * S;
+                const u32x4 v = bload128(rw, off, 0);
+                *reinterpret_cast<BSMM_LDS u32x4*>(stk + (e * B + r) * PW + cc * CH) = v;
+            }
+            // rows of a partial last step beyond the list must read as zero
+            for (int i = clen * B * PW + threadIdx.x; i < csteps * KS * PW; i += 256) stk[i] = (T)0;
+        }
+        u32x4 ring[D][MTW];
+#pragma unroll
+        for (int i = 0; i < D; i++) load_x(ring[i], i);
+        __syncthreads();   // stack ready
+        for (int j = 0; j < csteps; j += D) {
+#pragma unroll
+            for (int i = 0; i < D; i++) {
+                if (j + i < csteps) compute(ring[i], j + i);   // no loads inside: branch is harmless
+                load_x(ring[i], j + i + D);
+            }
+        }
+    }
+
+    const bool ovec = (N % 4) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MTW; mt++)
+#pragma unroll
+        for (int qt = 0; qt < QT; qt++) {
+            if constexpr (FA == 1) {
+                const int n = n0w + mt * 16 + r16;   // out[n][q .. q+3]
+                const int q = qt * 16 + 4 * g;
+                if (n < N && q < B) store4<DT>(a.out, (int64_t)n * a.fout + (int64_t)o * B + q, acc[mt][qt]);
+            } else {
+                const int q = qt * 16 + r16;          // out[q][n .. n+3]
+                const int n = n0w + mt * 16 + 4 * g;
+                if (q < B && n < N) {
+                    const int64_t base = ((int64_t)o * B + q) * N + n;
+                    if (ovec && n + 4 <= N) {
+                        store4<DT>(a.out, base, acc[mt][qt]);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; v++)
+                            if (n + v < N) store_elt(a.out, base + v, acc[mt][qt][v], DT);
+                    }
+                }
+            }
+        }
+}
+
+template <int DT, int B, int FA, bool TW, int MTW, int D>
+static hipError_t launch_large(MMArgs a, hipStream_t st, int pass) {
+    constexpr int NT = 64 * MTW;
+    a.ntiles = (int)((a.N + NT - 1) / NT);
+    int64_t grid;
+    if (a.ntiles >= 8)
+        grid = (int64_t)a.nout * ((a.ntiles + 7) / 8) * 8;
+    else
+        grid = (int64_t)((a.nout + 7) / 8) * 8 * a.ntiles;
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    return launch(pass, mml_kernel<DT, B, FA, TW, MTW, D>, dim3((unsigned)grid), dim3(256), st, a);
+}
+
+// ---------------------------------------------------------------------------------
 static int mm_grid(int nlist, int ntiles) {
     if (ntiles == 1) return nlist;
     return ((nlist + 7) / 8) * 8 * ntiles;
@@ -382,16 +634,11 @@ static hipError_t launch_mm_t(const MMArgs& a, hipStream_t st, int pass) {
     constexpr int DS = DT == BSMM_F32 ? 2 : 4;   // fp32 fragments take four loads each
     switch (mm_variant()) {
     case 1: return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
-    case 2: return launch_cfg<DT, B, FA, TW, 2, 1, 8, DS>(a, st, pass);
-    case 3: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
-    case 4: return launch_cfg<DT, B, FA, TW, 1, 1, 16, DS>(a, st, pass);
-    case 5: return launch_cfg<DT, B, FA, TW, 4, 1, 16, 2>(a, st, pass);
-    case 6: return launch_cfg<DT, B, FA, TW, 1, 1, 8, DS>(a, st, pass);
-    case 7: return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
-    case 8: return launch_cfg<DT, B, FA, TW, 2, 2, 4, DS>(a, st, pass);
-    case 9: return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
-    case 10: return launch_cfg<DT, B, FA, TW, 1, 4, 1, 4>(a, st, pass);
-    case 11: return launch_cfg<DT, B, FA, TW, 4, 4, 1, 2>(a, st, pass);
+    case 2: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
+    case 3: return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
+    case 4: return launch_large<DT, B, FA, TW, 1, 4>(a, st, pass);
+    case 5: return launch_large<DT, B, FA, TW, 2, 4>(a, st, pass);
+    case 6: return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
     default: break;
     }
     // Small minibatch: the weight stream dominates and there are few output tiles, so
@@ -399,7 +646,10 @@ static hipError_t launch_mm_t(const MMArgs& a, hipStream_t st, int pass) {
     // the shapes above).
     if (a.N <= 16) return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
     if (a.N <= 64) return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
-    // Otherwise 4 waves split 128 minibatch rows and each walks the whole list.
+    // Large minibatch (N >= 2048): weights staged once per workgroup, activations
+    // streamed, one minibatch tile per XCD at a time.  In between, 4 waves split 128
+    // rows and each walks the list (measured faster there).
+    if (a.N >= 2048) return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
     return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
 }
 

@@ -234,6 +234,232 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Grouped weight gradient for long contractions (many minibatch steps per block).
+// A workgroup owns a group of up to GM blocks of one layout row c (consecutive ids):
+// every step loads the x_t slab of row c once and the dy_t slab of each block's
+// column, so the x slab is shared by the group.  The 4 waves split the contraction
+// steps; their partial tiles are added in wave order through LDS and each block is
+// written once.  Groups are dealt to XCDs in contiguous row ranges, so neighbouring
+// rows (which share columns, e.g. in a banded layout) reuse dy slabs from one L2.
+template <int DT, int B, int FA, int GM, int D>
+struct UGCfg {
+    static constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;
+    static constexpr int PT = (B + 15) / 16;
+    static constexpr bool TR = FA == 1 && DT != BSMM_F32;
+    static constexpr int WCH = B / 8;
+    static constexpr int RR = TR ? (4 * B + 63) / 64 : PT;
+    static constexpr int NS = 1 + GM;   // slab 0: x, slabs 1..GM: dy of each block
+    static constexpr int PITCH = PT * 16 + 8;
+    static constexpr int TILE = 32 * PITCH;
+    static constexpr int TILE_BYTES = TR ? 4 * NS * TILE * 2 : 0;
+    static constexpr int RED_BYTES = 4 * GM * PT * PT * 64 * 16;
+    static constexpr int SMEM = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+};
+
+template <int DT, int B, int FA, int GM, int D>
+__global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restrict__ groups, int ngroups) {
+    using Cfg = UGCfg<DT, B, FA, GM, D>;
+    using T = typename Elt<DT>::T;
+    constexpr int S = (int)sizeof(T);
+    constexpr int VEC = Cfg::VEC, KS = Cfg::KS, PT = Cfg::PT, RR = Cfg::RR, NS = Cfg::NS;
+    constexpr int PITCH = Cfg::PITCH, TILE = Cfg::TILE, WCH = Cfg::WCH;
+    constexpr bool TR = Cfg::TR;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::SMEM];
+
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    // group index: XCD x takes the x-th contiguous range of groups (rows)
+    const int gpx = (ngroups + 7) / 8;
+    const int gi = (blockIdx.x & 7) * gpx + (blockIdx.x >> 3);
+    if (gi >= ngroups) return;   // whole workgroup
+    const int4 gr = groups[gi];
+    const int id0 = gr.x, cnt = gr.y, c = gr.z;
+    const int N = (int)a.N;
+    const int spt = (N + KS - 1) / KS;
+    const int nsb = a.G * spt;
+    const bool xvec = (N % VEC) == 0;
+    int kl = 0;
+    if (lane < cnt) kl = a.coords[2 * (id0 + lane) + 1];
+
+    BSMM_LDS uint16_t* tiles = (BSMM_LDS uint16_t*)smem + wk * NS * TILE;
+    if constexpr (TR && B == 8) {
+        for (int i = lane; i < NS * TILE; i += 64) tiles[i] = 0;
+    }
+
+    uint32_t xc[RR], dc[RR];
+#pragma unroll
+    for (int i = 0; i < RR; i++) {
+        if constexpr (TR) {
+            const int ch = lane + 64 * i;
+            const bool chv = ch < 4 * B;
+            const int r = chv ? ch / WCH : 0, cc = ch % WCH;
+            xc[i] = chv ? (uint32_t)(r * a.C + cc * 8) * S : kOffLane;
+            dc[i] = chv ? (uint32_t)(r * a.K + cc * 8) * S : kOffLane;
+        } else if constexpr (FA == 1) {
+            const int p = 16 * i + r16;
+            xc[i] = p < B ? (uint32_t)(4 * g * a.C + p) * S : kOffLane;
+            dc[i] = p < B ? (uint32_t)(4 * g * a.K + p) * S : kOffLane;
+        } else {
+            const int p = 16 * i + r16;
+            xc[i] = p < B ? ((uint32_t)p * N + g * VEC) * S : kOffLane;
+            dc[i] = xc[i];
+        }
+    }
+
+    struct Slot {
+        u32x4 v[NS][RR];
+    };
+
+    // one slab (rows nb.. of x_t at feature block fb, or of dy_t) into registers
+    auto load_slab = [&](u32x4* out, rsrc_t r, const uint32_t* lc, int F, int fb, int nb, bool ok) {
+        if constexpr (TR) {
+            const uint32_t so = ok ? (uint32_t)(nb * F + fb * B) * S : kOffOff;
+#pragma unroll
+            for (int i = 0; i < RR; i++) out[i] = bload128(r, lc[i], so);
+        } else if constexpr (FA == 1) {
+#pragma unroll
+            for (int i = 0; i < RR; i++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) out[i][v] = bload32(r, lc[i], ok ? (uint32_t)((nb + v) * F + fb * B) * S : kOffOff);
+        } else {
+            const uint32_t so = ok ? ((uint32_t)fb * B * N + nb) * S : kOffOff;
+            const int nl = nb + g * VEC;
+#pragma unroll
+            for (int i = 0; i < RR; i++) {
+                if (xvec) {
+                    out[i] = bload128(r, nl < N ? lc[i] : kOffLane, so);
+                } else {
+                    uint32_t h[VEC];
+#pragma unroll
+                    for (int v = 0; v < VEC; v++) {
+                        const uint32_t vo = nl + v < N ? lc[i] + v * S : kOffLane;
+                        h[v] = DT == BSMM_F32 ? bload32(r, vo, so) : bload16(r, vo, so);
+                    }
+                    if constexpr (DT == BSMM_F32)
+                        out[i] = u32x4{h[0], h[1], h[2], h[3]};
+                    else
+                        out[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                       h[6] | (h[7] << 16)};
+                }
+            }
+        }
+    };
+
+    auto load_slot = [&](Slot& sl, int st0) {
+        const bool sv = st0 < nsb;   // wave-uniform
+        const int st = sv ? st0 : 0;
+        const int t = st / spt;
+        const int nb = (st % spt) * KS;
+        const void* xp = a.xs[0];
+        const void* dp = a.dys[0];
+#pragma unroll
+        for (int u = 1; u < kMaxGroup; u++)
+            if (t == u) {
+                xp = a.xs[u];
+                dp = a.dys[u];
+            }
+        const rsrc_t rx = make_rsrc(xp, a.x_bytes), rd = make_rsrc(dp, a.dy_bytes);
+        load_slab(sl.v[0], rx, xc, a.C, c, nb, sv);
+#pragma unroll
+        for (int j = 0; j < GM; j++) {
+            const int k = __builtin_amdgcn_readlane(kl, j);
+            load_slab(sl.v[1 + j], rd, dc, a.K, k, nb, sv && j < cnt);
+        }
+    };
+
+    f32x4 acc[GM][PT][PT];
+#pragma unroll
+    for (int j = 0; j < GM; j++)
+#pragma unroll
+        for (int q = 0; q < PT; q++)
+#pragma unroll
+            for (int p = 0; p < PT; p++) acc[j][q][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Slot& sl) {
+        u32x4 fr[NS][PT];
+        if constexpr (TR) {
+#pragma unroll
+            for (int sidx = 0; sidx < NS; sidx++)
+#pragma unroll
+                for (int i = 0; i < RR; i++) {
+                    const int ch = lane + 64 * i;
+                    if (ch < 4 * B) lds_store16(tiles + sidx * TILE + (ch / WCH) * PITCH + (ch % WCH) * 8, sl.v[sidx][i]);
+                }
+            wave_lds_order();
+#pragma unroll
+            for (int sidx = 0; sidx < NS; sidx++)
+#pragma unroll
+                for (int pt = 0; pt < PT; pt++) fr[sidx][pt] = frag_tr16(tiles + sidx * TILE, PITCH, 16 * pt, lane);
+            wave_lds_order();
+        } else {
+#pragma unroll
+            for (int sidx = 0; sidx < NS; sidx++)
+#pragma unroll
+                for (int pt = 0; pt < PT; pt++) fr[sidx][pt] = sl.v[sidx][pt];
+        }
+#pragma unroll
+        for (int j = 0; j < GM; j++)
+            if (j < cnt)
+#pragma unroll
+                for (int qt = 0; qt < PT; qt++)
+#pragma unroll
+                    for (int pt = 0; pt < PT; pt++) mma<DT>(acc[j][qt][pt], fr[1 + j][qt], fr[0][pt]);   // D[q][p]
+    };
+
+    const int mysteps = nsb > wk ? (nsb - wk + 3) / 4 : 0;
+    Slot ring[D];
+#pragma unroll
+    for (int i = 0; i < D; i++) load_slot(ring[i], wk + 4 * i);
+    for (int j = 0; j < mysteps; j += D) {
+#pragma unroll
+        for (int i = 0; i < D; i++) {
+            if (j + i < mysteps) compute(ring[i]);   // no loads inside
+            load_slot(ring[i], wk + 4 * (j + i + D));
+        }
+    }
+
+    // partial tiles of the 4 waves, added in wave order
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(smem);   // [wave][block][qt][pt][lane]
+    constexpr int PER = GM * PT * PT * 64;
+#pragma unroll
+    for (int j = 0; j < GM; j++)
+#pragma unroll
+        for (int qt = 0; qt < PT; qt++)
+#pragma unroll
+            for (int pt = 0; pt < PT; pt++) red[wk * PER + ((j * PT + qt) * PT + pt) * 64 + lane] = acc[j][qt][pt];
+    __syncthreads();
+    for (int sidx = threadIdx.x; sidx < PER; sidx += 256) {
+        const int j = sidx / (PT * PT * 64);
+        if (j >= cnt) continue;
+        f32x4 sum = red[sidx];
+#pragma unroll
+        for (int w = 1; w < 4; w++) sum += red[w * PER + sidx];
+        const int rem = sidx % (PT * PT * 64);
+        const int qt = rem / (PT * 64), pt = (rem / 64) % PT, l = rem % 64;
+        const int p = pt * 16 + (l & 15), q = qt * 16 + 4 * (l >> 4);
+        if (p < B && q < B) {
+            const int64_t idx = (int64_t)(id0 + j) * B * B + p * B + q;
+            if (a.dwdt == BSMM_F32)
+                store4<BSMM_F32>(a.dw, idx, sum);
+            else if (a.dwdt == BSMM_BF16)
+                store4<BSMM_BF16>(a.dw, idx, sum);
+            else
+                store4<BSMM_F16>(a.dw, idx, sum);
+        }
+    }
+}
+
+template <int DT, int B, int FA>
+static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int ngroups, hipStream_t st) {
+    constexpr int GM = 8;
+    const int grid = ((ngroups + 7) / 8) * 8;
+    return launch(BSMM_PASS_UPDAT, updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, a, groups,
+                  ngroups);
+}
+
 // BSMM_UPDAT_VARIANT=<n> (read once) forces a ring depth / blocks-per-wave pair for
 // A/B measurements; 0 or unset: automatic.
 static int updat_variant() {
@@ -258,14 +484,22 @@ static hipError_t launch_updat_t(const UpArgs& a, hipStream_t st) {
     case 1: return launch_updat_cfg<DT, B, FA, 2>(a, 1, st);
     case 2: return launch_updat_cfg<DT, B, FA, 4>(a, 1, st);
     case 3: return launch_updat_cfg<DT, B, FA, 2>(a, 2, st);
-    case 4: return launch_updat_cfg<DT, B, FA, 4>(a, 2, st);
-    case 5: return launch_updat_cfg<DT, B, FA, 4>(a, 4, st);
-    case 6: return launch_updat_cfg<DT, B, FA, 8>(a, 4, st);
+    case 4: return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.groups, a.ngroups, st);
+    case 5: return launch_updat_cfg<DT, B, FA, 2>(a, 4, st);
+    case 6: return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
+    case 7: return launch_updat_cfg<DT, B, FA, 2>(a, 8, st);
+    case 8: return launch_updat_cfg<DT, B, FA, 1>(a, 4, st);
     default: break;
     }
-    // One block per wave: a wave loads, contracts, stores its block and exits, so no
-    // wave ever waits on its own stores (stores count in the same counter as loads).
-    return launch_updat_cfg<DT, B, FA, 4>(a, 1, st);
+    constexpr int KS = 4 * Elt<DT>::VEC;
+    const int64_t steps = (int64_t)a.G * ((a.N + KS - 1) / KS);
+    // Long contractions: row groups, 4 waves per block group.
+    if (steps >= 16) return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.groups, a.ngroups, st);
+    // Short ones: a wave takes one or two blocks (two once there are enough blocks for
+    // >= 2 waves per SIMD), loads, contracts, stores and exits; with two blocks a wave
+    // keeps no ring (measured best: waves, not the ring, hide the latency here).
+    if ((int64_t)a.nnz / 2 >= 2048) return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
+    return launch_updat_cfg<DT, B, FA, 2>(a, 1, st);
 }
 
 template <int DT>

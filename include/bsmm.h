@@ -156,6 +156,8 @@ BSMM_API const char* bsmm_last_error(void);
  *          6 roworder (R:       input blocks by descending entry count, ties ascending)
  *          7 colwork  (4*S:     per output block in colorder: (k, start, length, 0))
  *          8 rowwork  (4*R:     per input block in roworder: (c, start, length, 0))
+ *          9 ugroups  (4*groups: runs of <= 8 consecutive ids of one layout row, in id
+ *                     order: (first id, count, c, 0); the weight-gradient work units)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);

@@ -180,3 +180,19 @@ def test_autograd():
     bits = synth.to_bits
     assert_close(x.grad, oracle.bprop(P.layout, 32, 1, bits(P.dys[0]), bits(P.w), 70), "f32", "dx")
     assert_close(w.grad, oracle.updat(P.layout, 32, 1, [bits(P.xs[0])], [bits(P.dys[0])], 70), "f32", "dw")
+
+
+@pytest.mark.parametrize("N", [512, 530, 2048, 2100])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fa", [1, 0])
+@pytest.mark.parametrize("b", [32, 16, 8])
+def test_long_minibatch(b, fa, dtype, N):
+    """Minibatches that select the long-contraction kernels (grouped weight gradient,
+    weights staged in LDS for N >= 2048), aligned and ragged."""
+    print(f"case long b={b} fa={fa} dtype={dtype} N={N}", flush=True)
+    P = _prob(7 * b + 3 * fa + N, 4, 5, b, N, fa, dtype, G=2 if N < 1000 else 1)
+    y, dx, dw = _run_all(P, dtype)
+    ry, rdx, rdw = _oracle_all(P, dtype)
+    assert_close(y, ry, dtype, "fprop")
+    assert_close(dx, rdx, dtype, "bprop")
+    assert_close(dw, rdw, dtype, "updat")

@@ -73,3 +73,19 @@ def test_workload_layouts(name):
         assert int(L.sum()) == round(0.03 * R * R)
         c, k = np.meshgrid(np.arange(R), np.arange(R), indexing="ij")
         assert np.all(L[np.abs(c - k) <= 2] == 1)
+
+
+def test_updat_groups_cover_every_block_once():
+    rng = np.random.default_rng(3)
+    for R, S, p in [(5, 40, 0.5), (17, 9, 0.3), (1, 1, 1.0), (6, 6, 0.0)]:
+        L = (rng.random((R, S)) < p).astype(np.uint8)
+        m = bs.BlocksparseMatMul(L, block_size=8)
+        g = bs.bsmm_debug_lut(m.handle, 9).reshape(-1, 4)
+        coords = bs.bsmm_debug_lut(m.handle, 0).reshape(-1, 2)
+        seen = np.zeros(int(L.sum()), dtype=int)
+        for id0, cnt, c, _ in g:
+            assert 1 <= cnt <= 8
+            assert np.all(coords[id0:id0 + cnt, 0] == c)
+            seen[id0:id0 + cnt] += 1
+        assert np.all(seen == 1)
+        assert list(g[:, 0]) == sorted(g[:, 0])
