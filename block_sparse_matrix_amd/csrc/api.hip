@@ -75,9 +75,10 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         return BSMM_OK;
     }
     const HostLut& L = h->lut;
-    constexpr int NP = 10;
-    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,   &L.colent,  &L.rowptr, &L.rowent,
-                                             &L.colorder, &L.roworder, &L.colwork, &L.rowwork, &L.ugroups};
+    constexpr int NP = 12;
+    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,  &L.colent,  &L.rowptr,
+                                             &L.rowent,   &L.colorder, &L.roworder, &L.colwork,
+                                             &L.rowwork,  &L.ugroups,  &L.colrec,   &L.rowrec};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -109,6 +110,8 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
     d.colwork = (const int32_t*)(b + off[7]);
     d.rowwork = (const int32_t*)(b + off[8]);
     d.ugroups = (const int32_t*)(b + off[9]);
+    d.colrec = (const int32_t*)(b + off[10]);
+    d.rowrec = (const int32_t*)(b + off[11]);
     d.nugroups = (int32_t)(L.ugroups.size() / 4);
     auto res = h->dev.emplace(dev, d);
     *out = &res.first->second;
@@ -263,6 +266,8 @@ bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int
     a.out = y;
     a.work = d->colwork;
     a.ptr = d->colptr;
+    a.rec = d->colrec;
+    a.rsi = L.col_rsi;
     a.ent = d->colent;
     a.N = N;
     a.fin = (int32_t)(L.R * L.b);
@@ -290,6 +295,8 @@ bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, i
     a.out = dx;
     a.work = d->rowwork;
     a.ptr = d->rowptr;
+    a.rec = d->rowrec;
+    a.rsi = L.row_rsi;
     a.ent = d->rowent;
     a.N = N;
     a.fin = (int32_t)(L.S * L.b);
@@ -391,7 +398,9 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 7: v = &L.colwork; break;
     case 8: v = &L.rowwork; break;
     case 9: v = &L.ugroups; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 9]");
+    case 10: v = &L.colrec; break;
+    case 11: v = &L.rowrec; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 11]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

@@ -12,6 +12,8 @@
 
 namespace bsmm {
 
+constexpr int32_t kRecCap = 1024;   // entries kept inline in a list record
+
 // Host look-up tables compiled from a 0/1 block layout.
 //
 // Block ids number the layout's nonzeros in row-major order (the reading of
@@ -34,6 +36,11 @@ struct HostLut {
     // Per list in processing order (colorder / roworder): (list, start, length, 0);
     // one 16-byte scalar load gives a workgroup everything it needs to find its list.
     std::vector<int32_t> colwork, rowwork;
+    // Per list in processing order a fixed-stride record: the work descriptor (list,
+    // start, length, 0), then the first min(length, kRecCap) entries (blk, id).  A workgroup fetches its header and
+    // first entries with one load instead of a descriptor load followed by a list load.
+    std::vector<int32_t> colrec, rowrec;
+    int32_t col_rsi = 0, row_rsi = 0;   // record stride in int32
     // Weight-gradient groups: runs of up to 8 consecutive ids within one layout row,
     // in id order: (first id, count, row, 0).
     std::vector<int32_t> ugroups;
@@ -59,6 +66,8 @@ struct DeviceLut {
     const int32_t* rowwork = nullptr;
     const int32_t* ugroups = nullptr;
     int32_t nugroups = 0;
+    const int32_t* colrec = nullptr;
+    const int32_t* rowrec = nullptr;
 };
 
 }  // namespace bsmm

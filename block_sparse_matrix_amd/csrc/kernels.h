@@ -14,6 +14,8 @@ struct MMArgs {
     void* out;             // y (fprop) or dx (bprop)
     const int32_t* work;   // per list, longest first: (output block, start, length, 0)
     const int32_t* ptr;    // nout+1 list offsets (natural order)
+    const int32_t* rec;    // per list (processing order): (list, start, len, 0) + first entries
+    int32_t rsi;           // record stride, int32
     const int32_t* ent;    // (blk, id) pairs
     int64_t N;             // minibatch
     int32_t fin, fout;     // feature counts of in and out

@@ -97,6 +97,27 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
         }
     for (int64_t k = 0; k < S; k++) L.max_col = std::max(L.max_col, L.colptr[k + 1] - L.colptr[k]);
     for (int64_t c = 0; c < R; c++) L.max_row = std::max(L.max_row, L.rowptr[c + 1] - L.rowptr[c]);
+    auto records = [](const std::vector<int32_t>& order, const std::vector<int32_t>& ptr,
+                      const std::vector<int32_t>& ent, int32_t maxlen, std::vector<int32_t>& rec,
+                      int32_t& rsi) {
+        // an even entry count keeps every record 16-byte aligned
+        const int32_t rs = std::max<int32_t>(2, (std::min<int32_t>(maxlen, kRecCap) + 1) & ~1);
+        rsi = 4 + 2 * rs;
+        rec.assign(order.size() * rsi, 0);
+        for (size_t i = 0; i < order.size(); i++) {
+            int32_t* r = rec.data() + i * rsi;
+            const int32_t o = order[i], len = ptr[o + 1] - ptr[o];
+            r[0] = o;
+            r[1] = ptr[o];
+            r[2] = len;
+            for (int32_t e = 0; e < std::min(len, rs); e++) {
+                r[4 + 2 * e] = ent[2 * (ptr[o] + e)];
+                r[4 + 2 * e + 1] = ent[2 * (ptr[o] + e) + 1];
+            }
+        }
+    };
+    records(L.colorder, L.colptr, L.colent, L.max_col, L.colrec, L.col_rsi);
+    records(L.roworder, L.rowptr, L.rowent, L.max_row, L.rowrec, L.row_rsi);
     out = std::move(L);
     return true;
 }

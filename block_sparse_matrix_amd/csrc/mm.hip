@@ -85,8 +85,12 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
     int li, nt;
     wg_decode(blockIdx.x, a.nout, a.ntiles, li, nt);
     if (li < 0) return;   // the whole workgroup leaves together
-    const int4 wi = reinterpret_cast<const int4*>(a.work)[li];   // (output block, start, length)
-    const int o = wi.x, beg = wi.y, len = wi.z;
+    // the list's record: header (length, start) and its first entries, one load level
+    const int* rec = a.rec + (int64_t)li * a.rsi;
+    const int4 hdr = *reinterpret_cast<const int4*>(rec);
+    const int o = hdr.x, beg = hdr.y, len = hdr.z;
+    const int2* __restrict__ rent = reinterpret_cast<const int2*>(rec + 4);
+    const int rs = (a.rsi - 4) / 2;
     const int N = (int)a.N;
     const int n0w = nt * NT + wm * NTW;
     const int2* __restrict__ gent = reinterpret_cast<const int2*>(a.ent) + beg;
@@ -281,10 +285,16 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
             }
     };
 
+    {   // first chunk straight from the record (entries past the length are unused)
+        const int first = rs < LCAP ? rs : LCAP;
+        for (int i = threadIdx.x; i < first; i += Cfg::THREADS) lst[i] = rent[i];
+    }
     for (int cbeg = 0; cbeg < len; cbeg += LCAP) {
         clen = len - cbeg < LCAP ? len - cbeg : LCAP;
-        __syncthreads();   // the previous chunk is no longer read
-        for (int i = threadIdx.x; i < clen; i += Cfg::THREADS) lst[i] = gent[cbeg + i];
+        if (cbeg > 0) {
+            __syncthreads();   // the previous chunk is no longer read
+            for (int i = threadIdx.x; i < clen; i += Cfg::THREADS) lst[i] = gent[cbeg + i];
+        }
         __syncthreads();
         csteps = (clen * B + KS - 1) / KS;
         const int mysteps = csteps > wk ? (csteps - wk + WK - 1) / WK : 0;
@@ -415,8 +425,11 @@ __global__ __launch_bounds__(256) void mml_kernel(MMArgs a) {
             if (li >= a.nout) return;
         }
     }
-    const int o = li;
-    const int beg = a.ptr[o], len = a.ptr[o + 1] - beg;
+    const int* rec = a.rec + (int64_t)li * a.rsi;
+    const int4 hdr = *reinterpret_cast<const int4*>(rec);
+    const int o = hdr.x, beg = hdr.y, len = hdr.z;
+    const int2* __restrict__ rent = reinterpret_cast<const int2*>(rec + 4);
+    const int rs = (a.rsi - 4) / 2;
     const int N = (int)a.N;
     const int n0w = nt * NT + wave * NTW;
     const int2* __restrict__ gent = reinterpret_cast<const int2*>(a.ent) + beg;
@@ -533,12 +546,18 @@ __global__ __launch_bounds__(256) void mml_kernel(MMArgs a) {
             }
     };
 
+    {   // first chunk straight from the record
+        const int first = rs < ECAP ? rs : ECAP;
+        for (int i = threadIdx.x; i < first; i += 256) lst[i] = rent[i];
+    }
     for (int cbeg = 0; cbeg < len; cbeg += ECAP) {
         clen = len - cbeg < ECAP ? len - cbeg : ECAP;
         csteps = (clen * B + KS - 1) / KS;
         __syncthreads();   // previous chunk fully consumed (and the stack zeroed)
-        for (int i = threadIdx.x; i < clen; i += 256) lst[i] = gent[cbeg + i];
-        __syncthreads();
+        if (cbeg > 0) {
+            for (int i = threadIdx.x; i < clen; i += 256) lst[i] = gent[cbeg + i];
+            __syncthreads();
+        }
         // stage the chunk's weight blocks: block e's row r -> stack row e*B + r
         {
             constexpr int CPB = B * B / CH;   // chunks per block

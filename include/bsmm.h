@@ -158,6 +158,11 @@ BSMM_API const char* bsmm_last_error(void);
  *          8 rowwork  (4*R:     per input block in roworder: (c, start, length, 0))
  *          9 ugroups  (4*groups: runs of <= 8 consecutive ids of one layout row, in id
  *                     order: (first id, count, c, 0); the weight-gradient work units)
+ *         10 colrec   (S*stride: per output block in colorder, its colwork descriptor
+ *                     then its first min(length, 1024) fprop entries (c, id), zero
+ *                     padded; stride = 4 + 2*r, r = min(longest list, 1024) rounded
+ *                     up to even, at least 2)
+ *         11 rowrec   (the same for the bprop lists)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);

@@ -7,7 +7,8 @@ import pytest
 import block_sparse_matrix_amd as bs
 import synth
 
-COORDS, COLPTR, COLENT, ROWPTR, ROWENT, COLORDER, ROWORDER = range(7)
+COORDS, COLPTR, COLENT, ROWPTR, ROWENT, COLORDER, ROWORDER, COLWORK, ROWWORK = range(9)
+COLREC, ROWREC = 10, 11
 
 
 def check_layout(L, b=8, fa=1):
@@ -51,6 +52,25 @@ def check_layout(L, b=8, fa=1):
         key = [(-int(counts[i]), int(i)) for i in order]
         assert key == sorted(key)
 
+    # records: the work descriptor of each list in processing order, then its first
+    # entries inline (zero padded to the common stride)
+    for ow, ww, rw, ptr, ent in ((COLORDER, COLWORK, COLREC, colptr, colent),
+                                 (ROWORDER, ROWWORK, ROWREC, rowptr, rowent)):
+        order = bs.bsmm_debug_lut(h, ow)
+        work = bs.bsmm_debug_lut(h, ww).reshape(-1, 4)
+        lens = np.diff(ptr)
+        rs = max(2, (min(int(lens.max(initial=0)), 1024) + 1) // 2 * 2)
+        rec = bs.bsmm_debug_lut(h, rw).reshape(len(order), 4 + 2 * rs)
+        assert np.array_equal(work[:, 0], order)
+        assert np.array_equal(work[:, 1], ptr[order])
+        assert np.array_equal(work[:, 2], lens[order])
+        assert np.array_equal(rec[:, :4], work)
+        for i, o in enumerate(order):
+            n = min(int(lens[o]), rs)
+            inline = rec[i, 4:].reshape(-1, 2)
+            assert np.array_equal(inline[:n], ent[ptr[o]:ptr[o] + n])
+            assert np.all(inline[n:] == 0)
+
 
 def test_every_tiny_layout():
     for R, S in [(1, 1), (1, 2), (2, 1), (2, 2), (2, 3), (3, 2), (3, 3)]:
@@ -89,3 +109,12 @@ def test_updat_groups_cover_every_block_once():
             seen[id0:id0 + cnt] += 1
         assert np.all(seen == 1)
         assert list(g[:, 0]) == sorted(g[:, 0])
+
+
+def test_records_of_lists_longer_than_the_inline_cap():
+    # a column (fprop list) of 1100 blocks keeps only its first 1024 entries inline
+    L = np.zeros((1100, 3), dtype=np.uint8)
+    L[:, 1] = 1
+    L[::7, 2] = 1
+    check_layout(L)
+    check_layout(L.T.copy())
