@@ -69,6 +69,7 @@ def lib():
         "bsmm_updat": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
         "bsmm_identity_init": [vp, vp, i32, vp],
         "bsmm_debug_lut": [vp, i32, P64, i64, P64],
+        "bsmm_kernel_name": [vp, i32, i64, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
         "bsmm_profile_begin": [],
         "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
     }
@@ -157,6 +158,12 @@ def bsmm_workspace_size(h, pass_: int, N: int, dtype: torch.dtype) -> int:
     out = ctypes.c_size_t()
     _check(lib().bsmm_workspace_size(h, pass_, N, DTYPE_CODE[dtype], ctypes.byref(out)), "bsmm_workspace_size")
     return int(out.value)
+
+
+def bsmm_kernel_name(h, pass_: int, N: int, dtype: torch.dtype, group: int = 1) -> str:
+    out = ctypes.c_char_p()
+    _check(lib().bsmm_kernel_name(h, pass_, N, group, DTYPE_CODE[dtype], ctypes.byref(out)), "bsmm_kernel_name")
+    return out.value.decode()
 
 
 def bsmm_debug_lut(h, which: int) -> np.ndarray:
@@ -281,6 +288,10 @@ class BlocksparseMatMul:
 
     def block_coord(self, block: int):
         return bsmm_block_coord(self.handle, block)
+
+    def kernel_name(self, pass_: str, N: int, dtype: torch.dtype = torch.float32, group: int = 1) -> str:
+        """Kernel family `pass_` ("fprop", "bprop", "updat", "identity") launches at N."""
+        return bsmm_kernel_name(self.handle, PASS[pass_], N, dtype, group)
 
     def _N(self, t: torch.Tensor, feats: int, what: str) -> int:
         if t.dim() != 2:

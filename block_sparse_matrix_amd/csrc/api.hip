@@ -75,10 +75,11 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         return BSMM_OK;
     }
     const HostLut& L = h->lut;
-    constexpr int NP = 12;
-    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,  &L.colent,  &L.rowptr,
+    constexpr int NP = 16;
+    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,   &L.colent,  &L.rowptr,
                                              &L.rowent,   &L.colorder, &L.roworder, &L.colwork,
-                                             &L.rowwork,  &L.ugroups,  &L.colrec,   &L.rowrec};
+                                             &L.rowwork,  &L.ugroups,  &L.colrec,   &L.rowrec,
+                                             &L.cgptr,    &L.cgent,    &L.rgptr,    &L.rgent};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -112,10 +113,24 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
     d.ugroups = (const int32_t*)(b + off[9]);
     d.colrec = (const int32_t*)(b + off[10]);
     d.rowrec = (const int32_t*)(b + off[11]);
+    d.cgptr = (const int32_t*)(b + off[12]);
+    d.cgent = (const int32_t*)(b + off[13]);
+    d.rgptr = (const int32_t*)(b + off[14]);
+    d.rgent = (const int32_t*)(b + off[15]);
     d.nugroups = (int32_t)(L.ugroups.size() / 4);
     auto res = h->dev.emplace(dev, d);
     *out = &res.first->second;
     return BSMM_OK;
+}
+
+void set_groups(MMArgs& a, const std::vector<int32_t>& hptr, const int32_t* dptr, const int32_t* dent, int64_t nnz) {
+    a.ngroups = hptr.empty() ? 0 : (int32_t)hptr.size() - 1;
+    a.gptr = dptr;
+    a.gent = dent;
+    const int64_t entries = hptr.empty() ? 0 : hptr.back();
+    a.gfill = entries ? (int32_t)(100 * nnz / (entries * kGroupOut)) : 0;
+    a.gmax = 0;
+    for (size_t g = 0; g + 1 < hptr.size(); g++) a.gmax = std::max(a.gmax, hptr[g + 1] - hptr[g]);
 }
 
 bsmm_status check_call(bsmm_handle h, int64_t N, int dt) {
@@ -165,6 +180,60 @@ void prof_events(int pass, void** start, void** stop) {
     *stop = e1;
 }
 }  // namespace bsmm
+
+namespace {
+
+// Arguments of an fprop (transw false) or bprop launch; with d NULL only the fields
+// the kernel choice reads are meaningful.
+MMArgs mm_args(const HostLut& L, const DeviceLut* d, bool transw, int64_t N, int dt) {
+    MMArgs a{};
+    const bool bp = transw;
+    if (d) {
+        a.work = bp ? d->rowwork : d->colwork;
+        a.ptr = bp ? d->rowptr : d->colptr;
+        a.rec = bp ? d->rowrec : d->colrec;
+        a.ent = bp ? d->rowent : d->colent;
+    }
+    a.rsi = bp ? L.row_rsi : L.col_rsi;
+    set_groups(a, bp ? L.rgptr : L.cgptr, d ? (bp ? d->rgptr : d->cgptr) : nullptr,
+               d ? (bp ? d->rgent : d->cgent) : nullptr, L.nnz);
+    a.N = N;
+    a.fin = (int32_t)((bp ? L.S : L.R) * L.b);
+    a.fout = (int32_t)((bp ? L.R : L.S) * L.b);
+    a.nout = (int32_t)(bp ? L.R : L.S);
+    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+    a.in_bytes = bytes32((uint64_t)N * a.fin * es);
+    a.w_bytes = bytes32((uint64_t)L.nnz * L.b * L.b * es);
+    return a;
+}
+
+bsmm_status mm_pass(bsmm_handle h, const void* in, const void* w, void* out, int64_t N, bsmm_dtype dt,
+                    bool transw, void* stream) {
+    bsmm_status s = run_mm(h, in, w, out, N, dt, transw);
+    if (s != BSMM_OK || N == 0) return s;
+    const DeviceLut* d = nullptr;
+    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    const HostLut& L = h->lut;
+    MMArgs a = mm_args(L, d, transw, N, dt);
+    a.in = in;
+    a.w = w;
+    a.out = out;
+    const int pass = transw ? BSMM_PASS_BPROP : BSMM_PASS_FPROP;
+    hipError_t e = launch_mm(a, dt, L.b, L.fa, transw, stream, pass);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, transw ? "bprop launch" : "fprop launch");
+}
+
+UpArgs up_args(const HostLut& L, int64_t N, int group) {
+    UpArgs a{};
+    a.N = N;
+    a.C = (int32_t)(L.R * L.b);
+    a.K = (int32_t)(L.S * L.b);
+    a.nnz = (int32_t)L.nnz;
+    a.G = N > 0 ? group : 1;
+    return a;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -251,62 +320,39 @@ bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype d
     return BSMM_OK;
 }
 
+
 bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int64_t N, bsmm_dtype dt,
                        void* ws, size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
-    bsmm_status s = run_mm(h, x, w, y, N, dt, false);
-    if (s != BSMM_OK || N == 0) return s;
-    const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
-    const HostLut& L = h->lut;
-    MMArgs a{};
-    a.in = x;
-    a.w = w;
-    a.out = y;
-    a.work = d->colwork;
-    a.ptr = d->colptr;
-    a.rec = d->colrec;
-    a.rsi = L.col_rsi;
-    a.ent = d->colent;
-    a.N = N;
-    a.fin = (int32_t)(L.R * L.b);
-    a.fout = (int32_t)(L.S * L.b);
-    a.nout = (int32_t)L.S;
-    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
-    a.in_bytes = bytes32((uint64_t)N * a.fin * es);
-    a.w_bytes = bytes32((uint64_t)L.nnz * L.b * L.b * es);
-    hipError_t e = launch_mm(a, dt, L.b, L.fa, false, stream, BSMM_PASS_FPROP);
-    return e == hipSuccess ? BSMM_OK : dev_fail(e, "fprop launch");
+    return mm_pass(h, x, w, y, N, dt, false, stream);
 }
 
 bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, int64_t N, bsmm_dtype dt,
                        void* ws, size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
-    bsmm_status s = run_mm(h, dy, w, dx, N, dt, true);
-    if (s != BSMM_OK || N == 0) return s;
-    const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    return mm_pass(h, dy, w, dx, N, dt, true, stream);
+}
+
+bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm_dtype dt, const char** name) {
+    if (!h || !name) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    bsmm_status s = check_call(h, N, dt);
+    if (s != BSMM_OK) return s;
+    if (group < 1 || group > kMaxGroup) return fail(BSMM_ERR_INVALID_ARG, "group must be in [1, 8]");
     const HostLut& L = h->lut;
-    MMArgs a{};
-    a.in = dy;
-    a.w = w;
-    a.out = dx;
-    a.work = d->rowwork;
-    a.ptr = d->rowptr;
-    a.rec = d->rowrec;
-    a.rsi = L.row_rsi;
-    a.ent = d->rowent;
-    a.N = N;
-    a.fin = (int32_t)(L.S * L.b);
-    a.fout = (int32_t)(L.R * L.b);
-    a.nout = (int32_t)L.R;
-    const uint64_t es = dt == BSMM_F32 ? 4 : 2;
-    a.in_bytes = bytes32((uint64_t)N * a.fin * es);
-    a.w_bytes = bytes32((uint64_t)L.nnz * L.b * L.b * es);
-    hipError_t e = launch_mm(a, dt, L.b, L.fa, true, stream, BSMM_PASS_BPROP);
-    return e == hipSuccess ? BSMM_OK : dev_fail(e, "bprop launch");
+    *name = "none";
+    if (pass == BSMM_PASS_FPROP || pass == BSMM_PASS_BPROP) {
+        const bool tw = pass == BSMM_PASS_BPROP;
+        if (N > 0 && (tw ? L.R : L.S) > 0) *name = mm_kind_name(mm_kind(mm_args(L, nullptr, tw, N, dt), dt, L.b, L.fa));
+    } else if (pass == BSMM_PASS_UPDAT) {
+        if (L.nnz > 0) *name = updat_kind_name(updat_kind(up_args(L, N, group), dt));
+    } else if (pass == BSMM_PASS_IDENTITY) {
+        if (L.nnz > 0) *name = "identity";
+    } else {
+        return fail(BSMM_ERR_INVALID_ARG, "bad pass");
+    }
+    return BSMM_OK;
 }
 
 bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
@@ -334,18 +380,13 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
     }
     const DeviceLut* d = nullptr;
     if ((s = device_lut(h, &d)) != BSMM_OK) return s;
-    UpArgs a{};
+    UpArgs a = up_args(L, N, group);
     for (int t = 0; t < group; t++) {
         a.xs[t] = N > 0 ? xs[t] : nullptr;
         a.dys[t] = N > 0 ? dys[t] : nullptr;
     }
     a.dw = dw;
     a.coords = d->coords;
-    a.N = N;
-    a.C = (int32_t)(L.R * L.b);
-    a.K = (int32_t)(L.S * L.b);
-    a.nnz = (int32_t)L.nnz;
-    a.G = N > 0 ? group : 1;
     a.dwdt = dw_dt;
     const uint64_t es = dt == BSMM_F32 ? 4 : 2;
     a.x_bytes = (uint32_t)((uint64_t)N * a.C * es);
@@ -400,7 +441,11 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 9: v = &L.ugroups; break;
     case 10: v = &L.colrec; break;
     case 11: v = &L.rowrec; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 11]");
+    case 12: v = &L.cgptr; break;
+    case 13: v = &L.cgent; break;
+    case 14: v = &L.rgptr; break;
+    case 15: v = &L.rgent; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 15]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

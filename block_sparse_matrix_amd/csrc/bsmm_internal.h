@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "bsmm.h"
+#include "lut_format.h"
 
 namespace bsmm {
 
@@ -45,6 +46,13 @@ struct HostLut {
     // in id order: (first id, count, row, 0).
     std::vector<int32_t> ugroups;
     int32_t max_col = 0, max_row = 0;   // longest fprop / bprop list
+    // Output-block groups (32x32 blocks only): kGroupOut consecutive output blocks
+    // share one walk over the contraction blocks.  fprop: groups of block columns k,
+    // walking c ascending; bprop: groups of block rows c, walking k ascending.  Entry
+    // (kGroupInts int32): contraction block, mask of the group's blocks present there
+    // (bit j: output block kGroupOut*g + j), the ids of those blocks (0 where absent),
+    // 0, 0.  gptr holds groups+1 entry offsets.
+    std::vector<int32_t> cgptr, cgent, rgptr, rgent;
 };
 
 // Builds every table above.  Pure host code: never touches HIP.  Returns false with a
@@ -68,6 +76,10 @@ struct DeviceLut {
     int32_t nugroups = 0;
     const int32_t* colrec = nullptr;
     const int32_t* rowrec = nullptr;
+    const int32_t* cgptr = nullptr;
+    const int32_t* cgent = nullptr;
+    const int32_t* rgptr = nullptr;
+    const int32_t* rgent = nullptr;
 };
 
 }  // namespace bsmm

@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "lut_format.h"
+
 namespace bsmm {
 
 // fprop / bprop: out[:, o-block] = sum over list(o) of in[:, blk-block] . Wop.
@@ -23,6 +25,11 @@ struct MMArgs {
     int32_t ntiles;        // minibatch tiles (set by the launcher)
     uint32_t in_bytes;     // size of `in`, bytes (< 2^31)
     uint32_t w_bytes;      // size of `w`, bytes (< 2^31)
+    const int32_t* gptr;   // output-block groups (32x32 blocks): ngroups+1 offsets
+    const int32_t* gent;   // group entries, kGroupInts int32 each
+    int32_t ngroups;       // 0: no group table
+    int32_t gfill;         // blocks per group entry, percent of kGroupOut
+    int32_t gmax;          // most entries in one group
 };
 
 // Largest tensor the kernels address with 32-bit buffer offsets.
@@ -46,7 +53,17 @@ struct UpArgs {
     int32_t ngroups;
 };
 
+// Kernel choice of a pass for its arguments (the launchers use the same choice).
+enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2 };
+enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4 };
+int mm_kind(const MMArgs& a, int dt, int b, int fa);
+const char* mm_kind_name(int kind);
+int updat_kind(const UpArgs& a, int dt);
+const char* updat_kind_name(int kind);
+
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);
+// 32x32 blocks, 16-bit storage: output-block groups (a.gptr / a.gent / a.ngroups)
+hipError_t launch_mm_groups(const MMArgs& a, int dt, int fa, bool transw, void* stream, int pass);
 hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream);
 hipError_t launch_identity(void* w, const int32_t* coords, int64_t nnz, int b, int dt, void* stream);
 

@@ -118,6 +118,34 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
     };
     records(L.colorder, L.colptr, L.colent, L.max_col, L.colrec, L.col_rsi);
     records(L.roworder, L.rowptr, L.rowent, L.max_row, L.rowrec, L.row_rsi);
+    if (b == 32) {
+        // outer: the contraction index ascending; inner: its blocks, bucketed by group
+        auto groups = [](int64_t nouter, int64_t nout, const std::vector<int32_t>& ptr,
+                         const std::vector<int32_t>& ent, std::vector<int32_t>& gptr,
+                         std::vector<int32_t>& gent) {
+            const int64_t ng = (nout + kGroupOut - 1) / kGroupOut;
+            std::vector<std::vector<int32_t>> lists(ng);
+            for (int64_t u = 0; u < nouter; u++)
+                for (int32_t e = ptr[u]; e < ptr[u + 1]; e++) {
+                    const int32_t o = ent[2 * e], id = ent[2 * e + 1];
+                    std::vector<int32_t>& v = lists[o / kGroupOut];
+                    if (v.empty() || v[v.size() - kGroupInts] != (int32_t)u) v.resize(v.size() + kGroupInts, 0);
+                    int32_t* r = v.data() + v.size() - kGroupInts;
+                    r[0] = (int32_t)u;
+                    r[1] |= 1 << (o % kGroupOut);
+                    r[2 + o % kGroupOut] = id;
+                }
+            gptr.assign(ng + 1, 0);
+            gent.clear();
+            for (int64_t g = 0; g < ng; g++) {
+                gent.insert(gent.end(), lists[g].begin(), lists[g].end());
+                gptr[g + 1] = (int32_t)(gent.size() / kGroupInts);
+            }
+        };
+        // fprop groups: rows c outer, the row's blocks (k, id); bprop: columns outer
+        groups(R, S, L.rowptr, L.rowent, L.cgptr, L.cgent);
+        groups(S, R, L.colptr, L.colent, L.rgptr, L.rgent);
+    }
     out = std::move(L);
     return true;
 }

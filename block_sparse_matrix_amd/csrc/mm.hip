@@ -649,52 +649,89 @@ static int mm_variant() {
 }
 
 template <int DT, int B, int FA, bool TW>
-static hipError_t launch_mm_t(const MMArgs& a, hipStream_t st, int pass) {
+static hipError_t launch_mm_t(const MMArgs& a, int kind, hipStream_t st, int pass) {
     constexpr int DS = DT == BSMM_F32 ? 2 : 4;   // fp32 fragments take four loads each
-    switch (mm_variant()) {
-    case 1: return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
-    case 2: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
-    case 3: return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
-    case 4: return launch_large<DT, B, FA, TW, 1, 4>(a, st, pass);
-    case 5: return launch_large<DT, B, FA, TW, 2, 4>(a, st, pass);
-    case 6: return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
-    default: break;
+    switch (kind) {
+    case MM_N16: return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
+    case MM_N64: return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
+    case MM_MID: return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
+    case MM_STACK: return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
+    case MM_V_W16: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
+    case MM_V_STACK1: return launch_large<DT, B, FA, TW, 1, 4>(a, st, pass);
+    case MM_V_STACK2: return launch_large<DT, B, FA, TW, 2, 4>(a, st, pass);
     }
-    // Small minibatch: the weight stream dominates and there are few output tiles, so
-    // the 4 waves of a workgroup split each block list (measured fastest at N = 64 of
-    // the shapes above).
-    if (a.N <= 16) return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
-    if (a.N <= 64) return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
-    // Large minibatch (N >= 2048): weights staged once per workgroup, activations
-    // streamed, one minibatch tile per XCD at a time.  In between, 4 waves split 128
-    // rows and each walks the list (measured faster there).
-    if (a.N >= 2048) return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
-    return launch_cfg<DT, B, FA, TW, 2, 4, 1, 2>(a, st, pass);
+    return hipErrorInvalidValue;
 }
 
 template <int DT, bool TW>
-static hipError_t launch_mm_dt(const MMArgs& a, int b, int fa, hipStream_t st, int pass) {
+static hipError_t launch_mm_dt(const MMArgs& a, int kind, int b, int fa, hipStream_t st, int pass) {
     switch (b * 2 + fa) {
-    case 16: return launch_mm_t<DT, 8, 0, TW>(a, st, pass);
-    case 17: return launch_mm_t<DT, 8, 1, TW>(a, st, pass);
-    case 32: return launch_mm_t<DT, 16, 0, TW>(a, st, pass);
-    case 33: return launch_mm_t<DT, 16, 1, TW>(a, st, pass);
-    case 64: return launch_mm_t<DT, 32, 0, TW>(a, st, pass);
-    case 65: return launch_mm_t<DT, 32, 1, TW>(a, st, pass);
+    case 16: return launch_mm_t<DT, 8, 0, TW>(a, kind, st, pass);
+    case 17: return launch_mm_t<DT, 8, 1, TW>(a, kind, st, pass);
+    case 32: return launch_mm_t<DT, 16, 0, TW>(a, kind, st, pass);
+    case 33: return launch_mm_t<DT, 16, 1, TW>(a, kind, st, pass);
+    case 64: return launch_mm_t<DT, 32, 0, TW>(a, kind, st, pass);
+    case 65: return launch_mm_t<DT, 32, 1, TW>(a, kind, st, pass);
     }
     return hipErrorInvalidValue;
+}
+
+int mm_kind(const MMArgs& a, int dt, int b, int fa) {
+    // Output-block groups: 32x32 blocks, 16-bit storage, long minibatches (whole
+    // 8-row chunks when features lead), and groups dense enough that one activation
+    // slab feeds several blocks.
+    const bool groups_ok = b == 32 && dt != BSMM_F32 && a.ngroups > 0 && a.gmax <= kGroupMaxSteps &&
+                           (fa == 1 || a.N % 8 == 0);
+    switch (mm_variant()) {
+    case 1: return MM_N64;
+    case 2: return MM_V_W16;
+    case 3: return MM_MID;
+    case 4: return MM_V_STACK1;
+    case 5: return MM_V_STACK2;
+    case 6: return MM_STACK;
+    case 7:
+        if (groups_ok) return MM_GROUPS;
+        break;
+    default: break;
+    }
+    if (groups_ok && a.N >= 1024 && a.gfill >= 25) return MM_GROUPS;
+    // Small minibatch: the weight stream dominates and there are few output tiles, so
+    // the 4 waves of a workgroup split each block list (measured fastest at N = 64).
+    if (a.N <= 16) return MM_N16;
+    if (a.N <= 64) return MM_N64;
+    // Large minibatch (N >= 2048): weights staged once per workgroup, activations
+    // streamed, one minibatch tile per XCD at a time.  In between, 4 waves split 128
+    // rows and each walks the list (measured faster there).
+    if (a.N >= 2048) return MM_STACK;
+    return MM_MID;
+}
+
+const char* mm_kind_name(int kind) {
+    switch (kind) {
+    case MM_N16: return "list_n16";
+    case MM_N64: return "list_n64";
+    case MM_MID: return "list_rows128";
+    case MM_STACK: return "list_weight_stack";
+    case MM_GROUPS: return "output_groups";
+    case MM_V_W16: return "list_n64_16waves";
+    case MM_V_STACK1: return "list_weight_stack_64";
+    case MM_V_STACK2: return "list_weight_stack_128";
+    }
+    return "none";
 }
 
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass) {
     hipStream_t st = (hipStream_t)stream;
     if (a.nout == 0) return hipSuccess;
+    const int kind = mm_kind(a, dt, b, fa);
+    if (kind == MM_GROUPS) return launch_mm_groups(a, dt, fa, transw, stream, pass);
     switch (dt * 2 + (transw ? 1 : 0)) {
-    case 0: return launch_mm_dt<BSMM_F32, false>(a, b, fa, st, pass);
-    case 1: return launch_mm_dt<BSMM_F32, true>(a, b, fa, st, pass);
-    case 2: return launch_mm_dt<BSMM_BF16, false>(a, b, fa, st, pass);
-    case 3: return launch_mm_dt<BSMM_BF16, true>(a, b, fa, st, pass);
-    case 4: return launch_mm_dt<BSMM_F16, false>(a, b, fa, st, pass);
-    case 5: return launch_mm_dt<BSMM_F16, true>(a, b, fa, st, pass);
+    case 0: return launch_mm_dt<BSMM_F32, false>(a, kind, b, fa, st, pass);
+    case 1: return launch_mm_dt<BSMM_F32, true>(a, kind, b, fa, st, pass);
+    case 2: return launch_mm_dt<BSMM_BF16, false>(a, kind, b, fa, st, pass);
+    case 3: return launch_mm_dt<BSMM_BF16, true>(a, kind, b, fa, st, pass);
+    case 4: return launch_mm_dt<BSMM_F16, false>(a, kind, b, fa, st, pass);
+    case 5: return launch_mm_dt<BSMM_F16, true>(a, kind, b, fa, st, pass);
     }
     return hipErrorInvalidValue;
 }

@@ -479,38 +479,66 @@ static hipError_t launch_updat_cfg(UpArgs a, int bpw, hipStream_t st) {
 }
 
 template <int DT, int B, int FA>
-static hipError_t launch_updat_t(const UpArgs& a, hipStream_t st) {
+static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
+    switch (kind) {
+    case UP_D2B1: return launch_updat_cfg<DT, B, FA, 2>(a, 1, st);
+    case UP_D4B1: return launch_updat_cfg<DT, B, FA, 4>(a, 1, st);
+    case UP_D2B2: return launch_updat_cfg<DT, B, FA, 2>(a, 2, st);
+    case UP_ROWS: return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.groups, a.ngroups, st);
+    case UP_D2B4: return launch_updat_cfg<DT, B, FA, 2>(a, 4, st);
+    case UP_D1B2: return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
+    case UP_D2B8: return launch_updat_cfg<DT, B, FA, 2>(a, 8, st);
+    case UP_D1B4: return launch_updat_cfg<DT, B, FA, 1>(a, 4, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int updat_kind(const UpArgs& a, int dt) {
     switch (updat_variant()) {
-    case 1: return launch_updat_cfg<DT, B, FA, 2>(a, 1, st);
-    case 2: return launch_updat_cfg<DT, B, FA, 4>(a, 1, st);
-    case 3: return launch_updat_cfg<DT, B, FA, 2>(a, 2, st);
-    case 4: return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.groups, a.ngroups, st);
-    case 5: return launch_updat_cfg<DT, B, FA, 2>(a, 4, st);
-    case 6: return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
-    case 7: return launch_updat_cfg<DT, B, FA, 2>(a, 8, st);
-    case 8: return launch_updat_cfg<DT, B, FA, 1>(a, 4, st);
+    case 1: return UP_D2B1;
+    case 2: return UP_D4B1;
+    case 3: return UP_D2B2;
+    case 4: return UP_ROWS;
+    case 5: return UP_D2B4;
+    case 6: return UP_D1B2;
+    case 7: return UP_D2B8;
+    case 8: return UP_D1B4;
     default: break;
     }
-    constexpr int KS = 4 * Elt<DT>::VEC;
+    const int KS = dt == BSMM_F32 ? 16 : 32;
     const int64_t steps = (int64_t)a.G * ((a.N + KS - 1) / KS);
     // Long contractions: row groups, 4 waves per block group.
-    if (steps >= 16) return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.groups, a.ngroups, st);
+    if (steps >= 16) return UP_ROWS;
     // Short ones: a wave takes one or two blocks (two once there are enough blocks for
     // >= 2 waves per SIMD), loads, contracts, stores and exits; with two blocks a wave
     // keeps no ring (measured best: waves, not the ring, hide the latency here).
-    if ((int64_t)a.nnz / 2 >= 2048) return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
-    return launch_updat_cfg<DT, B, FA, 2>(a, 1, st);
+    if ((int64_t)a.nnz / 2 >= 2048) return UP_D1B2;
+    return UP_D2B1;
+}
+
+const char* updat_kind_name(int kind) {
+    switch (kind) {
+    case UP_D2B1: return "blocks_1perwave";
+    case UP_D1B2: return "blocks_2perwave";
+    case UP_ROWS: return "row_groups";
+    case UP_D4B1: return "blocks_1perwave_ring4";
+    case UP_D2B2: return "blocks_2perwave_ring2";
+    case UP_D2B4: return "blocks_4perwave";
+    case UP_D2B8: return "blocks_8perwave";
+    case UP_D1B4: return "blocks_4perwave_noring";
+    }
+    return "none";
 }
 
 template <int DT>
-static hipError_t launch_updat_dt(const UpArgs& a, int b, int fa, hipStream_t st) {
+static hipError_t launch_updat_dt(const UpArgs& a, int kind, int b, int fa, hipStream_t st) {
     switch (b * 2 + fa) {
-    case 16: return launch_updat_t<DT, 8, 0>(a, st);
-    case 17: return launch_updat_t<DT, 8, 1>(a, st);
-    case 32: return launch_updat_t<DT, 16, 0>(a, st);
-    case 33: return launch_updat_t<DT, 16, 1>(a, st);
-    case 64: return launch_updat_t<DT, 32, 0>(a, st);
-    case 65: return launch_updat_t<DT, 32, 1>(a, st);
+    case 16: return launch_updat_t<DT, 8, 0>(a, kind, st);
+    case 17: return launch_updat_t<DT, 8, 1>(a, kind, st);
+    case 32: return launch_updat_t<DT, 16, 0>(a, kind, st);
+    case 33: return launch_updat_t<DT, 16, 1>(a, kind, st);
+    case 64: return launch_updat_t<DT, 32, 0>(a, kind, st);
+    case 65: return launch_updat_t<DT, 32, 1>(a, kind, st);
     }
     return hipErrorInvalidValue;
 }
@@ -518,10 +546,11 @@ static hipError_t launch_updat_dt(const UpArgs& a, int b, int fa, hipStream_t st
 hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     if (a.nnz == 0) return hipSuccess;
+    const int kind = updat_kind(a, dt);
     switch (dt) {
-    case BSMM_F32: return launch_updat_dt<BSMM_F32>(a, b, fa, st);
-    case BSMM_BF16: return launch_updat_dt<BSMM_BF16>(a, b, fa, st);
-    case BSMM_F16: return launch_updat_dt<BSMM_F16>(a, b, fa, st);
+    case BSMM_F32: return launch_updat_dt<BSMM_F32>(a, kind, b, fa, st);
+    case BSMM_BF16: return launch_updat_dt<BSMM_BF16>(a, kind, b, fa, st);
+    case BSMM_F16: return launch_updat_dt<BSMM_F16>(a, kind, b, fa, st);
     }
     return hipErrorInvalidValue;
 }

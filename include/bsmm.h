@@ -146,6 +146,13 @@ BSMM_API const char* bsmm_status_string(bsmm_status s);
 /* Text of the last error raised on the calling thread ("" if none). */
 BSMM_API const char* bsmm_last_error(void);
 
+/* Name of the kernel family a pass would launch for these arguments (host only, no
+ * GPU needed; the launch uses the same choice).  *name is a static string: "none" when
+ * the call would launch nothing (N = 0, no blocks).  pass is a bsmm_pass value; group
+ * is the updat group count (1..8; ignored by the other passes). */
+BSMM_API bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm_dtype dt,
+                                      const char** name);
+
 /* Layout compiler output, for inspection and tests (host only, no GPU needed).
  *   which: 0 coords   (2*nnz:   c, k of every id, in id order)
  *          1 colptr   (S+1:     fprop segment starts, one per output block k)
@@ -163,6 +170,13 @@ BSMM_API const char* bsmm_last_error(void);
  *                     padded; stride = 4 + 2*r, r = min(longest list, 1024) rounded
  *                     up to even, at least 2)
  *         11 rowrec   (the same for the bprop lists)
+ *         12 cgptr    (block size 32 only, else empty: ceil(S/8)+1 offsets into cgent)
+ *         13 cgent    (12 per entry: groups of 8 consecutive block columns; per group,
+ *                     for every layout row c holding one of its blocks, ascending c:
+ *                     c, mask (bit j: block (c, 8g+j) present), the 8 ids (0 where
+ *                     absent), 0, 0)
+ *         14 rgptr    (block size 32 only: ceil(R/8)+1 offsets into rgent)
+ *         15 rgent    (the same for groups of 8 block rows, walking k ascending)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);

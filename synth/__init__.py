@@ -7,7 +7,7 @@ the CPU oracle (through the tests) and the HIP path consume what it produces.
 The workloads follow the kiteco/blocksparse README, section "Usage": a square
 hidden size, a block size from {8, 16, 32} ("API Documentation" ›
 blocksparse.matmul › BlocksparseMatMul.__init__), a random 0/1 block layout and a
-minibatch of activations.  Five named workloads are defined (WORKLOADS); any other
+minibatch of activations.  Six named workloads are defined (WORKLOADS); any other
 shape can be drawn with `random_problem`.
 
 Recipe (fixed so that every run and every consumer sees the same bits):
@@ -53,6 +53,10 @@ WORKLOADS = {
                                     "bern0.1_diag", 0.02, 1003),
     "hidden8192_b32_n4096_g8": Workload("hidden8192_b32_n4096_g8", 8192, 32, 4096, 1, ("bf16",), 8,
                                         "band_random3pct", 0.02, 1004),
+    # Supplementary: the same dimensions at half density, so that the contraction (not
+    # the activation stream) bounds every pass; large-N dense-block matrix-core shape.
+    "hidden8192_b32_n4096_dense50": Workload("hidden8192_b32_n4096_dense50", 8192, 32, 4096, 1,
+                                             ("bf16",), 1, "bern0.5_diag", 0.02, 1005),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -73,8 +77,8 @@ def make_layout(kind: str, R: int, S: int, rng: np.random.Generator) -> np.ndarr
             if not L[:, k].any():
                 L[rng.integers(R), k] = 1
         return L
-    if kind == "bern0.1_diag":
-        L = (rng.random((R, S)) < 0.1)
+    if kind.startswith("bern") and kind.endswith("_diag"):
+        L = (rng.random((R, S)) < float(kind[4:-5]))
         d = min(R, S)
         L[np.arange(d), np.arange(d)] = True
         return L.astype(np.uint8)

@@ -130,3 +130,23 @@ def test_no_cpu_path():
     w = torch.zeros(1, 8, 8)
     with pytest.raises(ValueError):
         m.fprop(x, w)
+
+
+def test_kernel_choice_names():
+    import torch
+    rng = np.random.default_rng(0)
+    L = (rng.random((16, 16)) < 0.5).astype(np.uint8)
+    m32 = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    m8 = bs.BlocksparseMatMul(L, block_size=8, feature_axis=0)
+    assert m32.kernel_name("fprop", 64, torch.bfloat16) == "list_n64"
+    assert m32.kernel_name("fprop", 4096, torch.bfloat16) == "output_groups"
+    assert m32.kernel_name("bprop", 4096, torch.float16) == "output_groups"
+    assert m32.kernel_name("fprop", 4096, torch.float32) == "list_weight_stack"
+    assert m8.kernel_name("fprop", 4096, torch.bfloat16) == "list_weight_stack"
+    assert m8.kernel_name("fprop", 512, torch.bfloat16) == "list_rows128"
+    assert m32.kernel_name("fprop", 0, torch.bfloat16) == "none"
+    assert m32.kernel_name("updat", 64, torch.bfloat16) in ("blocks_1perwave", "blocks_2perwave")
+    assert m32.kernel_name("updat", 4096, torch.bfloat16, group=8) == "row_groups"
+    assert m32.kernel_name("identity", 0, torch.bfloat16) == "identity"
+    with pytest.raises(bs.BsmmError):
+        m32.kernel_name("updat", 64, torch.bfloat16, group=9)

@@ -217,3 +217,32 @@ def test_lists_longer_than_one_chunk(b, fa, dtype, N):
     assert_close(y, ry, dtype, "fprop")
     assert_close(dx, rdx, dtype, "bprop")
     assert_close(dw, rdw, dtype, "updat")
+
+
+@pytest.mark.parametrize("N", [1024, 1032, 1100, 2048])
+@pytest.mark.parametrize("fa", [1, 0])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_output_groups(N, fa, dtype):
+    """The output-group kernel (32x32 blocks, long minibatch): a ragged last tile, an
+    output group with no block at all, a partial last group, an empty row and column."""
+    if fa == 0 and N % 8:
+        pytest.skip("features-first activations take the group kernel only for N % 8 == 0")
+    print(f"case groups N={N} fa={fa} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(N + fa)
+    L = (rng.random((12, 20)) < 0.5).astype(np.uint8)
+    L[0, :] = 0
+    L[:, 19] = 0
+    L[:, 8:16] = 0
+    L[3, 2] = 1
+    P = synth.random_problem(rng, L, 32, N, fa, dtype, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
+    for p in ("fprop", "bprop"):
+        assert m.kernel_name(p, N, TORCH_DT[dtype]) == "output_groups"
+    y, dx, dw = _run_all(P, dtype)
+    ry, rdx, rdw = _oracle_all(P, dtype)
+    assert_close(y, ry, dtype, "fprop")
+    assert_close(dx, rdx, dtype, "bprop")
+    assert_close(dw, rdw, dtype, "updat")
+    Kb = 32
+    ycols = y[:, 8 * Kb:16 * Kb] if fa == 1 else y[8 * Kb:16 * Kb, :]
+    assert torch.count_nonzero(ycols) == 0

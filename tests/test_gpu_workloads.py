@@ -1,4 +1,4 @@
-"""The five named workloads at full size, launched exactly as bench.py launches them,
+"""The named workloads (the five configurations plus a supplementary half-dense one) at full size, launched exactly as bench.py launches them,
 checked against the oracle on sampled outputs (GPU; calls through the C ABI).
 
 Sampling: fprop/bprop outputs for a few minibatch rows (the oracle runs on those

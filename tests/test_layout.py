@@ -72,6 +72,54 @@ def check_layout(L, b=8, fa=1):
             assert np.all(inline[n:] == 0)
 
 
+def check_groups(L, m):
+    """Output-block groups of 8 (block size 32): every present block appears exactly
+    once, under its contraction index, with its id; contraction indices ascend."""
+    h = m.handle
+    R, S = L.shape
+    cs, ks = np.nonzero(L)
+    id_of = -np.ones((R, S), dtype=np.int64)
+    id_of[cs, ks] = np.arange(len(cs))
+    for pw, ew, Lo in ((12, 13, L), (14, 15, L.T)):   # fprop: (c, k); bprop: (k, c)
+        gptr = bs.bsmm_debug_lut(h, pw)
+        gent = bs.bsmm_debug_lut(h, ew).reshape(-1, 12)
+        nout = Lo.shape[1]
+        assert len(gptr) == (nout + 7) // 8 + 1 and gptr[0] == 0 and gptr[-1] == len(gent)
+        seen = np.zeros(L.shape, dtype=int)
+        for g in range(len(gptr) - 1):
+            ent = gent[gptr[g]:gptr[g + 1]]
+            assert np.all(np.diff(ent[:, 0]) > 0)
+            blk = Lo[:, 8 * g:8 * g + 8]
+            assert np.array_equal(ent[:, 0], np.flatnonzero(blk.any(1)))
+            for u, mask, *rest in ent:
+                ids = rest[:8]
+                for j in range(8):
+                    o = 8 * g + j
+                    present = o < nout and Lo[u, o] == 1
+                    assert bool(mask >> j & 1) == present
+                    if present:
+                        ref = id_of[u, o] if pw == 12 else id_of[o, u]
+                        assert ids[j] == ref
+                        if pw == 12:
+                            seen[u, o] += 1
+                        else:
+                            seen[o, u] += 1
+                    else:
+                        assert ids[j] == 0
+                assert rest[8] == 0 and rest[9] == 0
+        assert np.array_equal(seen, L.astype(int))
+
+
+def test_groups_of_32_blocks():
+    rng = np.random.default_rng(5)
+    for R, S, p in [(5, 40, 0.5), (17, 9, 0.3), (1, 1, 1.0), (6, 6, 0.0), (33, 64, 0.05)]:
+        L = (rng.random((R, S)) < p).astype(np.uint8)
+        check_groups(L, bs.BlocksparseMatMul(L, block_size=32))
+    for b in (8, 16):   # only built for block size 32
+        m = bs.BlocksparseMatMul(np.ones((3, 3), np.uint8), block_size=b)
+        assert all(len(bs.bsmm_debug_lut(m.handle, w)) == 0 for w in (12, 13, 14, 15))
+
+
 def test_every_tiny_layout():
     for R, S in [(1, 1), (1, 2), (2, 1), (2, 2), (2, 3), (3, 2), (3, 3)]:
         for bits in itertools.product([0, 1], repeat=R * S):
