@@ -86,15 +86,23 @@ def roof(flops, nbytes, dtype):
     return ("mfma", t_mfma) if t_mfma >= t_hbm else ("hbm", t_hbm)
 
 
-def kernel_sources_sha256():
-    """Hash of the device sources (csrc/*.hip, csrc/*.h), to tell whether a stored
-    counter reading still describes the kernels that run."""
+# Sources that decide what a pass's kernels do (kernel code, shared device headers,
+# argument set-up and layout tables).  A stored counter reading is used only while the
+# hash of these files matches the one recorded with it.
+KERNEL_SOURCES = {
+    "fprop": ["mm.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
+    "bprop": ["mm.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
+    "updat": ["updat.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
+}
+
+
+def kernel_sources_sha256(kernel_key):
+    """Hash of the sources behind one pass's kernels (KERNEL_SOURCES)."""
     d = os.path.join(ROOT, "block_sparse_matrix_amd", "csrc")
     h = hashlib.sha256()
-    for fn in sorted(os.listdir(d)):
-        if fn.endswith((".hip", ".h")):
-            h.update(fn.encode())
-            h.update(open(os.path.join(d, fn), "rb").read())
+    for fn in KERNEL_SOURCES[kernel_key]:
+        h.update(fn.encode())
+        h.update(open(os.path.join(d, fn), "rb").read())
     return h.hexdigest()
 
 
@@ -109,7 +117,7 @@ def traffic_record(kernel_key, workload, dtype):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256(kernel_key):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
