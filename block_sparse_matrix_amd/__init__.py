@@ -70,6 +70,7 @@ def lib():
         "bsmm_identity_init": [vp, vp, i32, vp],
         "bsmm_debug_lut": [vp, i32, P64, i64, P64],
         "bsmm_kernel_name": [vp, i32, i64, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
+        "bsmm_force_kernel": [vp, i32, ctypes.c_char_p],
         "bsmm_profile_begin": [],
         "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
     }
@@ -164,6 +165,10 @@ def bsmm_kernel_name(h, pass_: int, N: int, dtype: torch.dtype, group: int = 1) 
     out = ctypes.c_char_p()
     _check(lib().bsmm_kernel_name(h, pass_, N, group, DTYPE_CODE[dtype], ctypes.byref(out)), "bsmm_kernel_name")
     return out.value.decode()
+
+
+def bsmm_force_kernel(h, pass_: int, name: Optional[str]) -> None:
+    _check(lib().bsmm_force_kernel(h, pass_, name.encode() if name else None), "bsmm_force_kernel")
 
 
 def bsmm_debug_lut(h, which: int) -> np.ndarray:
@@ -292,6 +297,10 @@ class BlocksparseMatMul:
     def kernel_name(self, pass_: str, N: int, dtype: torch.dtype = torch.float32, group: int = 1) -> str:
         """Kernel family `pass_` ("fprop", "bprop", "updat", "identity") launches at N."""
         return bsmm_kernel_name(self.handle, PASS[pass_], N, dtype, group)
+
+    def force_kernel(self, pass_: str, name: Optional[str]) -> None:
+        """Testing and tuning: launch the named kernel family for `pass_` (None: automatic)."""
+        bsmm_force_kernel(self.handle, PASS[pass_], name)
 
     def _N(self, t: torch.Tensor, feats: int, what: str) -> int:
         if t.dim() != 2:

@@ -75,11 +75,11 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         return BSMM_OK;
     }
     const HostLut& L = h->lut;
-    constexpr int NP = 16;
-    const std::vector<int32_t>* parts[NP] = {&L.coords,   &L.colptr,   &L.colent,  &L.rowptr,
-                                             &L.rowent,   &L.colorder, &L.roworder, &L.colwork,
-                                             &L.rowwork,  &L.ugroups,  &L.colrec,   &L.rowrec,
-                                             &L.cgptr,    &L.cgent,    &L.rgptr,    &L.rgent};
+    constexpr int NP = 20;
+    const std::vector<int32_t>* parts[NP] = {&L.coords,  &L.colptr,   &L.colent,   &L.rowptr,  &L.rowent,
+                                             &L.colorder, &L.roworder, &L.colwork, &L.rowwork, &L.ugroups,
+                                             &L.colrec,  &L.rowrec,   &L.cgptr,    &L.cgent,   &L.rgptr,
+                                             &L.rgent,   &L.utiles,   &L.utblk,    &L.urest,   &L.urids};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -117,6 +117,12 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
     d.cgent = (const int32_t*)(b + off[13]);
     d.rgptr = (const int32_t*)(b + off[14]);
     d.rgent = (const int32_t*)(b + off[15]);
+    d.utiles = (const int32_t*)(b + off[16]);
+    d.utblk = (const int32_t*)(b + off[17]);
+    d.urest = (const int32_t*)(b + off[18]);
+    d.urids = (const int32_t*)(b + off[19]);
+    d.nutiles = (int32_t)(L.utiles.size() / 4);
+    d.nurest = (int32_t)(L.urest.size() / 4);
     d.nugroups = (int32_t)(L.ugroups.size() / 4);
     auto res = h->dev.emplace(dev, d);
     *out = &res.first->second;
@@ -219,12 +225,17 @@ bsmm_status mm_pass(bsmm_handle h, const void* in, const void* w, void* out, int
     a.w = w;
     a.out = out;
     const int pass = transw ? BSMM_PASS_BPROP : BSMM_PASS_FPROP;
+    a.force = h->force[pass];
+    if (mm_kind(a, dt, L.b, L.fa) < 0)
+        return fail(BSMM_ERR_UNSUPPORTED, "the forced kernel does not apply to these arguments");
     hipError_t e = launch_mm(a, dt, L.b, L.fa, transw, stream, pass);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, transw ? "bprop launch" : "fprop launch");
 }
 
 UpArgs up_args(const HostLut& L, int64_t N, int group) {
     UpArgs a{};
+    a.ntiles = (int32_t)(L.utiles.size() / 4);
+    a.nrest = (int32_t)(L.urest.size() / 4);
     a.N = N;
     a.C = (int32_t)(L.R * L.b);
     a.K = (int32_t)(L.S * L.b);
@@ -344,9 +355,13 @@ bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm
     *name = "none";
     if (pass == BSMM_PASS_FPROP || pass == BSMM_PASS_BPROP) {
         const bool tw = pass == BSMM_PASS_BPROP;
-        if (N > 0 && (tw ? L.R : L.S) > 0) *name = mm_kind_name(mm_kind(mm_args(L, nullptr, tw, N, dt), dt, L.b, L.fa));
+        MMArgs a = mm_args(L, nullptr, tw, N, dt);
+        a.force = h->force[pass];
+        if (N > 0 && (tw ? L.R : L.S) > 0) *name = mm_kind_name(mm_kind(a, dt, L.b, L.fa));
     } else if (pass == BSMM_PASS_UPDAT) {
-        if (L.nnz > 0) *name = updat_kind_name(updat_kind(up_args(L, N, group), dt));
+        UpArgs a = up_args(L, N, group);
+        a.force = h->force[BSMM_PASS_UPDAT];
+        if (L.nnz > 0) *name = updat_kind_name(updat_kind(a, dt, L.b, L.fa));
     } else if (pass == BSMM_PASS_IDENTITY) {
         if (L.nnz > 0) *name = "identity";
     } else {
@@ -392,7 +407,16 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
     a.x_bytes = (uint32_t)((uint64_t)N * a.C * es);
     a.groups = d->ugroups;
     a.ngroups = d->nugroups;
+    a.tiles = d->utiles;
+    a.tblk = d->utblk;
+    a.ntiles = d->nutiles;
+    a.rest = d->urest;
+    a.rids = d->urids;
+    a.nrest = d->nurest;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
+    a.force = h->force[BSMM_PASS_UPDAT];
+    if (updat_kind(a, dt, L.b, L.fa) < 0)
+        return fail(BSMM_ERR_UNSUPPORTED, "the forced kernel does not apply to these arguments");
     hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "updat launch");
 }
@@ -424,6 +448,19 @@ const char* bsmm_status_string(bsmm_status s) {
 
 const char* bsmm_last_error(void) { return g_err.c_str(); }
 
+bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (pass < BSMM_PASS_FPROP || pass > BSMM_PASS_UPDAT) return fail(BSMM_ERR_INVALID_ARG, "pass must be fprop, bprop or updat");
+    if (!name || !*name) {
+        h->force[pass] = 0;
+        return BSMM_OK;
+    }
+    const int k = pass == BSMM_PASS_UPDAT ? updat_kind_of_name(name) : mm_kind_of_name(name);
+    if (k == 0) return fail(BSMM_ERR_INVALID_ARG, std::string("unknown kernel name for this pass: ") + name);
+    h->force[pass] = k;
+    return BSMM_OK;
+}
+
 bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len) {
     if (!h || !len || cap < 0 || (cap > 0 && !out)) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
     const HostLut& L = h->lut;
@@ -445,7 +482,11 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 13: v = &L.cgent; break;
     case 14: v = &L.rgptr; break;
     case 15: v = &L.rgent; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 15]");
+    case 16: v = &L.utiles; break;
+    case 17: v = &L.utblk; break;
+    case 18: v = &L.urest; break;
+    case 19: v = &L.urids; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 19]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

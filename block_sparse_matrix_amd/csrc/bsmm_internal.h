@@ -53,6 +53,12 @@ struct HostLut {
     // (bit j: output block kGroupOut*g + j), the ids of those blocks (0 where absent),
     // 0, 0.  gptr holds groups+1 entry offsets.
     std::vector<int32_t> cgptr, cgent, rgptr, rgent;
+    // Weight-gradient tiles (32x32 blocks only): utiles (r0, c0, blocks, first) per
+    // tile with at least kTileMin blocks, row-major tile order; utblk (row in tile,
+    // column in tile, id, 0) per block of those tiles, row-major within a tile; the
+    // other blocks in urest row groups (first, count, row, 1), whose ids are
+    // urids[first .. first+count-1].
+    std::vector<int32_t> utiles, utblk, urest, urids;
 };
 
 // Builds every table above.  Pure host code: never touches HIP.  Returns false with a
@@ -80,12 +86,18 @@ struct DeviceLut {
     const int32_t* cgent = nullptr;
     const int32_t* rgptr = nullptr;
     const int32_t* rgent = nullptr;
+    const int32_t* utiles = nullptr;
+    const int32_t* utblk = nullptr;
+    const int32_t* urest = nullptr;
+    const int32_t* urids = nullptr;
+    int32_t nutiles = 0, nurest = 0;
 };
 
 }  // namespace bsmm
 
 struct bsmm_plan {
     bsmm::HostLut lut;
+    int force[3] = {0, 0, 0};   // forced kernel kind per pass (fprop, bprop, updat), 0 = automatic
     std::mutex mu;
     std::map<int, bsmm::DeviceLut> dev;   // per HIP device ordinal
 };

@@ -193,6 +193,16 @@ __device__ __forceinline__ void wg_decode(int bid, int nlist, int ntiles, int& l
     if (li >= nlist) li = -1;
 }
 
+// Launch on `st` with explicit timing events (either may be null).
+template <typename K, typename... Args>
+static hipError_t launch_ev(K kernel, dim3 grid, dim3 block, hipStream_t st, void* e0, void* e1, Args... args) {
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, (hipEvent_t)e0, (hipEvent_t)e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    return hipGetLastError();
+}
+
 // Launch on `st`; when kernel timing is active the dispatch records start/stop events.
 template <typename K, typename... Args>
 static hipError_t launch(int pass, K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {

@@ -30,6 +30,7 @@ struct MMArgs {
     int32_t ngroups;       // 0: no group table
     int32_t gfill;         // blocks per group entry, percent of kGroupOut
     int32_t gmax;          // most entries in one group
+    int32_t force;         // MMKind to use (0: automatic)
 };
 
 // Largest tensor the kernels address with 32-bit buffer offsets.
@@ -51,15 +52,28 @@ struct UpArgs {
     int32_t bpw;            // blocks per wave (set by the launcher)
     const int32_t* groups;  // row groups of <= 8 consecutive ids: (first id, count, row, 0)
     int32_t ngroups;
+    // 32x32 blocks: dense tiles (r0, c0, blocks, first) with their blocks (row, column in
+    // the tile, id, 0), and the remaining blocks in row groups (first, count, row, 1)
+    // whose ids are rids[first ..]
+    const int32_t* tiles;
+    const int32_t* tblk;
+    int32_t ntiles;
+    const int32_t* rest;
+    const int32_t* rids;
+    int32_t nrest;
+    int32_t force;          // UpKind to use (0: automatic)
 };
 
-// Kernel choice of a pass for its arguments (the launchers use the same choice).
+// Kernel choice of a pass for its arguments (the launchers use the same choice).  A
+// forced kind that cannot serve the arguments gives -1.
 enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2 };
-enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4 };
+enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES };
 int mm_kind(const MMArgs& a, int dt, int b, int fa);
 const char* mm_kind_name(int kind);
-int updat_kind(const UpArgs& a, int dt);
+int updat_kind(const UpArgs& a, int dt, int b, int fa);
 const char* updat_kind_name(int kind);
+int mm_kind_of_name(const char* name);      // 0 if unknown
+int updat_kind_of_name(const char* name);
 
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);
 // 32x32 blocks, 16-bit storage: output-block groups (a.gptr / a.gent / a.ngroups)

@@ -145,6 +145,35 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
         // fprop groups: rows c outer, the row's blocks (k, id); bprop: columns outer
         groups(R, S, L.rowptr, L.rowent, L.cgptr, L.cgent);
         groups(S, R, L.colptr, L.colent, L.rgptr, L.rgent);
+        // weight-gradient tiles; ids of a tile row are consecutive in row-major order
+        const int64_t TR = (R + kTileSide - 1) / kTileSide, TC = (S + kTileSide - 1) / kTileSide;
+        std::vector<uint8_t> in_tile(nnz, 0);
+        for (int64_t tr = 0; tr < TR; tr++)
+            for (int64_t tc = 0; tc < TC; tc++) {
+                std::vector<int32_t> blk;
+                for (int64_t c = tr * kTileSide; c < std::min<int64_t>(R, (tr + 1) * kTileSide); c++)
+                    for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++) {
+                        const int32_t k = L.rowent[2 * e];
+                        if (k / kTileSide == tc)
+                            blk.insert(blk.end(), {(int32_t)(c - tr * kTileSide), k % kTileSide, L.rowent[2 * e + 1], 0});
+                    }
+                if ((int64_t)blk.size() / 4 < kTileMin) continue;
+                L.utiles.insert(L.utiles.end(), {(int32_t)(tr * kTileSide), (int32_t)(tc * kTileSide),
+                                                 (int32_t)(blk.size() / 4), (int32_t)(L.utblk.size() / 4)});
+                for (size_t i = 0; i < blk.size(); i += 4) in_tile[blk[i + 2]] = 1;
+                L.utblk.insert(L.utblk.end(), blk.begin(), blk.end());
+            }
+        for (int64_t c = 0; c < R; c++) {
+            int32_t n = 0;
+            for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++) {
+                const int32_t id = L.rowent[2 * e + 1];
+                if (in_tile[id]) continue;
+                if (n == 0) L.urest.insert(L.urest.end(), {(int32_t)L.urids.size(), 0, (int32_t)c, 1});
+                L.urids.push_back(id);
+                L.urest[L.urest.size() - 3]++;
+                n = n == 7 ? 0 : n + 1;
+            }
+        }
     }
     out = std::move(L);
     return true;

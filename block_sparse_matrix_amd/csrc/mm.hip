@@ -28,6 +28,8 @@
 // one row of the stored layout and writes them with one vector store.
 #include <cstdlib>
 
+#include <cstring>
+
 #include "common.h"
 
 namespace bsmm {
@@ -682,6 +684,7 @@ int mm_kind(const MMArgs& a, int dt, int b, int fa) {
     // slab feeds several blocks.
     const bool groups_ok = b == 32 && dt != BSMM_F32 && a.ngroups > 0 && a.gmax <= kGroupMaxSteps &&
                            (fa == 1 || a.N % 8 == 0);
+    if (a.force > 0) return a.force == MM_GROUPS && !groups_ok ? -1 : a.force;
     switch (mm_variant()) {
     case 1: return MM_N64;
     case 2: return MM_V_W16;
@@ -720,10 +723,17 @@ const char* mm_kind_name(int kind) {
     return "none";
 }
 
+int mm_kind_of_name(const char* name) {
+    for (int k = MM_N16; k <= MM_V_STACK2; k++)
+        if (std::strcmp(name, mm_kind_name(k)) == 0) return k;
+    return 0;
+}
+
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass) {
     hipStream_t st = (hipStream_t)stream;
     if (a.nout == 0) return hipSuccess;
     const int kind = mm_kind(a, dt, b, fa);
+    if (kind < 0) return hipErrorNotSupported;
     if (kind == MM_GROUPS) return launch_mm_groups(a, dt, fa, transw, stream, pass);
     switch (dt * 2 + (transw ? 1 : 0)) {
     case 0: return launch_mm_dt<BSMM_F32, false>(a, kind, b, fa, st, pass);

@@ -15,6 +15,7 @@
 // read directly with 16-byte loads.  The 16x16 result tiles are computed as
 // D[q][p] so that each lane stores four consecutive dW values of one row.
 #include <cstdlib>
+#include <cstring>
 
 #include "common.h"
 
@@ -274,14 +275,15 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
     const int gpx = (ngroups + 7) / 8;
     const int gi = (blockIdx.x & 7) * gpx + (blockIdx.x >> 3);
     if (gi >= ngroups) return;   // whole workgroup
-    const int4 gr = groups[gi];
+    const int4 gr = groups[gi];   // (first, count, row, 0: ids first.. / 1: ids rids[first..])
     const int id0 = gr.x, cnt = gr.y, c = gr.z;
+    const bool listed = gr.w != 0;
     const int N = (int)a.N;
     const int spt = (N + KS - 1) / KS;
     const int nsb = a.G * spt;
     const bool xvec = (N % VEC) == 0;
     int kl = 0;
-    if (lane < cnt) kl = a.coords[2 * (id0 + lane) + 1];
+    if (lane < cnt) kl = a.coords[2 * (listed ? a.rids[id0 + lane] : id0 + lane) + 1];
 
     BSMM_LDS uint16_t* tiles = (BSMM_LDS uint16_t*)smem + wk * NS * TILE;
     if constexpr (TR && B == 8) {
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         const int qt = rem / (PT * 64), pt = (rem / 64) % PT, l = rem % 64;
         const int p = pt * 16 + (l & 15), q = qt * 16 + 4 * (l >> 4);
         if (p < B && q < B) {
-            const int64_t idx = (int64_t)(id0 + j) * B * B + p * B + q;
+            const int64_t idx = (int64_t)(listed ? a.rids[id0 + j] : id0 + j) * B * B + p * B + q;
             if (a.dwdt == BSMM_F32)
                 store4<BSMM_F32>(a.dw, idx, sum);
             else if (a.dwdt == BSMM_BF16)
@@ -452,12 +454,229 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Weight gradient of dense tiles (32x32 blocks, 16-bit activations, long contractions).
+// A workgroup owns one tile of 8x8 layout blocks holding at least kTileMin blocks.
+// Every step of 32 minibatch rows stages the tile's 256 input features of x_t and its
+// 256 output features of dy_t in LDS once; the 8 waves split the tile's blocks (in
+// row-major order, so consecutive blocks of a wave mostly share their x rows) and
+// each block's 32x32 product accumulates in registers over the whole contraction.
+// Pipeline as in the output-group fprop: RD register stages of loads, three LDS
+// buffers, one barrier per step, no branch around a global load.  Features-last
+// activations sit in LDS as [row][feature] rows of 512 bytes (chunk-permuted so the
+// transposing reads hit each bank once per pass); features-first as [feature][row]
+// rows of 64 bytes read straight into fragments.
+__device__ __forceinline__ int aswz(int r) {   // 16-byte chunk permutation of 512-byte rows
+    return (((r ^ (r >> 1)) & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
+}
+__device__ __forceinline__ int bswz(int r) {   // the same for 64-byte rows
+    return (((r >> 1) ^ (r >> 2)) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
+
+template <int DT, int FA, int RD>
+__global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
+    constexpr int B = 32, T = kTileSide, TF = T * B, KS = 32, S = 2;
+    constexpr int TILE = KS * TF;             // elements of one operand tile
+    constexpr int STAGE = 2 * TILE;           // x tile, then dy tile
+    constexpr int MAXB = T * T / kTileWaves;  // blocks per wave at most
+    static_assert(T * T % kTileWaves == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int m16 = lane & 15, g4 = lane >> 4;
+    // tiles in row-major order, XCD x taking the x-th contiguous range (neighbouring
+    // tiles share x rows or dy columns in that XCD's L2)
+    const int per = (a.ntiles + 7) / 8;
+    const int ti = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (ti >= a.ntiles) return;   // whole workgroup
+    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
+    const int r0 = tl.x, c0 = tl.y, nblk = tl.z;
+    const int bbeg = wave * nblk / kTileWaves, nb = (wave + 1) * nblk / kTileWaves - bbeg;
+    int4 bi = int4{0, 0, 0, 0};
+    if (lane < nb) bi = reinterpret_cast<const int4*>(a.tblk)[tl.w + bbeg + lane];
+    const int N = (int)a.N;
+    const int spt = (N + KS - 1) / KS;
+    const int nsb = a.G * spt;
+
+    // staging: chunk q = t + 512 i of each operand tile
+    uint32_t xo[2], yo[2];
+    int ql[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int q = t + 512 * i;
+        if constexpr (FA == 1) {   // row n = q / 32, features 8 (q % 32) ..
+            const int r = q >> 5, ch = q & 31;
+            xo[i] = r0 * B + 8 * ch < a.C ? (uint32_t)(r * a.C + r0 * B + 8 * ch) * S : kOffLane;
+            yo[i] = c0 * B + 8 * ch < a.K ? (uint32_t)(r * a.K + c0 * B + 8 * ch) * S : kOffLane;
+            ql[i] = r * TF + ((ch ^ aswz(r)) << 3);
+        } else {                   // feature row q / 4, minibatch values 8 (q % 4) ..
+            const int r = q >> 2, ch = q & 3;
+            xo[i] = r0 * B + r < a.C ? ((uint32_t)(r0 * B + r) * N + 8 * ch) * S : kOffLane;
+            yo[i] = c0 * B + r < a.K ? ((uint32_t)(c0 * B + r) * N + 8 * ch) * S : kOffLane;
+            ql[i] = r * KS + ((ch ^ bswz(r)) << 3);
+        }
+    }
+    // rows n beyond N (features last) or chunks past N (features first) read zero
+    auto row_ok = [&](int i, int nb0) {
+        const int q = t + 512 * i;
+        return FA == 1 ? nb0 + (q >> 5) < N : nb0 + 8 * (q & 3) < N;
+    };
+
+    struct Stage {
+        u32x4 x[2], y[2];
+    };
+    auto issue = [&](Stage& st, int s) {
+        const bool sv = s < nsb;   // workgroup-uniform
+        const int ss = sv ? s : 0;
+        const int tt = ss / spt, nb0 = (ss % spt) * KS;
+        const void* xp = a.xs[0];
+        const void* dp = a.dys[0];
+#pragma unroll
+        for (int u = 1; u < kMaxGroup; u++)
+            if (tt == u) {
+                xp = a.xs[u];
+                dp = a.dys[u];
+            }
+        const rsrc_t rx = make_rsrc(xp, a.x_bytes), ry = make_rsrc(dp, a.dy_bytes);
+        const uint32_t so = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.C * S : (uint32_t)nb0 * S;
+        const uint32_t sy = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.K * S : (uint32_t)nb0 * S;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const bool ok = row_ok(i, nb0);
+            st.x[i] = bload128(rx, ok ? xo[i] : kOffLane, so);
+            st.y[i] = bload128(ry, ok ? yo[i] : kOffLane, sy);
+        }
+    };
+    auto stage_lds = [&](const Stage& st, BSMM_LDS uint16_t* buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            lds_store16(buf + ql[i], st.x[i]);
+            lds_store16(buf + TILE + ql[i], st.y[i]);
+        }
+    };
+    // Operand fragment of features [32 blk + 16 kt, +16) of a tile (contraction = rows
+    // n).  Features last: transposing reads of rows 8 g4 + m16/4 (+4), whose permuted
+    // chunk index splits into a lane constant and the block's XOR with a lane key, so a
+    // block costs two integer ops per read.
+    int fbase[2][2], fkey[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int r = 8 * g4 + (m16 >> 2) + 4 * h, sw = aswz(r);
+        fkey[h] = sw >> 2;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+            fbase[kt][h] = r * TF + 4 * (m16 & 1) + 8 * ((m16 & 3) >> 1) + 16 * (kt ^ ((sw >> 1) & 1));
+    }
+    auto frag = [&](const BSMM_LDS uint16_t* tile, int blk, int kt) -> u32x4 {
+        if constexpr (FA == 1) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (BSMM_LDS i16x4*)(tile + fbase[kt][0] + 32 * (blk ^ fkey[0])));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (BSMM_LDS i16x4*)(tile + fbase[kt][1] + 32 * (blk ^ fkey[1])));
+            const u32x2 ul = __builtin_bit_cast(u32x2, lo), uh = __builtin_bit_cast(u32x2, hi);
+            return u32x4{ul.x, ul.y, uh.x, uh.y};
+        } else {   // row blk*32 + 16 kt + m16: the permutation sees only 16 kt + m16
+            const int r = 16 * kt + m16;
+            return *reinterpret_cast<const BSMM_LDS u32x4*>(tile + blk * B * KS + r * KS + ((g4 ^ bswz(r)) << 3));
+        }
+    };
+
+    f32x4 acc[MAXB][2][2];
+#pragma unroll
+    for (int j = 0; j < MAXB; j++)
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++) acc[j][kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const BSMM_LDS uint16_t* buf) {
+        u32x4 af[2];
+        int prow = -1;
+#pragma unroll
+        for (int j = 0; j < MAXB; j++) {
+            if (j < nb) {   // wave-uniform
+                const int lr = __builtin_amdgcn_readlane(bi.x, j), lc = __builtin_amdgcn_readlane(bi.y, j);
+                if (lr != prow) {   // x fragments are shared by a wave's blocks of one row
+                    af[0] = frag(buf, lr, 0);
+                    af[1] = frag(buf, lr, 1);
+                    prow = lr;
+                }
+                const u32x4 bf0 = frag(buf + TILE, lc, 0), bf1 = frag(buf + TILE, lc, 1);
+#pragma unroll
+                for (int ct = 0; ct < 2; ct++) {
+                    mma<DT>(acc[j][0][ct], bf0, af[ct]);   // D[k][c]
+                    mma<DT>(acc[j][1][ct], bf1, af[ct]);
+                }
+            }
+        }
+    };
+
+    Stage ring[RD];
+    BSMM_LDS uint16_t* lds = (BSMM_LDS uint16_t*)smem;
+#pragma unroll
+    for (int k = 0; k < RD; k++) issue(ring[k], k);
+    stage_lds(ring[0], lds);
+    issue(ring[0], RD);
+    __syncthreads();
+    for (int s0 = 0; s0 < nsb; s0 += RD) {
+        const int b0 = s0 % 3;
+#pragma unroll
+        for (int r = 0; r < RD; r++) {
+            const int s = s0 + r, rn = (r + 1) % RD;
+            const int bc = (b0 + r) % 3, bn = (b0 + r + 1) % 3;
+            stage_lds(ring[rn], lds + bn * STAGE);   // step s+1
+            __syncthreads();
+            issue(ring[rn], s + 1 + RD);
+            compute(lds + bc * STAGE);
+        }
+    }
+
+    // D[k][c]: lane holds k = 16kt + 4 g4 + v, c = 16ct + m16 -> 4 consecutive dW values
+#pragma unroll
+    for (int j = 0; j < MAXB; j++) {
+        if (j >= nb) break;
+        const int id = __builtin_amdgcn_readlane(bi.z, j);
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++) {
+                const int64_t idx = (int64_t)id * B * B + (16 * ct + m16) * B + 16 * kt + 4 * g4;
+                if (a.dwdt == BSMM_F32)
+                    store4<BSMM_F32>(a.dw, idx, acc[j][kt][ct]);
+                else if (a.dwdt == BSMM_BF16)
+                    store4<BSMM_BF16>(a.dw, idx, acc[j][kt][ct]);
+                else
+                    store4<BSMM_F16>(a.dw, idx, acc[j][kt][ct]);
+            }
+    }
+}
+
 template <int DT, int B, int FA>
-static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int ngroups, hipStream_t st) {
+static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int ngroups, hipStream_t st,
+                                       void* e0 = nullptr, void* e1 = nullptr, bool own_events = true) {
     constexpr int GM = 8;
     const int grid = ((ngroups + 7) / 8) * 8;
-    return launch(BSMM_PASS_UPDAT, updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, a, groups,
-                  ngroups);
+    if (own_events)
+        return launch(BSMM_PASS_UPDAT, updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, a, groups,
+                      ngroups);
+    return launch_ev(updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, e0, e1, a, groups, ngroups);
+}
+
+// Dense tiles, then the remaining blocks in row groups; one timing record spans both.
+template <int DT, int B, int FA>
+static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
+    if constexpr (B != 32 || DT == BSMM_F32) {
+        return hipErrorInvalidValue;
+    } else {
+        void *e0 = nullptr, *e1 = nullptr;
+        prof_events(BSMM_PASS_UPDAT, &e0, &e1);
+        const int grid = ((a.ntiles + 7) / 8) * 8;
+        hipError_t e = launch_ev(updt_kernel<DT, FA, 2>, dim3((unsigned)grid), dim3(512), st, e0,
+                                 a.nrest > 0 ? nullptr : e1, a);
+        if (e != hipSuccess || a.nrest == 0) return e;
+        return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.rest, a.nrest, st, nullptr, e1, false);
+    }
 }
 
 // BSMM_UPDAT_VARIANT=<n> (read once) forces a ring depth / blocks-per-wave pair for
@@ -489,11 +708,21 @@ static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
     case UP_D1B2: return launch_updat_cfg<DT, B, FA, 1>(a, 2, st);
     case UP_D2B8: return launch_updat_cfg<DT, B, FA, 2>(a, 8, st);
     case UP_D1B4: return launch_updat_cfg<DT, B, FA, 1>(a, 4, st);
+    case UP_TILES: return launch_updat_tiles<DT, B, FA>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-int updat_kind(const UpArgs& a, int dt) {
+int updat_kind(const UpArgs& a, int dt, int b, int fa) {
+    const int KS0 = dt == BSMM_F32 ? 16 : 32;
+    const int64_t steps0 = (int64_t)a.G * ((a.N + KS0 - 1) / KS0);
+    // dense 8x8-block tiles: 32x32 blocks, 16-bit, long contractions (whole 8-row
+    // chunks when features lead)
+    const bool tiles_ok = b == 32 && dt != BSMM_F32 && a.ntiles > 0 && steps0 >= 16 && (fa == 1 || a.N % 8 == 0);
+    // enough tiles to occupy at least half the CUs: fewer tiles leave most of the chip
+    // idle for the whole contraction (the remaining blocks run after them)
+    const bool tiles_wide = a.ntiles >= 128;
+    if (a.force > 0) return a.force == UP_TILES && !tiles_ok ? -1 : a.force;
     switch (updat_variant()) {
     case 1: return UP_D2B1;
     case 2: return UP_D4B1;
@@ -503,8 +732,12 @@ int updat_kind(const UpArgs& a, int dt) {
     case 6: return UP_D1B2;
     case 7: return UP_D2B8;
     case 8: return UP_D1B4;
+    case 9:
+        if (tiles_ok) return UP_TILES;
+        break;
     default: break;
     }
+    if (tiles_ok && tiles_wide) return UP_TILES;
     const int KS = dt == BSMM_F32 ? 16 : 32;
     const int64_t steps = (int64_t)a.G * ((a.N + KS - 1) / KS);
     // Long contractions: row groups, 4 waves per block group.
@@ -514,6 +747,12 @@ int updat_kind(const UpArgs& a, int dt) {
     // keeps no ring (measured best: waves, not the ring, hide the latency here).
     if ((int64_t)a.nnz / 2 >= 2048) return UP_D1B2;
     return UP_D2B1;
+}
+
+int updat_kind_of_name(const char* name) {
+    for (int k = UP_D2B1; k <= UP_TILES; k++)
+        if (std::strcmp(name, updat_kind_name(k)) == 0) return k;
+    return 0;
 }
 
 const char* updat_kind_name(int kind) {
@@ -526,6 +765,7 @@ const char* updat_kind_name(int kind) {
     case UP_D2B4: return "blocks_4perwave";
     case UP_D2B8: return "blocks_8perwave";
     case UP_D1B4: return "blocks_4perwave_noring";
+    case UP_TILES: return "dense_tiles";
     }
     return "none";
 }
@@ -546,7 +786,8 @@ static hipError_t launch_updat_dt(const UpArgs& a, int kind, int b, int fa, hipS
 hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     if (a.nnz == 0) return hipSuccess;
-    const int kind = updat_kind(a, dt);
+    const int kind = updat_kind(a, dt, b, fa);
+    if (kind < 0) return hipErrorNotSupported;
     switch (dt) {
     case BSMM_F32: return launch_updat_dt<BSMM_F32>(a, kind, b, fa, st);
     case BSMM_BF16: return launch_updat_dt<BSMM_BF16>(a, kind, b, fa, st);

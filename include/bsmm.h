@@ -153,6 +153,14 @@ BSMM_API const char* bsmm_last_error(void);
 BSMM_API bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm_dtype dt,
                                       const char** name);
 
+/* Testing and tuning: make `pass` (fprop, bprop or updat) launch the kernel family
+ * `name` (one of the names bsmm_kernel_name reports, e.g. "output_groups",
+ * "dense_tiles") instead of the automatic choice.  A later call that the named family
+ * cannot serve fails with BSMM_ERR_UNSUPPORTED and launches nothing.  NULL or ""
+ * restores the automatic choice.  Unknown names give BSMM_ERR_INVALID_ARG.  This is a
+ * set-up step: it must not race with calls on the same handle. */
+BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name);
+
 /* Layout compiler output, for inspection and tests (host only, no GPU needed).
  *   which: 0 coords   (2*nnz:   c, k of every id, in id order)
  *          1 colptr   (S+1:     fprop segment starts, one per output block k)
@@ -177,6 +185,16 @@ BSMM_API bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int gr
  *                     absent), 0, 0)
  *         14 rgptr    (block size 32 only: ceil(R/8)+1 offsets into rgent)
  *         15 rgent    (the same for groups of 8 block rows, walking k ascending)
+ *         16 utiles   (block size 32 only: 4 per weight-gradient tile, row-major tile
+ *                     order: first block row, first block column, block count, index
+ *                     of its first block in utblk; tiles are 8x8 blocks of the layout
+ *                     holding at least 16 blocks)
+ *         17 utblk    (4 per block of those tiles, row-major within a tile: row and
+ *                     column inside the tile, id, 0)
+ *         18 urest    (4 per row group of the blocks outside those tiles, ascending
+ *                     row then k, at most 8 per group: index of its first id in
+ *                     urids, count, row, 1)
+ *         19 urids    (the ids of those groups)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);

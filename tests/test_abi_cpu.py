@@ -146,7 +146,32 @@ def test_kernel_choice_names():
     assert m8.kernel_name("fprop", 512, torch.bfloat16) == "list_rows128"
     assert m32.kernel_name("fprop", 0, torch.bfloat16) == "none"
     assert m32.kernel_name("updat", 64, torch.bfloat16) in ("blocks_1perwave", "blocks_2perwave")
-    assert m32.kernel_name("updat", 4096, torch.bfloat16, group=8) == "row_groups"
+    assert m32.kernel_name("updat", 4096, torch.bfloat16, group=8) == "row_groups"   # 4 tiles only
+    big = bs.BlocksparseMatMul((rng.random((128, 128)) < 0.5).astype(np.uint8), block_size=32)
+    assert big.kernel_name("updat", 4096, torch.bfloat16) == "dense_tiles"
+    assert big.kernel_name("updat", 4096, torch.float32) == "row_groups"
+    assert big.kernel_name("updat", 64, torch.bfloat16) == "blocks_2perwave"
+    assert m8.kernel_name("updat", 4096, torch.bfloat16) == "row_groups"
     assert m32.kernel_name("identity", 0, torch.bfloat16) == "identity"
     with pytest.raises(bs.BsmmError):
         m32.kernel_name("updat", 64, torch.bfloat16, group=9)
+
+
+def test_force_kernel():
+    import torch
+    rng = np.random.default_rng(1)
+    m = bs.BlocksparseMatMul((rng.random((16, 16)) < 0.5).astype(np.uint8), block_size=32)
+    m.force_kernel("updat", "dense_tiles")
+    assert m.kernel_name("updat", 4096, torch.bfloat16) == "dense_tiles"
+    m.force_kernel("fprop", "list_rows128")
+    assert m.kernel_name("fprop", 4096, torch.bfloat16) == "list_rows128"
+    assert m.kernel_name("bprop", 4096, torch.bfloat16) == "output_groups"   # per pass
+    m.force_kernel("fprop", None)
+    assert m.kernel_name("fprop", 4096, torch.bfloat16) == "output_groups"
+    with pytest.raises(bs.BsmmError):
+        m.force_kernel("fprop", "dense_tiles")   # an updat kernel
+    with pytest.raises(bs.BsmmError):
+        m.force_kernel("updat", "no_such_kernel")
+    # a forced family that cannot serve the call: reported as "none", rejected at call time
+    m.force_kernel("updat", "dense_tiles")
+    assert m.kernel_name("updat", 4096, torch.float32) == "none"

@@ -246,3 +246,32 @@ def test_output_groups(N, fa, dtype):
     Kb = 32
     ycols = y[:, 8 * Kb:16 * Kb] if fa == 1 else y[8 * Kb:16 * Kb, :]
     assert torch.count_nonzero(ycols) == 0
+
+
+@pytest.mark.parametrize("N,G", [(512, 1), (520, 3), (1000, 2)])
+@pytest.mark.parametrize("fa", [1, 0])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_updat_dense_tiles(N, G, fa, dtype):
+    """Weight gradient by dense 8x8-block tiles plus row groups of the remaining blocks
+    (32x32 blocks, long contraction): partial tiles at the layout's edges, a ragged
+    minibatch, grouped steps."""
+    if fa == 0 and N % 8:
+        pytest.skip("features-first activations take the tile kernel only for N % 8 == 0")
+    print(f"case tiles N={N} G={G} fa={fa} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(N + 10 * G + fa)
+    R, S = 20, 27
+    L = (rng.random((R, S)) < 0.12).astype(np.uint8)
+    L[np.abs(np.subtract.outer(np.arange(R), np.arange(S))) <= 2] = 1
+    L[16:20, 24:27] = 1
+    P = synth.random_problem(rng, L, 32, N, fa, dtype, G=G, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
+    # few tiles: the automatic choice prefers row groups, so the tile kernel is forced
+    assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == "row_groups"
+    assert len(bs.bsmm_debug_lut(m.handle, 16)) > 0 and len(bs.bsmm_debug_lut(m.handle, 18)) > 0
+    m.force_kernel("updat", "dense_tiles")
+    assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == "dense_tiles"
+    dw = m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys])
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    rdw = oracle.updat(P.layout, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype)
+    assert_close(dw, rdw, dtype, "updat")

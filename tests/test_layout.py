@@ -166,3 +166,36 @@ def test_records_of_lists_longer_than_the_inline_cap():
     L[::7, 2] = 1
     check_layout(L)
     check_layout(L.T.copy())
+
+
+def test_weight_gradient_tiles_and_rest_cover_every_block_once():
+    """32x32 blocks: dense 8x8 tiles (>= 16 blocks) plus row groups of the rest hold
+    every block exactly once, with the right coordinates."""
+    rng = np.random.default_rng(9)
+    for R, S, p in [(20, 27, 0.5), (16, 16, 0.03), (9, 40, 0.3), (1, 1, 1.0), (8, 8, 1.0), (5, 5, 0.0)]:
+        L = (rng.random((R, S)) < p).astype(np.uint8)
+        if R >= 16:
+            L[np.abs(np.subtract.outer(np.arange(R), np.arange(S))) <= 2] = 1
+        m = bs.BlocksparseMatMul(L, block_size=32)
+        coords = bs.bsmm_debug_lut(m.handle, 0).reshape(-1, 2)
+        tiles = bs.bsmm_debug_lut(m.handle, 16).reshape(-1, 4)
+        tblk = bs.bsmm_debug_lut(m.handle, 17).reshape(-1, 4)
+        rest = bs.bsmm_debug_lut(m.handle, 18).reshape(-1, 4)
+        rids = bs.bsmm_debug_lut(m.handle, 19)
+        seen = np.zeros(int(L.sum()), dtype=int)
+        for r0, c0, n, first in tiles:
+            assert r0 % 8 == 0 and c0 % 8 == 0 and n >= 16
+            assert n == int(L[r0:r0 + 8, c0:c0 + 8].sum())
+            blk = tblk[first:first + n]
+            assert list(map(tuple, blk[:, :2])) == sorted(map(tuple, blk[:, :2]))
+            for lr, lc, bid, z in blk:
+                assert z == 0 and tuple(coords[bid]) == (r0 + lr, c0 + lc)
+                seen[bid] += 1
+        for first, n, c, flag in rest:
+            assert flag == 1 and 1 <= n <= 8
+            ids = rids[first:first + n]
+            assert np.all(coords[ids, 0] == c) and np.all(np.diff(coords[ids, 1]) > 0)
+            seen[ids] += 1
+        assert np.all(seen == 1)
+    m8 = bs.BlocksparseMatMul(np.ones((16, 16), np.uint8), block_size=16)
+    assert all(len(bs.bsmm_debug_lut(m8.handle, w)) == 0 for w in (16, 17, 18, 19))
