@@ -54,9 +54,9 @@ struct HostLut {
     // 0, 0.  gptr holds groups+1 entry offsets.
     std::vector<int32_t> cgptr, cgent, rgptr, rgent;
     // Weight-gradient tiles (32x32 blocks only): utiles (r0, c0, blocks, first) per
-    // tile with at least kTileMin blocks, row-major tile order; utblk (row in tile,
-    // column in tile, id, 0) per block of those tiles, row-major within a tile; the
-    // other blocks in urest row groups (first, count, row, 1), whose ids are
+    // tile with at least kTileMin blocks, row-major tile order; utblk holds, per such
+    // tile from index first, the ids of its 8x8 positions row-major (-1 where absent);
+    // the other blocks in urest row groups (first, count, row, 1), whose ids are
     // urids[first .. first+count-1].
     std::vector<int32_t> utiles, utblk, urest, urids;
 };

@@ -150,18 +150,22 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
         std::vector<uint8_t> in_tile(nnz, 0);
         for (int64_t tr = 0; tr < TR; tr++)
             for (int64_t tc = 0; tc < TC; tc++) {
-                std::vector<int32_t> blk;
+                std::vector<int32_t> pos(kTileSide * kTileSide, -1);   // row-major ids, -1 absent
+                int32_t n = 0;
                 for (int64_t c = tr * kTileSide; c < std::min<int64_t>(R, (tr + 1) * kTileSide); c++)
                     for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++) {
                         const int32_t k = L.rowent[2 * e];
-                        if (k / kTileSide == tc)
-                            blk.insert(blk.end(), {(int32_t)(c - tr * kTileSide), k % kTileSide, L.rowent[2 * e + 1], 0});
+                        if (k / kTileSide == tc) {
+                            pos[(c - tr * kTileSide) * kTileSide + k % kTileSide] = L.rowent[2 * e + 1];
+                            n++;
+                        }
                     }
-                if ((int64_t)blk.size() / 4 < kTileMin) continue;
-                L.utiles.insert(L.utiles.end(), {(int32_t)(tr * kTileSide), (int32_t)(tc * kTileSide),
-                                                 (int32_t)(blk.size() / 4), (int32_t)(L.utblk.size() / 4)});
-                for (size_t i = 0; i < blk.size(); i += 4) in_tile[blk[i + 2]] = 1;
-                L.utblk.insert(L.utblk.end(), blk.begin(), blk.end());
+                if (n < kTileMin) continue;
+                L.utiles.insert(L.utiles.end(), {(int32_t)(tr * kTileSide), (int32_t)(tc * kTileSide), n,
+                                                 (int32_t)L.utblk.size()});
+                for (int32_t id : pos)
+                    if (id >= 0) in_tile[id] = 1;
+                L.utblk.insert(L.utblk.end(), pos.begin(), pos.end());
             }
         for (int64_t c = 0; c < R; c++) {
             int32_t n = 0;

@@ -458,16 +458,19 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
 // Weight gradient of dense tiles (32x32 blocks, 16-bit activations, long contractions).
 // A workgroup owns one tile of 8x8 layout blocks holding at least kTileMin blocks.
 // Every step of 32 minibatch rows stages the tile's 256 input features of x_t and its
-// 256 output features of dy_t in LDS once; the 8 waves split the tile's blocks (in
-// row-major order, so consecutive blocks of a wave mostly share their x rows) and
-// each block's 32x32 product accumulates in registers over the whole contraction.
+// 256 output features of dy_t in LDS once; wave w takes tile row w: its x fragments
+// are read once per step and feed every present block of the row, whose 32x32
+// products accumulate in registers over the whole contraction (register slots by
+// tile column, so every LDS offset is a lane constant plus a fixed part).
 // Pipeline as in the output-group fprop: RD register stages of loads, three LDS
 // buffers, one barrier per step, no branch around a global load.  Features-last
 // activations sit in LDS as [row][feature] rows of 512 bytes (chunk-permuted so the
 // transposing reads hit each bank once per pass); features-first as [feature][row]
 // rows of 64 bytes read straight into fragments.
-__device__ __forceinline__ int aswz(int r) {   // 16-byte chunk permutation of 512-byte rows
-    return (((r ^ (r >> 1)) & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
+// 16-byte chunk permutation of 512-byte rows; independent of row bit 2, so the two
+// transposing reads of a fragment (rows r and r + 4) differ by a fixed offset
+__device__ __forceinline__ int aswz(int r) {
+    return (((r ^ (r >> 1)) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2) | (((r ^ (r >> 4)) & 1) << 3);
 }
 __device__ __forceinline__ int bswz(int r) {   // the same for 64-byte rows
     return (((r >> 1) ^ (r >> 2)) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
@@ -476,14 +479,13 @@ __device__ __forceinline__ int bswz(int r) {   // the same for 64-byte rows
 template <int DT, int FA, int RD>
 __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     constexpr int B = 32, T = kTileSide, TF = T * B, KS = 32, S = 2;
-    constexpr int TILE = KS * TF;             // elements of one operand tile
-    constexpr int STAGE = 2 * TILE;           // x tile, then dy tile
-    constexpr int MAXB = T * T / kTileWaves;  // blocks per wave at most
-    static_assert(T * T % kTileWaves == 0, "tile split");
+    constexpr int TILE = KS * TF;      // elements of one operand tile
+    constexpr int STAGE = 2 * TILE;    // x tile, then dy tile
+    static_assert(T == 8 && kTileWaves == 8, "one wave per tile row");
     __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
 
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // = tile row
     const int m16 = lane & 15, g4 = lane >> 4;
     // tiles in row-major order, XCD x taking the x-th contiguous range (neighbouring
     // tiles share x rows or dy columns in that XCD's L2)
@@ -491,10 +493,16 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     const int ti = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (ti >= a.ntiles) return;   // whole workgroup
     const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
-    const int r0 = tl.x, c0 = tl.y, nblk = tl.z;
-    const int bbeg = wave * nblk / kTileWaves, nb = (wave + 1) * nblk / kTileWaves - bbeg;
-    int4 bi = int4{0, 0, 0, 0};
-    if (lane < nb) bi = reinterpret_cast<const int4*>(a.tblk)[tl.w + bbeg + lane];
+    const int r0 = tl.x, c0 = tl.y;
+    // ids of this wave's row (scalar loads), -1 where absent
+    const int* rowids = a.tblk + tl.w + wave * T;
+    int ids[T], mask = 0;
+#pragma unroll
+    for (int c = 0; c < T; c++) {
+        ids[c] = __builtin_amdgcn_readfirstlane(rowids[c]);
+        mask |= (ids[c] >= 0 ? 1 : 0) << c;
+    }
+    mask = __builtin_amdgcn_readfirstlane(mask);   // keeps the presence tests scalar
     const int N = (int)a.N;
     const int spt = (N + KS - 1) / KS;
     const int nsb = a.G * spt;
@@ -517,19 +525,18 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
             ql[i] = r * KS + ((ch ^ bswz(r)) << 3);
         }
     }
-    // rows n beyond N (features last) or chunks past N (features first) read zero
-    auto row_ok = [&](int i, int nb0) {
-        const int q = t + 512 * i;
-        return FA == 1 ? nb0 + (q >> 5) < N : nb0 + 8 * (q & 3) < N;
-    };
 
     struct Stage {
         u32x4 x[2], y[2];
     };
-    auto issue = [&](Stage& st, int s) {
-        const bool sv = s < nsb;   // workgroup-uniform
-        const int ss = sv ? s : 0;
-        const int tt = ss / spt, nb0 = (ss % spt) * KS;
+    // Descriptors of step s's tensors.  With one step group they are built once; with
+    // several, the group's pointers are selected from the argument block per step.
+    const rsrc_t rx0 = make_rsrc(a.xs[0], a.x_bytes), ry0 = make_rsrc(a.dys[0], a.dy_bytes);
+    auto pick_one = [&](int, rsrc_t& rx, rsrc_t& ry) {
+        rx = rx0;
+        ry = ry0;
+    };
+    auto pick_many = [&](int tt, rsrc_t& rx, rsrc_t& ry) {
         const void* xp = a.xs[0];
         const void* dp = a.dys[0];
 #pragma unroll
@@ -538,14 +545,26 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
                 xp = a.xs[u];
                 dp = a.dys[u];
             }
-        const rsrc_t rx = make_rsrc(xp, a.x_bytes), ry = make_rsrc(dp, a.dy_bytes);
+        rx = make_rsrc(xp, a.x_bytes);
+        ry = make_rsrc(dp, a.dy_bytes);
+    };
+    auto issue = [&](Stage& st, int s, auto pick) {
+        const bool sv = s < nsb;   // workgroup-uniform
+        const int ss = sv ? s : 0;
+        const int tt = ss / spt, nb0 = (ss % spt) * KS;
+        rsrc_t rx, ry;
+        pick(tt, rx, ry);
         const uint32_t so = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.C * S : (uint32_t)nb0 * S;
         const uint32_t sy = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.K * S : (uint32_t)nb0 * S;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const bool ok = row_ok(i, nb0);
-            st.x[i] = bload128(rx, ok ? xo[i] : kOffLane, so);
-            st.y[i] = bload128(ry, ok ? yo[i] : kOffLane, sy);
+            // Features last: rows past N lie past the tensor's end and read zero by the
+            // range check.  Features first: a chunk past N is switched off with the top
+            // offset bit (arithmetic, so no branch appears around the load).
+            uint32_t off = 0;
+            if constexpr (FA == 0) off = ((uint32_t)(N - 1 - nb0 - 8 * ((t + 512 * i) & 3)) >> 31) << 31;
+            st.x[i] = bload128(rx, xo[i] | off, so);
+            st.y[i] = bload128(ry, yo[i] | off, sy);
         }
     };
     auto stage_lds = [&](const Stage& st, BSMM_LDS uint16_t* buf) {
@@ -555,99 +574,118 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
             lds_store16(buf + TILE + ql[i], st.y[i]);
         }
     };
-    // Operand fragment of features [32 blk + 16 kt, +16) of a tile (contraction = rows
-    // n).  Features last: transposing reads of rows 8 g4 + m16/4 (+4), whose permuted
-    // chunk index splits into a lane constant and the block's XOR with a lane key, so a
-    // block costs two integer ops per read.
-    int fbase[2][2], fkey[2];
+
+    // LDS element offsets of the fragment reads (within an operand tile), per lane:
+    // fragment of features [32 blk + 16 kt, +16), contraction = rows n.  Features last:
+    // two transposing reads (rows 8 g4 + m16/4, +4) whose permuted chunk index is a lane
+    // constant plus 32 (blk ^ key); tile columns blk = 4 hi + lo give one lane constant
+    // per (lo, kt) and a fixed 128 hi (the read of row r + 4 is 4 rows further on).
+    int boff[4][2];   // [blk & 3][kt]
+    int aoff[2];      // this wave's row, [kt]
+    {
+        const int r = 8 * g4 + (m16 >> 2), sw = aswz(r), key = sw >> 2;   // rows r, r + 4
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int r = 8 * g4 + (m16 >> 2) + 4 * h, sw = aswz(r);
-        fkey[h] = sw >> 2;
+        for (int kt = 0; kt < 2; kt++) {
+            const int base = FA == 1 ? r * TF + 4 * (m16 & 1) + 8 * ((m16 & 3) >> 1) + 16 * (kt ^ ((sw >> 1) & 1))
+                                     : (16 * kt + m16) * KS + ((g4 ^ bswz(16 * kt + m16)) << 3);
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++)
-            fbase[kt][h] = r * TF + 4 * (m16 & 1) + 8 * ((m16 & 3) >> 1) + 16 * (kt ^ ((sw >> 1) & 1));
+            for (int lo = 0; lo < 4; lo++) boff[lo][kt] = FA == 1 ? base + 32 * (lo ^ key) : base + lo * B * KS;
+            aoff[kt] = FA == 1 ? base + 32 * (wave ^ key) : base + wave * B * KS;
+        }
     }
-    auto frag = [&](const BSMM_LDS uint16_t* tile, int blk, int kt) -> u32x4 {
+    auto frag_at = [&](const BSMM_LDS uint16_t* tile, int o) -> u32x4 {
         if constexpr (FA == 1) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (BSMM_LDS i16x4*)(tile + fbase[kt][0] + 32 * (blk ^ fkey[0])));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (BSMM_LDS i16x4*)(tile + fbase[kt][1] + 32 * (blk ^ fkey[1])));
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSMM_LDS i16x4*)(tile + o));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSMM_LDS i16x4*)(tile + o + 4 * TF));
             const u32x2 ul = __builtin_bit_cast(u32x2, lo), uh = __builtin_bit_cast(u32x2, hi);
             return u32x4{ul.x, ul.y, uh.x, uh.y};
-        } else {   // row blk*32 + 16 kt + m16: the permutation sees only 16 kt + m16
-            const int r = 16 * kt + m16;
-            return *reinterpret_cast<const BSMM_LDS u32x4*>(tile + blk * B * KS + r * KS + ((g4 ^ bswz(r)) << 3));
+        } else {
+            return *reinterpret_cast<const BSMM_LDS u32x4*>(tile + o);
+        }
+    };
+    // column blk's fragment kt: FA 1 tile columns 4..7 sit 128 elements on (the XOR
+    // leaves bit 2 of blk alone); FA 0 rows of 32 elements, blk*32 rows on
+    auto bfrag = [&](const BSMM_LDS uint16_t* tile, int blk, int kt) -> u32x4 {
+        return frag_at(tile + (blk >> 2) * (FA == 1 ? 128 : 4 * B * KS), boff[blk & 3][kt]);
+    };
+
+    f32x4 acc[T][2][2];
+#pragma unroll
+    for (int c = 0; c < T; c++)
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++) acc[c][kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const BSMM_LDS uint16_t* buf) {
+        if (mask == 0) return;
+        u32x4 af[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ct++) af[ct] = frag_at(buf, aoff[ct]);
+        constexpr int BB = 2;   // blocks per batch of reads
+#pragma unroll
+        for (int h0 = 0; h0 < T; h0 += BB) {
+            u32x4 bf[BB][2];
+#pragma unroll
+            for (int c = 0; c < BB; c++)
+                if ((mask >> (h0 + c)) & 1) {   // wave-uniform
+                    bf[c][0] = bfrag(buf + TILE, h0 + c, 0);
+                    bf[c][1] = bfrag(buf + TILE, h0 + c, 1);
+                }
+#pragma unroll
+            for (int c = 0; c < BB; c++)
+                if ((mask >> (h0 + c)) & 1) {
+#pragma unroll
+                    for (int ct = 0; ct < 2; ct++) {
+                        mma<DT>(acc[h0 + c][0][ct], bf[c][0], af[ct]);   // D[k][c]
+                        mma<DT>(acc[h0 + c][1][ct], bf[c][1], af[ct]);
+                    }
+                }
         }
     };
 
-    f32x4 acc[MAXB][2][2];
+    BSMM_LDS uint16_t* lds = (BSMM_LDS uint16_t*)smem;
+    auto run = [&](auto pick) {
+        Stage ring[RD];
 #pragma unroll
-    for (int j = 0; j < MAXB; j++)
+        for (int k = 0; k < RD; k++) issue(ring[k], k, pick);
+        stage_lds(ring[0], lds);
+        issue(ring[0], RD, pick);
+        __syncthreads();
+        for (int s0 = 0; s0 < nsb; s0 += RD) {
+            const int b0 = s0 % 3;
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-            for (int ct = 0; ct < 2; ct++) acc[j][kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const BSMM_LDS uint16_t* buf) {
-        u32x4 af[2];
-        int prow = -1;
-#pragma unroll
-        for (int j = 0; j < MAXB; j++) {
-            if (j < nb) {   // wave-uniform
-                const int lr = __builtin_amdgcn_readlane(bi.x, j), lc = __builtin_amdgcn_readlane(bi.y, j);
-                if (lr != prow) {   // x fragments are shared by a wave's blocks of one row
-                    af[0] = frag(buf, lr, 0);
-                    af[1] = frag(buf, lr, 1);
-                    prow = lr;
-                }
-                const u32x4 bf0 = frag(buf + TILE, lc, 0), bf1 = frag(buf + TILE, lc, 1);
-#pragma unroll
-                for (int ct = 0; ct < 2; ct++) {
-                    mma<DT>(acc[j][0][ct], bf0, af[ct]);   // D[k][c]
-                    mma<DT>(acc[j][1][ct], bf1, af[ct]);
-                }
+            for (int r = 0; r < RD; r++) {
+                const int s = s0 + r, rn = (r + 1) % RD;
+                const int bc = (b0 + r) % 3, bn = (b0 + r + 1) % 3;
+                stage_lds(ring[rn], lds + bn * STAGE);   // step s+1
+                __syncthreads();
+                issue(ring[rn], s + 1 + RD, pick);
+                compute(lds + bc * STAGE);
             }
         }
     };
-
-    Stage ring[RD];
-    BSMM_LDS uint16_t* lds = (BSMM_LDS uint16_t*)smem;
-#pragma unroll
-    for (int k = 0; k < RD; k++) issue(ring[k], k);
-    stage_lds(ring[0], lds);
-    issue(ring[0], RD);
-    __syncthreads();
-    for (int s0 = 0; s0 < nsb; s0 += RD) {
-        const int b0 = s0 % 3;
-#pragma unroll
-        for (int r = 0; r < RD; r++) {
-            const int s = s0 + r, rn = (r + 1) % RD;
-            const int bc = (b0 + r) % 3, bn = (b0 + r + 1) % 3;
-            stage_lds(ring[rn], lds + bn * STAGE);   // step s+1
-            __syncthreads();
-            issue(ring[rn], s + 1 + RD);
-            compute(lds + bc * STAGE);
-        }
-    }
+    if (a.G == 1)
+        run(pick_one);
+    else
+        run(pick_many);
 
     // D[k][c]: lane holds k = 16kt + 4 g4 + v, c = 16ct + m16 -> 4 consecutive dW values
 #pragma unroll
-    for (int j = 0; j < MAXB; j++) {
-        if (j >= nb) break;
-        const int id = __builtin_amdgcn_readlane(bi.z, j);
+    for (int c = 0; c < T; c++) {
+        if (!((mask >> c) & 1)) continue;
+        const int id = ids[c];
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int ct = 0; ct < 2; ct++) {
                 const int64_t idx = (int64_t)id * B * B + (16 * ct + m16) * B + 16 * kt + 4 * g4;
                 if (a.dwdt == BSMM_F32)
-                    store4<BSMM_F32>(a.dw, idx, acc[j][kt][ct]);
+                    store4<BSMM_F32>(a.dw, idx, acc[c][kt][ct]);
                 else if (a.dwdt == BSMM_BF16)
-                    store4<BSMM_BF16>(a.dw, idx, acc[j][kt][ct]);
+                    store4<BSMM_BF16>(a.dw, idx, acc[c][kt][ct]);
                 else
-                    store4<BSMM_F16>(a.dw, idx, acc[j][kt][ct]);
+                    store4<BSMM_F16>(a.dw, idx, acc[c][kt][ct]);
             }
     }
 }

@@ -187,10 +187,10 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  *         15 rgent    (the same for groups of 8 block rows, walking k ascending)
  *         16 utiles   (block size 32 only: 4 per weight-gradient tile, row-major tile
  *                     order: first block row, first block column, block count, index
- *                     of its first block in utblk; tiles are 8x8 blocks of the layout
+ *                     of its first entry in utblk; tiles are 8x8 blocks of the layout
  *                     holding at least 16 blocks)
- *         17 utblk    (4 per block of those tiles, row-major within a tile: row and
- *                     column inside the tile, id, 0)
+ *         17 utblk    (64 per tile: the ids of its 8x8 positions, row-major, -1 where
+ *                     the layout is 0)
  *         18 urest    (4 per row group of the blocks outside those tiles, ascending
  *                     row then k, at most 8 per group: index of its first id in
  *                     urids, count, row, 1)

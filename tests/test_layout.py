@@ -179,18 +179,23 @@ def test_weight_gradient_tiles_and_rest_cover_every_block_once():
         m = bs.BlocksparseMatMul(L, block_size=32)
         coords = bs.bsmm_debug_lut(m.handle, 0).reshape(-1, 2)
         tiles = bs.bsmm_debug_lut(m.handle, 16).reshape(-1, 4)
-        tblk = bs.bsmm_debug_lut(m.handle, 17).reshape(-1, 4)
+        tblk = bs.bsmm_debug_lut(m.handle, 17)
         rest = bs.bsmm_debug_lut(m.handle, 18).reshape(-1, 4)
         rids = bs.bsmm_debug_lut(m.handle, 19)
         seen = np.zeros(int(L.sum()), dtype=int)
-        for r0, c0, n, first in tiles:
-            assert r0 % 8 == 0 and c0 % 8 == 0 and n >= 16
+        for ti, (r0, c0, n, first) in enumerate(tiles):
+            assert r0 % 8 == 0 and c0 % 8 == 0 and n >= 16 and first == 64 * ti
             assert n == int(L[r0:r0 + 8, c0:c0 + 8].sum())
-            blk = tblk[first:first + n]
-            assert list(map(tuple, blk[:, :2])) == sorted(map(tuple, blk[:, :2]))
-            for lr, lc, bid, z in blk:
-                assert z == 0 and tuple(coords[bid]) == (r0 + lr, c0 + lc)
-                seen[bid] += 1
+            pos = tblk[first:first + 64].reshape(8, 8)
+            for lr in range(8):
+                for lc in range(8):
+                    bid = pos[lr, lc]
+                    inside = r0 + lr < R and c0 + lc < S
+                    if inside and L[r0 + lr, c0 + lc]:
+                        assert bid >= 0 and tuple(coords[bid]) == (r0 + lr, c0 + lc)
+                        seen[bid] += 1
+                    else:
+                        assert bid == -1
         for first, n, c, flag in rest:
             assert flag == 1 and 1 <= n <= 8
             ids = rids[first:first + n]
