@@ -181,10 +181,19 @@ __device__ __forceinline__ void wave_lds_order() { __atomic_signal_fence(__ATOMI
 // Workgroup -> (list index, minibatch tile).  Workgroups are dealt round-robin over
 // the 8 XCDs; the minibatch tiles of one list get ids equal mod 8, so they run on one
 // XCD and share its L2 copy of the list's weight blocks.
+// With 8 or more minibatch tiles the deal flips: XCD x takes tiles x, x+8, ... of every
+// list, so each XCD's L2 holds its own slice of the activations while all lists walk it
+// (measured 20-27 % faster on the b=8, N=1024 shape, where activations are re-read by
+// every list).
 __device__ __forceinline__ void wg_decode(int bid, int nlist, int ntiles, int& li, int& nt) {
     if (ntiles == 1) {
         li = bid;
         nt = 0;
+    } else if (ntiles >= 8) {
+        const int xcd = bid & 7, slot = bid >> 3, tpx = (ntiles + 7) / 8;
+        nt = (slot % tpx) * 8 + xcd;
+        li = slot / tpx;
+        if (nt >= ntiles) li = nlist;
     } else {
         const int xcd = bid & 7, slot = bid >> 3;
         nt = slot % ntiles;

@@ -628,6 +628,7 @@ static hipError_t launch_large(MMArgs a, hipStream_t st, int pass) {
 // ---------------------------------------------------------------------------------
 static int mm_grid(int nlist, int ntiles) {
     if (ntiles == 1) return nlist;
+    if (ntiles >= 8) return 8 * nlist * ((ntiles + 7) / 8);
     return ((nlist + 7) / 8) * 8 * ntiles;
 }
 

@@ -21,6 +21,34 @@
 
 namespace bsmm {
 
+// Descriptors of the tensors of step group t.  With one group (the common case) they are
+// built once, before the loops: selecting a group pointer from the argument block inside
+// a loop puts a scalar load and its wait in every step.
+struct PickOne {
+    rsrc_t rx, ry;
+    __device__ void operator()(const UpArgs&, int, rsrc_t& x, rsrc_t& y) const {
+        x = rx;
+        y = ry;
+    }
+};
+struct PickMany {
+    __device__ void operator()(const UpArgs& a, int t, rsrc_t& x, rsrc_t& y) const {
+        const void* xp = a.xs[0];
+        const void* dp = a.dys[0];
+#pragma unroll
+        for (int u = 1; u < kMaxGroup; u++)
+            if (t == u) {
+                xp = a.xs[u];
+                dp = a.dys[u];
+            }
+        x = make_rsrc(xp, a.x_bytes);
+        y = make_rsrc(dp, a.dy_bytes);
+    }
+};
+__device__ inline PickOne pick_one(const UpArgs& a) {
+    return PickOne{make_rsrc(a.xs[0], a.x_bytes), make_rsrc(a.dys[0], a.dy_bytes)};
+}
+
 template <int DT, int B, int FA, int D>
 __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
     using T = typename Elt<DT>::T;
@@ -87,22 +115,15 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
         u32x4 d[RR];
     };
 
-    auto load_slot = [&](SlotU& sl, int it0) {
+    auto load_slot = [&](SlotU& sl, int it0, auto pick) {
         const bool iv = it0 < items;   // wave-uniform
         const int it = iv ? it0 : 0;
         const int j = it / nsb, st = it % nsb;
         const int t = st / spt;
         const int nb = (st % spt) * KS;
         const int c = __builtin_amdgcn_readlane(cl, j), k = __builtin_amdgcn_readlane(kl, j);
-        const void* xp = a.xs[0];
-        const void* dp = a.dys[0];
-#pragma unroll
-        for (int u = 1; u < kMaxGroup; u++)
-            if (t == u) {
-                xp = a.xs[u];
-                dp = a.dys[u];
-            }
-        const rsrc_t rx = make_rsrc(xp, a.x_bytes), rd = make_rsrc(dp, a.dy_bytes);
+        rsrc_t rx, rd;
+        pick(a, t, rx, rd);
         if constexpr (TR) {
             const uint32_t xs = iv ? (uint32_t)(nb * a.C + c * B) * S : kOffOff;
             const uint32_t ds = iv ? (uint32_t)(nb * a.K + k * B) * S : kOffOff;
@@ -223,16 +244,22 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
         return;
     }
 
-    SlotU ring[D];
+    auto run = [&](auto pick) {
+        SlotU ring[D];
 #pragma unroll
-    for (int i = 0; i < D; i++) load_slot(ring[i], i);
-    for (int j = 0; j < items; j += D) {
+        for (int i = 0; i < D; i++) load_slot(ring[i], i, pick);
+        for (int j = 0; j < items; j += D) {
 #pragma unroll
-        for (int i = 0; i < D; i++) {
-            compute_slot(ring[i], j + i);   // items past the end add zeros and store nothing
-            load_slot(ring[i], j + i + D);
+            for (int i = 0; i < D; i++) {
+                compute_slot(ring[i], j + i);   // items past the end add zeros and store nothing
+                load_slot(ring[i], j + i + D, pick);
+            }
         }
-    }
+    };
+    if (a.G == 1)
+        run(pick_one(a));
+    else
+        run(PickMany{});
 }
 
 // ---------------------------------------------------------------------------------
@@ -349,20 +376,13 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         }
     };
 
-    auto load_slot = [&](Slot& sl, int st0) {
+    auto load_slot = [&](Slot& sl, int st0, auto pick) {
         const bool sv = st0 < nsb;   // wave-uniform
         const int st = sv ? st0 : 0;
         const int t = st / spt;
         const int nb = (st % spt) * KS;
-        const void* xp = a.xs[0];
-        const void* dp = a.dys[0];
-#pragma unroll
-        for (int u = 1; u < kMaxGroup; u++)
-            if (t == u) {
-                xp = a.xs[u];
-                dp = a.dys[u];
-            }
-        const rsrc_t rx = make_rsrc(xp, a.x_bytes), rd = make_rsrc(dp, a.dy_bytes);
+        rsrc_t rx, rd;
+        pick(a, t, rx, rd);
         load_slab(sl.v[0], rx, xc, a.C, c, nb, sv);
 #pragma unroll
         for (int j = 0; j < GM; j++) {
@@ -411,16 +431,22 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
     };
 
     const int mysteps = nsb > wk ? (nsb - wk + 3) / 4 : 0;
-    Slot ring[D];
+    auto run = [&](auto pick) {
+        Slot ring[D];
 #pragma unroll
-    for (int i = 0; i < D; i++) load_slot(ring[i], wk + 4 * i);
-    for (int j = 0; j < mysteps; j += D) {
+        for (int i = 0; i < D; i++) load_slot(ring[i], wk + 4 * i, pick);
+        for (int j = 0; j < mysteps; j += D) {
 #pragma unroll
-        for (int i = 0; i < D; i++) {
-            if (j + i < mysteps) compute(ring[i]);   // no loads inside
-            load_slot(ring[i], wk + 4 * (j + i + D));
+            for (int i = 0; i < D; i++) {
+                if (j + i < mysteps) compute(ring[i]);   // no loads inside
+                load_slot(ring[i], wk + 4 * (j + i + D), pick);
+            }
         }
-    }
+    };
+    if (a.G == 1)
+        run(pick_one(a));
+    else
+        run(PickMany{});
 
     // partial tiles of the 4 waves, added in wave order
     __syncthreads();
@@ -529,31 +555,12 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     struct Stage {
         u32x4 x[2], y[2];
     };
-    // Descriptors of step s's tensors.  With one step group they are built once; with
-    // several, the group's pointers are selected from the argument block per step.
-    const rsrc_t rx0 = make_rsrc(a.xs[0], a.x_bytes), ry0 = make_rsrc(a.dys[0], a.dy_bytes);
-    auto pick_one = [&](int, rsrc_t& rx, rsrc_t& ry) {
-        rx = rx0;
-        ry = ry0;
-    };
-    auto pick_many = [&](int tt, rsrc_t& rx, rsrc_t& ry) {
-        const void* xp = a.xs[0];
-        const void* dp = a.dys[0];
-#pragma unroll
-        for (int u = 1; u < kMaxGroup; u++)
-            if (tt == u) {
-                xp = a.xs[u];
-                dp = a.dys[u];
-            }
-        rx = make_rsrc(xp, a.x_bytes);
-        ry = make_rsrc(dp, a.dy_bytes);
-    };
     auto issue = [&](Stage& st, int s, auto pick) {
         const bool sv = s < nsb;   // workgroup-uniform
         const int ss = sv ? s : 0;
         const int tt = ss / spt, nb0 = (ss % spt) * KS;
         rsrc_t rx, ry;
-        pick(tt, rx, ry);
+        pick(a, tt, rx, ry);
         const uint32_t so = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.C * S : (uint32_t)nb0 * S;
         const uint32_t sy = !sv ? kOffOff : FA == 1 ? (uint32_t)nb0 * a.K * S : (uint32_t)nb0 * S;
 #pragma unroll
@@ -666,9 +673,9 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
         }
     };
     if (a.G == 1)
-        run(pick_one);
+        run(pick_one(a));
     else
-        run(pick_many);
+        run(PickMany{});
 
     // D[k][c]: lane holds k = 16kt + 4 g4 + v, c = 16ct + m16 -> 4 consecutive dW values
 #pragma unroll
