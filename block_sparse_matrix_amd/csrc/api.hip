@@ -234,6 +234,7 @@ bsmm_status mm_pass(bsmm_handle h, const void* in, const void* w, void* out, int
 
 UpArgs up_args(const HostLut& L, int64_t N, int group) {
     UpArgs a{};
+    a.split = 1;
     a.ntiles = (int32_t)(L.utiles.size() / 4);
     a.nrest = (int32_t)(L.urest.size() / 4);
     a.N = N;
@@ -328,6 +329,11 @@ bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype d
     if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     *bytes = 0;
+    if (pass == BSMM_PASS_UPDAT && N > 0 && dt != BSMM_F32 && h->lut.b == 32) {
+        const int nt = (int)(h->lut.utiles.size() / 4);
+        const int p = tile_split(nt);
+        if (p > 1) *bytes = (size_t)p * nt * kTileSide * kTileSide * 32 * 32 * sizeof(float);
+    }
     return BSMM_OK;
 }
 
@@ -361,6 +367,9 @@ bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm
     } else if (pass == BSMM_PASS_UPDAT) {
         UpArgs a = up_args(L, N, group);
         a.force = h->force[BSMM_PASS_UPDAT];
+        size_t need = 0;
+        (void)bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need);
+        if (need > 0) a.split = tile_split(a.ntiles);   // as when the workspace is given
         if (L.nnz > 0) *name = updat_kind_name(updat_kind(a, dt, L.b, L.fa));
     } else if (pass == BSMM_PASS_IDENTITY) {
         if (L.nnz > 0) *name = "identity";
@@ -415,6 +424,12 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
     a.nrest = d->nurest;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     a.force = h->force[BSMM_PASS_UPDAT];
+    {   // a contraction split of the tiles needs the workspace; without it, no split
+        size_t need = 0;
+        (void)bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need);
+        a.split = need > 0 && ws && ws_bytes >= need && ((uintptr_t)ws & 15u) == 0 ? tile_split(a.ntiles) : 1;
+        a.ws = (float*)ws;
+    }
     if (updat_kind(a, dt, L.b, L.fa) < 0)
         return fail(BSMM_ERR_UNSUPPORTED, "the forced kernel does not apply to these arguments");
     hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);

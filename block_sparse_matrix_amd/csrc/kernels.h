@@ -62,7 +62,18 @@ struct UpArgs {
     const int32_t* rids;
     int32_t nrest;
     int32_t force;          // UpKind to use (0: automatic)
+    int32_t split;          // tiles: contraction split in this many parts (1: none)
+    float* ws;              // tiles with split > 1: fp32 partial sums, split*ntiles*64 blocks
 };
+
+// Contraction split of the weight-gradient tiles: enough parts to give ~256 workgroups,
+// at most kMaxSplit.  Splits need split*ntiles*64*b*b*4 bytes of workspace.
+constexpr int kMaxSplit = 8;
+inline int tile_split(int ntiles) {
+    if (ntiles <= 0) return 1;
+    const int p = 256 / ntiles;
+    return p < 1 ? 1 : p > kMaxSplit ? kMaxSplit : p;
+}
 
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.

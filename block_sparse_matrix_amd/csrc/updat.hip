@@ -31,18 +31,27 @@ struct PickOne {
         y = ry;
     }
 };
+// Several groups: the descriptors of the last group asked for are kept, and rebuilt
+// (a scalar load from the argument block) only when a step of another group comes.
 struct PickMany {
-    __device__ void operator()(const UpArgs& a, int t, rsrc_t& x, rsrc_t& y) const {
-        const void* xp = a.xs[0];
-        const void* dp = a.dys[0];
+    int t = -1;
+    rsrc_t rx, ry;
+    __device__ void operator()(const UpArgs& a, int tt, rsrc_t& x, rsrc_t& y) {
+        if (tt != t) {   // uniform; once per group and pipeline position
+            const void* xp = a.xs[0];
+            const void* dp = a.dys[0];
 #pragma unroll
-        for (int u = 1; u < kMaxGroup; u++)
-            if (t == u) {
-                xp = a.xs[u];
-                dp = a.dys[u];
-            }
-        x = make_rsrc(xp, a.x_bytes);
-        y = make_rsrc(dp, a.dy_bytes);
+            for (int u = 1; u < kMaxGroup; u++)
+                if (tt == u) {
+                    xp = a.xs[u];
+                    dp = a.dys[u];
+                }
+            rx = make_rsrc(xp, a.x_bytes);
+            ry = make_rsrc(dp, a.dy_bytes);
+            t = tt;
+        }
+        x = rx;
+        y = ry;
     }
 };
 __device__ inline PickOne pick_one(const UpArgs& a) {
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
         u32x4 d[RR];
     };
 
-    auto load_slot = [&](SlotU& sl, int it0, auto pick) {
+    auto load_slot = [&](SlotU& sl, int it0, auto& pick) {
         const bool iv = it0 < items;   // wave-uniform
         const int it = iv ? it0 : 0;
         const int j = it / nsb, st = it % nsb;
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
         return;
     }
 
-    auto run = [&](auto pick) {
+    auto run = [&](auto&& pick) {
         SlotU ring[D];
 #pragma unroll
         for (int i = 0; i < D; i++) load_slot(ring[i], i, pick);
@@ -256,10 +265,13 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
             }
         }
     };
-    if (a.G == 1)
-        run(pick_one(a));
-    else
-        run(PickMany{});
+    if (a.G == 1) {
+        PickOne p1 = pick_one(a);
+        run(p1);
+    } else {
+        PickMany pm;
+        run(pm);
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         }
     };
 
-    auto load_slot = [&](Slot& sl, int st0, auto pick) {
+    auto load_slot = [&](Slot& sl, int st0, auto& pick) {
         const bool sv = st0 < nsb;   // wave-uniform
         const int st = sv ? st0 : 0;
         const int t = st / spt;
@@ -401,19 +413,23 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
 
     auto compute = [&](const Slot& sl) {
         u32x4 fr[NS][PT];
-        if constexpr (TR) {
+        if constexpr (TR) {   // only the slabs of the group's blocks (slab 0 = x, 1..cnt = dy)
 #pragma unroll
             for (int sidx = 0; sidx < NS; sidx++)
+                if (sidx <= cnt) {   // wave-uniform
 #pragma unroll
-                for (int i = 0; i < RR; i++) {
-                    const int ch = lane + 64 * i;
-                    if (ch < 4 * B) lds_store16(tiles + sidx * TILE + (ch / WCH) * PITCH + (ch % WCH) * 8, sl.v[sidx][i]);
+                    for (int i = 0; i < RR; i++) {
+                        const int ch = lane + 64 * i;
+                        if (ch < 4 * B) lds_store16(tiles + sidx * TILE + (ch / WCH) * PITCH + (ch % WCH) * 8, sl.v[sidx][i]);
+                    }
                 }
             wave_lds_order();
 #pragma unroll
             for (int sidx = 0; sidx < NS; sidx++)
+                if (sidx <= cnt) {
 #pragma unroll
-                for (int pt = 0; pt < PT; pt++) fr[sidx][pt] = frag_tr16(tiles + sidx * TILE, PITCH, 16 * pt, lane);
+                    for (int pt = 0; pt < PT; pt++) fr[sidx][pt] = frag_tr16(tiles + sidx * TILE, PITCH, 16 * pt, lane);
+                }
             wave_lds_order();
         } else {
 #pragma unroll
@@ -431,7 +447,7 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
     };
 
     const int mysteps = nsb > wk ? (nsb - wk + 3) / 4 : 0;
-    auto run = [&](auto pick) {
+    auto run = [&](auto&& pick) {
         Slot ring[D];
 #pragma unroll
         for (int i = 0; i < D; i++) load_slot(ring[i], wk + 4 * i, pick);
@@ -443,10 +459,13 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
             }
         }
     };
-    if (a.G == 1)
-        run(pick_one(a));
-    else
-        run(PickMany{});
+    if (a.G == 1) {
+        PickOne p1 = pick_one(a);
+        run(p1);
+    } else {
+        PickMany pm;
+        run(pm);
+    }
 
     // partial tiles of the 4 waves, added in wave order
     __syncthreads();
@@ -515,9 +534,12 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     const int m16 = lane & 15, g4 = lane >> 4;
     // tiles in row-major order, XCD x taking the x-th contiguous range (neighbouring
     // tiles share x rows or dy columns in that XCD's L2)
-    const int per = (a.ntiles + 7) / 8;
-    const int ti = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (ti >= a.ntiles) return;   // whole workgroup
+    // With a contraction split, workgroup (tile, part) sums steps [part*nsb/split, ..).
+    const int units = a.ntiles * a.split;
+    const int per = (units + 7) / 8;
+    const int un = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (un >= units) return;   // whole workgroup
+    const int ti = un / a.split, part = un % a.split;
     const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
     const int r0 = tl.x, c0 = tl.y;
     // ids of this wave's row (scalar loads), -1 where absent
@@ -531,7 +553,9 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     mask = __builtin_amdgcn_readfirstlane(mask);   // keeps the presence tests scalar
     const int N = (int)a.N;
     const int spt = (N + KS - 1) / KS;
-    const int nsb = a.G * spt;
+    const int nall = a.G * spt;
+    const int sbeg = (int)((int64_t)part * nall / a.split);
+    const int nsb = (int)((int64_t)(part + 1) * nall / a.split) - sbeg;   // this part's steps
 
     // staging: chunk q = t + 512 i of each operand tile
     uint32_t xo[2], yo[2];
@@ -555,9 +579,9 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     struct Stage {
         u32x4 x[2], y[2];
     };
-    auto issue = [&](Stage& st, int s, auto pick) {
+    auto issue = [&](Stage& st, int s, auto& pick) {
         const bool sv = s < nsb;   // workgroup-uniform
-        const int ss = sv ? s : 0;
+        const int ss = sbeg + (sv ? s : 0);
         const int tt = ss / spt, nb0 = (ss % spt) * KS;
         rsrc_t rx, ry;
         pick(a, tt, rx, ry);
@@ -652,7 +676,7 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     };
 
     BSMM_LDS uint16_t* lds = (BSMM_LDS uint16_t*)smem;
-    auto run = [&](auto pick) {
+    auto run = [&](auto&& pick) {
         Stage ring[RD];
 #pragma unroll
         for (int k = 0; k < RD; k++) issue(ring[k], k, pick);
@@ -672,22 +696,30 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
             }
         }
     };
-    if (a.G == 1)
-        run(pick_one(a));
-    else
-        run(PickMany{});
+    if (a.G == 1) {
+        PickOne p1 = pick_one(a);
+        run(p1);
+    } else {
+        PickMany pm;
+        run(pm);
+    }
 
-    // D[k][c]: lane holds k = 16kt + 4 g4 + v, c = 16ct + m16 -> 4 consecutive dW values
+    // D[k][c]: lane holds k = 16kt + 4 g4 + v, c = 16ct + m16 -> 4 consecutive dW values;
+    // with a split, fp32 partials go to workspace slot (part, tile, position)
 #pragma unroll
     for (int c = 0; c < T; c++) {
         if (!((mask >> c) & 1)) continue;
         const int id = ids[c];
+        const int64_t pslot = ((int64_t)part * a.ntiles + ti) * (T * T) + wave * T + c;
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int ct = 0; ct < 2; ct++) {
-                const int64_t idx = (int64_t)id * B * B + (16 * ct + m16) * B + 16 * kt + 4 * g4;
-                if (a.dwdt == BSMM_F32)
+                const int e = (16 * ct + m16) * B + 16 * kt + 4 * g4;
+                const int64_t idx = (int64_t)id * B * B + e;
+                if (a.split > 1)
+                    store4<BSMM_F32>(a.ws, pslot * B * B + e, acc[c][kt][ct]);
+                else if (a.dwdt == BSMM_F32)
                     store4<BSMM_F32>(a.dw, idx, acc[c][kt][ct]);
                 else if (a.dwdt == BSMM_BF16)
                     store4<BSMM_BF16>(a.dw, idx, acc[c][kt][ct]);
@@ -708,7 +740,32 @@ static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int 
     return launch_ev(updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, e0, e1, a, groups, ngroups);
 }
 
-// Dense tiles, then the remaining blocks in row groups; one timing record spans both.
+// Sum of the split parts of every tile block, in part order (deterministic), to dW.
+template <int B>
+__global__ __launch_bounds__(256) void updt_reduce(UpArgs a) {
+    const int ti = blockIdx.x;
+    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
+    constexpr int TT = kTileSide * kTileSide;
+    for (int pos = 0; pos < TT; pos++) {
+        const int id = a.tblk[tl.w + pos];
+        if (id < 0) continue;   // workgroup-uniform
+        for (int e = 4 * threadIdx.x; e < B * B; e += 4 * 256) {
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < a.split; p++)
+                s += *reinterpret_cast<const f32x4*>(a.ws + (((int64_t)p * a.ntiles + ti) * TT + pos) * B * B + e);
+            const int64_t idx = (int64_t)id * B * B + e;
+            if (a.dwdt == BSMM_F32)
+                store4<BSMM_F32>(a.dw, idx, s);
+            else if (a.dwdt == BSMM_BF16)
+                store4<BSMM_BF16>(a.dw, idx, s);
+            else
+                store4<BSMM_F16>(a.dw, idx, s);
+        }
+    }
+}
+
+// Dense tiles (with a contraction split: partials, then their sum), then the remaining
+// blocks in row groups; one timing record spans the launches.
 template <int DT, int B, int FA>
 static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
     if constexpr (B != 32 || DT == BSMM_F32) {
@@ -716,10 +773,15 @@ static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
     } else {
         void *e0 = nullptr, *e1 = nullptr;
         prof_events(BSMM_PASS_UPDAT, &e0, &e1);
-        const int grid = ((a.ntiles + 7) / 8) * 8;
-        hipError_t e = launch_ev(updt_kernel<DT, FA, 2>, dim3((unsigned)grid), dim3(512), st, e0,
-                                 a.nrest > 0 ? nullptr : e1, a);
-        if (e != hipSuccess || a.nrest == 0) return e;
+        const bool more = a.split > 1 || a.nrest > 0;
+        const int grid = ((a.ntiles * a.split + 7) / 8) * 8;
+        hipError_t e = launch_ev(updt_kernel<DT, FA, 2>, dim3((unsigned)grid), dim3(512), st, e0, more ? nullptr : e1, a);
+        if (e != hipSuccess) return e;
+        if (a.split > 1) {
+            e = launch_ev(updt_reduce<B>, dim3((unsigned)a.ntiles), dim3(256), st, nullptr, a.nrest > 0 ? nullptr : e1, a);
+            if (e != hipSuccess) return e;
+        }
+        if (a.nrest == 0) return hipSuccess;
         return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.rest, a.nrest, st, nullptr, e1, false);
     }
 }
@@ -764,9 +826,8 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
     // dense 8x8-block tiles: 32x32 blocks, 16-bit, long contractions (whole 8-row
     // chunks when features lead)
     const bool tiles_ok = b == 32 && dt != BSMM_F32 && a.ntiles > 0 && steps0 >= 16 && (fa == 1 || a.N % 8 == 0);
-    // enough tiles to occupy at least half the CUs: fewer tiles leave most of the chip
-    // idle for the whole contraction (the remaining blocks run after them)
-    const bool tiles_wide = a.ntiles >= 128;
+    // enough workgroups (tiles x contraction parts) to occupy at least half the CUs
+    const bool tiles_wide = a.ntiles * a.split >= 128;
     if (a.force > 0) return a.force == UP_TILES && !tiles_ok ? -1 : a.force;
     switch (updat_variant()) {
     case 1: return UP_D2B1;

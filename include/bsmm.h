@@ -105,9 +105,11 @@ BSMM_API bsmm_status bsmm_block_coord(bsmm_handle h, int64_t block, int64_t* c, 
 /* Layout description: out = {R, S, b, feature_axis, nnz}. */
 BSMM_API bsmm_status bsmm_plan_info(bsmm_handle h, int64_t out[5]);
 
-/* Bytes of device workspace a pass needs for minibatch N and dtype (0 today for every
- * pass; the ws arguments below exist so that later kernels may use one).
- * pass is a bsmm_pass value. */
+/* Bytes of device workspace a pass needs for minibatch N and dtype.  Non-zero only for
+ * updat with 32x32 blocks and 16-bit activations when the layout has few dense 8x8-block
+ * tiles: the tiles' contraction is then split in parts whose fp32 partial sums live in
+ * the workspace (parts x tiles x 64 x 4 KiB).  updat called with a smaller or NULL
+ * workspace runs unsplit (correct, slower).  pass is a bsmm_pass value. */
 BSMM_API bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype dt, size_t* bytes);
 
 /* fprop: y = x . W~.

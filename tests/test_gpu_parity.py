@@ -275,3 +275,23 @@ def test_updat_dense_tiles(N, G, fa, dtype):
     bits = synth.to_bits
     rdw = oracle.updat(P.layout, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype)
     assert_close(dw, rdw, dtype, "updat")
+
+
+@pytest.mark.parametrize("fa", [1, 0])
+def test_updat_dense_tiles_unsplit(fa):
+    """Enough dense tiles that the contraction is not split (no workspace), chosen
+    automatically."""
+    print(f"case tiles unsplit fa={fa}", flush=True)
+    N = 512
+    rng = np.random.default_rng(77 + fa)
+    L = (rng.random((128, 128)) < 0.3).astype(np.uint8)
+    P = synth.random_problem(rng, L, 32, N, fa, "bf16", w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
+    assert len(bs.bsmm_debug_lut(m.handle, 16)) // 4 >= 128
+    assert bs.bsmm_workspace_size(m.handle, 2, N, torch.bfloat16) == 0
+    assert m.kernel_name("updat", N, torch.bfloat16) == "dense_tiles"
+    dw = m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys])
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    rdw = oracle.updat(P.layout, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, "bf16")
+    assert_close(dw, rdw, "bf16", "updat")
