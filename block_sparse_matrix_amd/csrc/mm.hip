@@ -698,7 +698,11 @@ int mm_kind(const MMArgs& a, int dt, int b, int fa) {
         break;
     default: break;
     }
-    if (groups_ok && a.N >= 1024 && a.gfill >= 25) return MM_GROUPS;
+    // Sparser groups still win once they fill the chip twice over (>= 512 workgroups of
+    // 256 rows): measured on 256x256 layouts at N = 4096, from about 17 % fill (a
+    // Bernoulli(0.1) layout; band + 3 % random at 24 %) against the weight-stack kernel.
+    const int64_t gwgs = (int64_t)((a.N + 255) / 256) * a.ngroups;
+    if (groups_ok && a.N >= 1024 && (a.gfill >= 25 || (a.gfill >= 17 && gwgs >= 512))) return MM_GROUPS;
     // Small minibatch: the weight stream dominates and there are few output tiles, so
     // the 4 waves of a workgroup split each block list (measured fastest at N = 64).
     if (a.N <= 16) return MM_N16;

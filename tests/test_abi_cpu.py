@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import block_sparse_matrix_amd as bs
+import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INVALID, UNSUPPORTED, ALIGN = 1, 2, 3
@@ -153,6 +154,13 @@ def test_kernel_choice_names():
     assert big.kernel_name("updat", 64, torch.bfloat16) == "blocks_2perwave"
     assert m8.kernel_name("updat", 4096, torch.bfloat16) == "row_groups"
     assert m32.kernel_name("identity", 0, torch.bfloat16) == "identity"
+    # 256x256 layouts at N = 4096: the output groups take sparse layouts once there
+    # are >= 512 workgroups and the groups are >= 17 % full
+    band = synth.workload_problem("hidden8192_b32_n4096_g8", "bf16", N=8, G=1).layout   # 24 % full
+    assert bs.BlocksparseMatMul(band, block_size=32).kernel_name("fprop", 4096, torch.bfloat16) == "output_groups"
+    assert bs.BlocksparseMatMul(band, block_size=32).kernel_name("fprop", 1024, torch.bfloat16) == "list_rows128"
+    sparse = (rng.random((256, 256)) < 0.03).astype(np.uint8)   # about 14 % full
+    assert bs.BlocksparseMatMul(sparse, block_size=32).kernel_name("bprop", 4096, torch.bfloat16) == "list_weight_stack"
     with pytest.raises(bs.BsmmError):
         m32.kernel_name("updat", 64, torch.bfloat16, group=9)
 
