@@ -27,13 +27,14 @@ __all__ = [
     "bsmm_create", "bsmm_destroy", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_identity_init",
     "bsmm_w_shape", "bsmm_i_shape", "bsmm_o_shape", "bsmm_block_coord", "bsmm_workspace_size",
     "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
+    "bsmm_layer_norm", "bsmm_layer_norm_grad", "bsmm_layer_norm_workspace_size", "layer_norm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so")
 
 BSMM_OK = 0
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
-PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3}
+PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3, "layer_norm": 4, "layer_norm_grad": 5}
 
 
 class BsmmError(RuntimeError):
@@ -71,6 +72,9 @@ def lib():
         "bsmm_debug_lut": [vp, i32, P64, i64, P64],
         "bsmm_kernel_name": [vp, i32, i64, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
         "bsmm_force_kernel": [vp, i32, ctypes.c_char_p],
+        "bsmm_layer_norm_workspace_size": [i64, i64, i32, i32, i32, ctypes.POINTER(sz)],
+        "bsmm_layer_norm": [vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_float, i32, i32, vp, sz, vp],
+        "bsmm_layer_norm_grad": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, sz, vp],
         "bsmm_profile_begin": [],
         "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
     }
@@ -221,10 +225,93 @@ def bsmm_profile_begin() -> None:
 
 def bsmm_profile_end():
     """Returns {pass: (total_ms, count)} of the kernel times recorded since begin."""
-    ms = (ctypes.c_double * 4)()
-    cnt = (ctypes.c_int64 * 4)()
+    ms = (ctypes.c_double * len(PASS))()
+    cnt = (ctypes.c_int64 * len(PASS))()
     _check(lib().bsmm_profile_end(ms, cnt), "bsmm_profile_end")
     return {name: (ms[i], int(cnt[i])) for name, i in PASS.items()}
+
+
+# ---- layer norm (README, "API Documentation" › blocksparse.norms › layer_norm) -----------
+def bsmm_layer_norm_workspace_size(N: int, C: int, axis: int, grad: bool, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().bsmm_layer_norm_workspace_size(N, C, axis, int(bool(grad)), DTYPE_CODE[dtype], ctypes.byref(n)),
+           "bsmm_layer_norm_workspace_size")
+    return n.value
+
+
+def _ln_dims(x: torch.Tensor, axis: int):
+    if x.dim() != 2:
+        raise ValueError("layer_norm takes a 2-D activation: (N, C) for axis=1, (C, N) for axis=0")
+    if axis not in (0, 1):
+        raise ValueError("axis must be 0 or 1")
+    return (x.shape[0], x.shape[1]) if axis == 1 else (x.shape[1], x.shape[0])
+
+
+def _ln_ws(N, C, axis, grad, dtype, device):
+    nb = bsmm_layer_norm_workspace_size(N, C, axis, grad, dtype)
+    return (torch.empty(nb, dtype=torch.uint8, device=device), nb) if nb else (None, 0)
+
+
+def bsmm_layer_norm(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, y: torch.Tensor,
+                    mean: Optional[torch.Tensor], rstd: Optional[torch.Tensor], axis: int = 1,
+                    epsilon: float = 1e-6, relu: bool = False) -> None:
+    N, C = _ln_dims(x, axis)
+    ws, nb = _ln_ws(N, C, axis, False, x.dtype, x.device)
+    _check(lib().bsmm_layer_norm(_dev_ptr(x, "x"), _dev_ptr(g, "g"), _dev_ptr(b, "b"), _dev_ptr(y, "y"),
+                                 _dev_ptr(mean, "mean"), _dev_ptr(rstd, "rstd"), N, C, axis, float(epsilon),
+                                 int(bool(relu)), DTYPE_CODE[x.dtype], _dev_ptr(ws, "ws"), nb, _stream(x)),
+           "bsmm_layer_norm")
+
+
+def bsmm_layer_norm_grad(dy: torch.Tensor, x: torch.Tensor, g: torch.Tensor, b: torch.Tensor,
+                         mean: torch.Tensor, rstd: torch.Tensor, dx: torch.Tensor, dg: torch.Tensor,
+                         db: torch.Tensor, axis: int = 1, relu: bool = False) -> None:
+    N, C = _ln_dims(x, axis)
+    ws, nb = _ln_ws(N, C, axis, True, x.dtype, x.device)
+    _check(lib().bsmm_layer_norm_grad(_dev_ptr(dy, "dy"), _dev_ptr(x, "x"), _dev_ptr(g, "g"), _dev_ptr(b, "b"),
+                                      _dev_ptr(mean, "mean"), _dev_ptr(rstd, "rstd"), _dev_ptr(dx, "dx"),
+                                      _dev_ptr(dg, "dg"), _dev_ptr(db, "db"), N, C, axis, int(bool(relu)),
+                                      DTYPE_CODE[x.dtype], _dev_ptr(ws, "ws"), nb, _stream(x)),
+           "bsmm_layer_norm_grad")
+
+
+def _ln_param(p: torch.Tensor, C: int, name: str) -> torch.Tensor:
+    if p.dtype != torch.float32 or p.dim() != 1 or p.shape[0] != C:
+        raise ValueError(f"{name} must be a float32 vector of the {C} features")
+    return p
+
+
+class _LayerNormFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, g, b, axis, epsilon, relu):
+        N, C = _ln_dims(x, axis)
+        _ln_param(g, C, "g")
+        _ln_param(b, C, "b")
+        y = torch.empty_like(x)
+        mean = torch.empty(N, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(N, dtype=torch.float32, device=x.device)
+        bsmm_layer_norm(x, g, b, y, mean, rstd, axis, epsilon, relu)
+        ctx.save_for_backward(x, g, b, mean, rstd)
+        ctx.axis, ctx.relu = axis, relu
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, g, b, mean, rstd = ctx.saved_tensors
+        dx = torch.empty_like(x)
+        dg = torch.empty_like(g)
+        db = torch.empty_like(b)
+        bsmm_layer_norm_grad(dy.contiguous(), x, g, b, mean, rstd, dx, dg, db, ctx.axis, ctx.relu)
+        return dx, dg, db, None, None, None
+
+
+def layer_norm(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, axis: int = 1, epsilon: float = 1e-6,
+               relu: bool = False) -> torch.Tensor:
+    """Layer norm over the feature axis of a block-sparse matmul activation, with the
+    optional ReLU at the end (README, "API Documentation" › blocksparse.norms ›
+    layer_norm).  axis=1: x is (N, C); axis=0: x is (C, N).  g, b: float32 (C,).
+    Differentiable in x, g and b."""
+    return _LayerNormFunction.apply(x, g, b, axis, epsilon, relu)
 
 
 # ---- BlocksparseMatMul --------------------------------------------------------------

@@ -509,25 +509,122 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     return BSMM_OK;
 }
 
+// ---- layer norm ----
+namespace {
+bsmm_status ln_check(int64_t N, int64_t C, int axis, bsmm_dtype dt) {
+    if (N < 0 || C < 0) return fail(BSMM_ERR_INVALID_ARG, "N and C must be >= 0");
+    if (axis != 0 && axis != 1) return fail(BSMM_ERR_INVALID_ARG, "axis must be 0 or 1");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    if (N > INT32_MAX || C > INT32_MAX || N * C > INT32_MAX)
+        return fail(BSMM_ERR_UNSUPPORTED, "a tensor above 2^31 elements");
+    return BSMM_OK;
+}
+bsmm_status ln_plan_call(LnArgs& a, int64_t N, int64_t C, int axis, bsmm_dtype dt, bool grad, bool aligned) {
+    a.N = N;
+    a.C = C;
+    a.axis = axis;
+    a.dt = dt;
+    if (ln_plan(a, grad, aligned) != 0)
+        return fail(BSMM_ERR_UNSUPPORTED, "axis 1 row longer than the register-resident kernels hold");
+    return BSMM_OK;
+}
+bsmm_status ln_ws(int64_t N, int64_t C, int axis, bool grad, const void* ws, size_t ws_bytes) {
+    const size_t need = ln_workspace_bytes(N, C, axis, grad);
+    if (need == 0) return BSMM_OK;
+    if (!ws || ws_bytes < need) return fail(BSMM_ERR_INVALID_ARG, "workspace smaller than bsmm_layer_norm_workspace_size");
+    if (!aligned16(ws)) return fail(BSMM_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+    return BSMM_OK;
+}
+bool params_aligned(const float* g, const float* b) { return aligned16(g) && aligned16(b); }
+}  // namespace
+
+bsmm_status bsmm_layer_norm_workspace_size(int64_t N, int64_t C, int axis, int grad, bsmm_dtype dt, size_t* bytes) {
+    if (!bytes) return fail(BSMM_ERR_INVALID_ARG, "bytes is NULL");
+    bsmm_status s = ln_check(N, C, axis, dt);
+    if (s != BSMM_OK) return s;
+    *bytes = ln_workspace_bytes(N, C, axis, grad != 0);
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_layer_norm(const void* x, const float* g, const float* b, void* y, float* mean, float* rstd,
+                            int64_t N, int64_t C, int axis, float epsilon, int relu, bsmm_dtype dt, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!(epsilon >= 0.f) || epsilon > 3.0e38f) return fail(BSMM_ERR_INVALID_ARG, "epsilon must be finite and >= 0");
+    if ((mean == nullptr) != (rstd == nullptr)) return fail(BSMM_ERR_INVALID_ARG, "mean and rstd: both or neither");
+    bsmm_status s = ln_check(N, C, axis, dt);
+    if (s != BSMM_OK || N == 0 || C == 0) return s;
+    if (!g || !b) return fail(BSMM_ERR_INVALID_ARG, "g / b is NULL");
+    if ((s = check_ptr(x, "x")) != BSMM_OK || (s = check_ptr(y, "y")) != BSMM_OK) return s;
+    if ((s = ln_ws(N, C, axis, false, ws, ws_bytes)) != BSMM_OK) return s;
+    LnArgs a{};
+    // 16-byte parameter loads need aligned g, b (axis 1); else one value per load
+    if ((s = ln_plan_call(a, N, C, axis, dt, false, axis == 0 || params_aligned(g, b))) != BSMM_OK) return s;
+    a.x = x;
+    a.y = y;
+    a.g = g;
+    a.b = b;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.ws = (float*)ws;
+    a.eps = epsilon;
+    a.relu = relu ? 1 : 0;
+    prof_events(BSMM_PASS_LAYER_NORM, &a.e0, &a.e1);
+    hipError_t e = launch_layer_norm(a, false, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "layer_norm launch");
+}
+
+bsmm_status bsmm_layer_norm_grad(const void* dy, const void* x, const float* g, const float* b, const float* mean,
+                                 const float* rstd, void* dx, float* dg, float* db, int64_t N, int64_t C, int axis,
+                                 int relu, bsmm_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+    bsmm_status s = ln_check(N, C, axis, dt);
+    if (s != BSMM_OK || C == 0) return s;
+    if (!dg || !db) return fail(BSMM_ERR_INVALID_ARG, "dg / db is NULL");
+    if (N == 0) {   // no vectors: the parameter gradients are zero
+        hipError_t e = launch_ln_zero_params(dg, db, C, stream);
+        return e == hipSuccess ? BSMM_OK : dev_fail(e, "layer_norm_grad launch");
+    }
+    if (!g || !b || !mean || !rstd) return fail(BSMM_ERR_INVALID_ARG, "NULL parameter or statistics");
+    if ((s = check_ptr(x, "x")) != BSMM_OK || (s = check_ptr(dy, "dy")) != BSMM_OK ||
+        (s = check_ptr(dx, "dx")) != BSMM_OK)
+        return s;
+    if ((s = ln_ws(N, C, axis, true, ws, ws_bytes)) != BSMM_OK) return s;
+    LnArgs a{};
+    if ((s = ln_plan_call(a, N, C, axis, dt, true, axis == 0 || params_aligned(g, b))) != BSMM_OK) return s;
+    a.x = x;
+    a.dy = dy;
+    a.dx = dx;
+    a.g = g;
+    a.b = b;
+    a.mean = const_cast<float*>(mean);
+    a.rstd = const_cast<float*>(rstd);
+    a.dg = dg;
+    a.db = db;
+    a.ws = (float*)ws;
+    a.relu = relu ? 1 : 0;
+    prof_events(BSMM_PASS_LAYER_NORM_GRAD, &a.e0, &a.e1);
+    hipError_t e = launch_layer_norm(a, true, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "layer_norm_grad launch");
+}
+
 bsmm_status bsmm_profile_begin(void) {
     g_prof.on = true;
     return BSMM_OK;
 }
 
-bsmm_status bsmm_profile_end(double ms[4], int64_t count[4]) {
+bsmm_status bsmm_profile_end(double ms[BSMM_NUM_PASSES], int64_t count[BSMM_NUM_PASSES]) {
     if (!g_prof.on) return fail(BSMM_ERR_INVALID_ARG, "profiling was not begun on this thread");
     g_prof.on = false;
     if (ms)
-        for (int i = 0; i < 4; i++) ms[i] = 0.0;
+        for (int i = 0; i < BSMM_NUM_PASSES; i++) ms[i] = 0.0;
     if (count)
-        for (int i = 0; i < 4; i++) count[i] = 0;
+        for (int i = 0; i < BSMM_NUM_PASSES; i++) count[i] = 0;
     bsmm_status st = BSMM_OK;
     for (auto& r : g_prof.recs) {
         hipError_t e = hipEventSynchronize(r.e1);
         float t = 0.f;
         if (e == hipSuccess) e = hipEventElapsedTime(&t, r.e0, r.e1);
         if (e != hipSuccess && st == BSMM_OK) st = dev_fail(e, "profile event");
-        if (r.pass >= 0 && r.pass < 4) {
+        if (r.pass >= 0 && r.pass < BSMM_NUM_PASSES) {
             if (ms) ms[r.pass] += t;
             if (count) count[r.pass] += 1;
         }

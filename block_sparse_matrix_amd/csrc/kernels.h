@@ -92,6 +92,37 @@ hipError_t launch_mm_groups(const MMArgs& a, int dt, int fa, bool transw, void* 
 hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream);
 hipError_t launch_identity(void* w, const int32_t* coords, int64_t nnz, int b, int dt, void* stream);
 
+// Layer norm over the feature axis (norm.hip).  Axis 1: x, y (N, C); axis 0: (C, N).
+struct LnArgs {
+    const void* x;
+    void* y;
+    const void* dy;
+    void* dx;
+    const float* g;
+    const float* b;
+    float* mean;    // forward: written (may be NULL); gradient: read
+    float* rstd;
+    float* dg;
+    float* db;
+    float* ws;      // workspace (ln_workspace_bytes)
+    int64_t N, C;
+    int axis, dt, relu;
+    float eps;
+    // set by ln_plan
+    int vw;         // storage values per load: 16 bytes' worth, or 1
+    int nv;         // axis 1: loads per thread per row
+    int64_t rpb;    // axis 1 gradient: rows per workgroup
+    int nparts;     // gradient: partial dg/db sets in the workspace
+    int nchunks;    // axis 0: 128-row chunks
+    void *e0, *e1;  // timing events around the launches (or NULL)
+};
+// Fills the plan fields; -1 if a row (axis 1) is too long for the register-resident
+// kernels.  `aligned`: every tensor base is 16-byte aligned.
+int ln_plan(LnArgs& a, bool grad, bool aligned);
+size_t ln_workspace_bytes(int64_t N, int64_t C, int axis, bool grad);   // any plan fits
+hipError_t launch_layer_norm(const LnArgs& a, bool grad, void* stream);
+hipError_t launch_ln_zero_params(float* dg, float* db, int64_t C, void* stream);   // dg = db = 0
+
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.
 void prof_events(int pass, void** start, void** stop);

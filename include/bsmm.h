@@ -74,7 +74,15 @@ typedef enum {
 
 typedef enum { BSMM_F32 = 0, BSMM_BF16 = 1, BSMM_F16 = 2 } bsmm_dtype;
 
-typedef enum { BSMM_PASS_FPROP = 0, BSMM_PASS_BPROP = 1, BSMM_PASS_UPDAT = 2, BSMM_PASS_IDENTITY = 3 } bsmm_pass;
+typedef enum {
+    BSMM_PASS_FPROP = 0,
+    BSMM_PASS_BPROP = 1,
+    BSMM_PASS_UPDAT = 2,
+    BSMM_PASS_IDENTITY = 3,
+    BSMM_PASS_LAYER_NORM = 4,
+    BSMM_PASS_LAYER_NORM_GRAD = 5
+} bsmm_pass;
+#define BSMM_NUM_PASSES 6
 
 typedef struct bsmm_plan* bsmm_handle;
 
@@ -201,14 +209,48 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);
 
+/* Layer norm over the feature axis, with an optional ReLU at the end ([README] "API
+ * Documentation" › blocksparse.norms › layer_norm(x, g, b, axis=1, epsilon=1e-6,
+ * relu=False): a layer norm for both activation layouts of the matmul above).
+ * Per normalised vector -- a row of x (N, C) for axis = 1, a column of x (C, N) for
+ * axis = 0 -- with mean and biased variance over its C features:
+ *   y = (x - mean) * rstd * g + b,  rstd = 1/sqrt(var + epsilon),  then max(y, 0) if relu.
+ * x, y: dense row-major in dtype dt (y may not alias x); g, b: float32[C] (gain, bias);
+ * mean, rstd: float32[N] outputs for the gradient (both NULL to skip).  Statistics
+ * and sums are fp32, in a fixed order (deterministic); y is rounded to nearest even.
+ * ws: at least bsmm_layer_norm_workspace_size bytes (16-byte aligned; may be NULL when
+ * that is 0), caller-owned scratch.  Asynchronous on hip_stream.
+ * Errors: BSMM_ERR_INVALID_ARG (NULL tensor, N or C < 0, axis not 0/1, bad dtype,
+ * epsilon < 0 or not finite, mean/rstd only one of them NULL, small workspace);
+ * BSMM_ERR_ALIGNMENT (x or y not 16-byte aligned); BSMM_ERR_UNSUPPORTED (axis 1 with
+ * C above 16384 for 16-bit or 8192 for fp32 storage, or a tensor above 2^31 elements);
+ * BSMM_ERR_DEVICE.  Axis 0 also needs C <= 65535*128.  N = 0 or C = 0: no-op. */
+BSMM_API bsmm_status bsmm_layer_norm_workspace_size(int64_t N, int64_t C, int axis, int grad, bsmm_dtype dt,
+                                                    size_t* bytes);
+BSMM_API bsmm_status bsmm_layer_norm(const void* x, const float* g, const float* b, void* y, float* mean,
+                                     float* rstd, int64_t N, int64_t C, int axis, float epsilon, int relu,
+                                     bsmm_dtype dt, void* ws, size_t ws_bytes, void* hip_stream);
+/* Gradient of bsmm_layer_norm for upstream gradient dy (same layout and dtype as x),
+ * from the forward's mean and rstd (not recomputed):
+ *   dyr = dy, or dy * [xhat * g + b > 0] when relu,   xhat = (x - mean) * rstd,
+ *   dx = rstd * (dyr*g - mean_C(dyr*g) - xhat * mean_C(dyr*g * xhat)),
+ *   dg = sum over vectors of dyr * xhat,   db = sum over vectors of dyr   (float32[C]).
+ * dx, dg, db are overwritten; ws as above (bsmm_layer_norm_workspace_size with
+ * grad = 1).  Errors as for bsmm_layer_norm (dx, dy 16-byte aligned). */
+BSMM_API bsmm_status bsmm_layer_norm_grad(const void* dy, const void* x, const float* g, const float* b,
+                                          const float* mean, const float* rstd, void* dx, float* dg, float* db,
+                                          int64_t N, int64_t C, int axis, int relu, bsmm_dtype dt, void* ws,
+                                          size_t ws_bytes, void* hip_stream);
+
 /* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
  * every pass launched from the calling thread records HIP events around its kernels
  * (hipExtLaunchKernelGGL start/stop events, i.e. the dispatch's own timestamps).
- * bsmm_profile_end waits for those events and writes, per bsmm_pass index 0..3, the
- * summed milliseconds and the number of passes recorded (arrays of 4).  Errors:
+ * bsmm_profile_end waits for those events and writes, per bsmm_pass index
+ * 0..BSMM_NUM_PASSES-1, the summed milliseconds and the number of passes recorded
+ * (arrays of BSMM_NUM_PASSES).  Errors:
  * BSMM_ERR_INVALID_ARG when not begun; BSMM_ERR_DEVICE. */
 BSMM_API bsmm_status bsmm_profile_begin(void);
-BSMM_API bsmm_status bsmm_profile_end(double ms[4], int64_t count[4]);
+BSMM_API bsmm_status bsmm_profile_end(double ms[BSMM_NUM_PASSES], int64_t count[BSMM_NUM_PASSES]);
 
 #ifdef __cplusplus
 }

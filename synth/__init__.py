@@ -169,3 +169,38 @@ def to_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float32:
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclasses.dataclass
+class NormProblem:
+    """Seeded inputs of a layer norm over the feature axis (x and dy in the activation
+    layout of `axis`: (N, C) for 1, (C, N) for 0; g and b float32 (C,))."""
+    N: int
+    C: int
+    axis: int
+    dtype: str
+    x: torch.Tensor
+    dy: torch.Tensor
+    g: torch.Tensor
+    b: torch.Tensor
+
+
+def norm_problem(rng: np.random.Generator, N: int, C: int, axis: int, dtype: str,
+                 relu_margin: bool = False) -> NormProblem:
+    """x ~ N(shift, scale) per vector (shift and scale drawn per vector), dy ~ N(0, 1),
+    g ~ N(1, 0.25), b ~ N(0, 0.25).  With relu_margin, |g| <= 0.25 and |b| >= 2, so
+    g*xhat + b keeps the sign of b while |xhat| < 8 (no value near the ReLU's kink)."""
+    shape = act_shape(axis, N, C)
+    shift = rng.standard_normal(N).astype(np.float32) * 2
+    scale = (0.5 + rng.random(N)).astype(np.float32)
+    z = rng.standard_normal(shape).astype(np.float32)
+    xv = z * (scale[:, None] if axis == 1 else scale[None, :]) + (shift[:, None] if axis == 1 else shift[None, :])
+    x = torch.from_numpy(xv).to(DTYPES[dtype])
+    dy = _draw(rng, shape, 1.0, dtype)
+    if relu_margin:
+        g = (rng.random(C).astype(np.float32) - 0.5) * 0.5
+        b = (2 + rng.random(C).astype(np.float32)) * np.where(rng.random(C) < 0.5, -1, 1).astype(np.float32)
+    else:
+        g = (1 + 0.25 * rng.standard_normal(C)).astype(np.float32)
+        b = (0.25 * rng.standard_normal(C)).astype(np.float32)
+    return NormProblem(N, C, axis, dtype, x, dy, torch.from_numpy(g), torch.from_numpy(b))

@@ -183,3 +183,37 @@ def test_force_kernel():
     # a forced family that cannot serve the call: reported as "none", rejected at call time
     m.force_kernel("updat", "dense_tiles")
     assert m.kernel_name("updat", 4096, torch.float32) == "none"
+
+
+def test_layer_norm_arguments():
+    """Argument checks of the layer-norm entry points (all before any HIP call)."""
+    L = bs.lib()
+    sz = ctypes.c_size_t()
+    assert L.bsmm_layer_norm_workspace_size(4096, 8192, 1, 0, 1, ctypes.byref(sz)) == 0 and sz.value == 0
+    assert L.bsmm_layer_norm_workspace_size(4096, 8192, 1, 1, 1, ctypes.byref(sz)) == 0
+    assert sz.value == 2 * 256 * 8192 * 4              # 256 runs of 16 rows: dg and db partials
+    assert L.bsmm_layer_norm_workspace_size(100, 300, 0, 0, 0, ctypes.byref(sz)) == 0
+    assert sz.value == 3 * 100 * 8                     # 3 chunks of 128 rows x (mean, M2) per column
+    assert L.bsmm_layer_norm_workspace_size(100, 300, 0, 1, 0, ctypes.byref(sz)) == 0
+    assert sz.value == 3 * 100 * 8 + 2 * 4 * 300 * 4  # + 4 column blocks of dg and db partials
+    assert L.bsmm_layer_norm_workspace_size(8, 8, 2, 0, 1, ctypes.byref(sz)) == 1   # axis
+    assert L.bsmm_layer_norm_workspace_size(-1, 8, 1, 0, 1, ctypes.byref(sz)) == 1
+    assert L.bsmm_layer_norm_workspace_size(8, 8, 1, 0, 9, ctypes.byref(sz)) == 1   # dtype
+    vp = ctypes.c_void_p
+    A, B = vp(0x10000), vp(0x20000)   # never dereferenced: every call below fails its checks
+    f = ctypes.c_float
+
+    def ln(x, y, N, C, axis, eps=1e-6, dt=1, ws=None, nb=0, mean=None, rstd=None):
+        return L.bsmm_layer_norm(x, A, B, y, mean, rstd, N, C, axis, f(eps), 0, dt, ws, nb, None)
+
+    assert ln(None, B, 4, 8, 1) == 1                  # x NULL
+    assert ln(vp(0x10008), B, 4, 8, 1) == 3           # x not 16-byte aligned
+    assert ln(A, B, 4, 8, 1, eps=-1.0) == 1           # epsilon < 0
+    assert ln(A, B, 4, 8, 1, mean=A) == 1             # mean without rstd
+    assert ln(A, B, 4, 8, 3) == 1                     # axis
+    assert ln(A, B, 100, 300, 0) == 1                 # axis 0 needs a workspace
+    assert ln(A, B, 4, 16384, 1, dt=0) == 2           # fp32 rows above 8192 features
+    assert ln(A, B, 0, 8, 1) == 0                     # N = 0: no-op
+    assert L.bsmm_layer_norm_grad(A, A, A, B, A, B, None, A, B, 4, 8, 1, 0, 1, None, 0, None) == 1   # dx NULL
+    assert L.bsmm_layer_norm_grad(A, A, A, B, A, B, A, None, B, 4, 8, 1, 0, 1, None, 0, None) == 1   # dg NULL
+    assert L.bsmm_layer_norm_grad(A, A, A, B, A, B, A, A, B, 4, 8, 1, 0, 1, None, 0, None) == 1      # no workspace
