@@ -59,6 +59,7 @@ def parse():
                     help="run bprop and updat concurrently on two streams in the timed graph "
                          "(measured slower on MI355X: the two kernels compete rather than overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer-norm", action="store_true", help="skip the layer_norm timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -288,6 +289,46 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
                 identity_us=ident[0] / max(ident[1], 1) * 1e3, layout_ms=t_layout * 1e3, prep_s=t_prep)
 
 
+def run_layer_norm(reps=20):
+    """Kernel time of layer_norm and its gradient on the band workload's activation
+    (N = 4096 vectors of C = 8192 bf16 features), both feature axes, over rotating buffer
+    sets; HBM-bound: algorithmic bytes = |x| + |y| forward, |x| + |dy| + |dx| gradient."""
+    import numpy as np
+    import torch
+    import block_sparse_matrix_amd as bs
+    import synth
+    N, C, dt = 4096, 8192, "bf16"
+    out = {"workload": "layer_norm, N=4096 x C=8192 bf16 (hidden8192_b32_n4096_g8 activation)", "epsilon": 1e-6}
+    for axis in (1, 0):
+        P = synth.norm_problem(np.random.default_rng(7 + axis), N, C, axis, dt)
+        R = 4   # 4 sets x 4 tensors x 64 MiB: timed launches read HBM, not the 256 MiB cache
+        xs = [P.x.cuda() for _ in range(R)]
+        dys = [P.dy.cuda() for _ in range(R)]
+        ys = [torch.empty_like(xs[0]) for _ in range(R)]
+        dxs = [torch.empty_like(xs[0]) for _ in range(R)]
+        g, b = P.g.cuda(), P.b.cuda()
+        mean, rstd = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+        dg, db = torch.empty_like(g), torch.empty_like(b)
+        for i in range(4):
+            bs.bsmm_layer_norm(xs[i % R], g, b, ys[i % R], mean, rstd, axis, 1e-6, False)
+            bs.bsmm_layer_norm_grad(dys[i % R], xs[i % R], g, b, mean, rstd, dxs[i % R], dg, db, axis, False)
+        torch.cuda.synchronize()
+        bs.bsmm_profile_begin()
+        for i in range(reps):
+            bs.bsmm_layer_norm(xs[i % R], g, b, ys[i % R], mean, rstd, axis, 1e-6, False)
+            bs.bsmm_layer_norm_grad(dys[i % R], xs[i % R], g, b, mean, rstd, dxs[i % R], dg, db, axis, False)
+        torch.cuda.synchronize()
+        pr = bs.bsmm_profile_end()
+        act = N * C * 2
+        for key, nb in (("layer_norm", 2 * act + 2 * C * 4), ("layer_norm_grad", 3 * act + 4 * C * 4)):
+            us = pr[key][0] / pr[key][1] * 1e3
+            gbs = nb / (us * 1e-6) / 1e9
+            out[f"{key}_axis{axis}"] = {"kernel_us": round(us, 3), "alg_bytes": nb, "achieved_GBps": round(gbs, 1),
+                                        "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                        "bound": "hbm"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -341,6 +382,8 @@ def main():
                       "eager_ms_per_step": round(r["ms_eager"], 5), "per_pass": r["per"]}
     if extras:
         out["other_dtypes"] = extras
+    if not args.no_layer_norm:
+        out["layer_norm"] = run_layer_norm()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
     else:

@@ -181,7 +181,10 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_rows(LnArgs a) {
     }
 }
 
-// axis 1, gradient: rows [blockIdx.x*RPB, +RPB); per-run partial dg, db to the workspace
+// axis 1, gradient: rows [blockIdx.x*RPB, +RPB); per-run partial dg, db to the
+// workspace.  The next row's x and dy are loaded while the current row is reduced
+// (always issued: the last row re-reads itself; lanes past C read element 0, unused),
+// for rows of up to 32 values per thread.
 template <int DT, int VW, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
     __shared__ float red[8];
@@ -190,41 +193,53 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
     const int64_t r0 = (int64_t)blockIdx.x * a.rpb;
     const int64_t r1 = r0 + a.rpb < a.N ? r0 + a.rpb : a.N;
     float pg[NV][VW], pb[NV][VW], g[NV][VW], b[NV][VW];
+    int el[NV];
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         const int e = (i * kLnThreads + t) * VW;
+        el[i] = e < C ? e : 0;
+        ln_param<VW>(a.g, el[i], g[i]);
+        ln_param<VW>(a.b, el[i], b[i]);
 #pragma unroll
-        for (int k = 0; k < VW; k++) pg[i][k] = pb[i][k] = g[i][k] = b[i][k] = 0.f;
-        if (e < C) {
-            ln_param<VW>(a.g, e, g[i]);
-            ln_param<VW>(a.b, e, b[i]);
-        }
+        for (int k = 0; k < VW; k++) pg[i][k] = pb[i][k] = 0.f;
     }
+    float xn[NV][VW], dn[NV][VW];
+    auto load_row = [&](int64_t n) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            ln_load<DT, VW>(a.x, n * C + el[i], xn[i]);
+            ln_load<DT, VW>(a.dy, n * C + el[i], dn[i]);
+        }
+    };
+    // prefetch only while the two row copies fit the registers (<= 32 values per thread)
+    constexpr bool PF = NV * VW <= 32;
+    if constexpr (PF) load_row(r0);
     for (int64_t n = r0; n < r1; n++) {   // workgroup-uniform
-        const int64_t row = n * C;
+        if constexpr (!PF) load_row(n);
+        float x[NV][VW], dy[NV][VW];
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+#pragma unroll
+            for (int k = 0; k < VW; k++) {
+                x[i][k] = xn[i][k];
+                dy[i][k] = dn[i][k];
+            }
+        if constexpr (PF) load_row(n + 1 < r1 ? n + 1 : n);
         const float mean = a.mean[n], rstd = a.rstd[n];
-        float xh[NV][VW], dh[NV][VW];
+        // xhat and dyr*g are recomputed for dx below rather than kept (registers)
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int e = (i * kLnThreads + t) * VW;
+            const bool ok = (i * kLnThreads + t) * VW < C;
 #pragma unroll
-            for (int k = 0; k < VW; k++) xh[i][k] = dh[i][k] = 0.f;
-            if (e < C) {
-                float x[VW], dy[VW];
-                ln_load<DT, VW>(a.x, row + e, x);
-                ln_load<DT, VW>(a.dy, row + e, dy);
-#pragma unroll
-                for (int k = 0; k < VW; k++) {
-                    const float xhat = (x[k] - mean) * rstd;
-                    const float dyr = dy[k] * ln_keep(a.relu, xhat * g[i][k] + b[i][k]);
-                    pg[i][k] += dyr * xhat;
-                    pb[i][k] += dyr;
-                    xh[i][k] = xhat;
-                    dh[i][k] = dyr * g[i][k];
-                    s1 += dh[i][k];
-                    s2 += dh[i][k] * xhat;
-                }
+            for (int k = 0; k < VW; k++) {
+                const float xhat = (x[i][k] - mean) * rstd;
+                const float dyr = ok ? dy[i][k] * ln_keep(a.relu, xhat * g[i][k] + b[i][k]) : 0.f;
+                const float dh = dyr * g[i][k];
+                pg[i][k] += dyr * xhat;
+                pb[i][k] += dyr;
+                s1 += dh;
+                s2 += dh * xhat;
             }
         }
         ln_sum2(s1, s2, red);
@@ -235,8 +250,12 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
             if (e < C) {
                 float dx[VW];
 #pragma unroll
-                for (int k = 0; k < VW; k++) dx[k] = rstd * (dh[i][k] - m1 - xh[i][k] * m2);
-                ln_store<DT, VW>(a.dx, row + e, dx);
+                for (int k = 0; k < VW; k++) {
+                    const float xhat = (x[i][k] - mean) * rstd;
+                    const float dh = dy[i][k] * ln_keep(a.relu, xhat * g[i][k] + b[i][k]) * g[i][k];
+                    dx[k] = rstd * (dh - m1 - xhat * m2);
+                }
+                ln_store<DT, VW>(a.dx, n * C + e, dx);
             }
         }
     }
@@ -255,17 +274,81 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
     }
 }
 
-// dg[c], db[c]: the nparts partials of the workspace added in part order
+// dg[c], db[c] from the nparts partials of the workspace: a workgroup takes 32
+// features; lane l of 8 adds the parts p = l, l + 8, ... in order, then the 8 lane sums
+// are added in lane order (a fixed order: deterministic).
+constexpr int kLnRedCols = 32;
 __global__ __launch_bounds__(kLnThreads) void ln_param_reduce(LnArgs a, int64_t len, const float* wg, const float* wb) {
-    const int64_t c = (int64_t)blockIdx.x * kLnThreads + threadIdx.x;
-    if (c >= len) return;
+    __shared__ float red[2][8][kLnRedCols];
+    const int cl = threadIdx.x % kLnRedCols, pl = threadIdx.x / kLnRedCols;
+    const int64_t c = (int64_t)blockIdx.x * kLnRedCols + cl;
+    const bool ok = c < len;
+    const int64_t cc = ok ? c : 0;
     float sg = 0.f, sb = 0.f;
-    for (int p = 0; p < a.nparts; p++) {
-        sg += wg[(int64_t)p * len + c];
-        sb += wb[(int64_t)p * len + c];
+    int p = pl;
+    for (; p + 24 < a.nparts; p += 32) {   // four parts in flight per lane
+        const float g0 = wg[(int64_t)p * len + cc], g1 = wg[(int64_t)(p + 8) * len + cc];
+        const float g2 = wg[(int64_t)(p + 16) * len + cc], g3 = wg[(int64_t)(p + 24) * len + cc];
+        const float b0 = wb[(int64_t)p * len + cc], b1 = wb[(int64_t)(p + 8) * len + cc];
+        const float b2 = wb[(int64_t)(p + 16) * len + cc], b3 = wb[(int64_t)(p + 24) * len + cc];
+        sg = (((sg + g0) + g1) + g2) + g3;
+        sb = (((sb + b0) + b1) + b2) + b3;
     }
-    a.dg[c] = sg;
-    a.db[c] = sb;
+    for (; p < a.nparts; p += 8) {
+        sg += wg[(int64_t)p * len + cc];
+        sb += wb[(int64_t)p * len + cc];
+    }
+    red[0][pl][cl] = sg;
+    red[1][pl][cl] = sb;
+    __syncthreads();
+    if (pl == 0 && ok) {
+        float tg = 0.f, tb = 0.f;
+#pragma unroll
+        for (int l = 0; l < 8; l++) {
+            tg += red[0][l][cl];
+            tb += red[1][l][cl];
+        }
+        a.dg[c] = tg;
+        a.db[c] = tb;
+    }
+}
+
+// axis 0: the chunks' partial statistics of each column merged once, in chunk order,
+// into chunk 0's slot of the workspace: forward (mean, rstd) from (mean, M2) pairs
+// (pairwise update of count, mean and squared deviations); gradient (mean of dyr*g,
+// mean of dyr*g*xhat) from plain sums.
+__global__ __launch_bounds__(kLnThreads) void ln_cols_merge(LnArgs a, int grad) {
+    const int64_t n = (int64_t)blockIdx.x * kLnThreads + threadIdx.x;
+    if (n >= a.N) return;
+    float2* w = reinterpret_cast<float2*>(a.ws);
+    if (grad) {
+        float m1 = 0.f, m2 = 0.f;
+        for (int c = 0; c < a.nchunks; c++) {
+            const float2 st = w[(int64_t)c * a.N + n];
+            m1 += st.x;
+            m2 += st.y;
+        }
+        w[n] = make_float2(m1 / (float)a.C, m2 / (float)a.C);
+        return;
+    }
+    float mean = 0.f, m2 = 0.f;
+    double cnt = 0.0;
+    for (int c = 0; c < a.nchunks; c++) {
+        const int64_t left = a.C - (int64_t)c * kLnChunk;
+        const double nb = (double)(left < kLnChunk ? left : kLnChunk);
+        const double tot = cnt + nb;
+        const float2 st = w[(int64_t)c * a.N + n];
+        const float d = st.x - mean;
+        mean += d * (float)(nb / tot);
+        m2 += st.y + d * d * (float)(cnt * nb / tot);
+        cnt = tot;
+    }
+    const float rstd = 1.0f / sqrtf(m2 / (float)a.C + a.eps);
+    w[n] = make_float2(mean, rstd);
+    if (a.mean) {
+        a.mean[n] = mean;
+        a.rstd[n] = rstd;
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -304,35 +387,46 @@ template <int VW> __device__ __forceinline__ void ln_sum_lanes(float* v, float* 
     __syncthreads();
 }
 
+// Rows rl + 8j, j < RJ, of this thread's chunk: every load is issued, rows past the
+// chunk's end re-read its first row and are masked out of every use.
+constexpr int kLnRJ = kLnChunk / 8;
+template <int DT, int VW, int J>
+__device__ __forceinline__ void ln_load_rows(const void* base, const LnCols& p, int64_t N, int j0, float (*v)[VW]) {
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int r = p.rl + 8 * (j0 + j);
+        ln_load<DT, VW>(base, (p.r0 + (r < p.nrows ? r : 0)) * N + p.n0, v[j]);
+    }
+}
+
 // forward pass 1: per chunk and column, the chunk's mean and sum of squared deviations
+// (the chunk's rows stay in registers between the two sums)
 template <int DT, int VW>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_cols_stats(LnArgs a) {
     __shared__ float red[8 * 32 * VW];
-    const LnCols p = ln_cols<VW>(a);
-    float s[VW], q[VW];
+    LnCols p = ln_cols<VW>(a);
+    if (!p.colok) p.n0 = 0;   // loads stay in bounds; results unused
+    float x[kLnRJ][VW];
+    ln_load_rows<DT, VW, kLnRJ>(a.x, p, a.N, 0, x);
+    float s[VW], q[VW], m[VW];
 #pragma unroll
     for (int k = 0; k < VW; k++) s[k] = q[k] = 0.f;
-    if (p.colok)
-        for (int r = p.rl; r < p.nrows; r += 8) {
-            float x[VW];
-            ln_load<DT, VW>(a.x, (p.r0 + r) * a.N + p.n0, x);
 #pragma unroll
-            for (int k = 0; k < VW; k++) s[k] += x[k];
-        }
+    for (int j = 0; j < kLnRJ; j++)
+        if (p.rl + 8 * j < p.nrows)
+#pragma unroll
+            for (int k = 0; k < VW; k++) s[k] += x[j][k];
     ln_sum_lanes<VW>(s, red);
-    float m[VW];
 #pragma unroll
     for (int k = 0; k < VW; k++) m[k] = s[k] / (float)p.nrows;
-    if (p.colok)
-        for (int r = p.rl; r < p.nrows; r += 8) {   // second read of the chunk: from cache
-            float x[VW];
-            ln_load<DT, VW>(a.x, (p.r0 + r) * a.N + p.n0, x);
+#pragma unroll
+    for (int j = 0; j < kLnRJ; j++)
+        if (p.rl + 8 * j < p.nrows)
 #pragma unroll
             for (int k = 0; k < VW; k++) {
-                const float d = x[k] - m[k];
+                const float d = x[j][k] - m[k];
                 q[k] += d * d;
             }
-        }
     ln_sum_lanes<VW>(q, red);
     if (p.rl == 0 && p.colok) {
         float2* w = reinterpret_cast<float2*>(a.ws) + (int64_t)blockIdx.y * a.N + p.n0;
@@ -341,147 +435,143 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_cols_stats(LnArgs a) {
     }
 }
 
-// forward pass 2: merge the chunks' statistics (chunk order), normalise this chunk
+// forward pass 3 (after ln_cols_merge): normalise this chunk
 template <int DT, int VW>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_cols_norm(LnArgs a) {
     const LnCols p = ln_cols<VW>(a);
     if (!p.colok) return;   // no barrier below
-    float mean[VW], m2[VW];
-    double cnt = 0.0;
+    float x[kLnRJ][VW];
+    ln_load_rows<DT, VW, kLnRJ>(a.x, p, a.N, 0, x);
+    float mean[VW], rstd[VW];
+    const float2* w = reinterpret_cast<const float2*>(a.ws);   // merged: (mean, rstd)
 #pragma unroll
-    for (int k = 0; k < VW; k++) mean[k] = m2[k] = 0.f;
-    const float2* w = reinterpret_cast<const float2*>(a.ws);
-    for (int c = 0; c < a.nchunks; c++) {
-        const int64_t left = a.C - (int64_t)c * kLnChunk;
-        const double nb = (double)(left < kLnChunk ? left : kLnChunk);
-        const double tot = cnt + nb;
-        const float fa = (float)(nb / tot), fb = (float)(cnt * nb / tot);
-#pragma unroll
-        for (int k = 0; k < VW; k++) {
-            const float2 st = w[(int64_t)c * a.N + p.n0 + k];
-            const float d = st.x - mean[k];
-            mean[k] += d * fa;
-            m2[k] += st.y + d * d * fb;
-        }
-        cnt = tot;
+    for (int k = 0; k < VW; k++) {
+        const float2 st = w[p.n0 + k];
+        mean[k] = st.x;
+        rstd[k] = st.y;
     }
-    float rstd[VW];
 #pragma unroll
-    for (int k = 0; k < VW; k++) rstd[k] = 1.0f / sqrtf(m2[k] / (float)a.C + a.eps);
-    if (blockIdx.y == 0 && p.rl == 0 && a.mean) {
+    for (int j = 0; j < kLnRJ; j++) {
+        const int r = p.rl + 8 * j;
+        if (r < p.nrows) {
+            const int64_t c = p.r0 + r;
+            const float g = a.g[c], b = a.b[c];
+            float y[VW];
 #pragma unroll
-        for (int k = 0; k < VW; k++) {
-            a.mean[p.n0 + k] = mean[k];
-            a.rstd[p.n0 + k] = rstd[k];
+            for (int k = 0; k < VW; k++) {
+                y[k] = (x[j][k] - mean[k]) * rstd[k] * g + b;
+                if (a.relu) y[k] = fmaxf(y[k], 0.f);
+            }
+            ln_store<DT, VW>(a.y, c * a.N + p.n0, y);
         }
-    }
-    for (int r = p.rl; r < p.nrows; r += 8) {
-        const int64_t c = p.r0 + r;
-        const float g = a.g[c], b = a.b[c];
-        float x[VW], y[VW];
-        ln_load<DT, VW>(a.x, c * a.N + p.n0, x);
-#pragma unroll
-        for (int k = 0; k < VW; k++) {
-            y[k] = (x[k] - mean[k]) * rstd[k] * g + b;
-            if (a.relu) y[k] = fmaxf(y[k], 0.f);
-        }
-        ln_store<DT, VW>(a.y, c * a.N + p.n0, y);
     }
 }
 
 // gradient pass 1: per chunk and column the sums of dyr*g and dyr*g*xhat (workspace
-// part 1); per row and column block the sums of dyr*xhat and dyr (part 2)
+// part 1); per row and column block the sums of dyr*xhat and dyr (part 2).  The chunk
+// is taken in two halves of 8 rows per thread, each half's loads issued together.
 template <int DT, int VW>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_cols_stats(LnArgs a) {
     __shared__ float red[8 * 32 * VW];
-    const LnCols p = ln_cols<VW>(a);
+    LnCols p = ln_cols<VW>(a);
+    const bool colok = p.colok;
+    if (!colok) p.n0 = 0;   // loads stay in bounds; contributions masked
     float s1[VW], s2[VW], mean[VW], rstd[VW];
 #pragma unroll
     for (int k = 0; k < VW; k++) {
         s1[k] = s2[k] = 0.f;
-        mean[k] = p.colok ? a.mean[p.n0 + k] : 0.f;
-        rstd[k] = p.colok ? a.rstd[p.n0 + k] : 0.f;
+        mean[k] = a.mean[p.n0 + k];
+        rstd[k] = a.rstd[p.n0 + k];
     }
     float* pg = a.ws + (int64_t)a.nchunks * a.N * 2 + (int64_t)blockIdx.x * a.C;
     float* pb = pg + (int64_t)a.nparts * a.C;
-    for (int r = p.rl; r < kLnChunk; r += 8) {   // uniform trip count: shuffles below
-        const bool rok = r < p.nrows;
-        const int64_t c = p.r0 + (rok ? r : 0);
-        const float g = a.g[c], b = a.b[c];
-        float rg = 0.f, rb = 0.f;
-        if (p.colok && rok) {
-            float x[VW], dy[VW];
-            ln_load<DT, VW>(a.x, c * a.N + p.n0, x);
-            ln_load<DT, VW>(a.dy, c * a.N + p.n0, dy);
+    constexpr int H = kLnRJ / 2;
 #pragma unroll
-            for (int k = 0; k < VW; k++) {
-                const float xhat = (x[k] - mean[k]) * rstd[k];
-                const float dyr = dy[k] * ln_keep(a.relu, xhat * g + b);
-                const float dh = dyr * g;
-                s1[k] += dh;
-                s2[k] += dh * xhat;
-                rg += dyr * xhat;
-                rb += dyr;
+    for (int h = 0; h < kLnRJ; h += H) {
+        float x[H][VW], dy[H][VW];
+        ln_load_rows<DT, VW, H>(a.x, p, a.N, h, x);
+        ln_load_rows<DT, VW, H>(a.dy, p, a.N, h, dy);
+#pragma unroll
+        for (int j = 0; j < H; j++) {
+            const int r = p.rl + 8 * (h + j);
+            const bool rok = r < p.nrows;
+            const int64_t c = p.r0 + (rok ? r : 0);
+            const float g = a.g[c], b = a.b[c];
+            float rg = 0.f, rb = 0.f;
+            if (colok && rok) {
+#pragma unroll
+                for (int k = 0; k < VW; k++) {
+                    const float xhat = (x[j][k] - mean[k]) * rstd[k];
+                    const float dyr = dy[j][k] * ln_keep(a.relu, xhat * g + b);
+                    const float dh = dyr * g;
+                    s1[k] += dh;
+                    s2[k] += dh * xhat;
+                    rg += dyr * xhat;
+                    rb += dyr;
+                }
             }
-        }
-        // the row's sums over this block's columns: the 32 column lanes of a half wave
+            // the row's sums over this block's columns: the 32 column lanes of a half wave
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) {
-            rg += __shfl_xor(rg, o);
-            rb += __shfl_xor(rb, o);
-        }
-        if (p.cv == 0 && rok) {
-            pg[c] = rg;
-            pb[c] = rb;
+            for (int o = 16; o > 0; o >>= 1) {
+                rg += __shfl_xor(rg, o);
+                rb += __shfl_xor(rb, o);
+            }
+            if (p.cv == 0 && rok) {
+                pg[c] = rg;
+                pb[c] = rb;
+            }
         }
     }
     ln_sum_lanes<VW>(s1, red);
     ln_sum_lanes<VW>(s2, red);
-    if (p.rl == 0 && p.colok) {
+    if (p.rl == 0 && colok) {
         float2* w = reinterpret_cast<float2*>(a.ws) + (int64_t)blockIdx.y * a.N + p.n0;
 #pragma unroll
         for (int k = 0; k < VW; k++) w[k] = make_float2(s1[k], s2[k]);
     }
 }
 
-// gradient pass 2: the chunks' column sums added in chunk order, then dx of this chunk
+// gradient pass 3 (after ln_cols_merge): dx of this chunk
 template <int DT, int VW>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_cols_dx(LnArgs a) {
     const LnCols p = ln_cols<VW>(a);
     if (!p.colok) return;
+    constexpr int H = kLnRJ / 2;
+    float x[H][VW], dy[H][VW];
+    ln_load_rows<DT, VW, H>(a.x, p, a.N, 0, x);
+    ln_load_rows<DT, VW, H>(a.dy, p, a.N, 0, dy);
     float m1[VW], m2[VW], mean[VW], rstd[VW];
+    const float2* w = reinterpret_cast<const float2*>(a.ws);   // merged column means
 #pragma unroll
     for (int k = 0; k < VW; k++) {
-        m1[k] = m2[k] = 0.f;
+        const float2 st = w[p.n0 + k];
+        m1[k] = st.x;
+        m2[k] = st.y;
         mean[k] = a.mean[p.n0 + k];
         rstd[k] = a.rstd[p.n0 + k];
     }
-    const float2* w = reinterpret_cast<const float2*>(a.ws);
-    for (int c = 0; c < a.nchunks; c++)
 #pragma unroll
-        for (int k = 0; k < VW; k++) {
-            const float2 st = w[(int64_t)c * a.N + p.n0 + k];
-            m1[k] += st.x;
-            m2[k] += st.y;
+    for (int h = 0; h < kLnRJ; h += H) {
+        if (h > 0) {
+            ln_load_rows<DT, VW, H>(a.x, p, a.N, h, x);
+            ln_load_rows<DT, VW, H>(a.dy, p, a.N, h, dy);
         }
 #pragma unroll
-    for (int k = 0; k < VW; k++) {
-        m1[k] /= (float)a.C;
-        m2[k] /= (float)a.C;
-    }
-    for (int r = p.rl; r < p.nrows; r += 8) {
-        const int64_t c = p.r0 + r;
-        const float g = a.g[c], b = a.b[c];
-        float x[VW], dy[VW], dx[VW];
-        ln_load<DT, VW>(a.x, c * a.N + p.n0, x);
-        ln_load<DT, VW>(a.dy, c * a.N + p.n0, dy);
+        for (int j = 0; j < H; j++) {
+            const int r = p.rl + 8 * (h + j);
+            if (r < p.nrows) {
+                const int64_t c = p.r0 + r;
+                const float g = a.g[c], b = a.b[c];
+                float dx[VW];
 #pragma unroll
-        for (int k = 0; k < VW; k++) {
-            const float xhat = (x[k] - mean[k]) * rstd[k];
-            const float dyr = dy[k] * ln_keep(a.relu, xhat * g + b);
-            dx[k] = rstd[k] * (dyr * g - m1[k] - xhat * m2[k]);
+                for (int k = 0; k < VW; k++) {
+                    const float xhat = (x[j][k] - mean[k]) * rstd[k];
+                    const float dyr = dy[j][k] * ln_keep(a.relu, xhat * g + b);
+                    dx[k] = rstd[k] * (dyr * g - m1[k] - xhat * m2[k]);
+                }
+                ln_store<DT, VW>(a.dx, c * a.N + p.n0, dx);
+            }
         }
-        ln_store<DT, VW>(a.dx, c * a.N + p.n0, dx);
     }
 }
 
@@ -500,7 +590,7 @@ hipError_t ln_rows_nv(LnArgs a, int nv, bool grad, hipStream_t st) {
             hipError_t e = launch_ev(ln_bwd_rows<DT, VW, NVV>, dim3((unsigned)a.nparts), blk, st,   \
                                      a.e0, nullptr, a);                                          \
             if (e != hipSuccess) return e;                                                        \
-            return launch_ev(ln_param_reduce, dim3((unsigned)((a.C + kLnThreads - 1) / kLnThreads)), \
+            return launch_ev(ln_param_reduce, dim3((unsigned)((a.C + kLnRedCols - 1) / kLnRedCols)), \
                              blk, st, nullptr, a.e1, a, a.C, (const float*)a.ws,                  \
                              (const float*)(a.ws + (int64_t)a.nparts * a.C));                     \
         }                                                                                         \
@@ -520,17 +610,17 @@ hipError_t ln_rows_nv(LnArgs a, int nv, bool grad, hipStream_t st) {
 template <int DT, int VW>
 hipError_t ln_cols_launch(LnArgs a, bool grad, hipStream_t st) {
     const dim3 grid((unsigned)((a.N + 32 * VW - 1) / (32 * VW)), (unsigned)a.nchunks), blk(kLnThreads);
-    if (!grad) {
-        hipError_t e = launch_ev(ln_fwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a);
-        if (e != hipSuccess) return e;
-        return launch_ev(ln_fwd_cols_norm<DT, VW>, grid, blk, st, nullptr, a.e1, a);
-    }
-    hipError_t e = launch_ev(ln_bwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a);
+    const dim3 mgrid((unsigned)((a.N + kLnThreads - 1) / kLnThreads));
+    hipError_t e = grad ? launch_ev(ln_bwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a)
+                        : launch_ev(ln_fwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a);
     if (e != hipSuccess) return e;
+    e = launch_ev(ln_cols_merge, mgrid, blk, st, nullptr, nullptr, a, grad ? 1 : 0);
+    if (e != hipSuccess) return e;
+    if (!grad) return launch_ev(ln_fwd_cols_norm<DT, VW>, grid, blk, st, nullptr, a.e1, a);
     e = launch_ev(ln_bwd_cols_dx<DT, VW>, grid, blk, st, nullptr, nullptr, a);
     if (e != hipSuccess) return e;
     const float* pg = a.ws + (int64_t)a.nchunks * a.N * 2;
-    return launch_ev(ln_param_reduce, dim3((unsigned)((a.C + kLnThreads - 1) / kLnThreads)), blk, st, nullptr,
+    return launch_ev(ln_param_reduce, dim3((unsigned)((a.C + kLnRedCols - 1) / kLnRedCols)), blk, st, nullptr,
                      a.e1, a, a.C, pg, pg + (int64_t)a.nparts * a.C);
 }
 
@@ -589,7 +679,7 @@ hipError_t launch_ln_zero_params(float* dg, float* db, int64_t C, void* stream) 
     a.dg = dg;
     a.db = db;
     a.nparts = 0;
-    return launch_ev(ln_param_reduce, dim3((unsigned)((C + kLnThreads - 1) / kLnThreads)), dim3(kLnThreads),
+    return launch_ev(ln_param_reduce, dim3((unsigned)((C + kLnRedCols - 1) / kLnRedCols)), dim3(kLnThreads),
                      (hipStream_t)stream, nullptr, nullptr, a, C, (const float*)nullptr, (const float*)nullptr);
 }
 
