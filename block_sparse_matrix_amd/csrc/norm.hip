@@ -102,8 +102,9 @@ template <int VW> __device__ __forceinline__ void ln_param(const float* p, int64
 // `relu && !(pre > 0) ? 0 : dy` into a store of 0 for every lane of the ReLU branch.
 __device__ __forceinline__ float ln_keep(int relu, float pre) { return (relu == 0 || pre > 0.f) ? 1.f : 0.f; }
 
-// Sum of (a, b) over the 256 threads: butterfly within each wave, then the four wave
-// totals in wave order.  Every thread gets the result.
+// Sum of (a, b) over the workgroup's W waves: butterfly within each wave, then the W
+// wave totals in wave order.  Every thread gets the result.
+template <int W = kLnThreads / 64>
 __device__ __forceinline__ void ln_sum2(float& a, float& b, float* red) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -116,8 +117,13 @@ __device__ __forceinline__ void ln_sum2(float& a, float& b, float* red) {
         red[2 * w + 1] = b;
     }
     __syncthreads();
-    a = (red[0] + red[2]) + (red[4] + red[6]);
-    b = (red[1] + red[3]) + (red[5] + red[7]);
+    a = 0.f;
+    b = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; i++) {
+        a += red[2 * i];
+        b += red[2 * i + 1];
+    }
     __syncthreads();   // red is reused by the next call
 }
 
@@ -182,12 +188,14 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_rows(LnArgs a) {
 }
 
 // axis 1, gradient: rows [blockIdx.x*RPB, +RPB); per-run partial dg, db to the
-// workspace.  The next row's x and dy are loaded while the current row is reduced
-// (always issued: the last row re-reads itself; lanes past C read element 0, unused),
-// for rows of up to 32 values per thread.
+// workspace.  The next two rows' x and dy are in flight while the current row is
+// reduced (always issued: past the run's end a row re-reads itself; lanes past C read
+// element 0, unused).
+constexpr int kLnBwdThreads = 512;   // 8 waves: two per SIMD hide each other's latency
 template <int DT, int VW, int NV>
-__global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
-    __shared__ float red[8];
+__global__ __launch_bounds__(kLnBwdThreads) void ln_bwd_rows(LnArgs a) {
+    constexpr int kLnThreads = kLnBwdThreads;   // element e = (i*512 + t)*VW + k
+    __shared__ float red[16];
     const int t = threadIdx.x;
     const int C = (int)a.C;
     const int64_t r0 = (int64_t)blockIdx.x * a.rpb;
@@ -203,29 +211,47 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
 #pragma unroll
         for (int k = 0; k < VW; k++) pg[i][k] = pb[i][k] = 0.f;
     }
-    float xn[NV][VW], dn[NV][VW];
-    auto load_row = [&](int64_t n) {
+    // two rows ahead in registers (slots A = row n+1, B = row n+2 when the loop body
+    // starts), for rows of up to 16 values per thread; longer rows load in the body
+    constexpr bool PF = NV * VW <= 16;
+    // (the row's mean and rstd travel with it: a load issued after the prefetch and
+    // consumed at once would make the wave wait for the prefetch too)
+    float xa[NV][VW], da[NV][VW], xb[NV][VW], db_[NV][VW];
+    float ma = 0.f, ra = 0.f, mb = 0.f, rb = 0.f;
+    auto load_row = [&](int64_t n, float (*xo)[VW], float (*dout)[VW], float& mo, float& ro) {
+        mo = a.mean[n];
+        ro = a.rstd[n];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            ln_load<DT, VW>(a.x, n * C + el[i], xn[i]);
-            ln_load<DT, VW>(a.dy, n * C + el[i], dn[i]);
+            ln_load<DT, VW>(a.x, n * C + el[i], xo[i]);
+            ln_load<DT, VW>(a.dy, n * C + el[i], dout[i]);
         }
     };
-    // prefetch only while the two row copies fit the registers (<= 32 values per thread)
-    constexpr bool PF = NV * VW <= 32;
-    if constexpr (PF) load_row(r0);
+    if constexpr (PF) {
+        load_row(r0, xa, da, ma, ra);
+        load_row(r0 + 1 < r1 ? r0 + 1 : r0, xb, db_, mb, rb);
+    }
     for (int64_t n = r0; n < r1; n++) {   // workgroup-uniform
-        if constexpr (!PF) load_row(n);
         float x[NV][VW], dy[NV][VW];
+        float mean, rstd;
+        if constexpr (PF) {
 #pragma unroll
-        for (int i = 0; i < NV; i++)
+            for (int i = 0; i < NV; i++)
 #pragma unroll
-            for (int k = 0; k < VW; k++) {
-                x[i][k] = xn[i][k];
-                dy[i][k] = dn[i][k];
-            }
-        if constexpr (PF) load_row(n + 1 < r1 ? n + 1 : n);
-        const float mean = a.mean[n], rstd = a.rstd[n];
+                for (int k = 0; k < VW; k++) {
+                    x[i][k] = xa[i][k];
+                    dy[i][k] = da[i][k];
+                    xa[i][k] = xb[i][k];
+                    da[i][k] = db_[i][k];
+                }
+            mean = ma;
+            rstd = ra;
+            ma = mb;
+            ra = rb;
+            load_row(n + 2 < r1 ? n + 2 : n, xb, db_, mb, rb);
+        } else {
+            load_row(n, x, dy, mean, rstd);
+        }
         // xhat and dyr*g are recomputed for dx below rather than kept (registers)
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_rows(LnArgs a) {
                 s2 += dh * xhat;
             }
         }
-        ln_sum2(s1, s2, red);
+        ln_sum2<kLnBwdThreads / 64>(s1, s2, red);
         const float m1 = s1 / (float)C, m2 = s2 / (float)C;
 #pragma unroll
         for (int i = 0; i < NV; i++) {
@@ -313,40 +339,63 @@ __global__ __launch_bounds__(kLnThreads) void ln_param_reduce(LnArgs a, int64_t 
     }
 }
 
-// axis 0: the chunks' partial statistics of each column merged once, in chunk order,
-// into chunk 0's slot of the workspace: forward (mean, rstd) from (mean, M2) pairs
-// (pairwise update of count, mean and squared deviations); gradient (mean of dyr*g,
-// mean of dyr*g*xhat) from plain sums.
+// axis 0: the chunks' partial statistics of each column merged once into chunk 0's
+// slot of the workspace.  A workgroup takes 32 columns; lane l of 8 merges chunks
+// l, l + 8, ... in order, then the 8 lane results are merged in lane order (a fixed
+// order: deterministic).  Forward: (mean, rstd) from per-chunk (mean, M2) by the
+// pairwise update of count, mean and squared deviations; gradient: (mean of dyr*g,
+// mean of dyr*g*xhat) from plain per-chunk sums.
+struct LnStat {
+    double n;
+    float mean, m2;
+};
+__device__ __forceinline__ void ln_stat_add(LnStat& a, double nb, float mb, float m2b) {
+    const double tot = a.n + nb;
+    if (tot == 0.0) return;
+    const float d = mb - a.mean;
+    a.mean += d * (float)(nb / tot);
+    a.m2 += m2b + d * d * (float)(a.n * nb / tot);
+    a.n = tot;
+}
 __global__ __launch_bounds__(kLnThreads) void ln_cols_merge(LnArgs a, int grad) {
-    const int64_t n = (int64_t)blockIdx.x * kLnThreads + threadIdx.x;
-    if (n >= a.N) return;
+    __shared__ float red[3][8][32];
+    const int cl = threadIdx.x & 31, l = threadIdx.x >> 5;
+    const int64_t n = (int64_t)blockIdx.x * 32 + cl;
+    const bool ok = n < a.N;
+    const int64_t nn = ok ? n : 0;
     float2* w = reinterpret_cast<float2*>(a.ws);
-    if (grad) {
-        float m1 = 0.f, m2 = 0.f;
-        for (int c = 0; c < a.nchunks; c++) {
-            const float2 st = w[(int64_t)c * a.N + n];
-            m1 += st.x;
-            m2 += st.y;
+    LnStat st{0.0, 0.f, 0.f};
+    float s1 = 0.f, s2 = 0.f;
+    for (int c = l; c < a.nchunks; c += 8) {
+        const float2 v = w[(int64_t)c * a.N + nn];
+        if (grad) {
+            s1 += v.x;
+            s2 += v.y;
+        } else {
+            const int64_t left = a.C - (int64_t)c * kLnChunk;
+            ln_stat_add(st, (double)(left < kLnChunk ? left : kLnChunk), v.x, v.y);
         }
-        w[n] = make_float2(m1 / (float)a.C, m2 / (float)a.C);
+    }
+    red[0][l][cl] = grad ? s1 : st.mean;
+    red[1][l][cl] = grad ? s2 : st.m2;
+    red[2][l][cl] = (float)st.n;   // chunk rows: exact in float (at most C)
+    __syncthreads();   // every chunk's slot has been read: slot 0 may be overwritten
+    if (l != 0 || !ok) return;
+    if (grad) {
+        float t1 = 0.f, t2 = 0.f;
+        for (int k = 0; k < 8; k++) {
+            t1 += red[0][k][cl];
+            t2 += red[1][k][cl];
+        }
+        w[n] = make_float2(t1 / (float)a.C, t2 / (float)a.C);
         return;
     }
-    float mean = 0.f, m2 = 0.f;
-    double cnt = 0.0;
-    for (int c = 0; c < a.nchunks; c++) {
-        const int64_t left = a.C - (int64_t)c * kLnChunk;
-        const double nb = (double)(left < kLnChunk ? left : kLnChunk);
-        const double tot = cnt + nb;
-        const float2 st = w[(int64_t)c * a.N + n];
-        const float d = st.x - mean;
-        mean += d * (float)(nb / tot);
-        m2 += st.y + d * d * (float)(cnt * nb / tot);
-        cnt = tot;
-    }
-    const float rstd = 1.0f / sqrtf(m2 / (float)a.C + a.eps);
-    w[n] = make_float2(mean, rstd);
+    LnStat tot{0.0, 0.f, 0.f};
+    for (int k = 0; k < 8; k++) ln_stat_add(tot, (double)red[2][k][cl], red[0][k][cl], red[1][k][cl]);
+    const float rstd = 1.0f / sqrtf(tot.m2 / (float)a.C + a.eps);
+    w[n] = make_float2(tot.mean, rstd);
     if (a.mean) {
-        a.mean[n] = mean;
+        a.mean[n] = tot.mean;
         a.rstd[n] = rstd;
     }
 }
@@ -587,7 +636,7 @@ hipError_t ln_rows_nv(LnArgs a, int nv, bool grad, hipStream_t st) {
         if constexpr (VW == 1 || NVV <= 8) { /* 16-byte loads: at most 8 per thread */           \
             if (!grad)                                                                            \
                 return launch_ev(ln_fwd_rows<DT, VW, NVV>, dim3((unsigned)a.N), blk, st, a.e0, a.e1, a); \
-            hipError_t e = launch_ev(ln_bwd_rows<DT, VW, NVV>, dim3((unsigned)a.nparts), blk, st,   \
+            hipError_t e = launch_ev(ln_bwd_rows<DT, VW, NVV>, dim3((unsigned)a.nparts), dim3(kLnBwdThreads), st, \
                                      a.e0, nullptr, a);                                          \
             if (e != hipSuccess) return e;                                                        \
             return launch_ev(ln_param_reduce, dim3((unsigned)((a.C + kLnRedCols - 1) / kLnRedCols)), \
@@ -610,7 +659,7 @@ hipError_t ln_rows_nv(LnArgs a, int nv, bool grad, hipStream_t st) {
 template <int DT, int VW>
 hipError_t ln_cols_launch(LnArgs a, bool grad, hipStream_t st) {
     const dim3 grid((unsigned)((a.N + 32 * VW - 1) / (32 * VW)), (unsigned)a.nchunks), blk(kLnThreads);
-    const dim3 mgrid((unsigned)((a.N + kLnThreads - 1) / kLnThreads));
+    const dim3 mgrid((unsigned)((a.N + 31) / 32));
     hipError_t e = grad ? launch_ev(ln_bwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a)
                         : launch_ev(ln_fwd_cols_stats<DT, VW>, grid, blk, st, a.e0, nullptr, a);
     if (e != hipSuccess) return e;
@@ -641,7 +690,7 @@ int ln_plan(LnArgs& a, bool grad, bool aligned) {
     const int vec = a.dt == BSMM_F32 ? 4 : 8;
     if (a.axis == 1) {
         a.vw = (aligned && a.C % vec == 0) ? vec : 1;
-        const int64_t per = (int64_t)kLnThreads * a.vw;
+        const int64_t per = (int64_t)(grad ? kLnBwdThreads : kLnThreads) * a.vw;
         const int64_t need = (a.C + per - 1) / per;
         int nv = 1;
         while (nv < need) nv *= 2;
