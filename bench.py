@@ -59,7 +59,7 @@ def parse():
                     help="run bprop and updat concurrently on two streams in the timed graph "
                          "(measured slower on MI355X: the two kernels compete rather than overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-layer-norm", action="store_true", help="skip the layer_norm timing")
+    ap.add_argument("--no-layer-norm", action="store_true", help="skip the layer_norm and l2_normalize timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -329,6 +329,42 @@ def run_layer_norm(reps=20):
     return out
 
 
+def run_l2_normalize(P, reps=40):
+    """Kernel time of BlocksparseMatMul.l2_normalize (weight normalisation per output
+    feature, bf16 weights -> bf16) and its gradient (bf16 upstream -> fp32 dW) on this
+    workload's layout, over rotating weight sets; HBM-bound: algorithmic bytes = |W| read
+    + |W| written forward, |dOut| + |W| read + |dW| (fp32) written for the gradient."""
+    import torch
+    import block_sparse_matrix_amd as bs
+    m = bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
+    w0 = P.w.to(torch.bfloat16)
+    R = 16
+    ws = [w0.cuda() for _ in range(R)]
+    outs = [torch.empty_like(ws[0]) for _ in range(R)]
+    dys = [torch.ones_like(ws[0]) for _ in range(R)]
+    dws = [torch.empty(ws[0].shape, device="cuda") for _ in range(R)]
+    g = torch.ones(m.K, device="cuda")
+    dg = torch.empty_like(g)
+    for i in range(3):
+        bs.bsmm_l2_normalize(m.handle, ws[i], g, outs[i], None)
+        bs.bsmm_l2_normalize_grad(m.handle, dys[i], ws[i], g, dws[i], dg)
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    for i in range(reps):
+        bs.bsmm_l2_normalize(m.handle, ws[i % R], g, outs[i % R], None)
+        bs.bsmm_l2_normalize_grad(m.handle, dys[i % R], ws[i % R], g, dws[i % R], dg)
+    torch.cuda.synchronize()
+    pr = bs.bsmm_profile_end()
+    W = w0.numel() * 2
+    out = {"workload": f"l2_normalize on the {P.nnz}-block layout, bf16 weights"}
+    for key, nb in (("l2_normalize", 2 * W + 8 * m.K), ("l2_normalize_grad", 2 * W + 2 * W + 8 * m.K)):
+        us = pr[key][0] / pr[key][1] * 1e3
+        gbs = nb / (us * 1e-6) / 1e9
+        out[key] = {"kernel_us": round(us, 3), "alg_bytes": nb, "achieved_GBps": round(gbs, 1),
+                    "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -384,6 +420,7 @@ def main():
         out["other_dtypes"] = extras
     if not args.no_layer_norm:
         out["layer_norm"] = run_layer_norm()
+        out["l2_normalize"] = run_l2_normalize(P)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
     else:

@@ -28,13 +28,15 @@ __all__ = [
     "bsmm_w_shape", "bsmm_i_shape", "bsmm_o_shape", "bsmm_block_coord", "bsmm_workspace_size",
     "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
     "bsmm_layer_norm", "bsmm_layer_norm_grad", "bsmm_layer_norm_workspace_size", "layer_norm",
+    "bsmm_l2_normalize", "bsmm_l2_normalize_grad",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so")
 
 BSMM_OK = 0
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
-PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3, "layer_norm": 4, "layer_norm_grad": 5}
+PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3, "layer_norm": 4, "layer_norm_grad": 5,
+        "l2_normalize": 6, "l2_normalize_grad": 7}
 
 
 class BsmmError(RuntimeError):
@@ -75,6 +77,8 @@ def lib():
         "bsmm_layer_norm_workspace_size": [i64, i64, i32, i32, i32, ctypes.POINTER(sz)],
         "bsmm_layer_norm": [vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_float, i32, i32, vp, sz, vp],
         "bsmm_layer_norm_grad": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, sz, vp],
+        "bsmm_l2_normalize": [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
+        "bsmm_l2_normalize_grad": [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
         "bsmm_profile_begin": [],
         "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
     }
@@ -314,6 +318,41 @@ def layer_norm(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, axis: int = 1,
     return _LayerNormFunction.apply(x, g, b, axis, epsilon, relu)
 
 
+# ---- weight normalisation (README, BlocksparseMatMul.l2_normalize) --------------------
+def bsmm_l2_normalize(h, w: torch.Tensor, gain: Optional[torch.Tensor], w_out: torch.Tensor,
+                      norms: Optional[torch.Tensor], epsilon: float = 1e-6) -> None:
+    _check(lib().bsmm_l2_normalize(h, _dev_ptr(w, "w"), _dev_ptr(gain, "gain"), _dev_ptr(w_out, "w_out"),
+                                   _dev_ptr(norms, "norms"), float(epsilon), DTYPE_CODE[w.dtype],
+                                   DTYPE_CODE[w_out.dtype], _stream(w)), "bsmm_l2_normalize")
+
+
+def bsmm_l2_normalize_grad(h, dy: torch.Tensor, w: torch.Tensor, gain: Optional[torch.Tensor], dw: torch.Tensor,
+                           dgain: Optional[torch.Tensor], epsilon: float = 1e-6) -> None:
+    _check(lib().bsmm_l2_normalize_grad(h, _dev_ptr(dy, "dy"), _dev_ptr(w, "w"), _dev_ptr(gain, "gain"),
+                                        _dev_ptr(dw, "dw"), _dev_ptr(dgain, "dgain"), float(epsilon),
+                                        DTYPE_CODE[dy.dtype], DTYPE_CODE[w.dtype], _stream(w)),
+           "bsmm_l2_normalize_grad")
+
+
+class _L2NormalizeFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, bsmm, w, gain, epsilon, dtype):
+        out = torch.empty(w.shape, dtype=dtype, device=w.device)
+        bsmm_l2_normalize(bsmm.handle, w, gain, out, None, epsilon)
+        ctx.save_for_backward(w, gain if gain is not None else torch.empty(0))
+        ctx.bsmm, ctx.eps, ctx.has_gain = bsmm, epsilon, gain is not None
+        return out
+
+    @staticmethod
+    def backward(ctx, dy):
+        w, gain = ctx.saved_tensors
+        gain = gain if ctx.has_gain else None
+        dw = torch.empty(w.shape, dtype=torch.float32, device=w.device)
+        dgain = torch.empty_like(gain) if gain is not None else None
+        bsmm_l2_normalize_grad(ctx.bsmm.handle, dy.contiguous(), w, gain, dw, dgain, ctx.eps)
+        return None, dw.to(w.dtype), dgain, None, None
+
+
 # ---- BlocksparseMatMul --------------------------------------------------------------
 class _Handle:
     def __init__(self, h):
@@ -452,6 +491,17 @@ class BlocksparseMatMul:
         dw = out if out is not None else torch.empty(self.w_shape, dtype=dw_dtype, device=xs[0].device)
         bsmm_updat(self.handle, xs, dys, dw, N)
         return dw
+
+    def l2_normalize(self, w: torch.Tensor, gain: Optional[torch.Tensor] = None, epsilon: float = 1e-6,
+                     dtype=torch.float32) -> torch.Tensor:
+        """Weight normalisation of the stored blocks per output feature (README,
+        BlocksparseMatMul.l2_normalize): w * gain[o] / sqrt(max(sum over the output
+        feature's column of w^2, epsilon)); gain: float32 (K,) or None; the result in
+        `dtype`.  Differentiable in w and gain."""
+        self._check_w(w, w.dtype)
+        if gain is not None and (gain.dtype != torch.float32 or tuple(gain.shape) != (self.K,)):
+            raise ValueError("gain must be a float32 vector of the K output features")
+        return _L2NormalizeFunction.apply(self, w, gain, epsilon, dtype)
 
     def __call__(self, x: torch.Tensor, w: torch.Tensor, dw_dtype=torch.float32) -> torch.Tensor:
         """y = x . W, differentiable in x and w (bprop and updat kernels)."""

@@ -606,6 +606,69 @@ bsmm_status bsmm_layer_norm_grad(const void* dy, const void* x, const float* g, 
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "layer_norm_grad launch");
 }
 
+// ---- weight normalisation ----
+namespace {
+bsmm_status wn_setup(bsmm_handle h, float epsilon, int dt1, int dt2, WnArgs& a, const DeviceLut** d) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (!valid_dt(dt1) || !valid_dt(dt2)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    if (!(epsilon > 0.f) || epsilon > 3.0e38f) return fail(BSMM_ERR_INVALID_ARG, "epsilon must be finite and > 0");
+    a.S = h->lut.S;
+    a.b = h->lut.b;
+    a.eps = epsilon;
+    if (h->lut.nnz == 0) return BSMM_OK;
+    return device_lut(h, d);
+}
+}  // namespace
+
+bsmm_status bsmm_l2_normalize(bsmm_handle h, const void* w, const float* gain, void* w_out, float* norms,
+                              float epsilon, bsmm_dtype w_dt, bsmm_dtype out_dt, void* stream) {
+    WnArgs a{};
+    if (h && h->lut.nnz > 0) {
+        bsmm_status s;
+        if ((s = check_ptr(w, "w")) != BSMM_OK || (s = check_ptr(w_out, "w_out")) != BSMM_OK) return s;
+    }
+    const DeviceLut* d = nullptr;
+    bsmm_status s = wn_setup(h, epsilon, w_dt, out_dt, a, &d);
+    if (s != BSMM_OK || h->lut.nnz == 0) return s;
+    a.w = w;
+    a.out = w_out;
+    a.gain = gain;
+    a.norms = norms;
+    a.colptr = d->colptr;
+    a.colent = d->colent;
+    a.w_dt = w_dt;
+    a.out_dt = out_dt;
+    prof_events(BSMM_PASS_L2_NORMALIZE, &a.e0, &a.e1);
+    hipError_t e = launch_l2_normalize(a, false, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "l2_normalize launch");
+}
+
+bsmm_status bsmm_l2_normalize_grad(bsmm_handle h, const void* dy, const void* w, const float* gain, void* dw,
+                                   float* dgain, float epsilon, bsmm_dtype dy_dt, bsmm_dtype w_dt, void* stream) {
+    WnArgs a{};
+    if (h && h->lut.nnz > 0) {
+        bsmm_status s;
+        if ((s = check_ptr(dy, "dy")) != BSMM_OK || (s = check_ptr(w, "w")) != BSMM_OK ||
+            (s = check_ptr(dw, "dw")) != BSMM_OK)
+            return s;
+    }
+    const DeviceLut* d = nullptr;
+    bsmm_status s = wn_setup(h, epsilon, dy_dt, w_dt, a, &d);
+    if (s != BSMM_OK || h->lut.nnz == 0) return s;
+    a.w = w;
+    a.dy = dy;
+    a.out = dw;
+    a.gain = gain;
+    a.dgain = dgain;
+    a.colptr = d->colptr;
+    a.colent = d->colent;
+    a.w_dt = w_dt;
+    a.dy_dt = dy_dt;
+    prof_events(BSMM_PASS_L2_NORMALIZE_GRAD, &a.e0, &a.e1);
+    hipError_t e = launch_l2_normalize(a, true, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "l2_normalize_grad launch");
+}
+
 bsmm_status bsmm_profile_begin(void) {
     g_prof.on = true;
     return BSMM_OK;

@@ -123,6 +123,23 @@ size_t ln_workspace_bytes(int64_t N, int64_t C, int axis, bool grad);   // any p
 hipError_t launch_layer_norm(const LnArgs& a, bool grad, void* stream);
 hipError_t launch_ln_zero_params(float* dg, float* db, int64_t C, void* stream);   // dg = db = 0
 
+// Weight normalisation per output feature over the stored blocks (wnorm.hip).
+struct WnArgs {
+    const void* w;          // (nnz, b, b), w_dt
+    const void* dy;         // gradient: upstream gradient of the output, dy_dt
+    void* out;              // forward: normalised weights (out_dt); gradient: dW (float32)
+    const float* gain;      // K = S*b, or NULL (gain 1)
+    float* norms;           // forward: K column norms, or NULL
+    float* dgain;           // gradient: K, or NULL
+    const int32_t* colptr;  // fprop column lists (device layout tables)
+    const int32_t* colent;
+    int64_t S;
+    int b, w_dt, out_dt, dy_dt;
+    float eps;
+    void *e0, *e1;
+};
+hipError_t launch_l2_normalize(const WnArgs& a, bool grad, void* stream);
+
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.
 void prof_events(int pass, void** start, void** stop);

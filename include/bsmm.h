@@ -80,9 +80,11 @@ typedef enum {
     BSMM_PASS_UPDAT = 2,
     BSMM_PASS_IDENTITY = 3,
     BSMM_PASS_LAYER_NORM = 4,
-    BSMM_PASS_LAYER_NORM_GRAD = 5
+    BSMM_PASS_LAYER_NORM_GRAD = 5,
+    BSMM_PASS_L2_NORMALIZE = 6,
+    BSMM_PASS_L2_NORMALIZE_GRAD = 7
 } bsmm_pass;
-#define BSMM_NUM_PASSES 6
+#define BSMM_NUM_PASSES 8
 
 typedef struct bsmm_plan* bsmm_handle;
 
@@ -241,6 +243,28 @@ BSMM_API bsmm_status bsmm_layer_norm_grad(const void* dy, const void* x, const f
                                           const float* mean, const float* rstd, void* dx, float* dg, float* db,
                                           int64_t N, int64_t C, int axis, int relu, bsmm_dtype dt, void* ws,
                                           size_t ws_bytes, void* hip_stream);
+
+/* Weight normalisation of the stored blocks ([README] "API Documentation" ›
+ * blocksparse.matmul › BlocksparseMatMul.l2_normalize(W, gain=None, epsilon=1e-6,
+ * dtype): "to implement weight normalization").  Per output feature o = k*b + j
+ * (column j of the blocks of block column k, i.e. one column of the masked C x K
+ * weight):  n[o] = sqrt(max(sum of W^2 over that column's stored weights, epsilon)),
+ * w_out = W * gain[o] / n[o] (gain 1 when gain is NULL).
+ * w: (nnz, b, b) in w_dt; w_out: the same shape in out_dt (may not alias w); gain:
+ * float32[K] or NULL; norms: float32[K] output or NULL.  Sums are fp32 in a fixed
+ * order.  Errors: BSMM_ERR_INVALID_ARG (NULL handle / tensors, bad dtype, epsilon not
+ * finite and > 0); BSMM_ERR_ALIGNMENT (w, w_out not 16-byte aligned);
+ * BSMM_ERR_DEVICE.  nnz = 0: no-op. */
+BSMM_API bsmm_status bsmm_l2_normalize(bsmm_handle h, const void* w, const float* gain, void* w_out, float* norms,
+                                       float epsilon, bsmm_dtype w_dt, bsmm_dtype out_dt, void* hip_stream);
+/* Gradient of bsmm_l2_normalize for the upstream gradient dy (same shape as w, dtype
+ * dy_dt), with s[o] = the column's sum of dy * W:
+ *   dw = gain[o]/n[o] * dy - [sum of squares > epsilon] * gain[o]*s[o]/n[o]^3 * W,
+ *   dgain[o] = s[o] / n[o].
+ * dw: float32 (nnz, b, b), overwritten; dgain: float32[K] or NULL.  Errors as above. */
+BSMM_API bsmm_status bsmm_l2_normalize_grad(bsmm_handle h, const void* dy, const void* w, const float* gain,
+                                            void* dw, float* dgain, float epsilon, bsmm_dtype dy_dt,
+                                            bsmm_dtype w_dt, void* hip_stream);
 
 /* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
  * every pass launched from the calling thread records HIP events around its kernels
