@@ -11,11 +11,13 @@
 // Statistics and sums are fp32; every sum has a fixed order (deterministic).
 //
 // Axis 1: one workgroup per row holds the row in registers (one HBM read of x, one
-// write of y); the gradient takes a run of rows per workgroup and leaves per-run
-// partial dg/db in the workspace, added in run order by a second kernel.
-// Axis 0: a workgroup owns 32 16-byte column vectors x a chunk of 128 rows, so every
-// load is a coalesced row segment.  Column statistics are combined over the chunks
-// (per-chunk mean and squared deviations, merged in chunk order) through the workspace.
+// write of y); the gradient (512 threads) takes a run of rows per workgroup with the
+// next rows in flight and leaves per-run partial dg/db in the workspace, added in run
+// order by a second kernel.
+// Axis 0: a workgroup owns 32 16-byte column vectors x a chunk of 128 rows held in
+// registers, so every load is a coalesced row segment.  The chunks' column statistics
+// (mean and squared deviations, or plain sums for the gradient) go through the
+// workspace and are merged once per column in a fixed order (ln_cols_merge).
 // Bound: HBM (|x| + |y| forward, |x| + |dy| + |dx| backward, plus the small partials).
 #include "common.h"
 
