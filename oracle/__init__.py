@@ -173,6 +173,19 @@ def updat(layout, block: int, fa: int, xs: Sequence[np.ndarray], dys: Sequence[n
     return dw
 
 
+def updat_accumulate(layout, block: int, fa: int, dw0: np.ndarray, dw_dtype: str, xs: Sequence[np.ndarray],
+                     dys: Sequence[np.ndarray], N: int, dtype: Optional[str] = None, lib=None) -> np.ndarray:
+    """dW0 + sum_t x_t[:, c-block]^T . dy_t[:, k-block]: the weight gradient added into a
+    stored one.  Steps that share one weight contribute one summed gradient (README,
+    group_param_grads, which combines up to 8 of them per product); a sequence longer
+    than one group adds its groups' sums into the same gradient.  dw0 is raw storage of
+    dw_dtype ("f32": float32 values, "bf16" / "f16": uint16 bit patterns), decoded
+    exactly by the oracle's decoder."""
+    lib = lib or load()
+    base = np.asarray(dw0, dtype=np.float64) if dw_dtype == "f32" else decode(dw0, dw_dtype)
+    return base + updat(layout, block, fa, xs, dys, N, dtype, lib=lib)
+
+
 def identity(layout, block: int, lib=None) -> np.ndarray:
     """identity_init: I_b on present diagonal blocks, zero elsewhere (README, identity_init)."""
     lib = lib or load()

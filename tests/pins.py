@@ -224,6 +224,30 @@ def pin_grouping(lib, b=8, fa=1, R=2, S=3, N=5, G=3, seed=7):
     assert np.array_equal(sub[0], g[-1]) and np.array_equal(sub[1], g[0])
 
 
+def pin_accumulate(lib, b=8, fa=0, R=3, S=4, N=6, seed=12):
+    """Accumulating updat: onto zeros it is the plain weight gradient; a sequence of 7
+    steps split into groups of 3 and 4 and accumulated equals the 7-step sum (up to the
+    fp32 rounding of the stored partial); a bf16 / f16 stored gradient enters with the
+    value torch's own conversion gives its bits."""
+    P = _problem(seed, R, S, b, N, fa, "f32", G=7, density=0.6)
+    L = P.layout
+    xs = [_bits(t) for t in P.xs]
+    dys = [_bits(t) for t in P.dys]
+    nz = int(L.sum())
+    zero = np.zeros((nz, b, b), np.float32)
+    assert np.array_equal(oracle.updat_accumulate(L, b, fa, zero, "f32", xs[:3], dys[:3], N, lib=lib),
+                          oracle.updat(L, b, fa, xs[:3], dys[:3], N, lib=lib))
+    part = oracle.updat(L, b, fa, xs[:3], dys[:3], N, lib=lib).astype(np.float32)
+    whole = oracle.updat(L, b, fa, xs, dys, N, lib=lib)
+    acc = oracle.updat_accumulate(L, b, fa, part, "f32", xs[3:], dys[3:], N, lib=lib)
+    assert rel(acc, whole) < 1e-6
+    single = oracle.updat(L, b, fa, xs[3:], dys[3:], N, lib=lib)
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        stored = torch.from_numpy(part).to(tdt)
+        got = oracle.updat_accumulate(L, b, fa, _bits(stored), dt, xs[3:], dys[3:], N, lib=lib)
+        assert rel(got - single, to64(stored)) < 1e-12
+
+
 def pin_one_hot_rows(lib, b=8, R=3, S=3, seed=8):
     """x rows one-hot on distinct features: dW row (c, i) of block (c, k) copies dy's row for that feature."""
     rng = np.random.default_rng(seed)
@@ -305,5 +329,5 @@ def pin_bruteforce_tiny(lib, b=2, N=2, seed=10):
 ALL_PINS = [
     pin_decode_f16, pin_decode_bf16, pin_dense_masked, pin_all_ones_is_dense,
     pin_ones_input_gives_column_sums, pin_identity, pin_block_coord, pin_adjoints,
-    pin_transposed_plan, pin_grouping, pin_one_hot_rows, pin_feature_axis, pin_bruteforce_tiny,
+    pin_transposed_plan, pin_grouping, pin_accumulate, pin_one_hot_rows, pin_feature_axis, pin_bruteforce_tiny,
 ]
