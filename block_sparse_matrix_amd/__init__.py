@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "BlocksparseMatMul", "BsmmError", "group_param_grads", "lib", "LIB_PATH",
-    "bsmm_create", "bsmm_destroy", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_identity_init",
+    "bsmm_create", "bsmm_destroy", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_updat_accumulate",
+    "bsmm_identity_init",
     "bsmm_w_shape", "bsmm_i_shape", "bsmm_o_shape", "bsmm_block_coord", "bsmm_workspace_size",
     "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
     "bsmm_layer_norm", "bsmm_layer_norm_grad", "bsmm_layer_norm_workspace_size", "layer_norm",
@@ -70,6 +71,7 @@ def lib():
         "bsmm_fprop": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
         "bsmm_bprop": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
         "bsmm_updat": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
+        "bsmm_updat_accumulate": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
         "bsmm_identity_init": [vp, vp, i32, vp],
         "bsmm_debug_lut": [vp, i32, P64, i64, P64],
         "bsmm_kernel_name": [vp, i32, i64, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
@@ -207,7 +209,10 @@ def bsmm_bprop(h, dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, N: int) -
                             DTYPE_CODE[dy.dtype], _dev_ptr(ws, "ws"), nb, _stream(dy)), "bsmm_bprop")
 
 
-def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: torch.Tensor, N: int) -> None:
+def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: torch.Tensor, N: int,
+               accumulate: bool = False) -> None:
+    """dw = (or, with accumulate, dw +=) the sum over the steps of x_t^T . dy_t on the
+    present blocks (bsmm_updat / bsmm_updat_accumulate)."""
     G = len(xs)
     if G != len(dys):
         raise ValueError("xs and dys differ in length")
@@ -215,8 +220,9 @@ def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: t
     dp = (ctypes.c_void_p * max(G, 1))(*[_dev_ptr(t, "dys[t]").value for t in dys])
     dt = xs[0].dtype if G else dw.dtype
     ws, nb = _ws(h, 2, N, dt, dw.device)
-    _check(lib().bsmm_updat(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[dt], DTYPE_CODE[dw.dtype],
-                            _dev_ptr(ws, "ws"), nb, _stream(dw)), "bsmm_updat")
+    fn = "bsmm_updat_accumulate" if accumulate else "bsmm_updat"
+    _check(getattr(lib(), fn)(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[dt], DTYPE_CODE[dw.dtype],
+                              _dev_ptr(ws, "ws"), nb, _stream(dw)), fn)
 
 
 def bsmm_identity_init(h, w: torch.Tensor) -> None:
@@ -478,8 +484,12 @@ class BlocksparseMatMul:
         return dx
 
     def updat(self, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw_dtype=torch.float32,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """dW summed over the given steps (1 to 8), written in dw_dtype."""
+              out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+        """dW summed over the given steps (1 to 8), written in dw_dtype.  accumulate=True
+        adds that sum to `out` (required) instead of overwriting it, so sequences of more
+        than 8 steps sharing one weight sum their groups into one gradient."""
+        if accumulate and out is None:
+            raise ValueError("accumulate needs the gradient to add into (out=)")
         if not 1 <= len(xs) <= 8 or len(xs) != len(dys):
             raise ValueError("updat takes 1 to 8 (x, dy) pairs")
         N = self._N(xs[0], self.C, "x")
@@ -489,7 +499,7 @@ class BlocksparseMatMul:
             if x.dtype != xs[0].dtype or dy.dtype != xs[0].dtype:
                 raise ValueError("all steps must share a dtype")
         dw = out if out is not None else torch.empty(self.w_shape, dtype=dw_dtype, device=xs[0].device)
-        bsmm_updat(self.handle, xs, dys, dw, N)
+        bsmm_updat(self.handle, xs, dys, dw, N, accumulate=accumulate)
         return dw
 
     def l2_normalize(self, w: torch.Tensor, gain: Optional[torch.Tensor] = None, epsilon: float = 1e-6,
@@ -509,7 +519,16 @@ class BlocksparseMatMul:
 
 
 def group_param_grads(bsmm: BlocksparseMatMul, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor],
-                      dw_dtype=torch.float32) -> torch.Tensor:
-    """One weight gradient for up to 8 steps that share W: the sum of the per-step dWs,
-    formed by a single grouped updat launch (fp32 accumulation)."""
-    return bsmm.updat(xs, dys, dw_dtype=dw_dtype)
+                      dw_dtype=torch.float32, group_size: int = 8) -> torch.Tensor:
+    """One weight gradient for the steps that share W: the sum of the per-step dWs.  The
+    steps are taken group_size (1 to 8, the README's group_param_grads limit) at a time,
+    one grouped updat launch each (fp32 accumulation within a launch); the first launch
+    writes the gradient and every later one adds its group's sum into it."""
+    if not 1 <= group_size <= 8:
+        raise ValueError("group_size must be in [1, 8]")
+    if len(xs) == 0 or len(xs) != len(dys):
+        raise ValueError("xs and dys must be non-empty and of equal length")
+    dw = bsmm.updat(xs[:group_size], dys[:group_size], dw_dtype=dw_dtype)
+    for t in range(group_size, len(xs), group_size):
+        bsmm.updat(xs[t:t + group_size], dys[t:t + group_size], out=dw, accumulate=True)
+    return dw

@@ -379,10 +379,13 @@ bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm
     return BSMM_OK;
 }
 
-bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
-                       int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
+}  // extern "C"
+
+namespace {
+// updat and its accumulating form (acc: dW += the sum instead of dW = the sum).
+bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
+                       int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes, void* stream,
+                       bool acc) {
     bsmm_status s = check_call(h, N, dt);
     if (s != BSMM_OK) return s;
     if (!valid_dt(dw_dt)) return fail(BSMM_ERR_INVALID_ARG, "dw dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
@@ -402,9 +405,11 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
         if ((uint64_t)N * L.R * L.b * es > kMaxTensorBytes || (uint64_t)N * L.S * L.b * es > kMaxTensorBytes)
             return fail(BSMM_ERR_UNSUPPORTED, "an activation exceeds 2 GiB (the kernels use 32-bit offsets)");
     }
+    if (acc && N == 0) return BSMM_OK;   // the empty sum adds nothing
     const DeviceLut* d = nullptr;
     if ((s = device_lut(h, &d)) != BSMM_OK) return s;
     UpArgs a = up_args(L, N, group);
+    a.acc = acc ? 1 : 0;
     for (int t = 0; t < group; t++) {
         a.xs[t] = N > 0 ? xs[t] : nullptr;
         a.dys[t] = N > 0 ? dys[t] : nullptr;
@@ -434,6 +439,20 @@ bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* 
         return fail(BSMM_ERR_UNSUPPORTED, "the forced kernel does not apply to these arguments");
     hipError_t e = launch_updat(a, dt, L.b, L.fa, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "updat launch");
+}
+}  // namespace
+
+extern "C" {
+
+bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
+                       int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes, void* stream) {
+    return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, ws_bytes, stream, false);
+}
+
+bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs, const void* const* dys, int group,
+                                  void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, ws_bytes, stream, true);
 }
 
 bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream) {

@@ -64,6 +64,7 @@ struct UpArgs {
     int32_t force;          // UpKind to use (0: automatic)
     int32_t split;          // tiles: contraction split in this many parts (1: none)
     float* ws;              // tiles with split > 1: fp32 partial sums, split*ntiles*64 blocks
+    int32_t acc;            // 1: add the sum to what dw holds (dW += ...); 0: overwrite
 };
 
 // Contraction split of the weight-gradient tiles: enough parts to give ~256 workgroups,

@@ -21,6 +21,30 @@
 
 namespace bsmm {
 
+// Four consecutive dW values at element idx, in the weight-gradient dtype.  With a.acc
+// the fp32 sum is first added to the value dW holds (decoded exactly), and the total
+// is rounded once (RNE) to the storage type: dW += sum.
+__device__ __forceinline__ void store_dw4(const UpArgs& a, int64_t idx, f32x4 v) {
+    if (a.acc) {
+        if (a.dwdt == BSMM_F32) {
+            v += *reinterpret_cast<const f32x4*>((const float*)a.dw + idx);
+        } else {
+            const u32x2 o = *reinterpret_cast<const u32x2*>((const uint16_t*)a.dw + idx);
+            const uint32_t h[4] = {o.x & 0xffffu, o.x >> 16, o.y & 0xffffu, o.y >> 16};
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                v[i] += a.dwdt == BSMM_BF16 ? __uint_as_float(h[i] << 16)
+                                            : (float)__builtin_bit_cast(_Float16, (uint16_t)h[i]);
+        }
+    }
+    if (a.dwdt == BSMM_F32)
+        store4<BSMM_F32>(a.dw, idx, v);
+    else if (a.dwdt == BSMM_BF16)
+        store4<BSMM_BF16>(a.dw, idx, v);
+    else
+        store4<BSMM_F16>(a.dw, idx, v);
+}
+
 // Descriptors of the tensors of step group t.  With one group (the common case) they are
 // built once, before the loops: selecting a group pointer from the argument block inside
 // a loop puts a scalar load and its wait in every step.
@@ -232,12 +256,7 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
                     const int p = pt * 16 + r16, q = qt * 16 + 4 * g;
                     if (p < B && q < B) {
                         const int64_t idx = base + p * B + q;
-                        if (a.dwdt == BSMM_F32)
-                            store4<BSMM_F32>(a.dw, idx, acc[qt][pt]);
-                        else if (a.dwdt == BSMM_BF16)
-                            store4<BSMM_BF16>(a.dw, idx, acc[qt][pt]);
-                        else
-                            store4<BSMM_F16>(a.dw, idx, acc[qt][pt]);
+                        store_dw4(a, idx, acc[qt][pt]);
                     }
                     acc[qt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -245,8 +264,9 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
     };
 
     if (items == 0) {
-        // N = 0: every block of this wave is the empty sum
-        for (int j = 0; j < nblk; j++) {
+        // N = 0: every block of this wave is the empty sum (nothing to add when
+        // accumulating)
+        for (int j = 0; j < (a.acc ? 0 : nblk); j++) {
             const int64_t base = (b0 + j) * B * B;
             for (int e = lane; e < B * B; e += 64) store_elt(a.dw, base + e, 0.f, a.dwdt);
         }
@@ -489,12 +509,7 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         const int p = pt * 16 + (l & 15), q = qt * 16 + 4 * (l >> 4);
         if (p < B && q < B) {
             const int64_t idx = (int64_t)(listed ? a.rids[id0 + j] : id0 + j) * B * B + p * B + q;
-            if (a.dwdt == BSMM_F32)
-                store4<BSMM_F32>(a.dw, idx, sum);
-            else if (a.dwdt == BSMM_BF16)
-                store4<BSMM_BF16>(a.dw, idx, sum);
-            else
-                store4<BSMM_F16>(a.dw, idx, sum);
+            store_dw4(a, idx, sum);
         }
     }
 }
@@ -719,12 +734,8 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
                 const int64_t idx = (int64_t)id * B * B + e;
                 if (a.split > 1)
                     store4<BSMM_F32>(a.ws, pslot * B * B + e, acc[c][kt][ct]);
-                else if (a.dwdt == BSMM_F32)
-                    store4<BSMM_F32>(a.dw, idx, acc[c][kt][ct]);
-                else if (a.dwdt == BSMM_BF16)
-                    store4<BSMM_BF16>(a.dw, idx, acc[c][kt][ct]);
                 else
-                    store4<BSMM_F16>(a.dw, idx, acc[c][kt][ct]);
+                    store_dw4(a, idx, acc[c][kt][ct]);
             }
     }
 }
@@ -754,12 +765,7 @@ __global__ __launch_bounds__(256) void updt_reduce(UpArgs a) {
             for (int p = 0; p < a.split; p++)
                 s += *reinterpret_cast<const f32x4*>(a.ws + (((int64_t)p * a.ntiles + ti) * TT + pos) * B * B + e);
             const int64_t idx = (int64_t)id * B * B + e;
-            if (a.dwdt == BSMM_F32)
-                store4<BSMM_F32>(a.dw, idx, s);
-            else if (a.dwdt == BSMM_BF16)
-                store4<BSMM_BF16>(a.dw, idx, s);
-            else
-                store4<BSMM_F16>(a.dw, idx, s);
+            store_dw4(a, idx, s);
         }
     }
 }

@@ -149,6 +149,18 @@ BSMM_API bsmm_status bsmm_updat(bsmm_handle h, const void* const* xs, const void
                        void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* updat accumulating into dW: dW[id] += sum over t < group of x_t[:, c-block]^T .
+ * dy_t[:, k-block].  Arguments, layouts, ownership and errors as bsmm_updat; dw is read
+ * and written.  The fp32 sum of the call is added to the value dW holds (bf16 / f16
+ * decoded exactly) and the total rounded once with RNE to dw_dt.  N = 0 leaves dW as it
+ * is.  This is the weight gradient of a weight shared by more time steps than one
+ * grouped call takes: the kiteco/blocksparse README ("API Documentation" ›
+ * group_param_grads) combines the gradients of up to 8 time steps into one product, so
+ * longer sequences add their groups' sums into one dW. */
+BSMM_API bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs, const void* const* dys,
+                                           int group, void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt,
+                                           void* ws, size_t ws_bytes, void* stream);
+
 /* identity_init on the device: w (device, (nnz, b, b), dtype dt) is overwritten with
  * I_b for every present diagonal block (c == k) and zero for the other blocks. */
 BSMM_API bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream);

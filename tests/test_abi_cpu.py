@@ -109,6 +109,15 @@ def test_call_validation_before_gpu():
         assert L.bsmm_updat(h, None, arr, 1, good, 4, 0, 0, None, 0, None) == INVALID
         bad = (vp * 2)(0x10000, 0x10004)
         assert L.bsmm_updat(h, bad, bad, 2, good, 4, 0, 0, None, 0, None) == ALIGN
+        # the accumulating form validates the same way; with N = 0 it adds nothing
+        acc = L.bsmm_updat_accumulate
+        assert acc(h, arr, arr, 0, good, 4, 0, 0, None, 0, None) == INVALID
+        assert acc(h, arr, arr, 9, good, 4, 0, 0, None, 0, None) == INVALID
+        assert acc(h, arr, arr, 1, good, 4, 0, 5, None, 0, None) == INVALID
+        assert acc(h, arr, arr, 1, None, 4, 0, 0, None, 0, None) == INVALID
+        assert acc(h, arr, arr, 1, odd, 4, 0, 0, None, 0, None) == ALIGN
+        assert acc(h, bad, bad, 2, good, 4, 0, 0, None, 0, None) == ALIGN
+        assert acc(h, None, None, 1, good, 0, 0, 0, None, 0, None) == 0
         assert L.bsmm_identity_init(h, None, 0, None) == INVALID
         assert L.bsmm_identity_init(h, odd, 0, None) == ALIGN
         assert L.bsmm_identity_init(h, good, 9, None) == INVALID

@@ -295,3 +295,57 @@ def test_updat_dense_tiles_unsplit(fa):
     bits = synth.to_bits
     rdw = oracle.updat(P.layout, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, "bf16")
     assert_close(dw, rdw, "bf16", "updat")
+
+
+@pytest.mark.parametrize("dw_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("b,fa,dtype,N,G,kind", [
+    (32, 1, "bf16", 64, 1, None),            # blocks per wave, short contraction
+    (16, 0, "f16", 200, 2, None),
+    (32, 1, "f32", 37, 1, None),
+    (8, 0, "bf16", 1000, 1, "row_groups"),
+    (8, 1, "f32", 600, 3, "row_groups"),
+    (32, 0, "bf16", 520, 2, "dense_tiles"),  # split tiles: partials in the workspace, then their sum
+    (32, 1, "f16", 1024, 1, "dense_tiles"),
+])
+def test_updat_accumulate(b, fa, dtype, N, G, kind, dw_dtype):
+    """updat that adds into the stored gradient (dW += sum), for every weight-gradient
+    kernel family and every gradient dtype, against the oracle's stored value plus sum."""
+    print(f"case accumulate b={b} fa={fa} {dtype} N={N} G={G} {kind} dw={dw_dtype}", flush=True)
+    rng = np.random.default_rng(b + N + G)
+    L = (rng.random((16, 16) if b == 32 else (6, 9)) < 0.5).astype(np.uint8)
+    L[0, 0] = 1
+    P = synth.random_problem(rng, L, b, N, fa, dtype, G=G, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=fa)
+    if kind:
+        m.force_kernel("updat", kind)
+        assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == kind
+    dw0 = (torch.randn(m.w_shape) * 3.0).to(TORCH_DT[dw_dtype])
+    out = dev(dw0)
+    m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys], out=out, accumulate=True)
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    ref = oracle.updat_accumulate(L, b, fa, bits(dw0), dw_dtype, [bits(t) for t in P.xs],
+                                  [bits(t) for t in P.dys], N, dtype)
+    assert_close(out, ref, "f32" if dw_dtype == "f32" and dtype == "f32" else "bf16", "updat accumulate")
+    # N = 0 adds nothing
+    before = out.clone()
+    m.updat([dev(t[:0] if fa == 1 else t[:, :0]) for t in P.xs],
+            [dev(t[:0] if fa == 1 else t[:, :0]) for t in P.dys], out=out, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, before)
+
+
+@pytest.mark.parametrize("group_size", [8, 4])
+def test_group_param_grads_longer_than_a_group(group_size):
+    """11 steps sharing one weight: the first group's launch writes the gradient, the
+    later ones add into it; equal to the oracle's sum over all 11 steps."""
+    rng = np.random.default_rng(group_size)
+    L = (rng.random((5, 7)) < 0.5).astype(np.uint8)
+    L[0, 0] = 1
+    P = synth.random_problem(rng, L, 16, 96, 1, "bf16", G=11, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=16, feature_axis=1)
+    dw = bs.group_param_grads(m, [dev(t) for t in P.xs], [dev(t) for t in P.dys], group_size=group_size)
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    ref = oracle.updat(L, 16, 1, [bits(t) for t in P.xs], [bits(t) for t in P.dys], 96, "bf16")
+    assert_close(dw, ref, "bf16", "grouped dW over 11 steps")
