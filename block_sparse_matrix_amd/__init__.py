@@ -30,6 +30,8 @@ __all__ = [
     "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
     "bsmm_layer_norm", "bsmm_layer_norm_grad", "bsmm_layer_norm_workspace_size", "layer_norm",
     "bsmm_l2_normalize", "bsmm_l2_normalize_grad",
+    "SparseProj", "bsmm_proj_gather", "bsmm_proj_scatter", "bsmm_proj_scatter_add", "bsmm_proj_scatter_mul",
+    "bsmm_proj_gather_mul",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so")
@@ -37,7 +39,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so"
 BSMM_OK = 0
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3, "layer_norm": 4, "layer_norm_grad": 5,
-        "l2_normalize": 6, "l2_normalize_grad": 7}
+        "l2_normalize": 6, "l2_normalize_grad": 7, "proj_gather": 8, "proj_scatter": 9, "proj_scatter_add": 10,
+        "proj_scatter_mul": 11, "proj_gather_mul": 12}
 
 
 class BsmmError(RuntimeError):
@@ -81,6 +84,14 @@ def lib():
         "bsmm_layer_norm_grad": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, sz, vp],
         "bsmm_l2_normalize": [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
         "bsmm_l2_normalize_grad": [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
+        "bsmm_proj_create": [ctypes.POINTER(vp), i64, i64, i64, i64, vp],
+        "bsmm_proj_info": [vp, P64, P64],
+        "bsmm_proj_lut": [vp, vp, i64],
+        "bsmm_proj_gather": [vp, vp, vp, i64, i32, i32, vp],
+        "bsmm_proj_scatter": [vp, vp, vp, i64, i32, i32, vp],
+        "bsmm_proj_scatter_add": [vp, vp, vp, vp, i64, i32, i32, vp],
+        "bsmm_proj_scatter_mul": [vp, vp, vp, vp, i64, i32, i32, vp],
+        "bsmm_proj_gather_mul": [vp, vp, vp, vp, i64, i32, i32, vp],
         "bsmm_profile_begin": [],
         "bsmm_profile_end": [ctypes.POINTER(ctypes.c_double), P64],
     }
@@ -90,6 +101,8 @@ def lib():
         f.restype = ctypes.c_int
     L.bsmm_destroy.argtypes = [vp]
     L.bsmm_destroy.restype = None
+    L.bsmm_proj_destroy.argtypes = [vp]
+    L.bsmm_proj_destroy.restype = None
     L.bsmm_status_string.argtypes = [ctypes.c_int]
     L.bsmm_status_string.restype = ctypes.c_char_p
     L.bsmm_last_error.argtypes = []
@@ -532,3 +545,185 @@ def group_param_grads(bsmm: BlocksparseMatMul, xs: Sequence[torch.Tensor], dys: 
     for t in range(group_size, len(xs), group_size):
         bsmm.updat(xs[t:t + group_size], dys[t:t + group_size], out=dw, accumulate=True)
     return dw
+
+
+# ---- SparseProj (README, "API Documentation" › blocksparse.matmul › SparseProj) ---------
+def _proj_call(fn: str, h, *tensors_and_n, fa: int):
+    *ts, N = tensors_and_n
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise ValueError("SparseProj operands must share a dtype")
+    ptrs = [_dev_ptr(t, f"arg{i}") for i, t in enumerate(ts)]
+    _check(getattr(lib(), fn)(h, *ptrs, N, fa, DTYPE_CODE[dt], _stream(ts[0])), fn)
+
+
+def bsmm_proj_gather(h, x: torch.Tensor, y: torch.Tensor, N: int, fa: int = 1) -> None:
+    _proj_call("bsmm_proj_gather", h, x, y, N, fa=fa)
+
+
+def bsmm_proj_scatter(h, x: torch.Tensor, y: torch.Tensor, N: int, fa: int = 1) -> None:
+    _proj_call("bsmm_proj_scatter", h, x, y, N, fa=fa)
+
+
+def bsmm_proj_scatter_add(h, x: torch.Tensor, y: torch.Tensor, z: torch.Tensor, N: int, fa: int = 1) -> None:
+    _proj_call("bsmm_proj_scatter_add", h, x, y, z, N, fa=fa)
+
+
+def bsmm_proj_scatter_mul(h, x: torch.Tensor, y: torch.Tensor, z: torch.Tensor, N: int, fa: int = 1) -> None:
+    _proj_call("bsmm_proj_scatter_mul", h, x, y, z, N, fa=fa)
+
+
+def bsmm_proj_gather_mul(h, a: torch.Tensor, b: torch.Tensor, g: torch.Tensor, N: int, fa: int = 1) -> None:
+    _proj_call("bsmm_proj_gather_mul", h, a, b, g, N, fa=fa)
+
+
+class _ProjGather(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, proj, x):
+        ctx.proj = proj
+        return proj._gather(x)
+
+    @staticmethod
+    def backward(ctx, dy):
+        return None, ctx.proj._scatter(dy.contiguous())
+
+
+class _ProjScatter(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, proj, x):
+        ctx.proj = proj
+        return proj._scatter(x)
+
+    @staticmethod
+    def backward(ctx, dy):
+        return None, ctx.proj._gather(dy.contiguous())
+
+
+class _ProjScatterAdd(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, proj, x, y):
+        ctx.proj = proj
+        return proj._scatter_add(x, y)
+
+    @staticmethod
+    def backward(ctx, dz):
+        dz = dz.contiguous()
+        return None, dz, ctx.proj._gather(dz)
+
+
+class _ProjScatterMul(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, proj, x, y):
+        ctx.proj = proj
+        ctx.save_for_backward(x, y)
+        return proj._scatter_mul(x, y)
+
+    @staticmethod
+    def backward(ctx, dz):
+        x, y = ctx.saved_tensors
+        dz = dz.contiguous()
+        return None, ctx.proj._scatter_mul(dz, y), ctx.proj._gather_mul(dz, x)
+
+
+class SparseProj:
+    """Dense <-> projected feature maps (README, SparseProj(nhidden, nproj=None,
+    proj_stride=None, block_size=32, gather_lut=None)) over a one-to-one map lut of nproj
+    dense features: gather(x) = x[:, lut], scatter(x) puts the projected features back
+    (zeros elsewhere), scatter_add(x, y) / scatter_mul(x, y) add / multiply y into x at
+    lut.  Without gather_lut the map is nproj // block_size blocks of block_size
+    consecutive features, block j at j * proj_stride (nproj defaults to nhidden,
+    proj_stride to block_size).  feature_axis (an addition of this binding): 1 for (N,
+    features) activations, 0 for (features, N).  Every op is differentiable; the backward
+    ops are the same kernels (the map is one-to-one: no atomics)."""
+
+    def __init__(self, nhidden: int, nproj: Optional[int] = None, proj_stride: Optional[int] = None,
+                 block_size: int = 32, gather_lut=None, feature_axis: int = 1):
+        h = ctypes.c_void_p()
+        if gather_lut is not None:
+            lut = np.ascontiguousarray(np.asarray(gather_lut), dtype=np.int32)
+            if lut.ndim != 1 or (nproj is not None and nproj != lut.size):
+                raise ValueError("gather_lut must be 1-D with nproj entries")
+            _check(lib().bsmm_proj_create(ctypes.byref(h), int(nhidden), int(lut.size), 0, 0,
+                                          lut.ctypes.data_as(ctypes.c_void_p)), "bsmm_proj_create")
+        else:
+            _check(lib().bsmm_proj_create(ctypes.byref(h), int(nhidden), int(nproj or 0), int(proj_stride or 0),
+                                          int(block_size), None), "bsmm_proj_create")
+        self.handle = h
+        if feature_axis not in (0, 1):
+            raise ValueError("feature_axis must be 0 or 1")
+        self.feature_axis = feature_axis
+        nh, npj = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().bsmm_proj_info(h, ctypes.byref(nh), ctypes.byref(npj)), "bsmm_proj_info")
+        self.nhidden, self.nproj = nh.value, npj.value
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.bsmm_proj_destroy(h)
+            self.handle = None
+
+    @property
+    def gather_lut(self) -> np.ndarray:
+        out = np.empty(self.nproj, dtype=np.int32)
+        _check(lib().bsmm_proj_lut(self.handle, out.ctypes.data_as(ctypes.c_void_p), self.nproj), "bsmm_proj_lut")
+        return out
+
+    def _shape(self, N: int, feats: int):
+        return (N, feats) if self.feature_axis == 1 else (feats, N)
+
+    def _N(self, t: torch.Tensor, feats: int, what: str) -> int:
+        if t.dim() != 2:
+            raise ValueError(f"{what} must be 2-D")
+        fdim, ndim = (1, 0) if self.feature_axis == 1 else (0, 1)
+        if t.shape[fdim] != feats:
+            raise ValueError(f"{what} has {t.shape[fdim]} features, expected {feats}")
+        return t.shape[ndim]
+
+    def _gather(self, x):
+        N = self._N(x, self.nhidden, "x")
+        y = torch.empty(self._shape(N, self.nproj), dtype=x.dtype, device=x.device)
+        bsmm_proj_gather(self.handle, x, y, N, self.feature_axis)
+        return y
+
+    def _scatter(self, x):
+        N = self._N(x, self.nproj, "x")
+        y = torch.empty(self._shape(N, self.nhidden), dtype=x.dtype, device=x.device)
+        bsmm_proj_scatter(self.handle, x, y, N, self.feature_axis)
+        return y
+
+    def _scatter_add(self, x, y):
+        N = self._N(x, self.nhidden, "x")
+        if self._N(y, self.nproj, "y") != N:
+            raise ValueError("x and y differ in minibatch")
+        z = torch.empty_like(x)
+        bsmm_proj_scatter_add(self.handle, x, y, z, N, self.feature_axis)
+        return z
+
+    def _scatter_mul(self, x, y):
+        N = self._N(x, self.nhidden, "x")
+        if self._N(y, self.nproj, "y") != N:
+            raise ValueError("x and y differ in minibatch")
+        z = torch.empty_like(x)
+        bsmm_proj_scatter_mul(self.handle, x, y, z, N, self.feature_axis)
+        return z
+
+    def _gather_mul(self, a, b):
+        N = self._N(a, self.nhidden, "a")
+        if self._N(b, self.nhidden, "b") != N:
+            raise ValueError("a and b differ in minibatch")
+        g = torch.empty(self._shape(N, self.nproj), dtype=a.dtype, device=a.device)
+        bsmm_proj_gather_mul(self.handle, a, b, g, N, self.feature_axis)
+        return g
+
+    def gather(self, x: torch.Tensor) -> torch.Tensor:
+        return _ProjGather.apply(self, x.contiguous())
+
+    def scatter(self, x: torch.Tensor) -> torch.Tensor:
+        return _ProjScatter.apply(self, x.contiguous())
+
+    def scatter_add(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        return _ProjScatterAdd.apply(self, x.contiguous(), y.contiguous())
+
+    def scatter_mul(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        return _ProjScatterMul.apply(self, x.contiguous(), y.contiguous())

@@ -718,3 +718,163 @@ bsmm_status bsmm_profile_end(double ms[BSMM_NUM_PASSES], int64_t count[BSMM_NUM_
 }
 
 }  // extern "C"
+
+// ---- SparseProj ----
+namespace {
+
+bsmm_status proj_device(bsmm_proj_plan* h, const int32_t** d) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> guard(h->mu);
+    auto it = h->dev.find(dev);
+    if (it != h->dev.end()) {
+        *d = it->second;
+        return BSMM_OK;
+    }
+    const size_t n = h->lut.size() + h->inv.size();
+    int32_t* p = nullptr;
+    e = hipMalloc((void**)&p, (n > 0 ? n : 1) * sizeof(int32_t));
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of the projection map failed")
+                                                         : dev_fail(e, "hipMalloc");
+    std::vector<int32_t> both(h->lut);
+    both.insert(both.end(), h->inv.begin(), h->inv.end());
+    if (n > 0) e = hipMemcpy(p, both.data(), n * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return dev_fail(e, "hipMemcpy of the projection map");
+    }
+    h->dev.emplace(dev, p);
+    *d = p;
+    return BSMM_OK;
+}
+
+// base / src / out per ProjMode (see kernels.h); widths follow from the mode
+bsmm_status proj_call(bsmm_proj_handle h, int mode, const void* base, const void* src, void* out, int64_t N,
+                      int fa, bsmm_dtype dt, void* stream) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
+    if (fa != 0 && fa != 1) return fail(BSMM_ERR_INVALID_ARG, "feature_axis must be 0 or 1");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
+    const bool to_proj = mode == PROJ_GATHER || mode == PROJ_GATHER_MUL;
+    const int64_t wout = to_proj ? h->nproj : h->nhidden, wsrc = to_proj ? h->nhidden : h->nproj;
+    if (N == 0 || wout == 0) return BSMM_OK;
+    bsmm_status s;
+    if ((s = check_ptr(src, mode == PROJ_GATHER_MUL ? "b" : mode >= PROJ_ADD ? "y" : "x")) != BSMM_OK) return s;
+    if ((s = check_ptr(out, mode == PROJ_GATHER ? "y" : mode == PROJ_SCATTER ? "y" : mode == PROJ_GATHER_MUL ? "g" : "z")) != BSMM_OK)
+        return s;
+    if (mode >= PROJ_ADD && (s = check_ptr(base, mode == PROJ_GATHER_MUL ? "a" : "x")) != BSMM_OK) return s;
+    if (wsrc > 0 && (uint64_t)N > (uint64_t)INT64_MAX / 8 / (uint64_t)std::max(wout, wsrc))
+        return fail(BSMM_ERR_UNSUPPORTED, "tensor too large");
+    const int32_t* d = nullptr;
+    if ((s = proj_device(h, &d)) != BSMM_OK) return s;
+    ProjArgs a{};
+    a.base = base;
+    a.src = src;
+    a.out = out;
+    a.map = to_proj ? d : d + h->nproj;
+    a.N = N;
+    a.wout = wout;
+    a.wsrc = wsrc;
+    a.mode = mode;
+    a.fa = fa;
+    a.dt = dt;
+    hipError_t e = launch_proj(a, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, "SparseProj launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+bsmm_status bsmm_proj_create(bsmm_proj_handle* out, int64_t nhidden, int64_t nproj, int64_t proj_stride,
+                             int64_t block_size, const int32_t* gather_lut) {
+    if (!out) return fail(BSMM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (nhidden < 1 || nhidden > INT32_MAX) return fail(BSMM_ERR_INVALID_ARG, "nhidden must be in [1, 2^31-1]");
+    std::vector<int32_t> lut;
+    if (gather_lut) {
+        if (nproj < 0 || nproj > nhidden) return fail(BSMM_ERR_INVALID_ARG, "nproj must be in [0, nhidden]");
+        lut.assign(gather_lut, gather_lut + nproj);
+    } else {
+        if (block_size < 1) return fail(BSMM_ERR_INVALID_ARG, "block_size must be >= 1");
+        const int64_t np = nproj > 0 ? nproj : nhidden;
+        const int64_t st = proj_stride > 0 ? proj_stride : block_size;
+        if (np % block_size != 0) return fail(BSMM_ERR_INVALID_ARG, "nproj must be a multiple of block_size");
+        if (st < block_size) return fail(BSMM_ERR_INVALID_ARG, "proj_stride must be >= block_size");
+        const int64_t nb = np / block_size;
+        if (np > nhidden || (nb - 1) * st + block_size > nhidden)
+            return fail(BSMM_ERR_INVALID_ARG, "the projected blocks run past nhidden");
+        lut.reserve(np);
+        for (int64_t j = 0; j < nb; j++)
+            for (int64_t i = 0; i < block_size; i++) lut.push_back((int32_t)(j * st + i));
+    }
+    std::vector<int32_t> inv(nhidden, -1);
+    for (size_t p = 0; p < lut.size(); p++) {
+        const int32_t hf = lut[p];
+        if (hf < 0 || hf >= nhidden) return fail(BSMM_ERR_INVALID_ARG, "gather_lut entry outside [0, nhidden)");
+        if (inv[hf] >= 0) return fail(BSMM_ERR_INVALID_ARG, "gather_lut maps two projected features to one hidden feature");
+        inv[hf] = (int32_t)p;
+    }
+    bsmm_proj_plan* p = new (std::nothrow) bsmm_proj_plan();
+    if (!p) return fail(BSMM_ERR_OOM, "out of host memory");
+    p->nhidden = nhidden;
+    p->nproj = (int64_t)lut.size();
+    p->lut = std::move(lut);
+    p->inv = std::move(inv);
+    *out = p;
+    return BSMM_OK;
+}
+
+void bsmm_proj_destroy(bsmm_proj_handle h) {
+    if (!h) return;
+    for (auto& kv : h->dev) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+            (void)hipFree(kv.second);
+            (void)hipSetDevice(cur);
+        }
+    }
+    delete h;
+}
+
+bsmm_status bsmm_proj_info(bsmm_proj_handle h, int64_t* nhidden, int64_t* nproj) {
+    if (!h || !nhidden || !nproj) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    *nhidden = h->nhidden;
+    *nproj = h->nproj;
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_proj_lut(bsmm_proj_handle h, int32_t* out, int64_t cap) {
+    if (!h || (cap > 0 && !out) || cap < 0) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
+    const int64_t n = std::min<int64_t>(cap, h->nproj);
+    for (int64_t i = 0; i < n; i++) out[i] = h->lut[i];
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_proj_gather(bsmm_proj_handle h, const void* x, void* y, int64_t N, int feature_axis,
+                             bsmm_dtype dt, void* stream) {
+    return proj_call(h, PROJ_GATHER, nullptr, x, y, N, feature_axis, dt, stream);
+}
+
+bsmm_status bsmm_proj_scatter(bsmm_proj_handle h, const void* x, void* y, int64_t N, int feature_axis,
+                              bsmm_dtype dt, void* stream) {
+    return proj_call(h, PROJ_SCATTER, nullptr, x, y, N, feature_axis, dt, stream);
+}
+
+bsmm_status bsmm_proj_scatter_add(bsmm_proj_handle h, const void* x, const void* y, void* z, int64_t N,
+                                  int feature_axis, bsmm_dtype dt, void* stream) {
+    return proj_call(h, PROJ_ADD, x, y, z, N, feature_axis, dt, stream);
+}
+
+bsmm_status bsmm_proj_scatter_mul(bsmm_proj_handle h, const void* x, const void* y, void* z, int64_t N,
+                                  int feature_axis, bsmm_dtype dt, void* stream) {
+    return proj_call(h, PROJ_MUL, x, y, z, N, feature_axis, dt, stream);
+}
+
+bsmm_status bsmm_proj_gather_mul(bsmm_proj_handle h, const void* a, const void* b, void* g, int64_t N,
+                                 int feature_axis, bsmm_dtype dt, void* stream) {
+    return proj_call(h, PROJ_GATHER_MUL, a, b, g, N, feature_axis, dt, stream);
+}
+
+}  // extern "C"

@@ -101,3 +101,15 @@ struct bsmm_plan {
     std::mutex mu;
     std::map<int, bsmm::DeviceLut> dev;   // per HIP device ordinal
 };
+
+// SparseProj: a one-to-one map of nproj projected features into nhidden dense ones
+// (kiteco/blocksparse README, "API Documentation" › blocksparse.matmul › SparseProj).
+// lut[p] is the dense feature of projected feature p; inv[h] the projected feature of
+// dense feature h, or -1.  Immutable after create; the device copy (lut then inv, one
+// allocation) is made per device on first use.
+struct bsmm_proj_plan {
+    int64_t nhidden = 0, nproj = 0;
+    std::vector<int32_t> lut, inv;
+    std::mutex mu;
+    std::map<int, int32_t*> dev;   // per HIP device ordinal: lut (nproj) followed by inv (nhidden)
+};

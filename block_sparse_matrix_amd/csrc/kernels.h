@@ -141,6 +141,25 @@ struct WnArgs {
 };
 hipError_t launch_l2_normalize(const WnArgs& a, bool grad, void* stream);
 
+// SparseProj (proj.hip): out[., j] = combine(base[., j], src[., map[j]]) over the output
+// features j, for activations (N, features) (fa 1) or (features, N) (fa 0).
+enum ProjMode {
+    PROJ_GATHER = 0,    // out = src[map]                        (map: lut, out width nproj)
+    PROJ_SCATTER,       // out = map >= 0 ? src[map] : 0         (map: inv, out width nhidden)
+    PROJ_ADD,           // out = map >= 0 ? base + src[map] : base
+    PROJ_MUL,           // out = map >= 0 ? base * src[map] : base
+    PROJ_GATHER_MUL     // out = base[map] * src[map]            (map: lut; base and src both dense)
+};
+struct ProjArgs {
+    const void* base;      // ADD, MUL: dense (width wout); GATHER_MUL: dense (width wsrc)
+    const void* src;
+    void* out;
+    const int32_t* map;    // wout entries
+    int64_t N, wout, wsrc;
+    int mode, fa, dt;
+};
+hipError_t launch_proj(const ProjArgs& a, void* stream);
+
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.
 void prof_events(int pass, void** start, void** stop);

@@ -82,9 +82,14 @@ typedef enum {
     BSMM_PASS_LAYER_NORM = 4,
     BSMM_PASS_LAYER_NORM_GRAD = 5,
     BSMM_PASS_L2_NORMALIZE = 6,
-    BSMM_PASS_L2_NORMALIZE_GRAD = 7
+    BSMM_PASS_L2_NORMALIZE_GRAD = 7,
+    BSMM_PASS_PROJ_GATHER = 8,
+    BSMM_PASS_PROJ_SCATTER = 9,
+    BSMM_PASS_PROJ_SCATTER_ADD = 10,
+    BSMM_PASS_PROJ_SCATTER_MUL = 11,
+    BSMM_PASS_PROJ_GATHER_MUL = 12
 } bsmm_pass;
-#define BSMM_NUM_PASSES 8
+#define BSMM_NUM_PASSES 13
 
 typedef struct bsmm_plan* bsmm_handle;
 
@@ -277,6 +282,56 @@ BSMM_API bsmm_status bsmm_l2_normalize(bsmm_handle h, const void* w, const float
 BSMM_API bsmm_status bsmm_l2_normalize_grad(bsmm_handle h, const void* dy, const void* w, const float* gain,
                                             void* dw, float* dgain, float epsilon, bsmm_dtype dy_dt,
                                             bsmm_dtype w_dt, void* hip_stream);
+
+/* ---- SparseProj (kiteco/blocksparse README, "API Documentation" › blocksparse.matmul ›
+ * SparseProj(nhidden, nproj, proj_stride, block_size, gather_lut) with gather, scatter,
+ * scatter_add and scatter_mul): projections between a dense activation of nhidden
+ * features and a projected one of nproj features through a one-to-one feature map
+ * lut[p] (the dense feature of projected feature p).  Activations are (N, features) for
+ * feature_axis 1 and (features, N) for 0, dense and contiguous, 16-byte aligned device
+ * buffers of one dtype.  The page gives no formulas; the readings:
+ *   gather       y[n, p] = x[n, lut[p]]                                    y (N, nproj)
+ *   scatter      y[n, lut[p]] = x[n, p], 0 at every dense feature not in lut  y (N, nhidden)
+ *   scatter_add  z = x, then z[n, lut[p]] = x[n, lut[p]] + y[n, p]          z (N, nhidden)
+ *   scatter_mul  z = x, then z[n, lut[p]] = x[n, lut[p]] * y[n, p]          z (N, nhidden)
+ *   gather_mul   g[n, p] = a[n, lut[p]] * b[n, lut[p]]  (the y-gradient of scatter_mul)
+ * Copies keep the stored bits; add and mul compute in fp32 and round once (RNE) to the
+ * storage type.  Each output element is written once by one thread (the map is
+ * one-to-one), so no op, forward or backward, uses atomics.  Calls are asynchronous on
+ * `stream`; N = 0 is a no-op; errors as for the matmul calls (NULL or misaligned
+ * pointers, bad dtype or feature_axis). */
+typedef struct bsmm_proj_plan* bsmm_proj_handle;
+
+/* Build the feature map.  gather_lut (host, nproj entries, read during the call): the
+ * map itself; its entries must be distinct and in [0, nhidden) (BSMM_ERR_INVALID_ARG
+ * otherwise); proj_stride and block_size are then ignored.  gather_lut NULL: the map is
+ * nproj / block_size blocks of block_size consecutive dense features, block j starting
+ * at j * proj_stride; nproj <= 0 means nhidden and proj_stride <= 0 means block_size;
+ * nproj must be a multiple of block_size, proj_stride >= block_size, and the last block
+ * must end within nhidden.  The handle owns the host map and its per-device copies. */
+BSMM_API bsmm_status bsmm_proj_create(bsmm_proj_handle* out, int64_t nhidden, int64_t nproj, int64_t proj_stride,
+                                      int64_t block_size, const int32_t* gather_lut);
+/* Release the handle and its device copies (NULL-safe).  No call may be in flight. */
+BSMM_API void bsmm_proj_destroy(bsmm_proj_handle h);
+/* The dense and projected feature counts. */
+BSMM_API bsmm_status bsmm_proj_info(bsmm_proj_handle h, int64_t* nhidden, int64_t* nproj);
+/* The first min(cap, nproj) map entries into host array out. */
+BSMM_API bsmm_status bsmm_proj_lut(bsmm_proj_handle h, int32_t* out, int64_t cap);
+/* y = gather(x).  x and y must not overlap. */
+BSMM_API bsmm_status bsmm_proj_gather(bsmm_proj_handle h, const void* x, void* y, int64_t N, int feature_axis,
+                                      bsmm_dtype dt, void* stream);
+/* y = scatter(x), every element of y written.  x and y must not overlap. */
+BSMM_API bsmm_status bsmm_proj_scatter(bsmm_proj_handle h, const void* x, void* y, int64_t N, int feature_axis,
+                                       bsmm_dtype dt, void* stream);
+/* z = scatter_add(x, y).  z may be x (in place); y must not overlap z. */
+BSMM_API bsmm_status bsmm_proj_scatter_add(bsmm_proj_handle h, const void* x, const void* y, void* z, int64_t N,
+                                           int feature_axis, bsmm_dtype dt, void* stream);
+/* z = scatter_mul(x, y).  z may be x (in place); y must not overlap z. */
+BSMM_API bsmm_status bsmm_proj_scatter_mul(bsmm_proj_handle h, const void* x, const void* y, void* z, int64_t N,
+                                           int feature_axis, bsmm_dtype dt, void* stream);
+/* g = gather_mul(a, b): a, b (N, nhidden); g (N, nproj), not overlapping a or b. */
+BSMM_API bsmm_status bsmm_proj_gather_mul(bsmm_proj_handle h, const void* a, const void* b, void* g, int64_t N,
+                                          int feature_axis, bsmm_dtype dt, void* stream);
 
 /* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
  * every pass launched from the calling thread records HIP events around its kernels

@@ -204,3 +204,31 @@ def norm_problem(rng: np.random.Generator, N: int, C: int, axis: int, dtype: str
         g = (1 + 0.25 * rng.standard_normal(C)).astype(np.float32)
         b = (0.25 * rng.standard_normal(C)).astype(np.float32)
     return NormProblem(N, C, axis, dtype, x, dy, torch.from_numpy(g), torch.from_numpy(b))
+
+
+@dataclasses.dataclass
+class ProjProblem:
+    """Seeded inputs of SparseProj: x, a (dense, nhidden features), s (projected, nproj
+    features), in the activation layout of fa ((N, F) for 1, (F, N) for 0); lut the
+    feature map (None: the blocked default of the given proj_stride / block_size)."""
+    N: int
+    nhidden: int
+    nproj: int
+    fa: int
+    dtype: str
+    lut: Optional[np.ndarray]
+    x: torch.Tensor
+    a: torch.Tensor
+    s: torch.Tensor
+
+
+def proj_problem(rng: np.random.Generator, N: int, nhidden: int, nproj: int, fa: int, dtype: str,
+                 random_map: bool) -> ProjProblem:
+    """random_map: nproj distinct dense features in random order (rng.permutation), drawn
+    first; else lut is None (the blocked default).  Then x, a ~ N(0, 1) dense and
+    s ~ N(0, 1) projected."""
+    lut = rng.permutation(nhidden)[:nproj].astype(np.int64) if random_map else None
+    x = _draw(rng, act_shape(fa, N, nhidden), 1.0, dtype)
+    a = _draw(rng, act_shape(fa, N, nhidden), 1.0, dtype)
+    s = _draw(rng, act_shape(fa, N, nproj), 1.0, dtype)
+    return ProjProblem(N, nhidden, nproj, fa, dtype, lut, x, a, s)
