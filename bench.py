@@ -59,7 +59,8 @@ def parse():
                     help="run bprop and updat concurrently on two streams in the timed graph "
                          "(measured slower on MI355X: the two kernels compete rather than overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-layer-norm", action="store_true", help="skip the layer_norm and l2_normalize timing")
+    ap.add_argument("--no-layer-norm", action="store_true",
+                    help="skip the layer_norm, l2_normalize and SparseProj timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -272,6 +273,16 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     ms_eager = (time.perf_counter() - t0) * 1e3 / nsteps
     prof_cold = eager(R)
     prof_warm = eager(1)
+    # the accumulating weight gradient (dW += sum), cold over the rotating sets; it reads
+    # the stored dW as well, so its algorithmic bytes are G*(|x|+|dy|) + 2*|dW|
+    for i in range(warmup):
+        bs.bsmm_updat(h, sets[i % R]["xs"], sets[i % R]["dys"], sets[i % R]["dw"], N, accumulate=True)
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    for i in range(nsteps):
+        bs.bsmm_updat(h, sets[i % R]["xs"], sets[i % R]["dys"], sets[i % R]["dw"], N, accumulate=True)
+    torch.cuda.synchronize()
+    acc_tot, acc_cnt = bs.bsmm_profile_end()["updat"]
     cost = pass_cost(P, dtype)
     per = {}
     for p in PASSES:
@@ -284,8 +295,13 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
                   "alg_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "alg_bytes": int(nbytes), "flops": int(flops),
                   "bound": bound, "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 4),
                   "warm_kernel_us": round(wt / wc * 1e3, 3)}
+    aflops, abytes = cost["updat"][0], cost["updat"][1] + P.nnz * P.block * P.block * 4
+    aus = acc_tot / acc_cnt * 1e3
+    abound, atstar = roof(aflops, abytes, dtype)
+    acc = {"kernel_us": round(aus, 3), "alg_bytes": int(abytes), "alg_GBs": round(abytes / (aus * 1e-6) / 1e9, 1),
+           "bound": abound, "roofline_us": round(atstar * 1e6, 3), "frac": round(atstar / (aus * 1e-6), 4)}
     flops_step = sum(cost[p][0] for p in PASSES)
-    return dict(P=P, ms=ms_graph, ms_eager=ms_eager, per=per, flops_step=flops_step, R=R, steps=nsteps,
+    return dict(P=P, ms=ms_graph, ms_eager=ms_eager, per=per, acc=acc, flops_step=flops_step, R=R, steps=nsteps,
                 identity_us=ident[0] / max(ident[1], 1) * 1e3, layout_ms=t_layout * 1e3, prep_s=t_prep)
 
 
@@ -326,6 +342,56 @@ def run_layer_norm(reps=20):
             out[f"{key}_axis{axis}"] = {"kernel_us": round(us, 3), "alg_bytes": nb, "achieved_GBps": round(gbs, 1),
                                         "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
                                         "bound": "hbm"}
+    return out
+
+
+def run_sparse_proj(reps=20):
+    """Kernel time of the SparseProj ops on the band workload's activation: nhidden 8192
+    dense features projected to 4096 (every other block of 32, proj_stride 64), N = 4096,
+    bf16, features last, over rotating buffer sets; HBM-bound, algorithmic bytes: gather
+    2*N*P, scatter N*P + N*H, scatter_add / scatter_mul 2*N*H + N*P, gather_mul 3*N*P
+    (elements of 2 bytes; P = 4096, H = 8192)."""
+    import numpy as np
+    import torch
+    import block_sparse_matrix_amd as bs
+    import synth
+    N, H, Pn, dt = 4096, 8192, 4096, "bf16"
+    P = synth.proj_problem(np.random.default_rng(17), N, H, Pn, 1, dt, False)
+    proj = bs.SparseProj(H, Pn, 64, 32)
+    R = 4   # 4 sets x ~224 MiB: timed launches read HBM, not the 256 MiB cache
+    xs = [P.x.cuda() for _ in range(R)]
+    ss = [P.s.cuda() for _ in range(R)]
+    gs = [torch.empty(N, Pn, dtype=xs[0].dtype, device="cuda") for _ in range(R)]
+    zs = [torch.empty_like(xs[0]) for _ in range(R)]
+    h = proj.handle
+
+    def launch(i):
+        x, s, g, z = xs[i % R], ss[i % R], gs[i % R], zs[i % R]
+        bs.bsmm_proj_gather(h, x, g, N)
+        bs.bsmm_proj_scatter(h, s, z, N)
+        bs.bsmm_proj_scatter_add(h, x, s, z, N)
+        bs.bsmm_proj_scatter_mul(h, x, s, z, N)
+        bs.bsmm_proj_gather_mul(h, x, zs[(i + 1) % R], g, N)
+
+    for i in range(4):
+        launch(i)
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    for i in range(reps):
+        launch(i)
+    torch.cuda.synchronize()
+    pr = bs.bsmm_profile_end()
+    e = 2
+    nbytes = {"proj_gather": 2 * N * Pn * e, "proj_scatter": (N * Pn + N * H) * e,
+              "proj_scatter_add": (2 * N * H + N * Pn) * e, "proj_scatter_mul": (2 * N * H + N * Pn) * e,
+              "proj_gather_mul": 3 * N * Pn * e}
+    out = {"workload": "SparseProj nhidden 8192 -> nproj 4096 (blocks of 32, proj_stride 64), N=4096, bf16, "
+                       "features last"}
+    for key, nb in nbytes.items():
+        us = pr[key][0] / pr[key][1] * 1e3
+        gbs = nb / (us * 1e-6) / 1e9
+        out[key[5:]] = {"kernel_us": round(us, 3), "alg_bytes": nb, "achieved_GBps": round(gbs, 1),
+                        "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
     return out
 
 
@@ -404,6 +470,7 @@ def main():
                    "passes": "fprop+bprop+updat", "buffer_sets_rotated": res["R"]},
         "roofline": roofline,
         "per_pass": per,
+        "updat_accumulate": res["acc"],
         "timing": "ms_per_step: HIP-graph replay of the three launches per step over rotating buffer sets"
                   + (" (bprop and updat on two streams, joined each step)" if args.overlap else "")
                   + "; per_pass.kernel_us: dispatch timestamps of eager launches, one stream",
@@ -421,6 +488,7 @@ def main():
     if not args.no_layer_norm:
         out["layer_norm"] = run_layer_norm()
         out["l2_normalize"] = run_l2_normalize(P)
+        out["sparse_proj"] = run_sparse_proj()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
     else:
