@@ -107,11 +107,16 @@ def _as5(a: np.ndarray, spatial) -> np.ndarray:
     return a.reshape(a.shape[:2] + tuple(spatial))
 
 
+def _as6(F, cl, kl, TRS) -> np.ndarray:
+    """The filter as (nblocks, Bc, T, R, S, Bk) (1-D / 2-D filters get leading taps of 1)."""
+    return np.asarray(F, dtype=np.float64).reshape((len(cl), len(cl[0])) + tuple(TRS) + (len(kl[0]),))
+
+
 def fprop(bck, F, I, K: int, g) -> np.ndarray:
     TRS, DHW, MPQ = g[0], g[1], g[2]
     cl, kl = bck
     I5 = _as5(I, DHW)
-    F = np.asarray(F, dtype=np.float64)
+    F = _as6(F, cl, kl, TRS)
     N = I5.shape[0]
     O = np.zeros((N, K) + MPQ)
     for b in range(len(cl)):
@@ -126,7 +131,7 @@ def bprop(bck, F, dO, C: int, g) -> np.ndarray:
     TRS, DHW, MPQ, st, dl, pads = g
     cl, kl = bck
     dO5 = _as5(dO, MPQ)
-    F = np.asarray(F, dtype=np.float64)
+    F = _as6(F, cl, kl, TRS)
     N = dO5.shape[0]
     dI = np.zeros((N, C) + DHW)
     for b in range(len(cl)):
