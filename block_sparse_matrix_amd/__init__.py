@@ -31,7 +31,7 @@ __all__ = [
     "bsmm_layer_norm", "bsmm_layer_norm_grad", "bsmm_layer_norm_workspace_size", "layer_norm",
     "bsmm_l2_normalize", "bsmm_l2_normalize_grad",
     "SparseProj", "bsmm_proj_gather", "bsmm_proj_scatter", "bsmm_proj_scatter_add", "bsmm_proj_scatter_mul",
-    "bsmm_proj_gather_mul",
+    "bsmm_proj_gather_mul", "BlocksparseConv", "bsmm_conv_fprop", "bsmm_conv_bprop", "bsmm_conv_updat",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsmm.so")
@@ -40,7 +40,7 @@ BSMM_OK = 0
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 PASS = {"fprop": 0, "bprop": 1, "updat": 2, "identity": 3, "layer_norm": 4, "layer_norm_grad": 5,
         "l2_normalize": 6, "l2_normalize_grad": 7, "proj_gather": 8, "proj_scatter": 9, "proj_scatter_add": 10,
-        "proj_scatter_mul": 11, "proj_gather_mul": 12}
+        "proj_scatter_mul": 11, "proj_gather_mul": 12, "conv_fprop": 13, "conv_bprop": 14, "conv_updat": 15}
 
 
 class BsmmError(RuntimeError):
@@ -85,6 +85,11 @@ def lib():
         "bsmm_l2_normalize": [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
         "bsmm_l2_normalize_grad": [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, vp],
         "bsmm_proj_create": [ctypes.POINTER(vp), i64, i64, i64, i64, vp],
+        "bsmm_conv_create": [ctypes.POINTER(vp), i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, i32, vp],
+        "bsmm_conv_geometry": [vp, vp, vp],
+        "bsmm_conv_fprop": [vp, vp, vp, vp, i64, i32, vp],
+        "bsmm_conv_bprop": [vp, vp, vp, vp, i64, i32, vp],
+        "bsmm_conv_updat": [vp, vp, vp, vp, i64, i32, vp],
         "bsmm_proj_info": [vp, P64, P64],
         "bsmm_proj_lut": [vp, vp, i64],
         "bsmm_proj_gather": [vp, vp, vp, i64, i32, i32, vp],
@@ -103,6 +108,8 @@ def lib():
     L.bsmm_destroy.restype = None
     L.bsmm_proj_destroy.argtypes = [vp]
     L.bsmm_proj_destroy.restype = None
+    L.bsmm_conv_destroy.argtypes = [vp]
+    L.bsmm_conv_destroy.restype = None
     L.bsmm_status_string.argtypes = [ctypes.c_int]
     L.bsmm_status_string.restype = ctypes.c_char_p
     L.bsmm_last_error.argtypes = []
@@ -727,3 +734,141 @@ class SparseProj:
 
     def scatter_mul(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
         return _ProjScatterMul.apply(self, x.contiguous(), y.contiguous())
+
+
+# ---- BlocksparseConv (README, "API Documentation" › blocksparse.conv) -----------------------
+def bsmm_conv_fprop(h, F: torch.Tensor, I: torch.Tensor, O: torch.Tensor, N: int) -> None:
+    if F.dtype != I.dtype or O.dtype != I.dtype:
+        raise ValueError("F, I and O must share a dtype")
+    _check(lib().bsmm_conv_fprop(h, _dev_ptr(F, "F"), _dev_ptr(I, "I"), _dev_ptr(O, "O"), N, DTYPE_CODE[I.dtype],
+                                 _stream(I)), "bsmm_conv_fprop")
+
+
+def bsmm_conv_bprop(h, F: torch.Tensor, dO: torch.Tensor, dI: torch.Tensor, N: int) -> None:
+    if F.dtype != dO.dtype or dI.dtype != dO.dtype:
+        raise ValueError("F, dO and dI must share a dtype")
+    _check(lib().bsmm_conv_bprop(h, _dev_ptr(F, "F"), _dev_ptr(dO, "dO"), _dev_ptr(dI, "dI"), N,
+                                 DTYPE_CODE[dO.dtype], _stream(dO)), "bsmm_conv_bprop")
+
+
+def bsmm_conv_updat(h, I: torch.Tensor, dO: torch.Tensor, dF: torch.Tensor, N: int) -> None:
+    if I.dtype != dO.dtype or dF.dtype != torch.float32:
+        raise ValueError("I and dO must share a dtype; dF is float32")
+    _check(lib().bsmm_conv_updat(h, _dev_ptr(I, "I"), _dev_ptr(dO, "dO"), _dev_ptr(dF, "dF"), N,
+                                 DTYPE_CODE[I.dtype], _stream(I)), "bsmm_conv_updat")
+
+
+class _ConvFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, conv, F, I):
+        ctx.conv = conv
+        ctx.save_for_backward(F, I)
+        return conv.fprop(F, I)
+
+    @staticmethod
+    def backward(ctx, dO):
+        F, I = ctx.saved_tensors
+        conv = ctx.conv
+        dO = dO.contiguous()
+        dF = conv.updat(I, dO).to(F.dtype) if ctx.needs_input_grad[1] else None
+        dI = conv.bprop(F, dO) if ctx.needs_input_grad[2] else None
+        return None, dF, dI
+
+
+class BlocksparseConv:
+    """Convolution with a filter only for blocks of channels (README, BlocksparseConv(BCK,
+    TRS, DHW, MPQ=None, strides=(1,1,1), dilates=(1,1,1), padding="SAME",
+    edge_bias=False)).  BCK: one ((c0, c1, ...), (k0, k1, ...)) pair per block (every
+    block the same sizes Bc, Bk <= 64); TRS / DHW / strides / dilates: 1 to 3 spatial
+    dims; padding "SAME", "VALID", an int or a tuple of ints.  Activations (N, C, *DHW)
+    and (N, K, *MPQ) with C, K one past the largest channel index; the filter
+    (nblocks, Bc, *TRS, Bk).  edge_bias and MPQ (transposed convolution) are not
+    provided."""
+
+    def __init__(self, BCK, TRS, DHW, MPQ=None, strides=(1, 1, 1), dilates=(1, 1, 1), padding="SAME",
+                 edge_bias=False):
+        if edge_bias:
+            raise NotImplementedError("edge_bias is not provided")
+        nd = len(tuple(DHW))
+        if len(tuple(TRS)) != nd:
+            raise ValueError("TRS and DHW must have the same number of dims")
+        cl = np.ascontiguousarray([blk[0] for blk in BCK], dtype=np.int32)
+        kl = np.ascontiguousarray([blk[1] for blk in BCK], dtype=np.int32)
+        if cl.ndim != 2 or kl.ndim != 2:
+            raise ValueError("every block must list the same numbers of input and output channels")
+        self.nblocks, self.Bc = cl.shape
+        self.Bk = kl.shape[1]
+        self.C = int(cl.max()) + 1
+        self.K = int(kl.max()) + 1
+        self.nd = nd
+
+        def pad3(v, fill):
+            v = tuple(int(a) for a in (v if isinstance(v, (tuple, list)) else (v,) * nd))
+            v = v[-nd:] if len(v) >= nd else v
+            return (fill,) * (3 - len(v)) + v
+
+        arr = lambda v: (ctypes.c_int64 * 3)(*v)
+        if isinstance(padding, str):
+            mode, pads = {"SAME": 0, "VALID": 1}[padding.upper()], (0, 0, 0)
+        else:
+            mode, pads = 2, pad3(padding, 0)
+        h = ctypes.c_void_p()
+        _check(lib().bsmm_conv_create(ctypes.byref(h), self.nblocks, self.Bc, self.Bk,
+                                      cl.ctypes.data_as(ctypes.c_void_p), kl.ctypes.data_as(ctypes.c_void_p),
+                                      self.C, self.K, arr(pad3(TRS, 1)), arr(pad3(DHW, 1)), arr(pad3(strides, 1)),
+                                      arr(pad3(dilates, 1)), mode, arr(pads)), "bsmm_conv_create")
+        self.handle = h
+        m3, p3 = (ctypes.c_int64 * 3)(), (ctypes.c_int64 * 3)()
+        _check(lib().bsmm_conv_geometry(h, m3, p3), "bsmm_conv_geometry")
+        self.TRS, self.DHW = tuple(TRS), tuple(DHW)
+        self.MPQ = tuple(m3[3 - nd:])
+        self.pads = tuple(p3[3 - nd:])
+        if MPQ is not None and tuple(MPQ) != self.MPQ:
+            raise ValueError(f"MPQ {tuple(MPQ)} differs from the output size {self.MPQ} (transposed convolution "
+                             "is not provided)")
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.bsmm_conv_destroy(h)
+            self.handle = None
+
+    def f_shape(self, block=None):
+        one = (self.Bc,) + self.TRS + (self.Bk,)
+        return one if block is not None else (self.nblocks,) + one
+
+    def i_shape(self, N):
+        return (N, self.C) + self.DHW
+
+    def o_shape(self, N):
+        return (N, self.K) + self.MPQ
+
+    def _check_act(self, t, shape, what):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+    def fprop(self, F, I):
+        N = I.shape[0]
+        self._check_act(I, self.i_shape(N), "I")
+        self._check_act(F, self.f_shape(), "F")
+        O = torch.empty(self.o_shape(N), dtype=I.dtype, device=I.device)
+        bsmm_conv_fprop(self.handle, F.contiguous(), I.contiguous(), O, N)
+        return O
+
+    def bprop(self, F, dO):
+        N = dO.shape[0]
+        self._check_act(dO, self.o_shape(N), "dO")
+        dI = torch.empty(self.i_shape(N), dtype=dO.dtype, device=dO.device)
+        bsmm_conv_bprop(self.handle, F.contiguous(), dO.contiguous(), dI, N)
+        return dI
+
+    def updat(self, I, dO):
+        N = I.shape[0]
+        self._check_act(I, self.i_shape(N), "I")
+        self._check_act(dO, self.o_shape(N), "dO")
+        dF = torch.empty(self.f_shape(), dtype=torch.float32, device=I.device)
+        bsmm_conv_updat(self.handle, I.contiguous(), dO.contiguous(), dF, N)
+        return dF
+
+    def __call__(self, F, I):
+        return _ConvFn.apply(self, F, I)

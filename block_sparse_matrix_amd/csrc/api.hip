@@ -878,3 +878,216 @@ bsmm_status bsmm_proj_gather_mul(bsmm_proj_handle h, const void* a, const void* 
 }
 
 }  // extern "C"
+
+// ---- BlocksparseConv ----
+namespace {
+
+// device copy of the conv tables; offsets (int32 elements) of each array in `off`
+bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[6]) {
+    const std::vector<int32_t>* parts[6] = {&h->cidx, &h->kidx, &h->kptr, &h->kent, &h->cptr, &h->cent};
+    size_t total = 0;
+    for (int i = 0; i < 6; i++) {
+        off[i] = total;
+        total += parts[i]->size();
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> guard(h->mu);
+    auto it = h->dev.find(dev);
+    if (it != h->dev.end()) {
+        *d = it->second;
+        return BSMM_OK;
+    }
+    std::vector<int32_t> all;
+    all.reserve(total);
+    for (int i = 0; i < 6; i++) all.insert(all.end(), parts[i]->begin(), parts[i]->end());
+    int32_t* p = nullptr;
+    e = hipMalloc((void**)&p, (total > 0 ? total : 1) * sizeof(int32_t));
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of the conv tables failed")
+                                                         : dev_fail(e, "hipMalloc");
+    if (total > 0) e = hipMemcpy(p, all.data(), total * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return dev_fail(e, "hipMemcpy of the conv tables");
+    }
+    h->dev.emplace(dev, p);
+    *d = p;
+    return BSMM_OK;
+}
+
+bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b, void* out, int64_t N,
+                      bsmm_dtype dt, void* stream) {
+    if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
+    if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
+    if (N == 0 && pass != 2) return BSMM_OK;   // updat with N = 0 writes dF = 0
+    bsmm_status s;
+    const char* na = pass == 1 ? "dO" : "I";
+    const char* nb = pass == 2 ? "dO" : "F";
+    const char* no = pass == 0 ? "O" : pass == 1 ? "dI" : "dF";
+    if (pass == 2 && h->nb == 0) return BSMM_OK;
+    if ((s = check_ptr(out, no)) != BSMM_OK) return s;
+    if (N > 0 && (s = check_ptr(a, na)) != BSMM_OK) return s;
+    if (N > 0 && (h->nb > 0 || pass == 2) && (s = check_ptr(b, nb)) != BSMM_OK) return s;
+    const int64_t sp_in = (int64_t)h->DHW[0] * h->DHW[1] * h->DHW[2], sp_out = (int64_t)h->MPQ[0] * h->MPQ[1] * h->MPQ[2];
+    if ((uint64_t)N > (uint64_t)INT64_MAX / 8 / (uint64_t)std::max<int64_t>(1, std::max(h->C * sp_in, h->K * sp_out)))
+        return fail(BSMM_ERR_UNSUPPORTED, "tensor too large");
+    const int32_t* d = nullptr;
+    size_t off[6];
+    if ((s = conv_device(h, &d, off)) != BSMM_OK) return s;
+    ConvArgs x{};
+    x.a = a;
+    x.b = b;
+    x.out = out;
+    x.cidx = d + off[0];
+    x.kidx = d + off[1];
+    x.lptr = pass == 0 ? d + off[2] : d + off[4];
+    x.lent = pass == 0 ? d + off[3] : d + off[5];
+    x.N = N;
+    x.C = h->C;
+    x.K = h->K;
+    x.nb = h->nb;
+    x.Bc = h->Bc;
+    x.Bk = h->Bk;
+    x.T = h->TRS[0]; x.R = h->TRS[1]; x.S = h->TRS[2];
+    x.D = h->DHW[0]; x.H = h->DHW[1]; x.W = h->DHW[2];
+    x.M = h->MPQ[0]; x.P = h->MPQ[1]; x.Q = h->MPQ[2];
+    for (int i = 0; i < 3; i++) {
+        x.st[i] = h->st[i];
+        x.dl[i] = h->dl[i];
+        x.pad[i] = h->pad[i];
+    }
+    x.dt = dt;
+    hipError_t e = launch_conv(x, pass, stream);
+    return e == hipSuccess ? BSMM_OK : dev_fail(e, pass == 0 ? "conv fprop launch" : pass == 1 ? "conv bprop launch"
+                                                                                             : "conv updat launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+bsmm_status bsmm_conv_create(bsmm_conv_handle* out, int64_t nblocks, int64_t Bc, int64_t Bk, const int32_t* cidx,
+                             const int32_t* kidx, int64_t C, int64_t K, const int64_t TRS[3], const int64_t DHW[3],
+                             const int64_t strides[3], const int64_t dilates[3], int padding,
+                             const int64_t pads[3]) {
+    if (!out) return fail(BSMM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (nblocks < 0 || nblocks > INT32_MAX / 2) return fail(BSMM_ERR_INVALID_ARG, "nblocks out of range");
+    if (Bc < 1 || Bk < 1 || Bk > 64 || Bc > 65536) return fail(BSMM_ERR_INVALID_ARG, "Bc must be >= 1, Bk in [1, 64]");
+    if (nblocks > 0 && (!cidx || !kidx)) return fail(BSMM_ERR_INVALID_ARG, "channel lists are NULL");
+    if (C < 1 || K < 1 || C > INT32_MAX || K > INT32_MAX) return fail(BSMM_ERR_INVALID_ARG, "C and K must be >= 1");
+    if (!TRS || !DHW || !strides || !dilates) return fail(BSMM_ERR_INVALID_ARG, "geometry arrays are NULL");
+    if (padding < 0 || padding > 2 || (padding == 2 && !pads))
+        return fail(BSMM_ERR_INVALID_ARG, "padding must be 0 (SAME), 1 (VALID) or 2 (explicit pads)");
+    bsmm_conv_plan* p = new (std::nothrow) bsmm_conv_plan();
+    if (!p) return fail(BSMM_ERR_OOM, "out of host memory");
+    auto reject = [&](const char* msg) {
+        delete p;
+        return fail(BSMM_ERR_INVALID_ARG, msg);
+    };
+    for (int a = 0; a < 3; a++) {
+        if (TRS[a] < 1 || DHW[a] < 1 || strides[a] < 1 || dilates[a] < 1 || TRS[a] > 4096 || DHW[a] > (1 << 20) ||
+            strides[a] > 4096 || dilates[a] > 4096)
+            return reject("filter, image, stride and dilation sizes must be >= 1");
+        const int64_t X = DHW[a], F = TRS[a], st = strides[a], dl = dilates[a];
+        int64_t o, pd;
+        if (padding == 0) {            // SAME
+            o = (X + st - 1) / st;
+            pd = std::max<int64_t>(0, (o - 1) * st + (F - 1) * dl + 1 - X) / 2;
+        } else if (padding == 1) {     // VALID
+            pd = 0;
+            o = X - (F - 1) * dl - 1 >= 0 ? (X - (F - 1) * dl - 1) / st + 1 : 0;
+        } else {
+            pd = pads[a];
+            if (pd < 0 || pd > 4096) return reject("explicit pads must be in [0, 4096]");
+            o = X + 2 * pd - (F - 1) * dl - 1 >= 0 ? (X + 2 * pd - (F - 1) * dl - 1) / st + 1 : 0;
+        }
+        if (o < 1) return reject("the filter does not fit the padded image");
+        p->TRS[a] = (int)F;
+        p->DHW[a] = (int)X;
+        p->MPQ[a] = (int)o;
+        p->st[a] = (int)st;
+        p->dl[a] = (int)dl;
+        p->pad[a] = (int)pd;
+    }
+    p->C = C;
+    p->K = K;
+    p->nb = (int)nblocks;
+    p->Bc = (int)Bc;
+    p->Bk = (int)Bk;
+    p->cidx.assign(cidx ? cidx : nullptr, cidx ? cidx + nblocks * Bc : nullptr);
+    p->kidx.assign(kidx ? kidx : nullptr, kidx ? kidx + nblocks * Bk : nullptr);
+    for (int64_t b = 0; b < nblocks; b++) {
+        for (int64_t i = 0; i < Bc; i++) {
+            const int32_t c = p->cidx[b * Bc + i];
+            if (c < 0 || c >= C) return reject("an input channel index is outside [0, C)");
+            for (int64_t i2 = 0; i2 < i; i2++)
+                if (p->cidx[b * Bc + i2] == c) return reject("a block lists an input channel twice");
+        }
+        for (int64_t j = 0; j < Bk; j++) {
+            const int32_t k = p->kidx[b * Bk + j];
+            if (k < 0 || k >= K) return reject("an output channel index is outside [0, K)");
+            for (int64_t j2 = 0; j2 < j; j2++)
+                if (p->kidx[b * Bk + j2] == k) return reject("a block lists an output channel twice");
+        }
+    }
+    // per-channel (block, position) lists in block order: counting sort
+    auto lists = [&](int64_t nch, int64_t per, const std::vector<int32_t>& idx, std::vector<int32_t>& ptr,
+                     std::vector<int32_t>& ent) {
+        ptr.assign(nch + 1, 0);
+        for (int32_t v : idx) ptr[v + 1]++;
+        for (int64_t c = 0; c < nch; c++) ptr[c + 1] += ptr[c];
+        ent.assign(2 * idx.size(), 0);
+        std::vector<int32_t> fill(ptr.begin(), ptr.end() - 1);
+        for (int64_t b = 0; b < nblocks; b++)
+            for (int64_t i = 0; i < per; i++) {
+                const int32_t pos = fill[idx[b * per + i]]++;
+                ent[2 * pos] = (int32_t)b;
+                ent[2 * pos + 1] = (int32_t)i;
+            }
+    };
+    lists(K, Bk, p->kidx, p->kptr, p->kent);
+    lists(C, Bc, p->cidx, p->cptr, p->cent);
+    *out = p;
+    return BSMM_OK;
+}
+
+void bsmm_conv_destroy(bsmm_conv_handle h) {
+    if (!h) return;
+    for (auto& kv : h->dev) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+            (void)hipFree(kv.second);
+            (void)hipSetDevice(cur);
+        }
+    }
+    delete h;
+}
+
+bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[3]) {
+    if (!h || !MPQ || !pads) return fail(BSMM_ERR_INVALID_ARG, "NULL argument");
+    for (int a = 0; a < 3; a++) {
+        MPQ[a] = h->MPQ[a];
+        pads[a] = h->pad[a];
+    }
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N, bsmm_dtype dt,
+                            void* stream) {
+    return conv_call(h, 0, I, F, O, N, dt, stream);
+}
+
+bsmm_status bsmm_conv_bprop(bsmm_conv_handle h, const void* F, const void* dO, void* dI, int64_t N, bsmm_dtype dt,
+                            void* stream) {
+    return conv_call(h, 1, dO, F, dI, N, dt, stream);
+}
+
+bsmm_status bsmm_conv_updat(bsmm_conv_handle h, const void* I, const void* dO, float* dF, int64_t N, bsmm_dtype dt,
+                            void* stream) {
+    return conv_call(h, 2, I, dO, dF, N, dt, stream);
+}
+
+}  // extern "C"

@@ -113,3 +113,19 @@ struct bsmm_proj_plan {
     std::mutex mu;
     std::map<int, int32_t*> dev;   // per HIP device ordinal: lut (nproj) followed by inv (nhidden)
 };
+
+// BlocksparseConv: channel-list blocks and the convolution geometry (kiteco/blocksparse
+// README, "API Documentation" › blocksparse.conv › BlocksparseConv).  cidx / kidx hold
+// each block's Bc input and Bk output channels; kptr/kent list, per output channel, its
+// (block, position in the block's output list) pairs in block order (fprop), cptr/cent
+// the same per input channel (bprop).  Immutable after create; one device copy of the
+// tables per device, made on first use.
+struct bsmm_conv_plan {
+    int64_t C = 0, K = 0;
+    int nb = 0, Bc = 0, Bk = 0;
+    int TRS[3] = {1, 1, 1}, DHW[3] = {1, 1, 1}, MPQ[3] = {1, 1, 1};
+    int st[3] = {1, 1, 1}, dl[3] = {1, 1, 1}, pad[3] = {0, 0, 0};
+    std::vector<int32_t> cidx, kidx, kptr, kent, cptr, cent;
+    std::mutex mu;
+    std::map<int, int32_t*> dev;   // per HIP device: cidx, kidx, kptr, kent, cptr, cent back to back
+};

@@ -160,6 +160,24 @@ struct ProjArgs {
 };
 hipError_t launch_proj(const ProjArgs& a, void* stream);
 
+// BlocksparseConv (conv.hip).  Activations (N, channels, D, H, W); filter
+// (nblocks, Bc, T, R, S, Bk); channel lists and per-channel block lists on the device.
+struct ConvArgs {
+    const void* a;        // fprop: I; bprop: dO; updat: I
+    const void* b;        // fprop / bprop: F; updat: dO
+    void* out;            // O, dI (storage dtype) or dF (float32)
+    const int32_t* cidx;  // nblocks * Bc input channels
+    const int32_t* kidx;  // nblocks * Bk output channels
+    const int32_t* lptr;  // fprop: K+1 offsets of kent; bprop: C+1 offsets of cent
+    const int32_t* lent;  // (block, position in the block's list) pairs
+    int64_t N, C, K;
+    int nb, Bc, Bk;
+    int T, R, S, D, H, W, M, P, Q;
+    int st[3], dl[3], pad[3];
+    int dt;
+};
+hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 fprop, 1 bprop, 2 updat
+
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.
 void prof_events(int pass, void** start, void** stop);

@@ -87,9 +87,12 @@ typedef enum {
     BSMM_PASS_PROJ_SCATTER = 9,
     BSMM_PASS_PROJ_SCATTER_ADD = 10,
     BSMM_PASS_PROJ_SCATTER_MUL = 11,
-    BSMM_PASS_PROJ_GATHER_MUL = 12
+    BSMM_PASS_PROJ_GATHER_MUL = 12,
+    BSMM_PASS_CONV_FPROP = 13,
+    BSMM_PASS_CONV_BPROP = 14,
+    BSMM_PASS_CONV_UPDAT = 15
 } bsmm_pass;
-#define BSMM_NUM_PASSES 13
+#define BSMM_NUM_PASSES 16
 
 typedef struct bsmm_plan* bsmm_handle;
 
@@ -332,6 +335,50 @@ BSMM_API bsmm_status bsmm_proj_scatter_mul(bsmm_proj_handle h, const void* x, co
 /* g = gather_mul(a, b): a, b (N, nhidden); g (N, nproj), not overlapping a or b. */
 BSMM_API bsmm_status bsmm_proj_gather_mul(bsmm_proj_handle h, const void* a, const void* b, void* g, int64_t N,
                                           int feature_axis, bsmm_dtype dt, void* stream);
+
+/* ---- BlocksparseConv (kiteco/blocksparse README, "API Documentation" › blocksparse.conv ›
+ * BlocksparseConv(BCK, TRS, DHW, MPQ=None, strides, dilates, padding, edge_bias)): a
+ * convolution whose filter exists only for blocks of channels.  Block b lists Bc input
+ * channels C_b and Bk output channels K_b (the pages' BCK); its filter F[b] is
+ * (Bc, T, R, S, Bk), F as a whole (nblocks, Bc, T, R, S, Bk) contiguous.  Blocks may
+ * share channels; their contributions add.  The page gives no formulas; the readings:
+ *   activations  I (N, C, D, H, W), O (N, K, M, P, Q), dense, contiguous, 16-byte aligned;
+ *                1-D / 2-D images are 3-D with leading sizes of 1 (pass 1s).
+ *   geometry     per dim with image X, filter F, stride st, dilation dl:
+ *                SAME (padding 0): out = ceil(X/st), pad = max(0, (out-1)*st + (F-1)*dl + 1 - X) / 2;
+ *                VALID (1): pad = 0, out = (X - (F-1)*dl - 1)/st + 1;
+ *                explicit (2): pad = pads[d], out = (X + 2*pad - (F-1)*dl - 1)/st + 1.
+ *   fprop        O[n, K_b[j], m, p, q] += sum over i, t, r, s of
+ *                I[n, C_b[i], m*st-pad+t*dl, p*st-pad+r*dl, q*st-pad+s*dl] * F[b, i, t, r, s, j]
+ *                over all blocks (positions outside the image read as 0); O fully written.
+ *   bprop        dI = the gradient of fprop with respect to I for dO; dI fully written.
+ *   updat        dF[b, i, t, r, s, j] = sum over n, m, p, q of I[...] * dO[n, K_b[j], m, p, q];
+ *                dF float32, overwritten (N = 0 writes zeros).
+ * Storage dtype dt for I, F, O, dO, dI (fp32 accumulation, RNE to 16-bit outputs).
+ * edge_bias, MPQ (transposed convolution) and BlocksparseDeconv are not provided. */
+typedef struct bsmm_conv_plan* bsmm_conv_handle;
+
+/* Build a plan.  cidx (nblocks*Bc), kidx (nblocks*Bk): host channel lists, read during
+ * the call; entries in [0, C) / [0, K), distinct within a block.  Bk <= 64.  TRS, DHW,
+ * strides, dilates: 3 entries each, >= 1.  padding: 0 SAME, 1 VALID, 2 explicit (pads,
+ * 3 entries >= 0).  BSMM_ERR_INVALID_ARG when the filter does not fit the padded image. */
+BSMM_API bsmm_status bsmm_conv_create(bsmm_conv_handle* out, int64_t nblocks, int64_t Bc, int64_t Bk,
+                                      const int32_t* cidx, const int32_t* kidx, int64_t C, int64_t K,
+                                      const int64_t TRS[3], const int64_t DHW[3], const int64_t strides[3],
+                                      const int64_t dilates[3], int padding, const int64_t pads[3]);
+/* Release the plan and its device tables (NULL-safe).  No call may be in flight. */
+BSMM_API void bsmm_conv_destroy(bsmm_conv_handle h);
+/* Output image size (M, P, Q) and the leading pads of each dim. */
+BSMM_API bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[3]);
+/* O = fprop(F, I). */
+BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N,
+                                     bsmm_dtype dt, void* stream);
+/* dI = bprop(F, dO). */
+BSMM_API bsmm_status bsmm_conv_bprop(bsmm_conv_handle h, const void* F, const void* dO, void* dI, int64_t N,
+                                     bsmm_dtype dt, void* stream);
+/* dF = updat(I, dO), float32. */
+BSMM_API bsmm_status bsmm_conv_updat(bsmm_conv_handle h, const void* I, const void* dO, float* dF, int64_t N,
+                                     bsmm_dtype dt, void* stream);
 
 /* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
  * every pass launched from the calling thread records HIP events around its kernels

@@ -232,3 +232,33 @@ def proj_problem(rng: np.random.Generator, N: int, nhidden: int, nproj: int, fa:
     a = _draw(rng, act_shape(fa, N, nhidden), 1.0, dtype)
     s = _draw(rng, act_shape(fa, N, nproj), 1.0, dtype)
     return ProjProblem(N, nhidden, nproj, fa, dtype, lut, x, a, s)
+
+
+@dataclasses.dataclass
+class ConvProblem:
+    """Seeded inputs of BlocksparseConv: BCK (one (input channels, output channels) pair
+    per block), filter F (nblocks, Bc, *TRS, Bk), input I (N, C, *DHW) and output
+    gradient dO (N, K, *MPQ)."""
+    BCK: list
+    F: torch.Tensor
+    I: torch.Tensor
+    dO: torch.Tensor
+
+
+def conv_problem(rng: np.random.Generator, N: int, C: int, K: int, Bc: int, Bk: int, nblocks: int, TRS, DHW, MPQ,
+                 dtype: str, f_std: float = 0.1, contiguous_blocks: bool = False) -> ConvProblem:
+    """Channel lists first (contiguous_blocks: block b takes the b-th (c-block, k-block)
+    pair of a random choice of distinct cells of the (C/Bc) x (K/Bk) block grid, with
+    consecutive channels; else rng.permutation draws per block, so blocks may share
+    channels), then F ~ N(0, f_std), I ~ N(0, 1), dO ~ N(0, 1)."""
+    if contiguous_blocks:
+        cells = rng.choice((C // Bc) * (K // Bk), nblocks, replace=False)
+        BCK = [(tuple(range((c // (K // Bk)) * Bc, (c // (K // Bk)) * Bc + Bc)),
+                tuple(range((c % (K // Bk)) * Bk, (c % (K // Bk)) * Bk + Bk))) for c in sorted(cells)]
+    else:
+        BCK = [(tuple(int(v) for v in rng.permutation(C)[:Bc]), tuple(int(v) for v in rng.permutation(K)[:Bk]))
+               for _ in range(nblocks)]
+    F = _draw(rng, (nblocks, Bc) + tuple(TRS) + (Bk,), f_std, dtype)
+    I = _draw(rng, (N, C) + tuple(DHW), 1.0, dtype)
+    dO = _draw(rng, (N, K) + tuple(MPQ), 1.0, dtype)
+    return ConvProblem(BCK, F, I, dO)

@@ -1,0 +1,83 @@
+"""BlocksparseConv on the GPU against the CPU oracle (calls through the C ABI): fprop,
+the input gradient and the filter gradient for 1-D, 2-D and 3-D images, strides,
+dilations, SAME / VALID / explicit padding, blocks that share channels and channels in
+no block, fp32 / bf16 / f16 storage; autograd through BlocksparseConv.__call__."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_matrix_amd as bs
+import synth
+from gpu_util import assert_close, dev
+from oracle import conv as oc
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # N, C, K, Bc, Bk, nblocks, TRS, DHW, strides, dilates, padding
+    (3, 6, 5, 2, 3, 4, (3,), (9,), (1,), (1,), "SAME"),
+    (2, 8, 8, 4, 4, 3, (3, 3), (7, 6), (2, 1), (1, 1), "SAME"),
+    (2, 8, 6, 2, 2, 5, (2, 3), (8, 9), (1, 2), (2, 1), "VALID"),
+    (4, 16, 16, 8, 8, 3, (3, 3), (5, 5), (1, 1), (1, 1), 1),
+    (2, 6, 6, 3, 3, 2, (2, 3, 2), (4, 5, 6), (1, 2, 1), (1, 1, 2), "SAME"),
+    (2, 64, 64, 32, 32, 3, (3, 3), (12, 12), (1, 1), (1, 1), "SAME"),
+    (1, 9, 70, 3, 64, 2, (1, 1), (3, 4), (1, 1), (1, 1), "VALID"),
+]
+
+
+def _f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{len(c[6])}d-{c[10]}-B{c[3]}x{c[4]}" for c in CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_conv(case, dtype):
+    N, C, K, Bc, Bk, nb, TRS, DHW, st, dl, pad = case
+    print(f"case conv {case} {dtype}", flush=True)
+    g = oc.geometry(TRS, DHW, st, dl, pad)
+    MPQ = g[2][3 - len(DHW):]
+    rng = np.random.default_rng(C * 13 + K + len(DHW))
+    P = synth.conv_problem(rng, N, C, K, Bc, Bk, nb, TRS, DHW, MPQ, dtype)
+    # channel C-1 / K-1 in every problem: the plan's channel counts are one past the largest index
+    P.BCK[0] = (P.BCK[0][0][:-1] + (C - 1,) if C - 1 not in P.BCK[0][0] else P.BCK[0][0],
+                P.BCK[0][1][:-1] + (K - 1,) if K - 1 not in P.BCK[0][1] else P.BCK[0][1])
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, strides=st, dilates=dl, padding=pad)
+    assert conv.C == C and conv.K == K and conv.MPQ == MPQ
+    bck = oc.split_bck(P.BCK)
+    F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    O = conv.fprop(F, I)
+    dI = conv.bprop(F, dO)
+    dF = conv.updat(I, dO)
+    torch.cuda.synchronize()
+    Fr, Ir, dOr = _f64(P.F), _f64(P.I), _f64(P.dO)
+    assert_close(O, oc.fprop(bck, Fr, Ir, K, g).reshape(O.shape), dtype, "conv fprop")
+    assert_close(dI, oc.bprop(bck, Fr, dOr, C, g).reshape(dI.shape), dtype, "conv bprop")
+    assert_close(dF, oc.updat(bck, Ir, dOr, g).reshape(dF.shape), "f32" if dtype == "f32" else dtype, "conv updat")
+    # output channels in no block are zero, input channels in no block get zero gradient
+    used_k = set(int(k) for blk in P.BCK for k in blk[1])
+    used_c = set(int(c) for blk in P.BCK for c in blk[0])
+    for k in range(K):
+        if k not in used_k:
+            assert torch.count_nonzero(O[:, k]) == 0
+    for c in range(C):
+        if c not in used_c:
+            assert torch.count_nonzero(dI[:, c]) == 0
+
+
+def test_autograd_and_determinism():
+    rng = np.random.default_rng(3)
+    TRS, DHW = (3, 3), (10, 9)
+    g = oc.geometry(TRS, DHW)
+    P = synth.conv_problem(rng, 3, 32, 32, 8, 8, 6, TRS, DHW, g[2][1:], "f32", contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW)
+    F = dev(P.F).requires_grad_()
+    I = dev(P.I).requires_grad_()
+    O = conv(F, I)
+    O.backward(dev(P.dO))
+    bck = oc.split_bck(P.BCK)
+    assert_close(F.grad, oc.updat(bck, _f64(P.I), _f64(P.dO), g).reshape(F.shape), "f32", "dF")
+    assert_close(I.grad, oc.bprop(bck, _f64(P.F), _f64(P.dO), conv.C, g).reshape(I.shape), "f32", "dI")
+    O2 = conv.fprop(F.detach(), I.detach())
+    dF2 = conv.updat(I.detach(), dev(P.dO))
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(dF2, F.grad)
