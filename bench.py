@@ -60,7 +60,7 @@ def parse():
                          "(measured slower on MI355X: the two kernels compete rather than overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer-norm", action="store_true",
-                    help="skip the layer_norm, l2_normalize and SparseProj timing")
+                    help="skip the layer_norm, l2_normalize, SparseProj and BlocksparseConv timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -395,6 +395,52 @@ def run_sparse_proj(reps=20):
     return out
 
 
+def run_conv(reps=3):
+    """Kernel time of BlocksparseConv (fprop, input gradient, filter gradient) on a 2-D
+    workload: 256 input and output channels in blocks of 32 x 32 channels (half of the
+    8 x 8 block grid present, consecutive channels), 3 x 3 filter, 32 x 32 images,
+    N = 32, SAME, stride 1, bf16.  FLOPs per pass 2 * N * M*P*Q * nblocks * Bc * Bk * T*R*S;
+    algorithmic bytes |I| + |O| + |F| (fprop, bprop), |I| + |dO| + |dF| (float32 dF)."""
+    import numpy as np
+    import torch
+    import block_sparse_matrix_amd as bs
+    import synth
+    N, C, B, TRS, DHW, dt = 32, 256, 32, (3, 3), (32, 32), "bf16"
+    nb = (C // B) * (C // B) // 2
+    P = synth.conv_problem(np.random.default_rng(23), N, C, C, B, B, nb, TRS, DHW, DHW, dt,
+                           contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW)
+    F, I, dO = P.F.cuda(), P.I.cuda(), P.dO.cuda()
+    O, dI = torch.empty_like(dO), torch.empty_like(I)
+    dF = torch.empty(conv.f_shape(), dtype=torch.float32, device="cuda")
+    h = conv.handle
+
+    def launch():
+        bs.bsmm_conv_fprop(h, F, I, O, N)
+        bs.bsmm_conv_bprop(h, F, dO, dI, N)
+        bs.bsmm_conv_updat(h, I, dO, dF, N)
+
+    launch()
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    for _ in range(reps):
+        launch()
+    torch.cuda.synchronize()
+    pr = bs.bsmm_profile_end()
+    flops = 2.0 * N * DHW[0] * DHW[1] * nb * B * B * TRS[0] * TRS[1]
+    act, fb = N * C * DHW[0] * DHW[1] * 2, nb * B * B * TRS[0] * TRS[1]
+    nbytes = {"conv_fprop": 2 * act + 2 * fb, "conv_bprop": 2 * act + 2 * fb, "conv_updat": 2 * act + 4 * fb}
+    out = {"workload": f"BlocksparseConv 2-D, C = K = {C} in {B}x{B}-channel blocks ({nb} of 64), 3x3 filter, "
+                       f"32x32 images, N = {N}, SAME, bf16"}
+    for key, nbt in nbytes.items():
+        us = pr[key][0] / pr[key][1] * 1e3
+        bound, tstar = roof(flops, nbt, dt)
+        out[key[5:]] = {"kernel_us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+                        "alg_bytes": int(nbt), "flops": int(flops), "bound": bound,
+                        "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 5)}
+    return out
+
+
 def run_l2_normalize(P, reps=40):
     """Kernel time of BlocksparseMatMul.l2_normalize (weight normalisation per output
     feature, bf16 weights -> bf16) and its gradient (bf16 upstream -> fp32 dW) on this
@@ -489,6 +535,7 @@ def main():
         out["layer_norm"] = run_layer_norm()
         out["l2_normalize"] = run_l2_normalize(P)
         out["sparse_proj"] = run_sparse_proj()
+        out["conv"] = run_conv()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
     else:
