@@ -87,6 +87,7 @@ def lib():
         "bsmm_proj_create": [ctypes.POINTER(vp), i64, i64, i64, i64, vp],
         "bsmm_conv_create": [ctypes.POINTER(vp), i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, i32, vp],
         "bsmm_conv_geometry": [vp, vp, vp],
+        "bsmm_conv_kernel_name": [vp, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
         "bsmm_conv_fprop": [vp, vp, vp, vp, i64, i32, vp],
         "bsmm_conv_bprop": [vp, vp, vp, vp, i64, i32, vp],
         "bsmm_conv_updat": [vp, vp, vp, vp, i64, i32, vp],
@@ -832,6 +833,13 @@ class BlocksparseConv:
         if h is not None and _lib is not None:
             _lib.bsmm_conv_destroy(h)
             self.handle = None
+
+    def kernel_name(self, pass_: str, dtype=torch.bfloat16) -> str:
+        """Kernel family a pass ("fprop", "bprop", "updat") launches: "matrix_core" or "direct"."""
+        name = ctypes.c_char_p()
+        _check(lib().bsmm_conv_kernel_name(self.handle, {"fprop": 0, "bprop": 1, "updat": 2}[pass_],
+                                           DTYPE_CODE[dtype], ctypes.byref(name)), "bsmm_conv_kernel_name")
+        return name.value.decode()
 
     def f_shape(self, block=None):
         one = (self.Bc,) + self.TRS + (self.Bk,)

@@ -883,10 +883,13 @@ bsmm_status bsmm_proj_gather_mul(bsmm_proj_handle h, const void* a, const void* 
 namespace {
 
 // device copy of the conv tables; offsets (int32 elements) of each array in `off`
-bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[6]) {
-    const std::vector<int32_t>* parts[6] = {&h->cidx, &h->kidx, &h->kptr, &h->kent, &h->cptr, &h->cent};
+constexpr int kConvParts = 12;
+bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[kConvParts]) {
+    const std::vector<int32_t>* parts[kConvParts] = {&h->cidx,    &h->kidx,    &h->kptr,   &h->kent,
+                                                     &h->cptr,    &h->cent,    &h->gptr[0], &h->gblk[0],
+                                                     &h->zch[0],  &h->gptr[1], &h->gblk[1], &h->zch[1]};
     size_t total = 0;
-    for (int i = 0; i < 6; i++) {
+    for (int i = 0; i < kConvParts; i++) {
         off[i] = total;
         total += parts[i]->size();
     }
@@ -901,7 +904,7 @@ bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[6]) {
     }
     std::vector<int32_t> all;
     all.reserve(total);
-    for (int i = 0; i < 6; i++) all.insert(all.end(), parts[i]->begin(), parts[i]->end());
+    for (int i = 0; i < kConvParts; i++) all.insert(all.end(), parts[i]->begin(), parts[i]->end());
     int32_t* p = nullptr;
     e = hipMalloc((void**)&p, (total > 0 ? total : 1) * sizeof(int32_t));
     if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of the conv tables failed")
@@ -914,6 +917,26 @@ bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[6]) {
     h->dev.emplace(dev, p);
     *d = p;
     return BSMM_OK;
+}
+
+// the plan's sizes and geometry as kernel arguments (no device pointers)
+ConvArgs conv_args(const bsmm_conv_plan* h, int dt) {
+    ConvArgs x{};
+    x.C = h->C;
+    x.K = h->K;
+    x.nb = h->nb;
+    x.Bc = h->Bc;
+    x.Bk = h->Bk;
+    x.T = h->TRS[0]; x.R = h->TRS[1]; x.S = h->TRS[2];
+    x.D = h->DHW[0]; x.H = h->DHW[1]; x.W = h->DHW[2];
+    x.M = h->MPQ[0]; x.P = h->MPQ[1]; x.Q = h->MPQ[2];
+    for (int i = 0; i < 3; i++) {
+        x.st[i] = h->st[i];
+        x.dl[i] = h->dl[i];
+        x.pad[i] = h->pad[i];
+    }
+    x.dt = dt;
+    return x;
 }
 
 bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b, void* out, int64_t N,
@@ -934,9 +957,9 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
     if ((uint64_t)N > (uint64_t)INT64_MAX / 8 / (uint64_t)std::max<int64_t>(1, std::max(h->C * sp_in, h->K * sp_out)))
         return fail(BSMM_ERR_UNSUPPORTED, "tensor too large");
     const int32_t* d = nullptr;
-    size_t off[6];
+    size_t off[kConvParts];
     if ((s = conv_device(h, &d, off)) != BSMM_OK) return s;
-    ConvArgs x{};
+    ConvArgs x = conv_args(h, dt);
     x.a = a;
     x.b = b;
     x.out = out;
@@ -945,20 +968,14 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
     x.lptr = pass == 0 ? d + off[2] : d + off[4];
     x.lent = pass == 0 ? d + off[3] : d + off[5];
     x.N = N;
-    x.C = h->C;
-    x.K = h->K;
-    x.nb = h->nb;
-    x.Bc = h->Bc;
-    x.Bk = h->Bk;
-    x.T = h->TRS[0]; x.R = h->TRS[1]; x.S = h->TRS[2];
-    x.D = h->DHW[0]; x.H = h->DHW[1]; x.W = h->DHW[2];
-    x.M = h->MPQ[0]; x.P = h->MPQ[1]; x.Q = h->MPQ[2];
-    for (int i = 0; i < 3; i++) {
-        x.st[i] = h->st[i];
-        x.dl[i] = h->dl[i];
-        x.pad[i] = h->pad[i];
+    if (pass < 2 && h->gok[pass] && conv_mfma_plan(x, pass)) {
+        x.mfma = 1;
+        x.gptr = d + off[pass == 0 ? 6 : 9];
+        x.gblk = d + off[pass == 0 ? 7 : 10];
+        x.zch = d + off[pass == 0 ? 8 : 11];
+        x.ngroups = (int)h->gptr[pass].size() - 1;
+        x.nz = (int)h->zch[pass].size();
     }
-    x.dt = dt;
     hipError_t e = launch_conv(x, pass, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, pass == 0 ? "conv fprop launch" : pass == 1 ? "conv bprop launch"
                                                                                              : "conv updat launch");
@@ -1050,6 +1067,44 @@ bsmm_status bsmm_conv_create(bsmm_conv_handle* out, int64_t nblocks, int64_t Bc,
     };
     lists(K, Bk, p->kidx, p->kptr, p->kent);
     lists(C, Bc, p->cidx, p->cptr, p->cent);
+    // matrix-core grouping: blocks with identical output lists form a group; groups must
+    // not share a channel
+    auto group = [&](int pass, int64_t nch, int64_t per, const std::vector<int32_t>& idx) {
+        std::map<std::vector<int32_t>, int32_t> gid;
+        std::vector<std::vector<int32_t>> members;
+        for (int64_t b = 0; b < nblocks; b++) {
+            std::vector<int32_t> key(idx.begin() + b * per, idx.begin() + (b + 1) * per);
+            auto it = gid.find(key);
+            if (it == gid.end()) {
+                it = gid.emplace(key, (int32_t)members.size()).first;
+                members.emplace_back();
+            }
+            members[it->second].push_back((int32_t)b);
+        }
+        std::vector<int32_t> owner(nch, -1);
+        bool ok = true;
+        for (size_t g = 0; g < members.size(); g++) {
+            const int64_t b = members[g][0];
+            for (int64_t i = 0; i < per; i++) {
+                int32_t& o = owner[idx[b * per + i]];
+                if (o >= 0 && o != (int32_t)g) ok = false;
+                o = (int32_t)g;
+            }
+        }
+        p->gok[pass] = ok;
+        p->gptr[pass].assign(1, 0);
+        p->gblk[pass].clear();
+        p->zch[pass].clear();
+        if (!ok) return;
+        for (auto& m : members) {
+            p->gblk[pass].insert(p->gblk[pass].end(), m.begin(), m.end());
+            p->gptr[pass].push_back((int32_t)p->gblk[pass].size());
+        }
+        for (int64_t c = 0; c < nch; c++)
+            if (owner[c] < 0) p->zch[pass].push_back((int32_t)c);
+    };
+    group(0, K, Bk, p->kidx);
+    group(1, C, Bc, p->cidx);
     *out = p;
     return BSMM_OK;
 }
@@ -1072,6 +1127,14 @@ bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[
         MPQ[a] = h->MPQ[a];
         pads[a] = h->pad[a];
     }
+    return BSMM_OK;
+}
+
+bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, const char** name) {
+    if (!h || !name || pass < 0 || pass > 2) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    ConvArgs x = conv_args(h, dt);
+    *name = pass < 2 && h->gok[pass] && conv_mfma_plan(x, pass) ? "matrix_core" : "direct";
     return BSMM_OK;
 }
 

@@ -126,6 +126,11 @@ struct bsmm_conv_plan {
     int TRS[3] = {1, 1, 1}, DHW[3] = {1, 1, 1}, MPQ[3] = {1, 1, 1};
     int st[3] = {1, 1, 1}, dl[3] = {1, 1, 1}, pad[3] = {0, 0, 0};
     std::vector<int32_t> cidx, kidx, kptr, kent, cptr, cent;
+    // Matrix-core grouping per pass (0 fprop: blocks by output channel list; 1 bprop: by
+    // input channel list): group offsets, block ids, and the channels no block writes.
+    // gok[p] is false when two groups share a channel (the direct kernels run then).
+    std::vector<int32_t> gptr[2], gblk[2], zch[2];
+    bool gok[2] = {false, false};
     std::mutex mu;
-    std::map<int, int32_t*> dev;   // per HIP device: cidx, kidx, kptr, kent, cptr, cent back to back
+    std::map<int, int32_t*> dev;   // per HIP device: all the arrays above back to back
 };

@@ -168,8 +168,216 @@ __global__ __launch_bounds__(256) void conv_updat_kernel(ConvArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Matrix-core path: 2-D images, stride 1, dilation 1, 16-bit storage.  A workgroup (4
+// waves) owns one group of blocks that share an output channel list (CO = 16*OT
+// channels), one image and TH output rows.  For each block of the group and each slab
+// of 32 contraction channels it stages in LDS the slab's input rows (TH + R - 1 rows with
+// the halo, zero outside the image) once per column shift s of the filter, so that tap
+// (r, s) reads its operand at an aligned column: copy s holds column x + s - pad at x.
+// The filter slab is staged as [tap][output channel][32 contraction channels].  Each
+// tap is then one 32-deep v_mfma_f32_16x16x32 step per (16-position tile, 16-channel
+// tile): the position operand comes from the staged rows with the transposing LDS read
+// ([channel][position] tile), the filter operand with one 16-byte read.  Wave w takes
+// position tiles w, w+4, ... and all output tiles, accumulating in registers over the
+// group's blocks, taps and slabs in a fixed order.
+//
+// bprop runs the same kernel as the convolution of dO with the flipped, transposed
+// filter: contraction over each block's output channels, outputs its input channels,
+// pads F - 1 - pad.
+template <int DT, int OT, bool TR>
+__global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
+    constexpr int CO = 16 * OT;
+    const int CI = TR ? a.Bk : a.Bc;                       // contraction channels per block
+    const int32_t* in_idx = TR ? a.kidx : a.cidx;
+    const int32_t* out_idx = TR ? a.cidx : a.kidx;
+    const int Hi = TR ? a.P : a.H, Wi = TR ? a.Q : a.W;    // this pass's input image
+    const int Ho = TR ? a.H : a.P, Wo = TR ? a.W : a.Q;    // and output image
+    const int R = a.R, S = a.S, RS = R * S;
+    const int ph = TR ? R - 1 - a.pad[1] : a.pad[1], pw = TR ? S - 1 - a.pad[2] : a.pad[2];
+    const int64_t Cin = TR ? a.K : a.C, Cout = TR ? a.C : a.K;
+    const int PT = (Wo + 15) / 16, COLS = PT * 16;
+    const int TH = a.TH, ROWS = TH + R - 1, CP = a.cpitch;
+    BSMM_LDS uint16_t* xs = (BSMM_LDS uint16_t*)dsm;              // [s][32 channels][CP]
+    BSMM_LDS uint16_t* fs = xs + S * 32 * CP;                       // [tap][CO][40]
+
+    const int nyt = (Ho + TH - 1) / TH;
+    const int yt = blockIdx.x % nyt;
+    const int64_t rest = blockIdx.x / nyt;
+    const int64_t n = rest % a.N;
+    const int g = (int)(rest / a.N);
+    const int y0 = yt * TH;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int npt = TH * PT;
+
+    f32x4 acc[4][OT];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int o = 0; o < OT; o++) acc[u][o] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int gb = a.gptr[g], ge = a.gptr[g + 1];
+    for (int e = gb; e < ge; e++) {
+        const int b = a.gblk[e];
+        for (int slab = 0; slab < CI / 32; slab++) {
+            __syncthreads();   // the previous slab's LDS is no longer read
+            // input rows: a thread copies whole staged rows (channel c, row rr); each source
+            // element is read once and written to every shift s it serves
+            const int XW = COLS + S - 1;
+            for (int q = t; q < 32 * ROWS; q += 256) {
+                const int rr = q % ROWS, c = q / ROWS;
+                const int y = y0 + rr - ph;
+                const int ch = in_idx[b * CI + slab * 32 + c];
+                const bool yok = y >= 0 && y < Hi;
+                const uint16_t* src = (const uint16_t*)a.a + ((n * Cin + ch) * Hi + (yok ? y : 0)) * Wi;
+                BSMM_LDS uint16_t* dst = xs + c * CP + rr * COLS;
+                for (int xs_ = 0; xs_ < XW; xs_++) {
+                    const int x = xs_ - pw;
+                    const uint16_t v = yok && x >= 0 && x < Wi ? src[x] : (uint16_t)0;
+                    for (int s = 0; s < S; s++) {
+                        const int col = xs_ - s;
+                        if (col >= 0 && col < COLS) dst[s * 32 * CP + col] = v;
+                    }
+                }
+            }
+            // filter slab: fs[tap][o][ci] (o: this pass's output channel in the block, ci:
+            // contraction channel in the slab), read in 16-byte runs of the stored layout
+            if constexpr (TR) {
+                // stored F[b, i = o, tap', j = slab*32 + ci]: 32 consecutive j per (o, tap');
+                // the transposed convolution takes the flipped tap
+                for (int q = t; q < CO * RS * 4; q += 256) {
+                    const int part = q % 4, tp = (q / 4) % RS, o = q / (4 * RS);
+                    const int tap = (R - 1 - tp / S) * S + (S - 1 - tp % S);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(
+                        (const uint16_t*)a.b + (((int64_t)b * a.Bc + o) * RS + tp) * a.Bk + slab * 32 + part * 8);
+                    *reinterpret_cast<BSMM_LDS u32x4*>(fs + (tap * CO + o) * 40 + part * 8) = v;
+                }
+            } else {
+                // stored F[b, i = slab*32 + ci, tap, j = o]: CO consecutive o per (ci, tap)
+                for (int q = t; q < 32 * RS * (CO / 8); q += 256) {
+                    const int part = q % (CO / 8), tap = (q / (CO / 8)) % RS, ci = q / ((CO / 8) * RS);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(
+                        (const uint16_t*)a.b + (((int64_t)b * a.Bc + slab * 32 + ci) * RS + tap) * a.Bk + part * 8);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int h = 0; h < 8; h++)
+                        fs[(tap * CO + part * 8 + h) * 40 + ci] = (uint16_t)(h & 1 ? w[h >> 1] >> 16 : w[h >> 1] & 0xffffu);
+                }
+            }
+            __syncthreads();
+            for (int tap = 0; tap < RS; tap++) {
+                const int r = tap / S, s = tap % S;
+                u32x4 bf[OT];
+#pragma unroll
+                for (int o = 0; o < OT; o++)
+                    bf[o] = *reinterpret_cast<const BSMM_LDS u32x4*>(fs + (tap * CO + o * 16 + m16) * 40 + 8 * g4);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int pt = wave + 4 * u;
+                    if (pt < npt) {   // wave-uniform
+                        const int ty = pt / PT, px = pt % PT;
+                        const u32x4 af = frag_tr16(xs + s * 32 * CP + (ty + r) * COLS + px * 16, CP, 0, lane);
+#pragma unroll
+                        for (int o = 0; o < OT; o++) mma<DT>(acc[u][o], af, bf[o]);
+                    }
+                }
+            }
+        }
+    }
+    // lane holds D[position 4*g4 + v][channel m16] of each tile
+    const int b0 = a.gblk[gb];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int pt = wave + 4 * u;
+        if (pt >= npt) continue;
+        const int ty = pt / PT, px = pt % PT;
+        const int y = y0 + ty;
+        if (y >= Ho) continue;
+#pragma unroll
+        for (int o = 0; o < OT; o++) {
+            const int oc = out_idx[b0 * CO + o * 16 + m16];
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int x = px * 16 + 4 * g4 + v;
+                if (x < Wo) store_elt(a.out, ((n * Cout + oc) * Ho + y) * Wo + x, acc[u][o][v], DT);
+            }
+        }
+    }
+}
+
+// Output channels that no block writes: zero.
+template <int DT>
+__global__ __launch_bounds__(256) void conv_zero_kernel(ConvArgs a, int64_t Cout, int64_t HWo) {
+    const int64_t total = a.N * a.nz * HWo;
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+        const int64_t sp = o % HWo, zc = (o / HWo) % a.nz, n = o / (HWo * a.nz);
+        store_elt(a.out, (n * Cout + a.zch[zc]) * HWo + sp, 0.f, DT);
+    }
+}
+
+bool conv_mfma_plan(ConvArgs& a, int pass) {
+    if (pass > 1 || a.dt == BSMM_F32 || a.T != 1 || a.D != 1) return false;
+    for (int i = 0; i < 3; i++)
+        if (a.st[i] != 1 || a.dl[i] != 1) return false;
+    const int CI = pass == 1 ? a.Bk : a.Bc, CO = pass == 1 ? a.Bc : a.Bk;
+    if (CI % 32 != 0 || (CO != 16 && CO != 32 && CO != 64)) return false;
+    if (pass == 1 && (a.pad[1] > a.R - 1 || a.pad[2] > a.S - 1)) return false;   // transposed pads >= 0
+    const int Wo = pass == 1 ? a.W : a.Q;
+    const int PT = (Wo + 15) / 16;
+    if (PT > 16) return false;
+    const int Ho = pass == 1 ? a.H : a.P;
+    a.TH = PT >= 8 ? 1 : 8 / PT;
+    if (a.TH > Ho) a.TH = Ho;
+    const int ROWS = a.TH + a.R - 1;
+    a.cpitch = ROWS * PT * 16 + 8;
+    a.lds_bytes = (a.S * 32 * a.cpitch + a.R * a.S * CO * 40) * 2;
+    return a.lds_bytes <= 80 * 1024;   // two workgroups per compute unit
+}
+
+template <int DT, int OT, bool TR>
+static hipError_t launch_conv_mfma_t(const ConvArgs& a, hipStream_t st) {
+    const int Ho = TR ? a.H : a.P;
+    const int64_t grid = (int64_t)a.ngroups * a.N * ((Ho + a.TH - 1) / a.TH);
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int pass = TR ? BSMM_PASS_CONV_BPROP : BSMM_PASS_CONV_FPROP;
+    void *e0 = nullptr, *e1 = nullptr;
+    prof_events(pass, &e0, &e1);   // one timing record spans both launches
+    if (a.nz > 0) {   // zero the channels no block writes
+        const int64_t HWo = TR ? (int64_t)a.H * a.W : (int64_t)a.P * a.Q;
+        const int64_t Cout = TR ? a.C : a.K;
+        int64_t zg = (a.N * a.nz * HWo + 255) / 256;
+        if (zg > (1 << 20)) zg = 1 << 20;
+        hipError_t e = launch_ev(conv_zero_kernel<DT>, dim3((unsigned)zg), dim3(256), st, e0, nullptr, a, Cout, HWo);
+        if (e != hipSuccess) return e;
+        e0 = nullptr;
+    }
+    auto kern = conv_mfma_kernel<DT, OT, TR>;
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), a.lds_bytes, st, (hipEvent_t)e0, (hipEvent_t)e1,
+                              0, a);
+    else
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), a.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, bool TR>
+static hipError_t launch_conv_mfma(const ConvArgs& a, hipStream_t st) {
+    switch (TR ? a.Bc : a.Bk) {
+    case 16: return launch_conv_mfma_t<DT, 1, TR>(a, st);
+    case 32: return launch_conv_mfma_t<DT, 2, TR>(a, st);
+    case 64: return launch_conv_mfma_t<DT, 4, TR>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DT>
 static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
+    if constexpr (DT != BSMM_F32) {
+        if (a.mfma && pass == 0) return launch_conv_mfma<DT, false>(a, st);
+        if (a.mfma && pass == 1) return launch_conv_mfma<DT, true>(a, st);
+    }
     if (pass == 2) {
         const int64_t rows = (int64_t)a.nb * a.Bc * a.T * a.R * a.S;
         if (rows == 0) return hipSuccess;

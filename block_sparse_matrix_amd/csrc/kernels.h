@@ -175,8 +175,23 @@ struct ConvArgs {
     int T, R, S, D, H, W, M, P, Q;
     int st[3], dl[3], pad[3];
     int dt;
+    // Matrix-core path (2-D, stride 1, dilation 1, 16-bit; fprop, and bprop as the
+    // transposed convolution): blocks grouped by their output channel list (the
+    // pass's output role), the groups' lists disjoint.
+    int mfma;             // 1: take the matrix-core kernel
+    const int32_t* gptr;  // ngroups+1 offsets into gblk
+    const int32_t* gblk;  // block ids of each group, ascending
+    int ngroups;
+    const int32_t* zch;   // output channels in no block (written as zero), nz of them
+    int nz;
+    int TH;               // output rows per workgroup
+    int cpitch;           // LDS elements per staged channel
+    int lds_bytes;
 };
 hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 fprop, 1 bprop, 2 updat
+// LDS layout of the matrix-core conv kernel: fills a.TH, a.cpitch, a.lds_bytes; false
+// when the shape does not fit it (the direct kernels run instead).
+bool conv_mfma_plan(ConvArgs& a, int pass);
 
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.

@@ -370,6 +370,13 @@ BSMM_API bsmm_status bsmm_conv_create(bsmm_conv_handle* out, int64_t nblocks, in
 BSMM_API void bsmm_conv_destroy(bsmm_conv_handle h);
 /* Output image size (M, P, Q) and the leading pads of each dim. */
 BSMM_API bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[3]);
+/* Which kernel family a conv pass (0 fprop, 1 bprop, 2 updat) launches for dtype dt
+ * (host only): "matrix_core" — 2-D or 1-D images, stride and dilation 1, 16-bit
+ * storage, the pass's contraction channels per block a multiple of 32, its output
+ * channels per block 16, 32 or 64, and blocks with the same output channel list
+ * forming groups that share no channel (fprop: output lists, bprop: input lists) — or
+ * "direct" otherwise. */
+BSMM_API bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, const char** name);
 /* O = fprop(F, I). */
 BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N,
                                      bsmm_dtype dt, void* stream);

@@ -81,3 +81,44 @@ def test_autograd_and_determinism():
     dF2 = conv.updat(I.detach(), dev(P.dO))
     torch.cuda.synchronize()
     assert torch.equal(O, O2) and torch.equal(dF2, F.grad)
+
+
+MFMA_CASES = [
+    # N, C, K, Bc, Bk, nblocks, TRS, DHW, padding
+    (2, 64, 64, 32, 32, 3, (3, 3), (12, 20), "SAME"),   # 3 of 4 cells: channels in no block
+    (3, 96, 64, 32, 16, 10, (3, 3), (9, 33), "SAME"),   # Bk 16, ragged last column tile
+    (2, 128, 128, 64, 64, 3, (3, 1), (7, 16), "VALID"),  # two 32-channel slabs, Bk 64
+    (2, 64, 64, 32, 32, 4, (3, 3), (10, 10), 2),        # explicit padding
+    (4, 32, 32, 32, 32, 1, (7,), (50,), "SAME"),        # 1-D
+    (2, 64, 64, 32, 32, 4, (2, 2), (8, 8), "SAME"),     # even filter: the odd pad after
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=[f"{c[6]}-{c[7]}-{c[8]}-B{c[3]}x{c[4]}" for c in MFMA_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_conv_matrix_core(case, dtype):
+    """The matrix-core path (channel blocks on a grid, stride 1, 16-bit) against the oracle."""
+    N, C, K, Bc, Bk, nb, TRS, DHW, pad = case
+    print(f"case conv mfma {case} {dtype}", flush=True)
+    g = oc.geometry(TRS, DHW, padding=pad)
+    MPQ = g[2][3 - len(DHW):]
+    rng = np.random.default_rng(C + K + nb + len(DHW))
+    P = synth.conv_problem(rng, N, C, K, Bc, Bk, nb, TRS, DHW, MPQ, dtype, contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, padding=pad)
+    tdt = synth.DTYPES[dtype]
+    assert conv.kernel_name("fprop", tdt) == "matrix_core"
+    pads = g[5]
+    want_b = Bk % 32 == 0 and Bc in (16, 32, 64) and pads[1] <= g[0][1] - 1 and pads[2] <= g[0][2] - 1
+    assert conv.kernel_name("bprop", tdt) == ("matrix_core" if want_b else "direct")
+    bck = oc.split_bck(P.BCK)
+    F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    O = conv.fprop(F, I)
+    dI = conv.bprop(F, dO)
+    torch.cuda.synchronize()
+    Cn, Kn = conv.C, conv.K
+    Fr, Ir, dOr = _f64(P.F), _f64(P.I), _f64(P.dO)
+    assert_close(O, oc.fprop(bck, Fr, Ir, Kn, g).reshape(O.shape), dtype, "conv fprop (matrix cores)")
+    assert_close(dI, oc.bprop(bck, Fr, dOr, Cn, g).reshape(dI.shape), dtype, "conv bprop")
+    O2 = conv.fprop(F, I)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
