@@ -1134,7 +1134,8 @@ bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, c
     if (!h || !name || pass < 0 || pass > 2) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     ConvArgs x = conv_args(h, dt);
-    *name = pass < 2 && h->gok[pass] && conv_mfma_plan(x, pass) ? "matrix_core" : "direct";
+    const bool mc = pass < 2 ? h->gok[pass] && conv_mfma_plan(x, pass) : conv_mfma_updat_ok(x);
+    *name = mc ? "matrix_core" : "direct";
     return BSMM_OK;
 }
 

@@ -307,6 +307,146 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
     }
 }
 
+// Filter gradient on the matrix cores (2-D / 1-D, stride 1, dilation 1, 16-bit; Bc and
+// Bk multiples of 16, at most 64): one workgroup per (block, filter tap) owns
+// dF[b, :, tap, :] and contracts over every (image, output position) in steps of 128
+// positions, taken in the flattened (row, column) order of the output image:
+// dF[b, i, tap, j] = sum over positions of I[n, C_b[i], y + r - ph, x + s - pw] *
+// dO[n, K_b[j], y, x].  Each step stages the block's shifted input values (zero outside
+// the image or past the last position) and its output-gradient values in LDS as
+// [channel][128 positions]; a lane's operand is then 8 consecutive positions of one
+// channel (one 16-byte LDS read), four 32-deep steps per 16x16 tile.  The next step's
+// values are loaded into registers while the current one computes.  Every output has
+// one writer and a fixed summation order.
+template <int DT>
+__global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
+    constexpr int SP = 128, XP = SP + 8;          // positions per step, LDS row pitch
+    __shared__ __attribute__((aligned(16))) uint16_t smi[2][64 * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t smd[2][64 * XP];
+    const int RS = a.R * a.S;
+    const int b = blockIdx.x / RS, tap = blockIdx.x % RS;
+    const int r = tap / a.S, s = tap % a.S;
+    const int Bc = a.Bc, Bk = a.Bk;
+    const int H = a.H, W = a.W, P = a.P, Q = a.Q;
+    const int64_t PQ = (int64_t)P * Q, HW = (int64_t)H * W;
+    const int64_t nsteps_img = (PQ + SP - 1) / SP, nsteps = a.N * nsteps_img;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const uint16_t* I = (const uint16_t*)a.a;
+    const uint16_t* dO = (const uint16_t*)a.b;
+    // staging work per thread: input values (channel, position) and output-gradient
+    // 8-position pieces; at most 64 x 128 of each
+    const int ni = Bc * SP, nd = Bk * SP / 8;
+    constexpr int MI = 64 * SP / 256, MD = 64 * SP / 8 / 256;   // 32 and 4
+    uint16_t vi[MI];
+    u32x4 vd[MD];
+    const bool dvec = (PQ % 8) == 0;
+    __shared__ int sch[128];   // the block's input channels, then its output channels
+    if (t < Bc) sch[t] = a.cidx[b * Bc + t];
+    if (t < Bk) sch[64 + t] = a.kidx[b * Bk + t];
+    __syncthreads();
+    auto load = [&](int64_t st) {
+        const int64_t n = st / nsteps_img;
+        const int p0 = (int)(st % nsteps_img) * SP;
+#pragma unroll
+        for (int u = 0; u < MI; u++) {
+            const int q = t + 256 * u;
+            uint16_t v = 0;
+            if (q < ni && st < nsteps) {
+                const int c = q / SP, p = p0 + q % SP;
+                if (p < PQ) {
+                    const int y = p / Q + r - a.pad[1], x = p % Q + s - a.pad[2];
+                    if (y >= 0 && y < H && x >= 0 && x < W)
+                        v = I[(n * a.C + sch[c]) * HW + (int64_t)y * W + x];
+                }
+            }
+            vi[u] = v;
+        }
+#pragma unroll
+        for (int u = 0; u < MD; u++) {
+            const int q = t + 256 * u;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (q < nd && st < nsteps) {
+                const int k = q / (SP / 8), pc = q % (SP / 8);
+                const int p = p0 + 8 * pc;
+                const uint16_t* row = dO + (n * a.K + sch[64 + k]) * PQ;
+                if (dvec && p + 8 <= PQ) {
+                    v = *reinterpret_cast<const u32x4*>(row + p);
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) h[e] = p + e < PQ ? row[p + e] : 0u;
+                    v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                }
+            }
+            vd[u] = v;
+        }
+    };
+    auto stage = [&](int buf) {
+        BSMM_LDS uint16_t* li = (BSMM_LDS uint16_t*)smi[buf];
+        BSMM_LDS uint16_t* ld = (BSMM_LDS uint16_t*)smd[buf];
+#pragma unroll
+        for (int u = 0; u < MI; u++) {
+            const int q = t + 256 * u;
+            if (q < ni) li[(q / SP) * XP + q % SP] = vi[u];
+        }
+#pragma unroll
+        for (int u = 0; u < MD; u++) {
+            const int q = t + 256 * u;
+            if (q < nd) *reinterpret_cast<BSMM_LDS u32x4*>(ld + (q / (SP / 8)) * XP + 8 * (q % (SP / 8))) = vd[u];
+        }
+    };
+    // wave w: tiles (it, jt) = w, w+4, ... of the (Bc/16) x (Bk/16) grid
+    const int ti = Bc / 16, tj = Bk / 16, ntile = ti * tj;
+    f32x4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0);
+    for (int64_t st = 0; st < nsteps; st++) {
+        const int buf = (int)(st & 1);
+        stage(buf);
+        __syncthreads();
+        load(st + 1);   // in flight during this step's products
+        const BSMM_LDS uint16_t* li = (const BSMM_LDS uint16_t*)smi[buf];
+        const BSMM_LDS uint16_t* ld = (const BSMM_LDS uint16_t*)smd[buf];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int tile = wave + 4 * u;
+            if (tile < ntile) {   // wave-uniform
+                const int it = tile / tj, jt = tile % tj;
+#pragma unroll
+                for (int kk = 0; kk < SP / 32; kk++) {
+                    const u32x4 fa = *reinterpret_cast<const BSMM_LDS u32x4*>(li + (it * 16 + m16) * XP + kk * 32 + 8 * g4);
+                    const u32x4 fb = *reinterpret_cast<const BSMM_LDS u32x4*>(ld + (jt * 16 + m16) * XP + kk * 32 + 8 * g4);
+                    mma<DT>(acc[u], fb, fa);   // D[j][i]: lane holds j = 4*g4 + v, i = m16
+                }
+            }
+        }
+        // the other buffer is rewritten next step: no barrier needed here, the barrier
+        // after the next stage orders it (two buffers)
+    }
+    const int RSn = RS;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int tile = wave + 4 * u;
+        if (tile >= ntile) continue;
+        const int it = tile / tj, jt = tile % tj;
+        const int i = it * 16 + m16;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int j = jt * 16 + 4 * g4 + v;
+            ((float*)a.out)[(((int64_t)b * Bc + i) * RSn + tap) * Bk + j] = acc[u][v];
+        }
+    }
+}
+
+bool conv_mfma_updat_ok(const ConvArgs& a) {
+    if (a.dt == BSMM_F32 || a.T != 1 || a.D != 1) return false;
+    for (int i = 0; i < 3; i++)
+        if (a.st[i] != 1 || a.dl[i] != 1) return false;
+    return a.Bc % 16 == 0 && a.Bk % 16 == 0 && a.Bc <= 64 && a.Bk <= 64;
+}
+
 // Output channels that no block writes: zero.
 template <int DT>
 __global__ __launch_bounds__(256) void conv_zero_kernel(ConvArgs a, int64_t Cout, int64_t HWo) {
@@ -377,6 +517,12 @@ static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
     if constexpr (DT != BSMM_F32) {
         if (a.mfma && pass == 0) return launch_conv_mfma<DT, false>(a, st);
         if (a.mfma && pass == 1) return launch_conv_mfma<DT, true>(a, st);
+    }
+    if (pass == 2 && DT != BSMM_F32 && conv_mfma_updat_ok(a)) {
+        const int64_t wgs = (int64_t)a.nb * a.R * a.S;
+        if (wgs == 0) return hipSuccess;
+        if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
+        return launch(BSMM_PASS_CONV_UPDAT, conv_mfma_updat_kernel<DT>, dim3((unsigned)wgs), dim3(256), st, a);
     }
     if (pass == 2) {
         const int64_t rows = (int64_t)a.nb * a.Bc * a.T * a.R * a.S;

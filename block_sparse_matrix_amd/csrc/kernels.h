@@ -192,6 +192,9 @@ hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 
 // LDS layout of the matrix-core conv kernel: fills a.TH, a.cpitch, a.lds_bytes; false
 // when the shape does not fit it (the direct kernels run instead).
 bool conv_mfma_plan(ConvArgs& a, int pass);
+// The filter gradient's matrix-core kernel applies (2-D / 1-D, stride 1, dilation 1,
+// 16-bit, Bc and Bk multiples of 16 up to 64); no grouping needed.
+bool conv_mfma_updat_ok(const ConvArgs& a);
 
 // Kernel timing hook (api.hip): when profiling is active on this thread, hands out a
 // pair of HIP events to record around the next launch of `pass`; else sets both NULL.

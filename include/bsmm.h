@@ -371,11 +371,12 @@ BSMM_API void bsmm_conv_destroy(bsmm_conv_handle h);
 /* Output image size (M, P, Q) and the leading pads of each dim. */
 BSMM_API bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[3]);
 /* Which kernel family a conv pass (0 fprop, 1 bprop, 2 updat) launches for dtype dt
- * (host only): "matrix_core" — 2-D or 1-D images, stride and dilation 1, 16-bit
- * storage, the pass's contraction channels per block a multiple of 32, its output
- * channels per block 16, 32 or 64, and blocks with the same output channel list
- * forming groups that share no channel (fprop: output lists, bprop: input lists) — or
- * "direct" otherwise. */
+ * (host only): "matrix_core" or "direct".  All matrix-core kernels need 2-D or 1-D
+ * images, stride and dilation 1 and 16-bit storage.  fprop / bprop also need the pass's
+ * contraction channels per block (Bc / Bk) a multiple of 32, its output channels per
+ * block (Bk / Bc) 16, 32 or 64, blocks with the same output channel list forming groups
+ * that share no channel, and (bprop) pads below the filter size; updat needs Bc and Bk
+ * multiples of 16 up to 64. */
 BSMM_API bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, const char** name);
 /* O = fprop(F, I). */
 BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N,

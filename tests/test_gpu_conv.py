@@ -112,13 +112,19 @@ def test_conv_matrix_core(case, dtype):
     assert conv.kernel_name("bprop", tdt) == ("matrix_core" if want_b else "direct")
     bck = oc.split_bck(P.BCK)
     F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    assert conv.kernel_name("updat", tdt) == ("matrix_core" if Bc % 16 == 0 and Bk % 16 == 0 else "direct")
     O = conv.fprop(F, I)
     dI = conv.bprop(F, dO)
+    dF = conv.updat(I, dO)
     torch.cuda.synchronize()
     Cn, Kn = conv.C, conv.K
     Fr, Ir, dOr = _f64(P.F), _f64(P.I), _f64(P.dO)
     assert_close(O, oc.fprop(bck, Fr, Ir, Kn, g).reshape(O.shape), dtype, "conv fprop (matrix cores)")
     assert_close(dI, oc.bprop(bck, Fr, dOr, Cn, g).reshape(dI.shape), dtype, "conv bprop")
+    assert_close(dF, oc.updat(bck, Ir, dOr, g).reshape(dF.shape), dtype, "conv updat")
+    dF2 = conv.updat(I, dO)
+    torch.cuda.synchronize()
+    assert torch.equal(dF, dF2)
     O2 = conv.fprop(F, I)
     torch.cuda.synchronize()
     assert torch.equal(O, O2)
