@@ -308,19 +308,21 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
 }
 
 // Filter gradient on the matrix cores (2-D / 1-D, stride 1, dilation 1, 16-bit; Bc and
-// Bk multiples of 16, at most 64): one workgroup per (block, filter tap) owns
-// dF[b, :, tap, :] and contracts over every (image, output position) in steps of 128
+// Bk multiples of 16, at most 64): one workgroup (8 waves) per (block, filter tap) owns
+// dF[b, :, tap, :] and contracts over every (image, output position) in steps of 256
 // positions, taken in the flattened (row, column) order of the output image:
 // dF[b, i, tap, j] = sum over positions of I[n, C_b[i], y + r - ph, x + s - pw] *
 // dO[n, K_b[j], y, x].  Each step stages the block's shifted input values (zero outside
 // the image or past the last position) and its output-gradient values in LDS as
 // [channel][128 positions]; a lane's operand is then 8 consecutive positions of one
-// channel (one 16-byte LDS read), four 32-deep steps per 16x16 tile.  The next step's
+// channel (one 16-byte LDS read), eight 32-deep steps per 16x16 tile, wave w taking
+// tiles w and w + 8.  The next step's
 // values are loaded into registers while the current one computes.  Every output has
 // one writer and a fixed summation order.
 template <int DT>
-__global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
-    constexpr int SP = 128, XP = SP + 8;          // positions per step, LDS row pitch
+__global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
+    constexpr int SP = 256, XP = SP + 8;          // positions per step, LDS row pitch
+    constexpr int NTH = 512;
     __shared__ __attribute__((aligned(16))) uint16_t smi[2][64 * XP];
     __shared__ __attribute__((aligned(16))) uint16_t smd[2][64 * XP];
     const int RS = a.R * a.S;
@@ -336,8 +338,8 @@ __global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
     const uint16_t* dO = (const uint16_t*)a.b;
     // staging work per thread: input values (channel, position) and output-gradient
     // 8-position pieces; at most 64 x 128 of each
-    const int ni = Bc * SP, nd = Bk * SP / 8;
-    constexpr int MI = 64 * SP / 256, MD = 64 * SP / 8 / 256;   // 32 and 4
+    const int nd = Bk * SP / 8;
+    constexpr int MI = 64 * SP / NTH, MD = 64 * SP / 8 / NTH;   // 32 and 4
     uint16_t vi[MI];
     u32x4 vd[MD];
     const bool dvec = (PQ % 8) == 0;
@@ -345,26 +347,23 @@ __global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
     if (t < Bc) sch[t] = a.cidx[b * Bc + t];
     if (t < Bk) sch[64 + t] = a.kidx[b * Bk + t];
     __syncthreads();
+    // a thread stages one position of the step (t % SP) for channels t / SP + (NTH/SP)*u
+    const int tpp = t % SP, tc = t / SP;
     auto load = [&](int64_t st) {
         const int64_t n = st / nsteps_img;
         const int p0 = (int)(st % nsteps_img) * SP;
+        const int p = p0 + tpp;
+        const int y = p / Q + r - a.pad[1], x = p % Q + s - a.pad[2];
+        const bool ok = st < nsteps && p < PQ && y >= 0 && y < H && x >= 0 && x < W;
+        const uint16_t* base = I + n * a.C * HW + (ok ? (int64_t)y * W + x : 0);
 #pragma unroll
         for (int u = 0; u < MI; u++) {
-            const int q = t + 256 * u;
-            uint16_t v = 0;
-            if (q < ni && st < nsteps) {
-                const int c = q / SP, p = p0 + q % SP;
-                if (p < PQ) {
-                    const int y = p / Q + r - a.pad[1], x = p % Q + s - a.pad[2];
-                    if (y >= 0 && y < H && x >= 0 && x < W)
-                        v = I[(n * a.C + sch[c]) * HW + (int64_t)y * W + x];
-                }
-            }
-            vi[u] = v;
+            const int c = tc + (NTH / SP) * u;
+            vi[u] = ok && c < Bc ? base[(int64_t)sch[c] * HW] : (uint16_t)0;
         }
 #pragma unroll
         for (int u = 0; u < MD; u++) {
-            const int q = t + 256 * u;
+            const int q = t + NTH * u;
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (q < nd && st < nsteps) {
                 const int k = q / (SP / 8), pc = q % (SP / 8);
@@ -387,20 +386,20 @@ __global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
         BSMM_LDS uint16_t* ld = (BSMM_LDS uint16_t*)smd[buf];
 #pragma unroll
         for (int u = 0; u < MI; u++) {
-            const int q = t + 256 * u;
-            if (q < ni) li[(q / SP) * XP + q % SP] = vi[u];
+            const int c = tc + (NTH / SP) * u;
+            if (c < Bc) li[c * XP + tpp] = vi[u];
         }
 #pragma unroll
         for (int u = 0; u < MD; u++) {
-            const int q = t + 256 * u;
+            const int q = t + NTH * u;
             if (q < nd) *reinterpret_cast<BSMM_LDS u32x4*>(ld + (q / (SP / 8)) * XP + 8 * (q % (SP / 8))) = vd[u];
         }
     };
-    // wave w: tiles (it, jt) = w, w+4, ... of the (Bc/16) x (Bk/16) grid
+    // wave w: tiles (it, jt) = w, w+8 of the (Bc/16) x (Bk/16) grid
     const int ti = Bc / 16, tj = Bk / 16, ntile = ti * tj;
-    f32x4 acc[4];
+    f32x4 acc[2];
 #pragma unroll
-    for (int u = 0; u < 4; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     load(0);
     for (int64_t st = 0; st < nsteps; st++) {
         const int buf = (int)(st & 1);
@@ -410,8 +409,8 @@ __global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
         const BSMM_LDS uint16_t* li = (const BSMM_LDS uint16_t*)smi[buf];
         const BSMM_LDS uint16_t* ld = (const BSMM_LDS uint16_t*)smd[buf];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int tile = wave + 4 * u;
+        for (int u = 0; u < 2; u++) {
+            const int tile = wave + 8 * u;
             if (tile < ntile) {   // wave-uniform
                 const int it = tile / tj, jt = tile % tj;
 #pragma unroll
@@ -427,8 +426,8 @@ __global__ __launch_bounds__(256) void conv_mfma_updat_kernel(ConvArgs a) {
     }
     const int RSn = RS;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int tile = wave + 4 * u;
+    for (int u = 0; u < 2; u++) {
+        const int tile = wave + 8 * u;
         if (tile >= ntile) continue;
         const int it = tile / tj, jt = tile % tj;
         const int i = it * 16 + m16;
@@ -522,7 +521,7 @@ static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
         const int64_t wgs = (int64_t)a.nb * a.R * a.S;
         if (wgs == 0) return hipSuccess;
         if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
-        return launch(BSMM_PASS_CONV_UPDAT, conv_mfma_updat_kernel<DT>, dim3((unsigned)wgs), dim3(256), st, a);
+        return launch(BSMM_PASS_CONV_UPDAT, conv_mfma_updat_kernel<DT>, dim3((unsigned)wgs), dim3(512), st, a);
     }
     if (pass == 2) {
         const int64_t rows = (int64_t)a.nb * a.Bc * a.T * a.R * a.S;
