@@ -960,6 +960,11 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
     size_t off[kConvParts];
     if ((s = conv_device(h, &d, off)) != BSMM_OK) return s;
     ConvArgs x = conv_args(h, dt);
+    {
+        const uint64_t es = dt == BSMM_F32 ? 4 : 2;
+        const uint64_t ab = (uint64_t)N * es * (pass == 1 ? (uint64_t)h->K * sp_out : (uint64_t)h->C * sp_in);
+        x.a_bytes = ab <= kMaxTensorBytes ? (uint32_t)ab : 0u;
+    }
     x.a = a;
     x.b = b;
     x.out = out;
@@ -1134,6 +1139,7 @@ bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, c
     if (!h || !name || pass < 0 || pass > 2) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     ConvArgs x = conv_args(h, dt);
+    x.a_bytes = 1;   // the choice assuming the pass's input is below 2 GiB
     const bool mc = pass < 2 ? h->gok[pass] && conv_mfma_plan(x, pass) : conv_mfma_updat_ok(x);
     *name = mc ? "matrix_core" : "direct";
     return BSMM_OK;

@@ -201,6 +201,7 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
     const int TH = a.TH, ROWS = TH + R - 1, CP = a.cpitch;
     BSMM_LDS uint16_t* xs = (BSMM_LDS uint16_t*)dsm;              // [s][32 channels][CP]
     BSMM_LDS uint16_t* fs = xs + S * 32 * CP;                       // [tap][CO][40]
+    __shared__ int chs[32];                                         // the slab's input channels
 
     const int nyt = (Ho + TH - 1) / TH;
     const int yt = blockIdx.x % nyt;
@@ -219,26 +220,37 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
         for (int o = 0; o < OT; o++) acc[u][o] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int gb = a.gptr[g], ge = a.gptr[g + 1];
+    const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
     for (int e = gb; e < ge; e++) {
         const int b = a.gblk[e];
         for (int slab = 0; slab < CI / 32; slab++) {
             __syncthreads();   // the previous slab's LDS is no longer read
+            if (t < 32) chs[t] = in_idx[b * CI + slab * 32 + t];
+            __syncthreads();
             // input rows: a thread copies whole staged rows (channel c, row rr); each source
-            // element is read once and written to every shift s it serves
+            // element is read once and written to every shift s it serves.  Buffer loads:
+            // positions outside the image get an out-of-range offset and read as zero, so
+            // every load is issued unconditionally, 8 at a time.
             const int XW = COLS + S - 1;
             for (int q = t; q < 32 * ROWS; q += 256) {
                 const int rr = q % ROWS, c = q / ROWS;
                 const int y = y0 + rr - ph;
-                const int ch = in_idx[b * CI + slab * 32 + c];
                 const bool yok = y >= 0 && y < Hi;
-                const uint16_t* src = (const uint16_t*)a.a + ((n * Cin + ch) * Hi + (yok ? y : 0)) * Wi;
+                const uint32_t row = yok ? (uint32_t)(((n * Cin + chs[c]) * Hi + y) * Wi) * 2u : 0u;
                 BSMM_LDS uint16_t* dst = xs + c * CP + rr * COLS;
-                for (int xs_ = 0; xs_ < XW; xs_++) {
-                    const int x = xs_ - pw;
-                    const uint16_t v = yok && x >= 0 && x < Wi ? src[x] : (uint16_t)0;
-                    for (int s = 0; s < S; s++) {
-                        const int col = xs_ - s;
-                        if (col >= 0 && col < COLS) dst[s * 32 * CP + col] = v;
+                for (int x0 = 0; x0 < XW; x0 += 8) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (int h = 0; h < 8; h++) {
+                        const int x = x0 + h - pw;
+                        v[h] = bload16(rin, yok && x >= 0 && x < Wi ? row + 2u * x : kOffLane, 0);
+                    }
+#pragma unroll
+                    for (int h = 0; h < 8; h++) {
+                        for (int s = 0; s < S; s++) {
+                            const int col = x0 + h - s;
+                            if (col >= 0 && col < COLS) dst[s * 32 * CP + col] = (uint16_t)v[h];
+                        }
                     }
                 }
             }
@@ -255,9 +267,10 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
                     *reinterpret_cast<BSMM_LDS u32x4*>(fs + (tap * CO + o) * 40 + part * 8) = v;
                 }
             } else {
-                // stored F[b, i = slab*32 + ci, tap, j = o]: CO consecutive o per (ci, tap)
+                // stored F[b, i = slab*32 + ci, tap, j = o]: CO consecutive o per (ci, tap);
+                // adjacent lanes take adjacent ci, so their LDS writes are consecutive
                 for (int q = t; q < 32 * RS * (CO / 8); q += 256) {
-                    const int part = q % (CO / 8), tap = (q / (CO / 8)) % RS, ci = q / ((CO / 8) * RS);
+                    const int ci = q % 32, part = (q / 32) % (CO / 8), tap = q / (32 * (CO / 8));
                     const u32x4 v = *reinterpret_cast<const u32x4*>(
                         (const uint16_t*)a.b + (((int64_t)b * a.Bc + slab * 32 + ci) * RS + tap) * a.Bk + part * 8);
                     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
     const int64_t nsteps_img = (PQ + SP - 1) / SP, nsteps = a.N * nsteps_img;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m16 = lane & 15, g4 = lane >> 4;
-    const uint16_t* I = (const uint16_t*)a.a;
+    const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
     const uint16_t* dO = (const uint16_t*)a.b;
     // staging work per thread: input values (channel, position) and output-gradient
     // 8-position pieces; at most 64 x 128 of each
@@ -355,11 +368,11 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
         const int p = p0 + tpp;
         const int y = p / Q + r - a.pad[1], x = p % Q + s - a.pad[2];
         const bool ok = st < nsteps && p < PQ && y >= 0 && y < H && x >= 0 && x < W;
-        const uint16_t* base = I + n * a.C * HW + (ok ? (int64_t)y * W + x : 0);
+        const uint32_t base = ok ? (uint32_t)(n * a.C * HW + (int64_t)y * W + x) * 2u : 0u;
 #pragma unroll
-        for (int u = 0; u < MI; u++) {
+        for (int u = 0; u < MI; u++) {   // unconditional buffer loads; misses read zero
             const int c = tc + (NTH / SP) * u;
-            vi[u] = ok && c < Bc ? base[(int64_t)sch[c] * HW] : (uint16_t)0;
+            vi[u] = (uint16_t)bload16(rin, ok && c < Bc ? base + (uint32_t)(sch[c] * HW) * 2u : kOffLane, 0);
         }
 #pragma unroll
         for (int u = 0; u < MD; u++) {
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
 }
 
 bool conv_mfma_updat_ok(const ConvArgs& a) {
-    if (a.dt == BSMM_F32 || a.T != 1 || a.D != 1) return false;
+    if (a.dt == BSMM_F32 || a.T != 1 || a.D != 1 || a.a_bytes == 0) return false;
     for (int i = 0; i < 3; i++)
         if (a.st[i] != 1 || a.dl[i] != 1) return false;
     return a.Bc % 16 == 0 && a.Bk % 16 == 0 && a.Bc <= 64 && a.Bk <= 64;
@@ -457,7 +470,7 @@ __global__ __launch_bounds__(256) void conv_zero_kernel(ConvArgs a, int64_t Cout
 }
 
 bool conv_mfma_plan(ConvArgs& a, int pass) {
-    if (pass > 1 || a.dt == BSMM_F32 || a.T != 1 || a.D != 1) return false;
+    if (pass > 1 || a.dt == BSMM_F32 || a.T != 1 || a.D != 1 || a.a_bytes == 0) return false;
     for (int i = 0; i < 3; i++)
         if (a.st[i] != 1 || a.dl[i] != 1) return false;
     const int CI = pass == 1 ? a.Bk : a.Bc, CO = pass == 1 ? a.Bc : a.Bk;

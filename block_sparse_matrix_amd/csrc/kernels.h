@@ -187,6 +187,7 @@ struct ConvArgs {
     int TH;               // output rows per workgroup
     int cpitch;           // LDS elements per staged channel
     int lds_bytes;
+    uint32_t a_bytes;     // size of `a` in bytes when below 2^31 (32-bit buffer offsets), else 0
 };
 hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 fprop, 1 bprop, 2 updat
 // LDS layout of the matrix-core conv kernel: fills a.TH, a.cpitch, a.lds_bytes; false

@@ -376,7 +376,8 @@ BSMM_API bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int6
  * contraction channels per block (Bc / Bk) a multiple of 32, its output channels per
  * block (Bk / Bc) 16, 32 or 64, blocks with the same output channel list forming groups
  * that share no channel, and (bprop) pads below the filter size; updat needs Bc and Bk
- * multiples of 16 up to 64. */
+ * multiples of 16 up to 64.  A call whose input activation exceeds 2 GiB takes the
+ * direct kernels (the matrix-core kernels address it with 32-bit offsets). */
 BSMM_API bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, const char** name);
 /* O = fprop(F, I). */
 BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N,
