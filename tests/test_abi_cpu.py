@@ -149,6 +149,7 @@ def test_kernel_choice_names():
     m32 = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
     m8 = bs.BlocksparseMatMul(L, block_size=8, feature_axis=0)
     assert m32.kernel_name("fprop", 64, torch.bfloat16) == "list_n64"
+    assert m32.kernel_name("fprop", 64, torch.float32) == "list_n64_8waves"
     assert m32.kernel_name("fprop", 4096, torch.bfloat16) == "output_groups"
     assert m32.kernel_name("bprop", 4096, torch.float16) == "output_groups"
     assert m32.kernel_name("fprop", 4096, torch.float32) == "list_weight_stack"
