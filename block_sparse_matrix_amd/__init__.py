@@ -90,7 +90,8 @@ def lib():
         "bsmm_conv_kernel_name": [vp, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
         "bsmm_conv_fprop": [vp, vp, vp, vp, i64, i32, vp],
         "bsmm_conv_bprop": [vp, vp, vp, vp, i64, i32, vp],
-        "bsmm_conv_updat": [vp, vp, vp, vp, i64, i32, vp],
+        "bsmm_conv_updat": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
+        "bsmm_conv_workspace_size": [vp, i64, i32, ctypes.POINTER(sz)],
         "bsmm_proj_info": [vp, P64, P64],
         "bsmm_proj_lut": [vp, vp, i64],
         "bsmm_proj_gather": [vp, vp, vp, i64, i32, i32, vp],
@@ -753,10 +754,14 @@ def bsmm_conv_bprop(h, F: torch.Tensor, dO: torch.Tensor, dI: torch.Tensor, N: i
 
 
 def bsmm_conv_updat(h, I: torch.Tensor, dO: torch.Tensor, dF: torch.Tensor, N: int) -> None:
+    """dF = the filter gradient; allocates the contraction-split workspace the library asks for."""
     if I.dtype != dO.dtype or dF.dtype != torch.float32:
         raise ValueError("I and dO must share a dtype; dF is float32")
+    nb = ctypes.c_size_t()
+    _check(lib().bsmm_conv_workspace_size(h, N, DTYPE_CODE[I.dtype], ctypes.byref(nb)), "bsmm_conv_workspace_size")
+    ws = torch.empty(nb.value, dtype=torch.uint8, device=I.device) if nb.value else None
     _check(lib().bsmm_conv_updat(h, _dev_ptr(I, "I"), _dev_ptr(dO, "dO"), _dev_ptr(dF, "dF"), N,
-                                 DTYPE_CODE[I.dtype], _stream(I)), "bsmm_conv_updat")
+                                 DTYPE_CODE[I.dtype], _dev_ptr(ws, "ws"), nb.value, _stream(I)), "bsmm_conv_updat")
 
 
 class _ConvFn(torch.autograd.Function):

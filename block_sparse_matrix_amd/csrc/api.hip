@@ -939,8 +939,20 @@ ConvArgs conv_args(const bsmm_conv_plan* h, int dt) {
     return x;
 }
 
+// Workspace bytes of the filter gradient's contraction split for N images (0: none).
+size_t conv_ws_bytes(const bsmm_conv_plan* h, int64_t N, int dt) {
+    if (N <= 0 || h->nb == 0) return 0;
+    ConvArgs x = conv_args(h, dt);
+    x.N = N;
+    x.a_bytes = 1;
+    if (!conv_mfma_updat_ok(x)) return 0;
+    const int p = conv_updat_parts(x);
+    if (p <= 1) return 0;
+    return (size_t)p * h->nb * h->Bc * h->TRS[0] * h->TRS[1] * h->TRS[2] * h->Bk * sizeof(float);
+}
+
 bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b, void* out, int64_t N,
-                      bsmm_dtype dt, void* stream) {
+                      bsmm_dtype dt, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
     if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
     if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
@@ -973,6 +985,14 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
     x.lptr = pass == 0 ? d + off[2] : d + off[4];
     x.lent = pass == 0 ? d + off[3] : d + off[5];
     x.N = N;
+    x.nparts = 1;
+    if (pass == 2) {   // split the matrix-core filter gradient when the workspace allows it
+        const size_t need = conv_ws_bytes(h, N, dt);
+        if (need > 0 && ws && ws_bytes >= need && aligned16(ws)) {
+            x.nparts = conv_updat_parts(x);
+            x.ws = (float*)ws;
+        }
+    }
     if (pass < 2 && h->gok[pass] && conv_mfma_plan(x, pass)) {
         x.mfma = 1;
         x.gptr = d + off[pass == 0 ? 6 : 9];
@@ -1155,9 +1175,16 @@ bsmm_status bsmm_conv_bprop(bsmm_conv_handle h, const void* F, const void* dO, v
     return conv_call(h, 1, dO, F, dI, N, dt, stream);
 }
 
+bsmm_status bsmm_conv_workspace_size(bsmm_conv_handle h, int64_t N, bsmm_dtype dt, size_t* bytes) {
+    if (!h || !bytes || N < 0) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
+    if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
+    *bytes = conv_ws_bytes(h, N, dt);
+    return BSMM_OK;
+}
+
 bsmm_status bsmm_conv_updat(bsmm_conv_handle h, const void* I, const void* dO, float* dF, int64_t N, bsmm_dtype dt,
-                            void* stream) {
-    return conv_call(h, 2, I, dO, dF, N, dt, stream);
+                            void* ws, size_t ws_bytes, void* stream) {
+    return conv_call(h, 2, I, dO, dF, N, dt, stream, ws, ws_bytes);
 }
 
 }  // extern "C"

@@ -336,15 +336,19 @@ template <int DT>
 __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
     constexpr int SP = 256, XP = SP + 8;          // positions per step, LDS row pitch
     constexpr int NTH = 512;
-    __shared__ __attribute__((aligned(16))) uint16_t smi[2][64 * XP];
-    __shared__ __attribute__((aligned(16))) uint16_t smd[2][64 * XP];
+    // LDS sized to the block (conv_updat_lds_bytes): two buffers of the input values
+    // [Bc][XP], then two of the output-gradient values [Bk][XP]
+    extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
     const int RS = a.R * a.S;
-    const int b = blockIdx.x / RS, tap = blockIdx.x % RS;
+    const int part = blockIdx.x % a.nparts, bt = blockIdx.x / a.nparts;
+    const int b = bt / RS, tap = bt % RS;
     const int r = tap / a.S, s = tap % a.S;
     const int Bc = a.Bc, Bk = a.Bk;
     const int H = a.H, W = a.W, P = a.P, Q = a.Q;
     const int64_t PQ = (int64_t)P * Q, HW = (int64_t)H * W;
     const int64_t nsteps_img = (PQ + SP - 1) / SP, nsteps = a.N * nsteps_img;
+    // this workgroup's share of the contraction steps
+    const int64_t st0 = nsteps * part / a.nparts, st1 = nsteps * (part + 1) / a.nparts;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m16 = lane & 15, g4 = lane >> 4;
     const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
@@ -394,9 +398,11 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
             vd[u] = v;
         }
     };
+    BSMM_LDS uint16_t* smi = (BSMM_LDS uint16_t*)dsm;
+    BSMM_LDS uint16_t* smd = smi + 2 * Bc * XP;
     auto stage = [&](int buf) {
-        BSMM_LDS uint16_t* li = (BSMM_LDS uint16_t*)smi[buf];
-        BSMM_LDS uint16_t* ld = (BSMM_LDS uint16_t*)smd[buf];
+        BSMM_LDS uint16_t* li = smi + buf * Bc * XP;
+        BSMM_LDS uint16_t* ld = smd + buf * Bk * XP;
 #pragma unroll
         for (int u = 0; u < MI; u++) {
             const int c = tc + (NTH / SP) * u;
@@ -413,14 +419,14 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
     f32x4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load(0);
-    for (int64_t st = 0; st < nsteps; st++) {
-        const int buf = (int)(st & 1);
+    load(st0);
+    for (int64_t st = st0; st < st1; st++) {
+        const int buf = (int)((st - st0) & 1);
         stage(buf);
         __syncthreads();
         load(st + 1);   // in flight during this step's products
-        const BSMM_LDS uint16_t* li = (const BSMM_LDS uint16_t*)smi[buf];
-        const BSMM_LDS uint16_t* ld = (const BSMM_LDS uint16_t*)smd[buf];
+        const BSMM_LDS uint16_t* li = smi + buf * Bc * XP;
+        const BSMM_LDS uint16_t* ld = smd + buf * Bk * XP;
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int tile = wave + 8 * u;
@@ -447,9 +453,31 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int j = jt * 16 + 4 * g4 + v;
-            ((float*)a.out)[(((int64_t)b * Bc + i) * RSn + tap) * Bk + j] = acc[u][v];
+            const int64_t e = (((int64_t)b * Bc + i) * RSn + tap) * Bk + j;
+            if (a.nparts > 1)
+                a.ws[(int64_t)part * a.nb * Bc * RSn * Bk + e] = acc[u][v];
+            else
+                ((float*)a.out)[e] = acc[u][v];
         }
     }
+}
+
+// Sum of the filter gradient's parts in part order (deterministic).
+__global__ __launch_bounds__(256) void conv_updat_reduce(ConvArgs a, int64_t E) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < E; e += (int64_t)gridDim.x * 256) {
+        float v = 0.f;
+        for (int p = 0; p < a.nparts; p++) v += a.ws[p * E + e];
+        ((float*)a.out)[e] = v;
+    }
+}
+
+int conv_updat_parts(const ConvArgs& a) {
+    const int64_t wgs = (int64_t)a.nb * a.R * a.S;
+    const int64_t steps = a.N * (((int64_t)a.P * a.Q + 255) / 256);
+    int64_t p = wgs > 0 ? (4096 + wgs - 1) / wgs : 1;   // ~16 workgroups per compute unit
+    if (p > 16) p = 16;
+    if (p > steps / 4) p = steps / 4;
+    return p < 1 ? 1 : (int)p;
 }
 
 bool conv_mfma_updat_ok(const ConvArgs& a) {
@@ -531,10 +559,25 @@ static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
         if (a.mfma && pass == 1) return launch_conv_mfma<DT, true>(a, st);
     }
     if (pass == 2 && DT != BSMM_F32 && conv_mfma_updat_ok(a)) {
-        const int64_t wgs = (int64_t)a.nb * a.R * a.S;
+        const int64_t wgs = (int64_t)a.nb * a.R * a.S * a.nparts;
         if (wgs == 0) return hipSuccess;
         if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
-        return launch(BSMM_PASS_CONV_UPDAT, conv_mfma_updat_kernel<DT>, dim3((unsigned)wgs), dim3(512), st, a);
+        const int lds = 2 * (a.Bc + a.Bk) * (256 + 8) * 2;
+        // one timing record spans the partial sums and their reduction
+        void *e0 = nullptr, *e1 = nullptr;
+        prof_events(BSMM_PASS_CONV_UPDAT, &e0, &e1);
+        auto kern = conv_mfma_updat_kernel<DT>;
+        if (e0 || e1)
+            hipExtLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(512), lds, st, (hipEvent_t)e0,
+                                  (hipEvent_t)(a.nparts == 1 ? e1 : nullptr), 0, a);
+        else
+            hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(512), lds, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.nparts == 1) return e;
+        const int64_t E = (int64_t)a.nb * a.Bc * a.R * a.S * a.Bk;
+        int64_t rg = (E + 255) / 256;
+        if (rg > 4096) rg = 4096;
+        return launch_ev(conv_updat_reduce, dim3((unsigned)rg), dim3(256), st, nullptr, e1, a, E);
     }
     if (pass == 2) {
         const int64_t rows = (int64_t)a.nb * a.Bc * a.T * a.R * a.S;

@@ -188,7 +188,14 @@ struct ConvArgs {
     int cpitch;           // LDS elements per staged channel
     int lds_bytes;
     uint32_t a_bytes;     // size of `a` in bytes when below 2^31 (32-bit buffer offsets), else 0
+    // matrix-core filter gradient: contraction split in nparts parts (fp32 partials in
+    // ws, nparts * nblocks*Bc*T*R*S*Bk floats, then their sum in part order); 1: none
+    int nparts;
+    float* ws;
 };
+// Parts of the matrix-core filter gradient's contraction for N images (enough
+// workgroups to fill the chip twice, at least 4 steps of 256 positions each, at most 16).
+int conv_updat_parts(const ConvArgs& a);
 hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 fprop, 1 bprop, 2 updat
 // LDS layout of the matrix-core conv kernel: fills a.TH, a.cpitch, a.lds_bytes; false
 // when the shape does not fit it (the direct kernels run instead).

@@ -385,9 +385,15 @@ BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const vo
 /* dI = bprop(F, dO). */
 BSMM_API bsmm_status bsmm_conv_bprop(bsmm_conv_handle h, const void* F, const void* dO, void* dI, int64_t N,
                                      bsmm_dtype dt, void* stream);
-/* dF = updat(I, dO), float32. */
+/* Device workspace bytes bsmm_conv_updat can use for N images (0: it uses none).  With
+ * it the matrix-core filter gradient splits its contraction over the images into parts
+ * whose fp32 partial sums live in the workspace, then adds them in part order. */
+BSMM_API bsmm_status bsmm_conv_workspace_size(bsmm_conv_handle h, int64_t N, bsmm_dtype dt, size_t* bytes);
+/* dF = updat(I, dO), float32.  ws, ws_bytes: device workspace of at least
+ * bsmm_conv_workspace_size bytes, 16-byte aligned, or NULL / smaller (then unsplit:
+ * correct, slower).  The workspace must not be in use by another call. */
 BSMM_API bsmm_status bsmm_conv_updat(bsmm_conv_handle h, const void* I, const void* dO, float* dF, int64_t N,
-                                     bsmm_dtype dt, void* stream);
+                                     bsmm_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel timing for measurement.  Between bsmm_profile_begin() and bsmm_profile_end()
  * every pass launched from the calling thread records HIP events around its kernels

@@ -43,7 +43,8 @@ def test_call_validation_before_gpu():
     vp = ctypes.c_void_p
     good, odd = vp(0x10000), vp(0x10008)
     INVALID, ALIGN = 1, 3
-    for fn in (L.bsmm_conv_fprop, L.bsmm_conv_bprop, L.bsmm_conv_updat):
+    upd = lambda *a: L.bsmm_conv_updat(*a[:-1], None, 0, a[-1])   # no workspace
+    for fn in (L.bsmm_conv_fprop, L.bsmm_conv_bprop, upd):
         assert fn(h, good, good, good, 2, 7, None) == INVALID
         assert fn(h, good, good, good, -1, 0, None) == INVALID
         assert fn(h, good, good, None, 2, 0, None) == INVALID
@@ -51,5 +52,11 @@ def test_call_validation_before_gpu():
         assert fn(h, good, None, good, 2, 0, None) == INVALID
         assert fn(h, good, odd, good, 2, 1, None) == ALIGN
         assert fn(None, good, good, good, 2, 0, None) == INVALID
+    n = ctypes.c_size_t(7)
+    assert L.bsmm_conv_workspace_size(h, 64, 1, ctypes.byref(n)) == 0 and n.value == 0   # 2-channel blocks: direct
+    c16 = bs.BlocksparseConv([(tuple(range(16)), tuple(range(16)))], (3, 3), (8, 8))
+    assert L.bsmm_conv_workspace_size(c16.handle, 64, 0, ctypes.byref(n)) == 0 and n.value == 0   # fp32: direct
+    assert L.bsmm_conv_workspace_size(c16.handle, 64, 1, ctypes.byref(n)) == 0
+    assert n.value == 16 * 16 * 16 * 9 * 4                      # 16 parts of 16 x 9 x 16 fp32 partials
     assert L.bsmm_conv_fprop(h, None, None, None, 0, 0, None) == 0
     assert L.bsmm_conv_bprop(h, None, None, None, 0, 0, None) == 0

@@ -128,3 +128,29 @@ def test_conv_matrix_core(case, dtype):
     O2 = conv.fprop(F, I)
     torch.cuda.synchronize()
     assert torch.equal(O, O2)
+
+
+def test_conv_filter_gradient_split():
+    """The matrix-core filter gradient with its contraction split over the images (fp32
+    partials in the workspace, summed in part order) and without a workspace (one part),
+    both against the oracle."""
+    import ctypes
+    N, C, B, TRS, DHW = 8, 32, 32, (3, 3), (32, 32)
+    g = oc.geometry(TRS, DHW)
+    rng = np.random.default_rng(77)
+    P = synth.conv_problem(rng, N, C, C, B, B, 1, TRS, DHW, g[2][1:], "bf16", contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW)
+    n = ctypes.c_size_t()
+    assert bs.lib().bsmm_conv_workspace_size(conv.handle, N, 1, ctypes.byref(n)) == 0
+    assert n.value == 8 * B * 9 * B * 4        # 8 parts
+    I, dO = dev(P.I), dev(P.dO)
+    dF = conv.updat(I, dO)
+    dF1 = torch.empty_like(dF)
+    bs.lib().bsmm_conv_updat(conv.handle, ctypes.c_void_p(I.data_ptr()), ctypes.c_void_p(dO.data_ptr()),
+                             ctypes.c_void_p(dF1.data_ptr()), N, 1, None, 0,
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ref = oc.updat(oc.split_bck(P.BCK), _f64(P.I), _f64(P.dO), g).reshape(dF.shape)
+    assert_close(dF, ref, "bf16", "split filter gradient")
+    assert_close(dF1, ref, "bf16", "unsplit filter gradient")
+    assert torch.equal(dF, conv.updat(I, dO))   # deterministic
