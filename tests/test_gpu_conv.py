@@ -154,3 +154,34 @@ def test_conv_filter_gradient_split():
     assert_close(dF, ref, "bf16", "split filter gradient")
     assert_close(dF1, ref, "bf16", "unsplit filter gradient")
     assert torch.equal(dF, conv.updat(I, dO))   # deterministic
+
+
+def test_bench_configuration_sampled_images():
+    """The configuration bench.py times (C = K = 256 in 32x32-channel blocks, 32 of 64,
+    3x3, 32x32 images, N = 32, SAME, bf16, the same seed), on the kernels it launches;
+    fprop / input gradient checked on two images (each image's outputs depend on that
+    image only), the filter gradient (a sum over all images) on three sampled blocks
+    (each block's gradient depends on its own channel lists only)."""
+    N, C, B, TRS, DHW = 32, 256, 32, (3, 3), (32, 32)
+    nb = (C // B) * (C // B) // 2
+    P = synth.conv_problem(np.random.default_rng(23), N, C, C, B, B, nb, TRS, DHW, DHW, "bf16",
+                           contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW)
+    for p in ("fprop", "bprop", "updat"):
+        assert conv.kernel_name(p) == "matrix_core"
+    F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    O = conv.fprop(F, I)
+    dI = conv.bprop(F, dO)
+    dF = conv.updat(I, dO)
+    torch.cuda.synchronize()
+    g = oc.geometry(TRS, DHW)
+    bck = oc.split_bck(P.BCK)
+    Fr = _f64(P.F)
+    for n in (0, N - 1):
+        Irn, dOn = _f64(P.I[n:n + 1]), _f64(P.dO[n:n + 1])
+        assert_close(O[n:n + 1], oc.fprop(bck, Fr, Irn, conv.K, g).reshape(1, conv.K, *DHW), "bf16", "fprop")
+        assert_close(dI[n:n + 1], oc.bprop(bck, Fr, dOn, conv.C, g).reshape(1, conv.C, *DHW), "bf16", "bprop")
+    blocks = [0, nb // 2, nb - 1]
+    sub = (bck[0][blocks], bck[1][blocks])
+    ref = oc.updat(sub, _f64(P.I), _f64(P.dO), g).reshape((len(blocks),) + tuple(dF.shape[1:]))
+    assert_close(dF[blocks], ref, "bf16", "updat")

@@ -116,3 +116,29 @@ def test_autograd(fa):
     proj.scatter_mul(x, s).backward(dzh)
     assert_close(x.grad, sp.scatter_mul(lut, DH, S, fa), "f32", "d scatter_mul / x")
     assert_close(s.grad, sp.gather_mul(lut, DH, X, fa), "f32", "d scatter_mul / y")
+
+
+def test_bench_configuration_full_size():
+    """The configuration bench.py times (nhidden 8192 -> nproj 4096 in blocks of 32 every
+    64 features, N = 4096, bf16, features last, the same seed), every output compared
+    with the oracle: copies bit for bit, add / mul to the dtype gate."""
+    N, H, Pn = 4096, 8192, 4096
+    P = synth.proj_problem(np.random.default_rng(17), N, H, Pn, 1, "bf16", False)
+    proj = bs.SparseProj(H, Pn, 64, 32)
+    lut = proj.gather_lut.astype(np.int64)
+    x, s = dev(P.x), dev(P.s)
+    g = proj.gather(x)
+    sc = proj.scatter(s)
+    za = proj.scatter_add(x, s)
+    zm = proj.scatter_mul(x, s)
+    torch.cuda.synchronize()
+    X, S = _f64(P.x), _f64(P.s)
+    assert _bits_equal(g, X[:, lut], "bf16")
+    ref_sc = np.zeros_like(X)
+    ref_sc[:, lut] = S
+    assert _bits_equal(sc, ref_sc, "bf16")
+    ref_a, ref_m = X.copy(), X.copy()
+    ref_a[:, lut] += S
+    ref_m[:, lut] *= S
+    assert_close(za, ref_a, "bf16", "scatter_add")
+    assert_close(zm, ref_m, "bf16", "scatter_mul")
