@@ -53,3 +53,20 @@ def test_workload(name, dtype):
         np.concatenate([rng.choice(nnz, 30, replace=False), [0, nnz - 1]]))
     rdw = oracle.updat(P.layout, b, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype, ids=ids)
     assert_close(dw[torch.from_numpy(ids).cuda()], rdw, dtype, "updat")
+
+
+def test_accumulate_at_benchmark_size():
+    """The accumulating weight gradient as bench.py times it (hidden 4096, block 32, N = 64,
+    bf16, fp32 dW): dW0 + sum, on sampled block ids against the oracle."""
+    P = synth.workload_problem("hidden4096_b32_n64", "bf16")
+    m = bs.BlocksparseMatMul(P.layout, block_size=32, feature_axis=1)
+    rng = np.random.default_rng(9)
+    dw0 = torch.from_numpy(rng.standard_normal(m.w_shape).astype(np.float32))
+    out = dev(dw0)
+    m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys], out=out, accumulate=True)
+    torch.cuda.synchronize()
+    ids = np.unique(np.concatenate([rng.choice(P.nnz, 30, replace=False), [0, P.nnz - 1]]))
+    bits = synth.to_bits
+    ref = dw0.numpy()[ids].astype(np.float64) + oracle.updat(P.layout, 32, 1, [bits(t) for t in P.xs],
+                                                             [bits(t) for t in P.dys], P.N, "bf16", ids=ids)
+    assert_close(out[torch.from_numpy(ids).cuda()], ref, "bf16", "updat accumulate")
