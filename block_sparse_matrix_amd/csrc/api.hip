@@ -993,7 +993,7 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
             x.ws = (float*)ws;
         }
     }
-    if (pass < 2 && h->gok[pass] && conv_mfma_plan(x, pass)) {
+    if (pass < 2 && h->gok[pass] && h->gptr[pass].size() > 1 && conv_mfma_plan(x, pass)) {
         x.mfma = 1;
         x.gptr = d + off[pass == 0 ? 6 : 9];
         x.gblk = d + off[pass == 0 ? 7 : 10];
@@ -1160,7 +1160,8 @@ bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, c
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     ConvArgs x = conv_args(h, dt);
     x.a_bytes = 1;   // the choice assuming the pass's input is below 2 GiB
-    const bool mc = pass < 2 ? h->gok[pass] && conv_mfma_plan(x, pass) : conv_mfma_updat_ok(x);
+    const bool mc = pass < 2 ? h->gok[pass] && h->gptr[pass].size() > 1 && conv_mfma_plan(x, pass)
+                             : conv_mfma_updat_ok(x);
     *name = mc ? "matrix_core" : "direct";
     return BSMM_OK;
 }

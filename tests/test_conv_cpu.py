@@ -60,3 +60,17 @@ def test_call_validation_before_gpu():
     assert n.value == 16 * 16 * 16 * 9 * 4                      # 16 parts of 16 x 9 x 16 fp32 partials
     assert L.bsmm_conv_fprop(h, None, None, None, 0, 0, None) == 0
     assert L.bsmm_conv_bprop(h, None, None, None, 0, 0, None) == 0
+
+
+def test_plan_without_blocks_takes_the_direct_kernels():
+    """A plan with no block (C API only) writes zero outputs through the direct kernels."""
+    L = bs.lib()
+    h = ctypes.c_void_p()
+    a3 = lambda *v: (ctypes.c_int64 * 3)(*v)
+    assert L.bsmm_conv_create(ctypes.byref(h), 0, 32, 32, None, None, 64, 64, a3(1, 3, 3), a3(1, 8, 8),
+                              a3(1, 1, 1), a3(1, 1, 1), 0, None) == 0
+    name = ctypes.c_char_p()
+    for p in (0, 1, 2):
+        assert L.bsmm_conv_kernel_name(h, p, 1, ctypes.byref(name)) == 0
+        assert name.value == (b"direct" if p < 2 else b"matrix_core")
+    L.bsmm_conv_destroy(h)
