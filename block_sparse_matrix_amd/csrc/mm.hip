@@ -302,7 +302,12 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
         const int mysteps = csteps > wk ? (csteps - wk + WK - 1) / WK : 0;
         Slot<WR, MT> ring[D];
 #pragma unroll
-        for (int i = 0; i < D; i++) load_slot(ring[i], wk + WK * i);
+        for (int i = 0; i < D; i++) {
+            load_slot(ring[i], wk + WK * i);
+            // issue the slots oldest first, as the loop does: the wait at the loop's top
+            // then covers only the slot it consumes, not every load in flight
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // steps past the end compute on zeros; the trip count stays a multiple of D
         for (int j = 0; j < mysteps; j += D) {
 #pragma unroll
