@@ -480,8 +480,8 @@ def run_l2_normalize(P, reps=40):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is described in DESIGN.md, not implemented).", file=sys.stderr)
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the passes are single-device kernels; multi-GPU sharding is not implemented).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
