@@ -168,6 +168,21 @@ __global__ __launch_bounds__(256) void conv_updat_kernel(ConvArgs a) {
     }
 }
 
+// Eight 16-bit values starting D elements past the start of the middle chunk of
+// c[0..11] (three consecutive 8-element chunks), |D| <= 3: whole dwords for even D, a
+// 16-bit funnel of neighbouring dwords for odd D.
+template <int D>
+__device__ __forceinline__ u32x4 conv_shifted(const uint32_t (&c)[12]) {
+    if constexpr ((D & 1) == 0) {
+        constexpr int o = 4 + D / 2;
+        return u32x4{c[o], c[o + 1], c[o + 2], c[o + 3]};
+    } else {
+        constexpr int m = (7 + D) / 2;
+        return u32x4{__builtin_amdgcn_alignbyte(c[m + 1], c[m], 2), __builtin_amdgcn_alignbyte(c[m + 2], c[m + 1], 2),
+                     __builtin_amdgcn_alignbyte(c[m + 3], c[m + 2], 2), __builtin_amdgcn_alignbyte(c[m + 4], c[m + 3], 2)};
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // Matrix-core path: 2-D images, stride 1, dilation 1, 16-bit storage.  A workgroup (4
 // waves) owns one group of blocks that share an output channel list (CO = 16*OT
@@ -227,17 +242,48 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(ConvArgs a) {
             __syncthreads();   // the previous slab's LDS is no longer read
             if (t < 32) chs[t] = in_idx[b * CI + slab * 32 + t];
             __syncthreads();
-            // input rows: a thread copies whole staged rows (channel c, row rr); each source
-            // element is read once and written to every shift s it serves.  Buffer loads:
-            // positions outside the image get an out-of-range offset and read as zero, so
-            // every load is issued unconditionally, 8 at a time.
+            // input rows: a thread copies whole staged rows (channel c, row rr), each source
+            // element read once for every shift s it serves.  Buffer loads: positions
+            // outside the image get an out-of-range offset and read as zero, so every load
+            // is issued unconditionally.
             const int XW = COLS + S - 1;
+            // Rows of a multiple of 8 elements start 16-byte aligned: read them in aligned
+            // 8-element chunks (each wholly inside or outside the row) and write each copy
+            // s as 16-byte chunks, staged columns col .. col+7 holding source columns
+            // col + s - pw ..; shifts of at most 3 either way.
+            const bool vec = Wi % 8 == 0 && pw <= 3 && S - 1 - pw <= 3;
             for (int q = t; q < 32 * ROWS; q += 256) {
                 const int rr = q % ROWS, c = q / ROWS;
                 const int y = y0 + rr - ph;
                 const bool yok = y >= 0 && y < Hi;
                 const uint32_t row = yok ? (uint32_t)(((n * Cin + chs[c]) * Hi + y) * Wi) * 2u : 0u;
                 BSMM_LDS uint16_t* dst = xs + c * CP + rr * COLS;
+                if (vec) {
+                    auto chunk = [&](int x0) {
+                        return bload128(rin, yok && x0 >= 0 && x0 < Wi ? row + 2u * x0 : kOffLane, 0);
+                    };
+                    u32x4 ca = chunk(-8), cb = chunk(0), cc = chunk(8);
+                    for (int col = 0; col < COLS; col += 8) {
+                        const uint32_t w[12] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w, cc.x, cc.y, cc.z, cc.w};
+                        for (int sh = 0; sh < S; sh++) {
+                            u32x4 v;
+                            switch (sh - pw) {
+                            case -3: v = conv_shifted<-3>(w); break;
+                            case -2: v = conv_shifted<-2>(w); break;
+                            case -1: v = conv_shifted<-1>(w); break;
+                            case 0: v = conv_shifted<0>(w); break;
+                            case 1: v = conv_shifted<1>(w); break;
+                            case 2: v = conv_shifted<2>(w); break;
+                            default: v = conv_shifted<3>(w); break;
+                            }
+                            lds_store16(dst + sh * 32 * CP + col, v);
+                        }
+                        ca = cb;
+                        cb = cc;
+                        cc = chunk(col + 16);
+                    }
+                    continue;
+                }
                 for (int x0 = 0; x0 < XW; x0 += 8) {
                     uint32_t v[8];
 #pragma unroll

@@ -91,6 +91,8 @@ MFMA_CASES = [
     (2, 64, 64, 32, 32, 4, (3, 3), (10, 10), 2),        # explicit padding
     (4, 32, 32, 32, 32, 1, (7,), (50,), "SAME"),        # 1-D
     (2, 64, 64, 32, 32, 4, (2, 2), (8, 8), "SAME"),     # even filter: the odd pad after
+    (4, 32, 32, 32, 32, 1, (7,), (48,), "SAME"),        # 1-D, width a multiple of 8: shifts -3 .. 3
+    (2, 64, 64, 32, 32, 3, (1, 5), (8, 24), "SAME"),    # width a multiple of 8: shifts -2 .. 2
 ]
 
 
