@@ -8,19 +8,21 @@ compile and the one-time table upload happen before timing; identity_init is tim
 once on its own and reported beside the step.
 
 Workload (default): hidden 4096, block 32, minibatch 64, a Bernoulli(0.5) 128x128
-block layout (the usage example of the kiteco/blocksparse README), bf16 storage
-with fp32 accumulation, feature_axis 1, seed 1001.  Inputs are seeded synthetic data
-(synth.workload_problem); there is no dataset.
+block layout (the usage example of the kiteco/blocksparse README, whose placeholders
+and weight are float32), float32 storage and arithmetic, feature_axis 1, seed 1001;
+bf16 storage with fp32 accumulation is timed beside it (other_dtypes).  Inputs are
+seeded synthetic data (synth.workload_problem); there is no dataset.
 
-Timing: the step is captured once in a HIP graph that runs it on each of R copies of
-its buffers in turn (at least --rotate-mib MiB in total, so the timed passes read
-HBM rather than the 256 MiB Infinity Cache); after W warm-up steps the graph is
-replayed to run K steps, bracketed by torch.cuda.synchronize(): that is
-ms_per_step and value.  (--overlap runs bprop and updat, the independent halves of
-the backward pass, on two streams joined at the end of each step.)  The same K steps are then launched eagerly with each
-kernel's dispatch timestamps recorded (hipExtLaunchKernelGGL start/stop events via
-bsmm_profile_begin/end, on the launch stream), each pass timed on its own over the
-rotating sets so that every launch starts cold: per-pass kernel durations, the
+Timing: R copies of the step's buffers are made, R chosen so that every pass cycles
+through at least --rotate-mib MiB of its own operands (the timed launches then read
+HBM rather than the 256 MiB Infinity Cache).  After W untimed warm-up steps, exactly
+K steps run from HIP graphs (one captured over min(R, K) buffer sets, replayed, and
+one for the remainder), bracketed by torch.cuda.synchronize(): that is ms_per_step
+and value.  (--overlap runs bprop and updat, the independent halves of the backward
+pass, on two streams joined at the end of each step.)  Then each pass is launched
+eagerly K times on its own over the rotating sets, with each kernel's dispatch
+timestamps recorded (hipExtLaunchKernelGGL start/stop events via
+bsmm_profile_begin/end, on the launch stream): the per-pass kernel durations, the
 roofline fractions, and a "warm" duration on a single buffer set.
 
 Prints one JSON line (rank 0, N = 1).
@@ -43,7 +45,6 @@ HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense, per dtype
 DT_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 PASSES = ("fprop", "bprop", "updat")
-KERNEL_NAME = {"fprop": "mm_kernel (fprop)", "bprop": "mm_kernel (bprop)", "updat": "updat_kernel"}
 
 
 def parse():
@@ -52,8 +53,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="hidden4096_b32_n64")
-    ap.add_argument("--dtype", default=None, help="storage dtype (default: bf16 if the workload has it)")
-    ap.add_argument("--extra-dtypes", default="f32", help="comma list of further dtypes to time (reported aside)")
+    ap.add_argument("--dtype", default=None, help="storage dtype (default: the workload's first, f32 for the "
+                                                  "usage-example workload)")
+    ap.add_argument("--extra-dtypes", default="bf16", help="comma list of further dtypes to time (reported aside)")
     ap.add_argument("--rotate-mib", type=float, default=1024.0)
     ap.add_argument("--overlap", action="store_true",
                     help="run bprop and updat concurrently on two streams in the timed graph "
@@ -162,7 +164,28 @@ def cpu_baseline(P, dtype, target_s):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} full steps (fprop+bprop+updat) of the same workload and seed, "
-                      f"{dt:.1f} s on the host, fp64 accumulation"}
+                      f"{dt:.1f} s on the host, fp64 accumulation",
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "threads_note": "cores = the oracle's OpenMP threads (OMP_NUM_THREADS, else every CPU in the "
+                            "affinity set)"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def rotation_sets(P, dtype, rotate_mib, set_bytes, cap_bytes=16 << 30):
+    """Buffer sets so that each pass cycles through at least rotate_mib MiB of its own
+    operands (at most 64 sets, and at most cap_bytes in all)."""
+    cost = pass_cost(P, dtype)
+    need = max(int(np.ceil(rotate_mib * 2**20 / cost[p][1])) for p in PASSES)
+    return max(1, min(64, need, cap_bytes // max(set_bytes, 1)))
 
 
 def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
@@ -185,18 +208,31 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     es = xs0[0].element_size()
     set_bytes = (sum(t.numel() for t in xs0 + dys0) + w0.numel()) * es + (xs0[0].numel() + dys0[0].numel()) * es \
         + w0.numel() * 4
-    R = max(1, min(64, int(np.ceil(rotate_mib * 2**20 / set_bytes))))
+    R = rotation_sets(P, dtype, rotate_mib, set_bytes)
     sets = []
     for _ in range(R):
         sets.append(dict(xs=[t.clone() for t in xs0], dys=[t.clone() for t in dys0], w=w0.clone(),
                          y=torch.empty(m.o_shape(N), dtype=w0.dtype, device=dev),
                          dx=torch.empty(m.i_shape(N), dtype=w0.dtype, device=dev),
                          dw=torch.empty(m.w_shape, dtype=torch.float32, device=dev)))
+    ws = {}   # workspaces, allocated once (the graphs replay them)
+    for p, code in (("fprop", 0), ("bprop", 1), ("updat", 2)):
+        nb = bs.bsmm_workspace_size(h, code, N, w0.dtype)
+        ws[p] = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
+
+    def fprop(s):
+        bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N, ws=ws["fprop"])
+
+    def bprop(s):
+        bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N, ws=ws["bprop"])
+
+    def updat(s, accumulate=False):
+        bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N, accumulate=accumulate, ws=ws["updat"])
 
     def step(s):
-        bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
-        bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
-        bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
+        fprop(s)
+        bprop(s)
+        updat(s)
 
     side = torch.cuda.Stream(device=dev)   # default priority
 
@@ -204,11 +240,11 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
         # dx and dW of a backward pass are independent: the weight-read-bound bprop and
         # the gradient-write-bound updat run concurrently on two streams, joined per step
         cur = torch.cuda.current_stream(dev)
-        bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
+        fprop(s)
         side.wait_stream(cur)
         with torch.cuda.stream(side):
-            bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
-        bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
+            updat(s)
+        bprop(s)
         cur.wait_stream(side)
 
     # identity_init, timed once on its own (after a warm-up launch)
@@ -219,46 +255,46 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     bs.bsmm_identity_init(h, wi)
     ident = bs.bsmm_profile_end()["identity"]
 
-    # Graph: one replay runs one step on each of the R buffer sets in turn.
-    for i in range(max(warmup, R)):
+    # Graphs: exactly `steps` steps, the i-th on buffer set i % R.
+    def capture(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in sets[:nsets]:
+                (step_overlap if args.overlap else step)(s)
+        return g
+
+    for i in range(max(warmup, 1)):
         step(sets[i % R])
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for s in sets:
-            (step_overlap if args.overlap else step)(s)
-    reps = max(1, steps // R)
-    nsteps = reps * R
-    for _ in range(max(1, warmup // R)):
-        graph.replay()
+    full = capture(min(R, steps))
+    reps, rem = (steps // R, steps % R) if steps > R else (1, 0)
+    tail = capture(rem) if rem else None
+    for i in range(warmup):   # untimed warm-up steps
+        step(sets[i % R])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
-        graph.replay()
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
-    ms_graph = (time.perf_counter() - t0) * 1e3 / nsteps
+    ms_graph = (time.perf_counter() - t0) * 1e3 / steps
 
     # Eager launches with each kernel's dispatch timestamps recorded (HIP events on the
     # launch stream): the per-kernel durations behind the roofline figures.  Each pass
     # is timed on its own over the rotating sets, so every launch starts from cold
     # buffers (within a step, bprop would find W still cached by fprop).
-    def one(p, s):
-        if p == "fprop":
-            bs.bsmm_fprop(h, s["xs"][0], s["w"], s["y"], N)
-        elif p == "bprop":
-            bs.bsmm_bprop(h, s["dys"][0], s["w"], s["dx"], N)
-        else:
-            bs.bsmm_updat(h, s["xs"], s["dys"], s["dw"], N)
+    one = {"fprop": fprop, "bprop": bprop, "updat": updat}
 
     def eager(nsets):
         prof = {}
         for p in PASSES:
             for i in range(warmup):
-                one(p, sets[i % nsets])
+                one[p](sets[i % nsets])
             torch.cuda.synchronize()
             bs.bsmm_profile_begin()
-            for i in range(nsteps):
-                one(p, sets[i % nsets])
+            for i in range(steps):
+                one[p](sets[i % nsets])
             torch.cuda.synchronize()
             prof[p] = bs.bsmm_profile_end()[p]
         return prof
@@ -267,20 +303,20 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
         step(sets[i % R])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(nsteps):
+    for i in range(steps):
         step(sets[i % R])
     torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) * 1e3 / nsteps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / steps
     prof_cold = eager(R)
     prof_warm = eager(1)
     # the accumulating weight gradient (dW += sum), cold over the rotating sets; it reads
     # the stored dW as well, so its algorithmic bytes are G*(|x|+|dy|) + 2*|dW|
     for i in range(warmup):
-        bs.bsmm_updat(h, sets[i % R]["xs"], sets[i % R]["dys"], sets[i % R]["dw"], N, accumulate=True)
+        updat(sets[i % R], accumulate=True)
     torch.cuda.synchronize()
     bs.bsmm_profile_begin()
-    for i in range(nsteps):
-        bs.bsmm_updat(h, sets[i % R]["xs"], sets[i % R]["dys"], sets[i % R]["dw"], N, accumulate=True)
+    for i in range(steps):
+        updat(sets[i % R], accumulate=True)
     torch.cuda.synchronize()
     acc_tot, acc_cnt = bs.bsmm_profile_end()["updat"]
     cost = pass_cost(P, dtype)
@@ -291,7 +327,8 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
         us = tot / cnt * 1e3
         bound, tstar = roof(flops, nbytes, dtype)
         wt, wc = prof_warm[p]
-        per[p] = {"kernel_us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        per[p] = {"kernel": m.kernel_name(p, N, w0.dtype, G if p == "updat" else 1),
+                  "kernel_us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 3),
                   "alg_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "alg_bytes": int(nbytes), "flops": int(flops),
                   "bound": bound, "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 4),
                   "warm_kernel_us": round(wt / wc * 1e3, 3)}
@@ -301,8 +338,22 @@ def run_dtype(args, name, dtype, rotate_mib, steps, warmup):
     acc = {"kernel_us": round(aus, 3), "alg_bytes": int(abytes), "alg_GBs": round(abytes / (aus * 1e-6) / 1e9, 1),
            "bound": abound, "roofline_us": round(atstar * 1e6, 3), "frac": round(atstar / (aus * 1e-6), 4)}
     flops_step = sum(cost[p][0] for p in PASSES)
-    return dict(P=P, ms=ms_graph, ms_eager=ms_eager, per=per, acc=acc, flops_step=flops_step, R=R, steps=nsteps,
+    return dict(P=P, ms=ms_graph, ms_eager=ms_eager, per=per, acc=acc, flops_step=flops_step, R=R, steps=steps,
                 identity_us=ident[0] / max(ident[1], 1) * 1e3, layout_ms=t_layout * 1e3, prep_s=t_prep)
+
+
+def roofline_of(per, workload, dtype):
+    """The roofline object of the slowest pass (the dominant kernel of a step)."""
+    dom = max(PASSES, key=lambda p: per[p]["kernel_us"])
+    d = per[dom]
+    if d["bound"] == "hbm":
+        achieved, peak, unit = d["alg_bytes"] / (d["kernel_us"] * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = d["flops"] / (d["kernel_us"] * 1e-6) / 1e12, MFMA_PEAK_TFLOPS[dtype], "TFLOP/s"
+    return {"bound": d["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_record(dom, workload, dtype),
+            "pass": dom, "kernel": d["kernel"], "kernel_us": d["kernel_us"],
+            "alg_bytes_per_launch": d["alg_bytes"], "flops_per_launch": d["flops"]}
 
 
 def run_layer_norm(reps=20):
@@ -492,19 +543,10 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     wl = synth.WORKLOADS[args.workload]
-    dtype = args.dtype or ("bf16" if "bf16" in wl.dtypes else wl.dtypes[0])
+    dtype = args.dtype or wl.dtypes[0]
     res = run_dtype(args, args.workload, dtype, args.rotate_mib, args.steps, args.warmup)
     P, per = res["P"], res["per"]
-    dom = max(PASSES, key=lambda p: per[p]["kernel_us"])
-    d = per[dom]
-    if d["bound"] == "hbm":
-        achieved, peak, unit = d["alg_bytes"] / (d["kernel_us"] * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved, peak, unit = d["flops"] / (d["kernel_us"] * 1e-6) / 1e12, MFMA_PEAK_TFLOPS[dtype], "TFLOP/s"
-    roofline = {"bound": d["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic_record(dom, args.workload, dtype),
-                "kernel": KERNEL_NAME[dom], "kernel_us": d["kernel_us"],
-                "alg_bytes_per_launch": d["alg_bytes"], "flops_per_launch": d["flops"]}
+    roofline = roofline_of(per, args.workload, dtype)
     value = res["flops_step"] / (res["ms"] * 1e-3) / 1e12
     out = {
         "metric": "effective TFLOP/s (nonzero blocks) fprop/bprop/updat; % MFMA or HBM roofline",
@@ -528,7 +570,9 @@ def main():
     for xd in [t for t in args.extra_dtypes.split(",") if t and t in wl.dtypes and t != dtype]:
         r = run_dtype(args, args.workload, xd, args.rotate_mib, args.steps, args.warmup)
         extras[xd] = {"value": round(r["flops_step"] / (r["ms"] * 1e-3) / 1e12, 3), "ms_per_step": round(r["ms"], 5),
-                      "eager_ms_per_step": round(r["ms_eager"], 5), "per_pass": r["per"]}
+                      "eager_ms_per_step": round(r["ms_eager"], 5),
+                      "roofline": roofline_of(r["per"], args.workload, xd), "per_pass": r["per"],
+                      "updat_accumulate": r["acc"], "buffer_sets_rotated": r["R"]}
     if extras:
         out["other_dtypes"] = extras
     if not args.no_layer_norm:

@@ -212,36 +212,80 @@ def bsmm_debug_lut(h, which: int) -> np.ndarray:
     return out[:n.value]
 
 
-def _ws(h, pass_, N, dtype, device):
+_STORAGE = (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None) -> None:
+    """The library writes and reads exactly prod(shape) elements through t's pointer:
+    reject a tensor of another size, storage type or device before any call."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.numel() != int(np.prod(shape)):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)} elements' worth")
+    if t.dtype not in _STORAGE:
+        raise ValueError(f"{name} must be float32, bfloat16 or float16, not {t.dtype}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} is {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _mm_check(h, a: torch.Tensor, w: torch.Tensor, out: torch.Tensor, N: int, names, bprop: bool) -> None:
+    ishape, oshape = bsmm_i_shape(h, N), bsmm_o_shape(h, N)
+    if bprop:
+        ishape, oshape = oshape, ishape
+    _need(a, names[0], ishape)
+    _need(w, names[1], bsmm_w_shape(h), a.dtype, a.device)
+    _need(out, names[2], oshape, a.dtype, a.device)
+
+
+def _ws(h, pass_, N, dtype, device, ws: Optional[torch.Tensor] = None):
+    """The pass's workspace: `ws` when given (at least bsmm_workspace_size bytes, reused
+    across calls, e.g. by a captured graph), else a fresh allocation when one is needed."""
     nbytes = bsmm_workspace_size(h, pass_, N, dtype)
+    if ws is not None:
+        if ws.device != device or ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"ws must hold at least {nbytes} bytes on {device}")
+        return ws, ws.numel() * ws.element_size()
     if nbytes == 0:
         return None, 0
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def bsmm_fprop(h, x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, N: int) -> None:
-    ws, nb = _ws(h, 0, N, x.dtype, x.device)
+def bsmm_fprop(h, x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, N: int,
+               ws: Optional[torch.Tensor] = None) -> None:
+    _mm_check(h, x, w, y, N, ("x", "w", "y"), False)
+    ws, nb = _ws(h, 0, N, x.dtype, x.device, ws)
     _check(lib().bsmm_fprop(h, _dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(y, "y"), N, DTYPE_CODE[x.dtype],
                             _dev_ptr(ws, "ws"), nb, _stream(x)), "bsmm_fprop")
 
 
-def bsmm_bprop(h, dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, N: int) -> None:
-    ws, nb = _ws(h, 1, N, dy.dtype, dy.device)
+def bsmm_bprop(h, dy: torch.Tensor, w: torch.Tensor, dx: torch.Tensor, N: int,
+               ws: Optional[torch.Tensor] = None) -> None:
+    _mm_check(h, dy, w, dx, N, ("dy", "w", "dx"), True)
+    ws, nb = _ws(h, 1, N, dy.dtype, dy.device, ws)
     _check(lib().bsmm_bprop(h, _dev_ptr(dy, "dy"), _dev_ptr(w, "w"), _dev_ptr(dx, "dx"), N,
                             DTYPE_CODE[dy.dtype], _dev_ptr(ws, "ws"), nb, _stream(dy)), "bsmm_bprop")
 
 
 def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: torch.Tensor, N: int,
-               accumulate: bool = False) -> None:
+               accumulate: bool = False, ws: Optional[torch.Tensor] = None) -> None:
     """dw = (or, with accumulate, dw +=) the sum over the steps of x_t^T . dy_t on the
     present blocks (bsmm_updat / bsmm_updat_accumulate)."""
     G = len(xs)
     if G != len(dys):
         raise ValueError("xs and dys differ in length")
+    if not 1 <= G <= 8:
+        raise ValueError("updat takes 1 to 8 (x, dy) pairs")
+    ishape, oshape = bsmm_i_shape(h, N), bsmm_o_shape(h, N)
+    for x, dy in zip(xs, dys):
+        _need(x, "xs[t]", ishape, xs[0].dtype, xs[0].device)
+        _need(dy, "dys[t]", oshape, xs[0].dtype, xs[0].device)
+    _need(dw, "dw", bsmm_w_shape(h), None, xs[0].device)
     xp = (ctypes.c_void_p * max(G, 1))(*[_dev_ptr(t, "xs[t]").value for t in xs])
     dp = (ctypes.c_void_p * max(G, 1))(*[_dev_ptr(t, "dys[t]").value for t in dys])
     dt = xs[0].dtype if G else dw.dtype
-    ws, nb = _ws(h, 2, N, dt, dw.device)
+    ws, nb = _ws(h, 2, N, dt, dw.device, ws)
     fn = "bsmm_updat_accumulate" if accumulate else "bsmm_updat"
     _check(getattr(lib(), fn)(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[dt], DTYPE_CODE[dw.dtype],
                               _dev_ptr(ws, "ws"), nb, _stream(dw)), fn)
@@ -520,6 +564,10 @@ class BlocksparseMatMul:
                 raise ValueError("every step must have the same minibatch")
             if x.dtype != xs[0].dtype or dy.dtype != xs[0].dtype:
                 raise ValueError("all steps must share a dtype")
+        if out is not None:
+            if tuple(out.shape) != tuple(self.w_shape):
+                raise ValueError(f"out has shape {tuple(out.shape)}, expected {self.w_shape}")
+            _need(out, "out", self.w_shape, None, xs[0].device)
         dw = out if out is not None else torch.empty(self.w_shape, dtype=dw_dtype, device=xs[0].device)
         bsmm_updat(self.handle, xs, dys, dw, N, accumulate=accumulate)
         return dw

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsmm.so")
 
-SOURCES = ["layout.cpp", "api.hip", "mm.hip", "mmt.hip", "updat.hip", "init.hip", "norm.hip", "wnorm.hip", "proj.hip", "conv.hip"]
+SOURCES = ["layout.cpp", "api.hip", "mm.hip", "mmt.hip", "rows.hip", "updat.hip", "init.hip", "norm.hip", "wnorm.hip", "proj.hip", "conv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -4,6 +4,7 @@
 // without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -64,7 +65,34 @@ size_t bytes_of(const V& v) {
     return v.size() * sizeof(typename V::value_type);
 }
 
-bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
+// A handle's tables reach a device on its first call there: one allocation, filled by
+// an asynchronous copy on the caller's stream from the host image the handle keeps
+// (so the copy is ordered before the kernels that read it and never blocks the host).
+// Refused while the stream is being captured into a graph: the allocation and the
+// copy would become part of the graph.
+bsmm_status upload_tables(const void* host, size_t bytes, void* stream, const char* what, void** out) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+    if (e != hipSuccess) return dev_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(BSMM_ERR_UNSUPPORTED, std::string("first use of the ") + what +
+                                              " on this device inside a stream capture: the tables are uploaded on "
+                                              "a handle's first call per device; make one call before capturing");
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes > 0 ? bytes : 256);
+    if (e != hipSuccess)
+        return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, std::string("hipMalloc of the ") + what + " failed")
+                                        : dev_fail(e, "hipMalloc");
+    if (bytes > 0) e = hipMemcpyAsync(p, host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return dev_fail(e, "hipMemcpyAsync of the tables");
+    }
+    *out = p;
+    return BSMM_OK;
+}
+
+bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
@@ -86,18 +114,14 @@ bsmm_status device_lut(bsmm_plan* h, const DeviceLut** out) {
         total += (bytes_of(*parts[i]) + 255) & ~(size_t)255;
     }
     if (total == 0) total = 256;
-    std::vector<char> staging(total, 0);
-    for (int i = 0; i < NP; i++)
-        if (!parts[i]->empty()) std::memcpy(staging.data() + off[i], parts[i]->data(), bytes_of(*parts[i]));
-    void* base = nullptr;
-    e = hipMalloc(&base, total);
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of layout tables failed")
-                                                         : dev_fail(e, "hipMalloc");
-    e = hipMemcpy(base, staging.data(), total, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(base);
-        return dev_fail(e, "hipMemcpy of layout tables");
+    if (h->image.empty()) {   // built once, kept for the copies to later devices
+        h->image.assign(total, 0);
+        for (int i = 0; i < NP; i++)
+            if (!parts[i]->empty()) std::memcpy(h->image.data() + off[i], parts[i]->data(), bytes_of(*parts[i]));
     }
+    void* base = nullptr;
+    bsmm_status st = upload_tables(h->image.data(), total, stream, "layout tables", &base);
+    if (st != BSMM_OK) return st;
     DeviceLut d;
     d.base = base;
     const char* b = (const char*)base;
@@ -201,6 +225,8 @@ MMArgs mm_args(const HostLut& L, const DeviceLut* d, bool transw, int64_t N, int
         a.ent = bp ? d->rowent : d->colent;
     }
     a.rsi = bp ? L.row_rsi : L.col_rsi;
+    a.rec_bytes = bytes32((uint64_t)(bp ? L.R : L.S) * a.rsi * 4);
+    a.maxlen = bp ? L.max_row : L.max_col;
     set_groups(a, bp ? L.rgptr : L.cgptr, d ? (bp ? d->rgptr : d->cgptr) : nullptr,
                d ? (bp ? d->rgent : d->cgent) : nullptr, L.nnz);
     a.N = N;
@@ -218,7 +244,7 @@ bsmm_status mm_pass(bsmm_handle h, const void* in, const void* w, void* out, int
     bsmm_status s = run_mm(h, in, w, out, N, dt, transw);
     if (s != BSMM_OK || N == 0) return s;
     const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    if ((s = device_lut(h, stream, &d)) != BSMM_OK) return s;
     const HostLut& L = h->lut;
     MMArgs a = mm_args(L, d, transw, N, dt);
     a.in = in;
@@ -340,14 +366,14 @@ bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype d
 
 bsmm_status bsmm_fprop(bsmm_handle h, const void* x, const void* w, void* y, int64_t N, bsmm_dtype dt,
                        void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
+    (void)ws;   // no fprop kernel takes a workspace
     (void)ws_bytes;
     return mm_pass(h, x, w, y, N, dt, false, stream);
 }
 
 bsmm_status bsmm_bprop(bsmm_handle h, const void* dy, const void* w, void* dx, int64_t N, bsmm_dtype dt,
                        void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
+    (void)ws;   // no bprop kernel takes a workspace
     (void)ws_bytes;
     return mm_pass(h, dy, w, dx, N, dt, true, stream);
 }
@@ -407,7 +433,7 @@ bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* 
     }
     if (acc && N == 0) return BSMM_OK;   // the empty sum adds nothing
     const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    if ((s = device_lut(h, stream, &d)) != BSMM_OK) return s;
     UpArgs a = up_args(L, N, group);
     a.acc = acc ? 1 : 0;
     for (int t = 0; t < group; t++) {
@@ -463,7 +489,7 @@ bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stre
     bsmm_status s = check_ptr(w, "w");
     if (s != BSMM_OK) return s;
     const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, &d)) != BSMM_OK) return s;
+    if ((s = device_lut(h, stream, &d)) != BSMM_OK) return s;
     hipError_t e = launch_identity(w, d->coords, L.nnz, L.b, dt, stream);
     return e == hipSuccess ? BSMM_OK : dev_fail(e, "identity_init launch");
 }
@@ -627,7 +653,8 @@ bsmm_status bsmm_layer_norm_grad(const void* dy, const void* x, const float* g, 
 
 // ---- weight normalisation ----
 namespace {
-bsmm_status wn_setup(bsmm_handle h, float epsilon, int dt1, int dt2, WnArgs& a, const DeviceLut** d) {
+bsmm_status wn_setup(bsmm_handle h, float epsilon, int dt1, int dt2, WnArgs& a, const DeviceLut** d,
+                     void* stream) {
     if (!h) return fail(BSMM_ERR_INVALID_ARG, "handle is NULL");
     if (!valid_dt(dt1) || !valid_dt(dt2)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     if (!(epsilon > 0.f) || epsilon > 3.0e38f) return fail(BSMM_ERR_INVALID_ARG, "epsilon must be finite and > 0");
@@ -635,7 +662,7 @@ bsmm_status wn_setup(bsmm_handle h, float epsilon, int dt1, int dt2, WnArgs& a, 
     a.b = h->lut.b;
     a.eps = epsilon;
     if (h->lut.nnz == 0) return BSMM_OK;
-    return device_lut(h, d);
+    return device_lut(h, stream, d);
 }
 }  // namespace
 
@@ -647,7 +674,7 @@ bsmm_status bsmm_l2_normalize(bsmm_handle h, const void* w, const float* gain, v
         if ((s = check_ptr(w, "w")) != BSMM_OK || (s = check_ptr(w_out, "w_out")) != BSMM_OK) return s;
     }
     const DeviceLut* d = nullptr;
-    bsmm_status s = wn_setup(h, epsilon, w_dt, out_dt, a, &d);
+    bsmm_status s = wn_setup(h, epsilon, w_dt, out_dt, a, &d, stream);
     if (s != BSMM_OK || h->lut.nnz == 0) return s;
     a.w = w;
     a.out = w_out;
@@ -672,7 +699,7 @@ bsmm_status bsmm_l2_normalize_grad(bsmm_handle h, const void* dy, const void* w,
             return s;
     }
     const DeviceLut* d = nullptr;
-    bsmm_status s = wn_setup(h, epsilon, dy_dt, w_dt, a, &d);
+    bsmm_status s = wn_setup(h, epsilon, dy_dt, w_dt, a, &d, stream);
     if (s != BSMM_OK || h->lut.nnz == 0) return s;
     a.w = w;
     a.dy = dy;
@@ -722,7 +749,7 @@ bsmm_status bsmm_profile_end(double ms[BSMM_NUM_PASSES], int64_t count[BSMM_NUM_
 // ---- SparseProj ----
 namespace {
 
-bsmm_status proj_device(bsmm_proj_plan* h, const int32_t** d) {
+bsmm_status proj_device(bsmm_proj_plan* h, void* stream, const int32_t** d) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
@@ -732,20 +759,15 @@ bsmm_status proj_device(bsmm_proj_plan* h, const int32_t** d) {
         *d = it->second;
         return BSMM_OK;
     }
-    const size_t n = h->lut.size() + h->inv.size();
-    int32_t* p = nullptr;
-    e = hipMalloc((void**)&p, (n > 0 ? n : 1) * sizeof(int32_t));
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of the projection map failed")
-                                                         : dev_fail(e, "hipMalloc");
-    std::vector<int32_t> both(h->lut);
-    both.insert(both.end(), h->inv.begin(), h->inv.end());
-    if (n > 0) e = hipMemcpy(p, both.data(), n * sizeof(int32_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return dev_fail(e, "hipMemcpy of the projection map");
+    if (h->image.empty()) {   // lut then inv, kept for the copies to later devices
+        h->image = h->lut;
+        h->image.insert(h->image.end(), h->inv.begin(), h->inv.end());
     }
-    h->dev.emplace(dev, p);
-    *d = p;
+    void* p = nullptr;
+    bsmm_status st = upload_tables(h->image.data(), h->image.size() * sizeof(int32_t), stream, "projection map", &p);
+    if (st != BSMM_OK) return st;
+    h->dev.emplace(dev, (int32_t*)p);
+    *d = (const int32_t*)p;
     return BSMM_OK;
 }
 
@@ -767,7 +789,7 @@ bsmm_status proj_call(bsmm_proj_handle h, int mode, const void* base, const void
     if (wsrc > 0 && (uint64_t)N > (uint64_t)INT64_MAX / 8 / (uint64_t)std::max(wout, wsrc))
         return fail(BSMM_ERR_UNSUPPORTED, "tensor too large");
     const int32_t* d = nullptr;
-    if ((s = proj_device(h, &d)) != BSMM_OK) return s;
+    if ((s = proj_device(h, stream, &d)) != BSMM_OK) return s;
     ProjArgs a{};
     a.base = base;
     a.src = src;
@@ -884,7 +906,7 @@ namespace {
 
 // device copy of the conv tables; offsets (int32 elements) of each array in `off`
 constexpr int kConvParts = 12;
-bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[kConvParts]) {
+bsmm_status conv_device(bsmm_conv_plan* h, void* stream, const int32_t** d, size_t off[kConvParts]) {
     const std::vector<int32_t>* parts[kConvParts] = {&h->cidx,    &h->kidx,    &h->kptr,   &h->kent,
                                                      &h->cptr,    &h->cent,    &h->gptr[0], &h->gblk[0],
                                                      &h->zch[0],  &h->gptr[1], &h->gblk[1], &h->zch[1]};
@@ -902,20 +924,15 @@ bsmm_status conv_device(bsmm_conv_plan* h, const int32_t** d, size_t off[kConvPa
         *d = it->second;
         return BSMM_OK;
     }
-    std::vector<int32_t> all;
-    all.reserve(total);
-    for (int i = 0; i < kConvParts; i++) all.insert(all.end(), parts[i]->begin(), parts[i]->end());
-    int32_t* p = nullptr;
-    e = hipMalloc((void**)&p, (total > 0 ? total : 1) * sizeof(int32_t));
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(BSMM_ERR_OOM, "hipMalloc of the conv tables failed")
-                                                         : dev_fail(e, "hipMalloc");
-    if (total > 0) e = hipMemcpy(p, all.data(), total * sizeof(int32_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return dev_fail(e, "hipMemcpy of the conv tables");
+    if (h->image.empty() && total > 0) {   // kept for the copies to later devices
+        h->image.reserve(total);
+        for (int i = 0; i < kConvParts; i++) h->image.insert(h->image.end(), parts[i]->begin(), parts[i]->end());
     }
-    h->dev.emplace(dev, p);
-    *d = p;
+    void* p = nullptr;
+    bsmm_status st = upload_tables(h->image.data(), total * sizeof(int32_t), stream, "conv tables", &p);
+    if (st != BSMM_OK) return st;
+    h->dev.emplace(dev, (int32_t*)p);
+    *d = (const int32_t*)p;
     return BSMM_OK;
 }
 
@@ -970,7 +987,7 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
         return fail(BSMM_ERR_UNSUPPORTED, "tensor too large");
     const int32_t* d = nullptr;
     size_t off[kConvParts];
-    if ((s = conv_device(h, &d, off)) != BSMM_OK) return s;
+    if ((s = conv_device(h, stream, &d, off)) != BSMM_OK) return s;
     ConvArgs x = conv_args(h, dt);
     {
         const uint64_t es = dt == BSMM_F32 ? 4 : 2;

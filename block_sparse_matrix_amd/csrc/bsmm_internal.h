@@ -99,6 +99,7 @@ struct bsmm_plan {
     bsmm::HostLut lut;
     int force[3] = {0, 0, 0};   // forced kernel kind per pass (fprop, bprop, updat), 0 = automatic
     std::mutex mu;
+    std::vector<char> image;              // the tables packed as on the device (source of the uploads)
     std::map<int, bsmm::DeviceLut> dev;   // per HIP device ordinal
 };
 
@@ -111,6 +112,7 @@ struct bsmm_proj_plan {
     int64_t nhidden = 0, nproj = 0;
     std::vector<int32_t> lut, inv;
     std::mutex mu;
+    std::vector<int32_t> image;    // lut followed by inv (source of the uploads)
     std::map<int, int32_t*> dev;   // per HIP device ordinal: lut (nproj) followed by inv (nhidden)
 };
 
@@ -132,5 +134,6 @@ struct bsmm_conv_plan {
     std::vector<int32_t> gptr[2], gblk[2], zch[2];
     bool gok[2] = {false, false};
     std::mutex mu;
-    std::map<int, int32_t*> dev;   // per HIP device: all the arrays above back to back
+    std::vector<int32_t> image;    // all the arrays above back to back (source of the uploads)
+    std::map<int, int32_t*> dev;   // per HIP device: the same, on the device
 };

@@ -202,6 +202,13 @@ __device__ __forceinline__ void wg_decode(int bid, int nlist, int ntiles, int& l
     if (li >= nlist) li = -1;
 }
 
+// Grid size for nlist lists x ntiles minibatch tiles in the wg_decode mapping.
+inline int mm_grid(int nlist, int ntiles) {
+    if (ntiles == 1) return nlist;
+    if (ntiles >= 8) return 8 * nlist * ((ntiles + 7) / 8);
+    return ((nlist + 7) / 8) * 8 * ntiles;
+}
+
 // Launch on `st` with explicit timing events (either may be null).
 template <typename K, typename... Args>
 static hipError_t launch_ev(K kernel, dim3 grid, dim3 block, hipStream_t st, void* e0, void* e1, Args... args) {

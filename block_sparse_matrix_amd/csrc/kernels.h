@@ -31,7 +31,12 @@ struct MMArgs {
     int32_t gfill;         // blocks per group entry, percent of kGroupOut
     int32_t gmax;          // most entries in one group
     int32_t force;         // MMKind to use (0: automatic)
+    uint32_t rec_bytes;    // size of the record array (`rec`), bytes
+    int32_t maxlen;        // longest list
 };
+
+// The small-minibatch kernel (rows.hip) takes lists of at most this many entries.
+constexpr int kRowsMaxLen = 256;
 
 // Largest tensor the kernels address with 32-bit buffer offsets.
 constexpr uint64_t kMaxTensorBytes = 0x7fff0000ull;
@@ -78,7 +83,7 @@ inline int tile_split(int ntiles) {
 
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.
-enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2, MM_N64_W8 };
+enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2, MM_N64_W8, MM_ROWS };
 enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES };
 int mm_kind(const MMArgs& a, int dt, int b, int fa);
 const char* mm_kind_name(int kind);
@@ -90,6 +95,8 @@ int updat_kind_of_name(const char* name);
 hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* stream, int pass);
 // 32x32 blocks, 16-bit storage: output-block groups (a.gptr / a.gent / a.ngroups)
 hipError_t launch_mm_groups(const MMArgs& a, int dt, int fa, bool transw, void* stream, int pass);
+// 32x32 blocks, N <= 64, feature_axis 1, lists of at most kRowsMaxLen entries
+hipError_t launch_mm_rows(const MMArgs& a, int dt, bool transw, void* stream, int pass);
 hipError_t launch_updat(const UpArgs& a, int dt, int b, int fa, void* stream);
 hipError_t launch_identity(void* w, const int32_t* coords, int64_t nnz, int b, int dt, void* stream);
 

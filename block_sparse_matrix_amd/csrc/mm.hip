@@ -631,11 +631,6 @@ static hipError_t launch_large(MMArgs a, hipStream_t st, int pass) {
 }
 
 // ---------------------------------------------------------------------------------
-static int mm_grid(int nlist, int ntiles) {
-    if (ntiles == 1) return nlist;
-    if (ntiles >= 8) return 8 * nlist * ((ntiles + 7) / 8);
-    return ((nlist + 7) / 8) * 8 * ntiles;
-}
 
 template <int DT, int B, int FA, bool TW, int MT, int WM, int WK, int D>
 static hipError_t launch_cfg(MMArgs a, hipStream_t st, int pass) {
@@ -694,7 +689,14 @@ int mm_kind(const MMArgs& a, int dt, int b, int fa) {
     // slab feeds several blocks.
     const bool groups_ok = b == 32 && dt != BSMM_F32 && a.ngroups > 0 && a.gmax <= kGroupMaxSteps &&
                            (fa == 1 || a.N % 8 == 0);
-    if (a.force > 0) return a.force == MM_GROUPS && !groups_ok ? -1 : a.force;
+    // Small minibatch, 32x32 blocks, features last (rows.hip): lists of at most 256
+    // entries (64 per wave)
+    const bool rows_ok = b == 32 && fa == 1 && a.N > 0 && a.N <= 64 && a.maxlen <= kRowsMaxLen;
+    if (a.force > 0) {
+        if (a.force == MM_GROUPS && !groups_ok) return -1;
+        if (a.force == MM_ROWS && !rows_ok) return -1;
+        return a.force;
+    }
     switch (mm_variant()) {
     case 1: return MM_N64;
     case 2: return MM_V_W16;
@@ -712,6 +714,7 @@ int mm_kind(const MMArgs& a, int dt, int b, int fa) {
     // Bernoulli(0.1) layout; band + 3 % random at 24 %) against the weight-stack kernel.
     const int64_t gwgs = (int64_t)((a.N + 255) / 256) * a.ngroups;
     if (groups_ok && a.N >= 1024 && (a.gfill >= 25 || (a.gfill >= 17 && gwgs >= 512))) return MM_GROUPS;
+    if (rows_ok) return MM_ROWS;
     // Small minibatch: the weight stream dominates and there are few output tiles, so
     // the 4 waves of a workgroup split each block list (measured fastest at N = 64).
     if (a.N <= 16) return MM_N16;
@@ -735,6 +738,7 @@ const char* mm_kind_name(int kind) {
     case MM_GROUPS: return "output_groups";
     case MM_V_W16: return "list_n64_16waves";
     case MM_N64_W8: return "list_n64_8waves";
+    case MM_ROWS: return "rows_n64";
     case MM_V_STACK1: return "list_weight_stack_64";
     case MM_V_STACK2: return "list_weight_stack_128";
     }
@@ -742,7 +746,7 @@ const char* mm_kind_name(int kind) {
 }
 
 int mm_kind_of_name(const char* name) {
-    for (int k = MM_N16; k <= MM_N64_W8; k++)
+    for (int k = MM_N16; k <= MM_ROWS; k++)
         if (std::strcmp(name, mm_kind_name(k)) == 0) return k;
     return 0;
 }
@@ -753,6 +757,7 @@ hipError_t launch_mm(const MMArgs& a, int dt, int b, int fa, bool transw, void* 
     const int kind = mm_kind(a, dt, b, fa);
     if (kind < 0) return hipErrorNotSupported;
     if (kind == MM_GROUPS) return launch_mm_groups(a, dt, fa, transw, stream, pass);
+    if (kind == MM_ROWS) return launch_mm_rows(a, dt, transw, stream, pass);
     switch (dt * 2 + (transw ? 1 : 0)) {
     case 0: return launch_mm_dt<BSMM_F32, false>(a, kind, b, fa, st, pass);
     case 1: return launch_mm_dt<BSMM_F32, true>(a, kind, b, fa, st, pass);

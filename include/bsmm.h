@@ -45,7 +45,12 @@
  *     empty sum).  Activation pointers may be NULL only when N = 0.
  *   - A handle is immutable after bsmm_create; it may be used from several host
  *     threads and streams at once.  Its look-up tables are copied to a device
- *     the first time a kernel call runs on that device.
+ *     the first time a kernel call runs on that device: one hipMalloc and an
+ *     asynchronous copy on that call's stream, from a host image the handle keeps.
+ *     That first call must not be made while its stream is being captured into a
+ *     HIP graph (it returns BSMM_ERR_UNSUPPORTED and enqueues nothing); later calls
+ *     allocate nothing and may be captured.  (The same holds for the SparseProj
+ *     and BlocksparseConv handles below.)
  */
 #ifndef BSMM_H
 #define BSMM_H

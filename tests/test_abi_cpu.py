@@ -142,14 +142,54 @@ def test_no_cpu_path():
         m.fprop(x, w)
 
 
+def test_binding_rejects_wrong_sizes_before_any_call():
+    """The C ABI sees pointers only; the binding checks every tensor's size, storage type
+    and device against the plan first, so a wrong-shaped buffer is a ValueError rather
+    than an out-of-bounds device access."""
+    import torch
+    m = bs.BlocksparseMatMul(np.ones((2, 3)), block_size=8)   # C = 16, K = 24, 6 blocks
+    N = 4
+    x, dy = torch.zeros(N, 16), torch.zeros(N, 24)
+    w, y = torch.zeros(6, 8, 8), torch.zeros(N, 24)
+    with pytest.raises(ValueError, match="shape"):
+        bs.bsmm_fprop(m.handle, x, torch.zeros(5, 8, 8), y, N)
+    with pytest.raises(ValueError, match="shape"):
+        bs.bsmm_fprop(m.handle, x, w, torch.zeros(N, 16), N)
+    with pytest.raises(ValueError, match="shape"):
+        bs.bsmm_bprop(m.handle, dy, w, torch.zeros(N + 1, 16), N)
+    with pytest.raises(ValueError, match="expected"):
+        bs.bsmm_fprop(m.handle, x, w.to(torch.bfloat16), y, N)
+    with pytest.raises(ValueError, match="shape"):
+        bs.bsmm_updat(m.handle, [x], [dy], torch.zeros(5, 8, 8), N)
+    with pytest.raises(ValueError, match="shape"):
+        bs.bsmm_updat(m.handle, [x], [torch.zeros(N, 16)], w, N)
+    with pytest.raises(ValueError):
+        bs.bsmm_updat(m.handle, [x], [dy], w.to(torch.int32), N)
+    # the class method: a wrong-shaped gradient to accumulate into
+    with pytest.raises(ValueError, match="shape"):
+        m.updat([x], [dy], out=torch.zeros(6, 8, 4), accumulate=True)
+    with pytest.raises(ValueError, match="shape"):
+        m.updat([x], [dy], out=torch.zeros(6 * 64), accumulate=True)
+    with pytest.raises(ValueError):
+        m.updat([x], [dy], out=torch.zeros(6, 8, 8, dtype=torch.float64), accumulate=True)
+
+
 def test_kernel_choice_names():
     import torch
     rng = np.random.default_rng(0)
     L = (rng.random((16, 16)) < 0.5).astype(np.uint8)
     m32 = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
     m8 = bs.BlocksparseMatMul(L, block_size=8, feature_axis=0)
-    assert m32.kernel_name("fprop", 64, torch.bfloat16) == "list_n64"
-    assert m32.kernel_name("fprop", 64, torch.float32) == "list_n64_8waves"
+    assert m32.kernel_name("fprop", 64, torch.bfloat16) == "rows_n64"
+    assert m32.kernel_name("bprop", 64, torch.float32) == "rows_n64"
+    assert m32.kernel_name("fprop", 65, torch.float32) == "list_rows128"
+    assert m8.kernel_name("fprop", 64, torch.float32) == "list_n64_8waves"   # the rows kernel is 32x32 only
+    long_col = np.zeros((300, 2), dtype=np.uint8)
+    long_col[:, 0] = 1   # a 300-entry column list: more than the rows kernel takes
+    mlong = bs.BlocksparseMatMul(long_col, block_size=32)
+    assert mlong.kernel_name("fprop", 64, torch.bfloat16) == "list_n64"
+    assert mlong.kernel_name("bprop", 64, torch.bfloat16) == "rows_n64"
+    assert bs.BlocksparseMatMul(L, block_size=32, feature_axis=0).kernel_name("fprop", 64, torch.bfloat16) == "list_n64"
     assert m32.kernel_name("fprop", 4096, torch.bfloat16) == "output_groups"
     assert m32.kernel_name("bprop", 4096, torch.float16) == "output_groups"
     assert m32.kernel_name("fprop", 4096, torch.float32) == "list_weight_stack"

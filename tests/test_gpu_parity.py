@@ -182,6 +182,53 @@ def test_autograd():
     assert_close(w.grad, oracle.updat(P.layout, 32, 1, [bits(P.xs[0])], [bits(P.dys[0])], 70), "f32", "dw")
 
 
+@pytest.mark.parametrize("N", [1, 5, 16, 17, 32, 33, 63, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_rows_small_minibatch(N, dtype):
+    """The small-minibatch kernel (32x32 blocks, features last, N <= 64; one workgroup
+    per list and 32-row minibatch tile): lists of 40 entries and of few, empty lists
+    (zeros), every minibatch-tile count and ragged tail, bit-reproducible."""
+    print(f"case rows N={N} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(500 + N)
+    R = S = 40
+    L = (rng.random((R, S)) < 0.3).astype(np.uint8)
+    L[:, 0] = 1          # a 40-entry column list
+    L[2, :] = 1          # a 40-entry row list
+    L[:, 5] = 0          # an empty column: y zero there
+    L[9, :] = 0          # an empty row: dx zero there
+    P = synth.random_problem(rng, L, 32, N, 1, dtype, G=1, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    for p in ("fprop", "bprop"):
+        assert m.kernel_name(p, N, TORCH_DT[dtype]) == "rows_n64"
+    y, dx = m.fprop(dev(P.xs[0]), dev(P.w)), m.bprop(dev(P.dys[0]), dev(P.w))
+    ry, rdx, _ = _oracle_all(P, dtype)
+    assert_close(y, ry, dtype, "fprop")
+    assert_close(dx, rdx, dtype, "bprop")
+    assert torch.count_nonzero(y[:, 5 * 32:6 * 32]) == 0 and torch.count_nonzero(dx[:, 9 * 32:10 * 32]) == 0
+    # bit-reproducible: a second run gives the same bits
+    y2, dx2 = m.fprop(dev(P.xs[0]), dev(P.w)), m.bprop(dev(P.dys[0]), dev(P.w))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(dx, dx2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rows_all_zero_layout(dtype):
+    """No stored blocks: every list is empty and the small-minibatch kernel writes zeros."""
+    L = np.zeros((3, 4), dtype=np.uint8)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    assert m.kernel_name("fprop", 40, TORCH_DT[dtype]) == "rows_n64"
+    N = 40
+    x = torch.randn(N, 96, device="cuda").to(TORCH_DT[dtype])
+    dy = torch.randn(N, 128, device="cuda").to(TORCH_DT[dtype])
+    w = torch.empty(0, 32, 32, dtype=TORCH_DT[dtype], device="cuda")
+    y = torch.full((N, 128), 7.0, device="cuda").to(TORCH_DT[dtype])
+    dx = torch.full((N, 96), 7.0, device="cuda").to(TORCH_DT[dtype])
+    bs.bsmm_fprop(m.handle, x, w, y, N)
+    bs.bsmm_bprop(m.handle, dy, w, dx, N)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0 and torch.count_nonzero(dx) == 0
+
+
 @pytest.mark.parametrize("N", [512, 530, 2048, 2100])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fa", [1, 0])

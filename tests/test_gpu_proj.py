@@ -47,9 +47,10 @@ def test_ops(case, fa, dtype):
     rng = np.random.default_rng(N + H + Pn + fa)
     P = synth.proj_problem(rng, N, H, Pn, fa, dtype, rnd)
     proj = bs.SparseProj(H, Pn, stride, bsz or 32, gather_lut=P.lut, feature_axis=fa)
-    lut = proj.gather_lut.astype(np.int64)
-    if P.lut is None:
-        assert np.array_equal(lut, sp.default_lut(H, Pn, stride, bsz or 32))
+    # the oracle takes the map from the inputs (the given map, or the oracle's own
+    # default), never from the library; the library's copy must equal it
+    lut = sp.check_lut(P.lut, H) if P.lut is not None else sp.default_lut(H, Pn, stride, bsz or 32)
+    assert np.array_equal(proj.gather_lut.astype(np.int64), lut)
     x, a, s = dev(P.x), dev(P.a), dev(P.s)
     g = proj.gather(x)
     sc = proj.scatter(s)
@@ -120,25 +121,25 @@ def test_autograd(fa):
 
 def test_bench_configuration_full_size():
     """The configuration bench.py times (nhidden 8192 -> nproj 4096 in blocks of 32 every
-    64 features, N = 4096, bf16, features last, the same seed), every output compared
-    with the oracle: copies bit for bit, add / mul to the dtype gate."""
+    64 features, N = 4096, bf16, features last, the same seed), all five ops against the
+    oracle: copies bit for bit, add / mul to the dtype gate.  The map is the oracle's
+    default map for these arguments."""
     N, H, Pn = 4096, 8192, 4096
+    print(f"case proj full size N={N} H={H} P={Pn} bf16", flush=True)
     P = synth.proj_problem(np.random.default_rng(17), N, H, Pn, 1, "bf16", False)
     proj = bs.SparseProj(H, Pn, 64, 32)
-    lut = proj.gather_lut.astype(np.int64)
-    x, s = dev(P.x), dev(P.s)
+    lut = sp.default_lut(H, Pn, 64, 32)
+    assert np.array_equal(proj.gather_lut.astype(np.int64), lut)
+    x, a, s = dev(P.x), dev(P.a), dev(P.s)
     g = proj.gather(x)
     sc = proj.scatter(s)
     za = proj.scatter_add(x, s)
     zm = proj.scatter_mul(x, s)
+    gm = proj._gather_mul(x, a)
     torch.cuda.synchronize()
-    X, S = _f64(P.x), _f64(P.s)
-    assert _bits_equal(g, X[:, lut], "bf16")
-    ref_sc = np.zeros_like(X)
-    ref_sc[:, lut] = S
-    assert _bits_equal(sc, ref_sc, "bf16")
-    ref_a, ref_m = X.copy(), X.copy()
-    ref_a[:, lut] += S
-    ref_m[:, lut] *= S
-    assert_close(za, ref_a, "bf16", "scatter_add")
-    assert_close(zm, ref_m, "bf16", "scatter_mul")
+    X, A, S = _f64(P.x), _f64(P.a), _f64(P.s)
+    assert _bits_equal(g, sp.gather(lut, X, 1), "bf16")
+    assert _bits_equal(sc, sp.scatter(lut, S, H, 1), "bf16")
+    assert_close(za, sp.scatter_add(lut, X, S, 1), "bf16", "scatter_add")
+    assert_close(zm, sp.scatter_mul(lut, X, S, 1), "bf16", "scatter_mul")
+    assert_close(gm, sp.gather_mul(lut, X, A, 1), "bf16", "gather_mul")
