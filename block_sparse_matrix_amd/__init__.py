@@ -25,6 +25,7 @@ import torch
 __all__ = [
     "BlocksparseMatMul", "BsmmError", "group_param_grads", "lib", "LIB_PATH",
     "bsmm_create", "bsmm_destroy", "bsmm_fprop", "bsmm_bprop", "bsmm_updat", "bsmm_updat_accumulate",
+    "bsmm_updat_noalloc",
     "bsmm_identity_init",
     "bsmm_w_shape", "bsmm_i_shape", "bsmm_o_shape", "bsmm_block_coord", "bsmm_workspace_size",
     "bsmm_debug_lut", "bsmm_profile_begin", "bsmm_profile_end", "bsmm_plan_info",
@@ -75,6 +76,7 @@ def lib():
         "bsmm_bprop": [vp, vp, vp, vp, i64, i32, vp, sz, vp],
         "bsmm_updat": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
         "bsmm_updat_accumulate": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp, sz, vp],
+        "bsmm_updat_noalloc": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i64, i32, i32, vp],
         "bsmm_identity_init": [vp, vp, i32, vp],
         "bsmm_debug_lut": [vp, i32, P64, i64, P64],
         "bsmm_kernel_name": [vp, i32, i64, i32, i32, ctypes.POINTER(ctypes.c_char_p)],
@@ -289,6 +291,26 @@ def bsmm_updat(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: t
     fn = "bsmm_updat_accumulate" if accumulate else "bsmm_updat"
     _check(getattr(lib(), fn)(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[dt], DTYPE_CODE[dw.dtype],
                               _dev_ptr(ws, "ws"), nb, _stream(dw)), fn)
+
+
+def bsmm_updat_noalloc(h, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], dw: torch.Tensor,
+                       N: int) -> None:
+    """dw = the sum over the steps of x_t^T . dy_t (as bsmm_updat), with the library's fixed
+    device scratch instead of a workspace: the call allocates nothing (bsmm_updat_noalloc)."""
+    G = len(xs)
+    if G != len(dys):
+        raise ValueError("xs and dys differ in length")
+    if not 1 <= G <= 8:
+        raise ValueError("updat takes 1 to 8 (x, dy) pairs")
+    ishape, oshape = bsmm_i_shape(h, N), bsmm_o_shape(h, N)
+    for x, dy in zip(xs, dys):
+        _need(x, "xs[t]", ishape, xs[0].dtype, xs[0].device)
+        _need(dy, "dys[t]", oshape, xs[0].dtype, xs[0].device)
+    _need(dw, "dw", bsmm_w_shape(h), None, xs[0].device)
+    xp = (ctypes.c_void_p * G)(*[_dev_ptr(t, "xs[t]").value for t in xs])
+    dp = (ctypes.c_void_p * G)(*[_dev_ptr(t, "dys[t]").value for t in dys])
+    _check(lib().bsmm_updat_noalloc(h, xp, dp, G, _dev_ptr(dw, "dw"), N, DTYPE_CODE[xs[0].dtype],
+                                    DTYPE_CODE[dw.dtype], _stream(dw)), "bsmm_updat_noalloc")
 
 
 def bsmm_identity_init(h, w: torch.Tensor) -> None:

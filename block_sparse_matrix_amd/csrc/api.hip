@@ -6,6 +6,8 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -92,7 +94,7 @@ bsmm_status upload_tables(const void* host, size_t bytes, void* stream, const ch
     return BSMM_OK;
 }
 
-bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out) {
+bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out, bool may_upload = true) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
@@ -102,6 +104,10 @@ bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out) {
         *out = &it->second;
         return BSMM_OK;
     }
+    if (!may_upload)
+        return fail(BSMM_ERR_UNSUPPORTED,
+                    "the layout tables are not on this device yet and this call allocates nothing: make one call "
+                    "of an allocating entry point on this device first");
     const HostLut& L = h->lut;
     constexpr int NP = 20;
     const std::vector<int32_t>* parts[NP] = {&L.coords,  &L.colptr,   &L.colent,   &L.rowptr,  &L.rowent,
@@ -409,9 +415,11 @@ bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm
 
 namespace {
 // updat and its accumulating form (acc: dW += the sum instead of dW = the sum).
+// noalloc: the caller's ws is the library's fixed scratch; the tables must already be
+// on the device (no upload, so no allocation).
 bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
                        int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes, void* stream,
-                       bool acc) {
+                       bool acc, bool noalloc = false) {
     bsmm_status s = check_call(h, N, dt);
     if (s != BSMM_OK) return s;
     if (!valid_dt(dw_dt)) return fail(BSMM_ERR_INVALID_ARG, "dw dtype must be BSMM_F32, BSMM_BF16 or BSMM_F16");
@@ -433,7 +441,7 @@ bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* 
     }
     if (acc && N == 0) return BSMM_OK;   // the empty sum adds nothing
     const DeviceLut* d = nullptr;
-    if ((s = device_lut(h, stream, &d)) != BSMM_OK) return s;
+    if ((s = device_lut(h, stream, &d, !noalloc)) != BSMM_OK) return s;
     UpArgs a = up_args(L, N, group);
     a.acc = acc ? 1 : 0;
     for (int t = 0; t < group; t++) {
@@ -479,6 +487,58 @@ bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs, const vo
                                   void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* ws, size_t ws_bytes,
                                   void* stream) {
     return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+// ---- weight gradient without allocation ----
+// The split weight-gradient kernels keep fp32 partial sums in a workspace.  For callers
+// that cannot allocate, bsmm_updat_noalloc uses this fixed device array instead: one
+// copy per GPU, held until the process ends, shared by every call on that GPU.  Host
+// code never passes `scratch` itself (on the host the name is only a stand-in); it
+// passes the device address hipGetSymbolAddress reports for the current device.
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;   // device ordinal -> that device's scratch address
+
+// The current device's scratch address, looked up once per device (first call there).
+bsmm_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return BSMM_OK;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return dev_fail(e, "hipGetSymbolAddress of the scratch array");
+    g_scratch.emplace(dev, p);
+    *out = p;
+    return BSMM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bsmm_status bsmm_updat_noalloc(bsmm_handle h, const void* const* xs, const void* const* dys, int group, void* dw,
+                               int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* stream) {
+    bsmm_status s = check_call(h, N, dt);
+    if (s != BSMM_OK) return s;
+    size_t need = 0;
+    if ((s = bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need)) != BSMM_OK) return s;
+    if (need > kScratchBytes)
+        return fail(BSMM_ERR_UNSUPPORTED, "this weight gradient needs " + std::to_string(need) +
+                                              " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
+                                              "-byte scratch of the allocation-free entry point");
+    void* ws = nullptr;
+    if (need > 0 && (s = scratch_address(&ws)) != BSMM_OK) return s;
+    return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, need, stream, false, true);
 }
 
 bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream) {

@@ -174,6 +174,22 @@ BSMM_API bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs,
                                            int group, void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt,
                                            void* ws, size_t ws_bytes, void* stream);
 
+/* updat for callers that cannot allocate device memory (code under HIP-graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same result as bsmm_updat
+ * (same kernels, bit for bit), with the split weight-gradient kernels' fp32 partial sums
+ * in a fixed 64 MiB device array of the library instead of a caller workspace.  The
+ * call makes no hipMalloc / hipFree and calls no allocating routine.
+ *   Arguments as bsmm_updat without ws / ws_bytes.
+ *   Errors as bsmm_updat, and BSMM_ERR_UNSUPPORTED when bsmm_workspace_size(h,
+ *   BSMM_PASS_UPDAT, N, dt) exceeds 64 MiB, or when the handle's layout tables are not
+ *   on the current device yet (they are uploaded by the first call of any other entry
+ *   point on that device).
+ * The array is one per GPU, held until the process ends, and shared by every call on
+ * that GPU: calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must be serialised by the caller.  Nothing in it needs to start at zero. */
+BSMM_API bsmm_status bsmm_updat_noalloc(bsmm_handle h, const void* const* xs, const void* const* dys, int group,
+                                        void* dw, int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* stream);
+
 /* identity_init on the device: w (device, (nnz, b, b), dtype dt) is overwritten with
  * I_b for every present diagonal block (c == k) and zero for the other blocks. */
 BSMM_API bsmm_status bsmm_identity_init(bsmm_handle h, void* w, bsmm_dtype dt, void* stream);

@@ -118,6 +118,14 @@ def test_call_validation_before_gpu():
         assert acc(h, arr, arr, 1, odd, 4, 0, 0, None, 0, None) == ALIGN
         assert acc(h, bad, bad, 2, good, 4, 0, 0, None, 0, None) == ALIGN
         assert acc(h, None, None, 1, good, 0, 0, 0, None, 0, None) == 0
+        # the allocation-free form validates the same way before touching the device
+        na = L.bsmm_updat_noalloc
+        assert na(None, arr, arr, 1, good, 4, 0, 0, None) == INVALID
+        assert na(h, arr, arr, 0, good, 4, 0, 0, None) == INVALID
+        assert na(h, arr, arr, 1, good, 4, 7, 0, None) == INVALID
+        assert na(h, arr, arr, 1, None, 4, 0, 0, None) == INVALID
+        assert na(h, arr, arr, 1, odd, 4, 0, 0, None) == ALIGN
+        assert na(h, bad, bad, 2, good, 4, 0, 0, None) == ALIGN
         assert L.bsmm_identity_init(h, None, 0, None) == INVALID
         assert L.bsmm_identity_init(h, odd, 0, None) == ALIGN
         assert L.bsmm_identity_init(h, good, 9, None) == INVALID

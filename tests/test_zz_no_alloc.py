@@ -1,0 +1,63 @@
+"""The allocation-free weight gradient (bsmm_updat_noalloc) against bsmm_updat, through
+the C ABI: the same kernels with the library's fixed scratch in place of the caller's
+workspace, so the results must be identical bit for bit (and within the tolerance of
+the oracle).  Two calls in a row on one handle, the second with a smaller minibatch and
+fewer steps, on a layout whose dense weight-gradient tiles take the split path (the
+scratch is used), and on one that needs no scratch at all."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_matrix_amd as bs
+import oracle
+import synth
+from gpu_util import assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _band(R, width):
+    c = np.arange(R)
+    return (np.abs(c[:, None] - c[None, :]) <= width).astype(np.uint8)
+
+
+@pytest.mark.parametrize("b,fa,dtype,layout", [(32, 1, "bf16", "band"), (32, 0, "f16", "band"),
+                                                (16, 0, "f16", "random")])
+def test_noalloc_matches_updat(b, fa, dtype, layout):
+    rng = np.random.default_rng(77 + b + fa)
+    L = _band(64, 2) if layout == "band" else (rng.random((24, 20)) < 0.3).astype(np.uint8)
+    m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=fa)
+    h = m.handle
+    for call, (N, G) in enumerate([(512, 2), (256, 2)]):   # second call: a smaller input
+        print(f"case noalloc b={b} fa={fa} {dtype} {layout} call={call} N={N} G={G}", flush=True)
+        P = synth.random_problem(rng, L, b, N, fa, dtype, G=G, w_std=0.1)
+        xs = [dev(t) for t in P.xs]
+        dys = [dev(t) for t in P.dys]
+        need = bs.bsmm_workspace_size(h, 2, N, xs[0].dtype)
+        if layout == "band":
+            assert need > 0, "the band layout must take the split tile path"
+        ref = torch.empty(m.w_shape, dtype=torch.float32, device="cuda")
+        bs.bsmm_updat(h, xs, dys, ref, N)                  # also uploads the layout tables
+        got = torch.full(m.w_shape, float("nan"), device="cuda")
+        bs.bsmm_updat_noalloc(h, xs, dys, got, N)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "the allocation-free call differs from bsmm_updat"
+        bits = synth.to_bits
+        rdw = oracle.updat(L, b, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype)
+        assert_close(got, rdw, dtype, "updat_noalloc")
+
+
+def test_noalloc_needs_tables_on_the_device():
+    """Before any other call on the device the tables are not there: the call refuses
+    (it would have to allocate) and leaves dW untouched."""
+    L = _band(16, 1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    N = 64
+    x = torch.randn(N, 512, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(N, 512, device="cuda").to(torch.bfloat16)
+    dw = torch.full(m.w_shape, 3.0, device="cuda")
+    with pytest.raises(bs.BsmmError) as ei:
+        bs.bsmm_updat_noalloc(m.handle, [x], [dy], dw, N)
+    assert "allocating entry point" in str(ei.value)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 3.0)
