@@ -269,6 +269,7 @@ UpArgs up_args(const HostLut& L, int64_t N, int group) {
     a.split = 1;
     a.ntiles = (int32_t)(L.utiles.size() / 4);
     a.nrest = (int32_t)(L.urest.size() / 4);
+    a.ngroups = (int32_t)(L.ugroups.size() / 4);
     a.N = N;
     a.C = (int32_t)(L.R * L.b);
     a.K = (int32_t)(L.S * L.b);

@@ -84,7 +84,7 @@ inline int tile_split(int ntiles) {
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.
 enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2, MM_N64_W8, MM_ROWS };
-enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES };
+enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES, UP_RUNS };
 int mm_kind(const MMArgs& a, int dt, int b, int fa);
 const char* mm_kind_name(int kind);
 int updat_kind(const UpArgs& a, int dt, int b, int fa);

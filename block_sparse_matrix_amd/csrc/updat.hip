@@ -820,6 +820,245 @@ static hipError_t launch_updat_cfg(UpArgs a, int bpw, hipStream_t st) {
     return launch(BSMM_PASS_UPDAT, updat_kernel<DT, B, FA, D>, dim3((unsigned)grid), dim3(256), st, a);
 }
 
+// ---------------------------------------------------------------------------------
+// Short contractions (one step group of N <= 64 rows) with 32x32 blocks and
+// feature_axis 1.  A wave takes a run of RL consecutive ids of one layout row c (a part
+// of a row group): it loads the x slab of row c once, then for each block the dy slab
+// of its column, contracts over the N rows and writes the block.  Stores write whole 128-byte
+// dW rows: fp32 pairs output columns 2r, 2r+1 in lane r (the operand map of rows.hip),
+// 16-bit storage (operands through the transposing LDS read) passes the finished
+// block through a wave-private LDS tile.
+// Two consecutive dW values (as store_dw4: accumulate when asked, round once, stream).
+__device__ __forceinline__ void store_dw2(const UpArgs& a, int64_t idx, float v0, float v1) {
+    if (a.dwdt == BSMM_F32) {
+        if (a.acc) {
+            const float2 o = *reinterpret_cast<const float2*>((const float*)a.dw + idx);
+            v0 += o.x;
+            v1 += o.y;
+        }
+        __builtin_nontemporal_store(u32x2{__float_as_uint(v0), __float_as_uint(v1)},
+                                    reinterpret_cast<u32x2*>((float*)a.dw + idx));
+        return;
+    }
+    const bool bf = a.dwdt == BSMM_BF16;
+    if (a.acc) {
+        const uint32_t o = *reinterpret_cast<const uint32_t*>((const uint16_t*)a.dw + idx);
+        const uint32_t h0 = o & 0xffffu, h1 = o >> 16;
+        v0 += bf ? __uint_as_float(h0 << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h0);
+        v1 += bf ? __uint_as_float(h1 << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h1);
+    }
+    const uint32_t w = bf ? to_storage16<BSMM_BF16>(v0) | (to_storage16<BSMM_BF16>(v1) << 16)
+                          : to_storage16<BSMM_F16>(v0) | (to_storage16<BSMM_F16>(v1) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>((uint16_t*)a.dw + idx));
+}
+
+__device__ __forceinline__ u32x2 bload64u(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+template <int DT, int D, int RL>
+__global__ __launch_bounds__(256) void updr_kernel(UpArgs a) {
+    constexpr int B = 32;
+    constexpr bool F32 = DT == BSMM_F32;
+    constexpr int S = F32 ? 4 : 2;
+    // fp32: 4 chunks of 16 rows, 4 matrix-core steps of 4 rows each; 16-bit: 2 chunks
+    // of 32 rows, one step each
+    constexpr int NCH = F32 ? 4 : 2;
+    constexpr int PITCH = 40;            // staged 32-row chunk, 16-bit elements per row
+    constexpr int OPITCH = 36;           // finished block, floats per row
+    __shared__ __attribute__((aligned(16))) uint16_t stg[F32 ? 8 : 4 * 32 * PITCH];
+    __shared__ __attribute__((aligned(16))) float otl[F32 ? 4 : 4 * 32 * OPITCH];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    // wave -> (row group, run of RL of its blocks)
+    constexpr int RPG = (8 + RL - 1) / RL;   // runs per row group
+    const int wid = blockIdx.x * 4 + wave, gi = wid / RPG, ri = wid % RPG;
+    if (gi >= a.ngroups) return;   // no workgroup barrier in this kernel
+    const int4 grp = reinterpret_cast<const int4*>(a.groups)[gi];
+    const int first = grp.x + ri * RL, crow = grp.z;
+    const int cnt = grp.y - ri * RL < RL ? grp.y - ri * RL : RL;
+    if (cnt <= 0) return;
+    int kl = 0;
+    if (lane < cnt) kl = a.coords[2 * (first + lane) + 1];
+    const int N = (int)a.N;
+    const rsrc_t rx = make_rsrc(a.xs[0], a.x_bytes);
+    const rsrc_t ry = make_rsrc(a.dys[0], a.dy_bytes);
+    BSMM_LDS uint16_t* st = (BSMM_LDS uint16_t*)stg + wave * 32 * PITCH;
+    BSMM_LDS float* ot = (BSMM_LDS float*)otl + wave * 32 * OPITCH;
+
+    if constexpr (F32) {
+        // lane (r16, g), chunk ch, step v: row 16 ch + 4 v + g, columns 2 r16, 2 r16 + 1
+        uint32_t xo[NCH * 4], yo[NCH * 4];
+#pragma unroll
+        for (int i = 0; i < NCH * 4; i++) {
+            const int n = 4 * i + g;
+            xo[i] = n < N ? ((uint32_t)n * a.C + 2 * r16) * 4u : kOffLane;
+            yo[i] = n < N ? ((uint32_t)n * a.K + 2 * r16) * 4u : kOffLane;
+        }
+        u32x2 xf[NCH * 4];
+#pragma unroll
+        for (int i = 0; i < NCH * 4; i++) xf[i] = bload64u(rx, xo[i], (uint32_t)crow * (B * 4));
+        struct Slot {
+            u32x2 y[NCH * 4];
+        };
+        auto load = [&](Slot& sl, int j) {
+            const bool ok = j < cnt;
+            const int k = __builtin_amdgcn_readlane(kl, ok ? j : 0);
+            const uint32_t so = ok ? (uint32_t)k * (B * 4) : kOffOff;
+#pragma unroll
+            for (int i = 0; i < NCH * 4; i++) sl.y[i] = bload64u(ry, yo[i], so);
+        };
+        Slot ring[D];
+#pragma unroll
+        for (int i = 0; i < D; i++) {
+            load(ring[i], i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int j = 0; j < cnt; j += D) {
+#pragma unroll
+            for (int i = 0; i < D; i++) {
+                if (j + i < cnt) {
+                    f32x4 acc[2][2];
+#pragma unroll
+                    for (int pt = 0; pt < 2; pt++) acc[pt][0] = acc[pt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < NCH * 4; s++)
+#pragma unroll
+                        for (int pt = 0; pt < 2; pt++)
+#pragma unroll
+                            for (int qt = 0; qt < 2; qt++)
+                                acc[pt][qt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    __uint_as_float(xf[s][pt]), __uint_as_float(ring[i].y[s][qt]), acc[pt][qt], 0, 0, 0);
+                    // lane holds dW[p = 8 g + 2 v + pt][q = 2 r16 + qt]
+                    const int64_t base = (int64_t)(first + j + i) * B * B;
+#pragma unroll
+                    for (int pt = 0; pt < 2; pt++)
+#pragma unroll
+                        for (int v = 0; v < 4; v++)
+                            store_dw2(a, base + (8 * g + 2 * v + pt) * B + 2 * r16, acc[pt][0][v], acc[pt][1][v]);
+                }
+                load(ring[i], j + i + D);
+            }
+        }
+    } else {
+        // 16-byte chunk c = lane + 64 h of a 32-row chunk: row c / 4, columns 8 (c % 4) ..
+        uint32_t xo[NCH * 2], yo[NCH * 2];
+#pragma unroll
+        for (int i = 0; i < NCH * 2; i++) {
+            const int ch = i / 2, c = lane + 64 * (i % 2);
+            const int n = 32 * ch + (c >> 2);
+            xo[i] = n < N ? ((uint32_t)n * a.C + 8 * (c & 3)) * 2u : kOffLane;
+            yo[i] = n < N ? ((uint32_t)n * a.K + 8 * (c & 3)) * 2u : kOffLane;
+        }
+        auto frags = [&](const u32x4* v, u32x4* f) {   // two 32x32 tiles -> 2 chunks x 2 fragments
+#pragma unroll
+            for (int ch = 0; ch < NCH; ch++) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int c = lane + 64 * h;
+                    lds_store16(st + (c >> 2) * PITCH + 8 * (c & 3), v[ch * 2 + h]);
+                }
+                wave_lds_order();
+                f[ch * 2] = frag_tr16(st, PITCH, 0, lane);
+                f[ch * 2 + 1] = frag_tr16(st, PITCH, 16, lane);
+                wave_lds_order();
+            }
+        };
+        u32x4 xf[NCH * 2];
+        {
+            u32x4 xv[NCH * 2];
+#pragma unroll
+            for (int i = 0; i < NCH * 2; i++) xv[i] = bload128(rx, xo[i], (uint32_t)crow * (B * 2));
+            frags(xv, xf);
+        }
+        struct Slot {
+            u32x4 y[NCH * 2];
+        };
+        auto load = [&](Slot& sl, int j) {
+            const bool ok = j < cnt;
+            const int k = __builtin_amdgcn_readlane(kl, ok ? j : 0);
+            const uint32_t so = ok ? (uint32_t)k * (B * 2) : kOffOff;
+#pragma unroll
+            for (int i = 0; i < NCH * 2; i++) sl.y[i] = bload128(ry, yo[i], so);
+        };
+        Slot ring[D];
+#pragma unroll
+        for (int i = 0; i < D; i++) {
+            load(ring[i], i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int j = 0; j < cnt; j += D) {
+#pragma unroll
+            for (int i = 0; i < D; i++) {
+                if (j + i < cnt) {
+                    u32x4 yf[NCH * 2];
+                    frags(ring[i].y, yf);
+                    f32x4 acc[2][2];
+#pragma unroll
+                    for (int pt = 0; pt < 2; pt++) acc[pt][0] = acc[pt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ch = 0; ch < NCH; ch++)
+#pragma unroll
+                        for (int pt = 0; pt < 2; pt++)
+#pragma unroll
+                            for (int qt = 0; qt < 2; qt++) mma<DT>(acc[pt][qt], xf[ch * 2 + pt], yf[ch * 2 + qt]);
+                    // lane holds D[p = 16 pt + 4 g + v][q = 16 qt + r16]: through LDS so that
+                    // 8 lanes store one whole row
+#pragma unroll
+                    for (int pt = 0; pt < 2; pt++)
+#pragma unroll
+                        for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+                            for (int v = 0; v < 4; v++) ot[(16 * pt + 4 * g + v) * OPITCH + 16 * qt + r16] = acc[pt][qt][v];
+                    wave_lds_order();
+                    const int64_t base = (int64_t)(first + j + i) * B * B;
+#pragma unroll
+                    for (int h = 0; h < 4; h++) {
+                        const int row = 8 * h + (lane >> 3), col = 4 * (lane & 7);
+                        const f32x4 v = *reinterpret_cast<const BSMM_LDS f32x4*>(ot + row * OPITCH + col);
+                        store_dw4(a, base + row * B + col, v);
+                    }
+                    wave_lds_order();
+                }
+                load(ring[i], j + i + D);
+            }
+        }
+    }
+}
+
+template <int DT, int RL>
+static hipError_t launch_updat_runs_t(const UpArgs& a, hipStream_t st) {
+    const int64_t waves = (int64_t)a.ngroups * ((8 + RL - 1) / RL);
+    const int64_t grid = (waves + 3) / 4;
+    if (grid == 0) return hipSuccess;
+    return launch(BSMM_PASS_UPDAT, updr_kernel<DT, 2, RL>, dim3((unsigned)grid), dim3(256), st, a);
+}
+
+// Blocks per wave: 1 for fp32 (the contraction is the work: more waves hide more
+// latency), 2 for 16-bit storage (measured on the 4096-wide N = 64 workload among 1, 2,
+// 4 and 8: fp32 20.4 / 21.2 / 27.4 / 30.2 us, bf16 10.6 / 10.1 / 10.8 / 10.9 us).
+// BSMM_UPDAT_RUN=<1|2|4|8> (read once) overrides it for A/B measurements.
+static int updat_run_len(int dt) {
+    static const int forced = [] {
+        const char* e = getenv("BSMM_UPDAT_RUN");
+        return e ? atoi(e) : 0;
+    }();
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+    return dt == BSMM_F32 ? 1 : 2;
+}
+
+template <int DT>
+static hipError_t launch_updat_runs(const UpArgs& a, hipStream_t st) {
+    switch (updat_run_len(DT)) {
+    case 1: return launch_updat_runs_t<DT, 1>(a, st);
+    case 2: return launch_updat_runs_t<DT, 2>(a, st);
+    case 8: return launch_updat_runs_t<DT, 8>(a, st);
+    default: return launch_updat_runs_t<DT, 4>(a, st);
+    }
+}
+
 template <int DT, int B, int FA>
 static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
     switch (kind) {
@@ -832,6 +1071,9 @@ static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
     case UP_D2B8: return launch_updat_cfg<DT, B, FA, 2>(a, 8, st);
     case UP_D1B4: return launch_updat_cfg<DT, B, FA, 1>(a, 4, st);
     case UP_TILES: return launch_updat_tiles<DT, B, FA>(a, st);
+    case UP_RUNS:
+        if constexpr (B == 32 && FA == 1) return launch_updat_runs<DT>(a, st);
+        break;
     }
     return hipErrorInvalidValue;
 }
@@ -844,7 +1086,13 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
     const bool tiles_ok = b == 32 && dt != BSMM_F32 && a.ntiles > 0 && steps0 >= 16 && (fa == 1 || a.N % 8 == 0);
     // enough workgroups (tiles x contraction parts) to occupy at least half the CUs
     const bool tiles_wide = a.ntiles * a.split >= 128;
-    if (a.force > 0) return a.force == UP_TILES && !tiles_ok ? -1 : a.force;
+    // one step group of at most 64 rows, 32x32 blocks, features last: row runs
+    const bool runs_ok = b == 32 && fa == 1 && a.G == 1 && a.N > 0 && a.N <= 64 && a.ngroups > 0;
+    if (a.force > 0) {
+        if (a.force == UP_TILES && !tiles_ok) return -1;
+        if (a.force == UP_RUNS && !runs_ok) return -1;
+        return a.force;
+    }
     switch (updat_variant()) {
     case 1: return UP_D2B1;
     case 2: return UP_D4B1;
@@ -860,6 +1108,7 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
     default: break;
     }
     if (tiles_ok && tiles_wide) return UP_TILES;
+    if (runs_ok) return UP_RUNS;
     const int KS = dt == BSMM_F32 ? 16 : 32;
     const int64_t steps = (int64_t)a.G * ((a.N + KS - 1) / KS);
     // Long contractions: row groups, 4 waves per block group.
@@ -872,7 +1121,7 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
 }
 
 int updat_kind_of_name(const char* name) {
-    for (int k = UP_D2B1; k <= UP_TILES; k++)
+    for (int k = UP_D2B1; k <= UP_RUNS; k++)
         if (std::strcmp(name, updat_kind_name(k)) == 0) return k;
     return 0;
 }
@@ -888,6 +1137,7 @@ const char* updat_kind_name(int kind) {
     case UP_D2B8: return "blocks_8perwave";
     case UP_D1B4: return "blocks_4perwave_noring";
     case UP_TILES: return "dense_tiles";
+    case UP_RUNS: return "row_runs";
     }
     return "none";
 }

@@ -204,12 +204,14 @@ def test_kernel_choice_names():
     assert m8.kernel_name("fprop", 4096, torch.bfloat16) == "list_weight_stack"
     assert m8.kernel_name("fprop", 512, torch.bfloat16) == "list_rows128"
     assert m32.kernel_name("fprop", 0, torch.bfloat16) == "none"
-    assert m32.kernel_name("updat", 64, torch.bfloat16) in ("blocks_1perwave", "blocks_2perwave")
+    assert m32.kernel_name("updat", 64, torch.bfloat16) == "row_runs"
     assert m32.kernel_name("updat", 4096, torch.bfloat16, group=8) == "row_groups"   # 4 tiles only
     big = bs.BlocksparseMatMul((rng.random((128, 128)) < 0.5).astype(np.uint8), block_size=32)
     assert big.kernel_name("updat", 4096, torch.bfloat16) == "dense_tiles"
     assert big.kernel_name("updat", 4096, torch.float32) == "row_groups"
-    assert big.kernel_name("updat", 64, torch.bfloat16) == "blocks_2perwave"
+    assert big.kernel_name("updat", 64, torch.bfloat16) == "row_runs"
+    assert big.kernel_name("updat", 64, torch.bfloat16, group=2) == "blocks_2perwave"
+    assert big.kernel_name("updat", 65, torch.float32) == "blocks_2perwave"
     assert m8.kernel_name("updat", 4096, torch.bfloat16) == "row_groups"
     assert m32.kernel_name("identity", 0, torch.bfloat16) == "identity"
     # 256x256 layouts at N = 4096: the output groups take sparse layouts once there

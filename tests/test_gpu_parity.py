@@ -346,9 +346,11 @@ def test_updat_dense_tiles_unsplit(fa):
 
 @pytest.mark.parametrize("dw_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("b,fa,dtype,N,G,kind", [
-    (32, 1, "bf16", 64, 1, None),            # blocks per wave, short contraction
+    (32, 1, "bf16", 64, 1, None),            # row runs (one step group, N <= 64)
     (16, 0, "f16", 200, 2, None),
     (32, 1, "f32", 37, 1, None),
+    (32, 1, "f32", 64, 1, "blocks_2perwave"),
+    (32, 1, "f16", 20, 1, "row_runs"),
     (8, 0, "bf16", 1000, 1, "row_groups"),
     (8, 1, "f32", 600, 3, "row_groups"),
     (32, 0, "bf16", 520, 2, "dense_tiles"),  # split tiles: partials in the workspace, then their sum
@@ -380,6 +382,33 @@ def test_updat_accumulate(b, fa, dtype, N, G, kind, dw_dtype):
             [dev(t[:0] if fa == 1 else t[:, :0]) for t in P.dys], out=out, accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(out, before)
+
+
+@pytest.mark.parametrize("N", [1, 16, 33, 64])
+@pytest.mark.parametrize("dtype,dw_dtype", [("f32", "f32"), ("bf16", "f32"), ("f16", "f32"), ("f32", "bf16"),
+                                            ("bf16", "f16")])
+def test_updat_row_runs(N, dtype, dw_dtype):
+    """The short-contraction weight gradient (32x32 blocks, features last, one step group
+    of N <= 64 rows): row groups of up to 8 blocks, a row group that is a whole row's
+    single block, empty rows; every gradient dtype; bit-reproducible."""
+    print(f"case row_runs N={N} {dtype} dw={dw_dtype}", flush=True)
+    rng = np.random.default_rng(900 + N)
+    L = (rng.random((20, 24)) < 0.4).astype(np.uint8)
+    L[3, :] = 1          # a 24-block row: three full row groups
+    L[5, :] = 0
+    L[5, 7] = 1          # a row of one block
+    L[8, :] = 0          # an empty row
+    P = synth.random_problem(rng, L, 32, N, 1, dtype, G=1, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    assert m.kernel_name("updat", N, TORCH_DT[dtype]) == "row_runs"
+    xs, dys = [dev(P.xs[0])], [dev(P.dys[0])]
+    dw = m.updat(xs, dys, dw_dtype=TORCH_DT[dw_dtype])
+    dw2 = m.updat(xs, dys, dw_dtype=TORCH_DT[dw_dtype])
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    ref = oracle.updat(L, 32, 1, [bits(P.xs[0])], [bits(P.dys[0])], N, dtype)
+    assert_close(dw, ref, "f32" if dtype == "f32" and dw_dtype == "f32" else "bf16", "updat row_runs")
+    assert torch.equal(dw, dw2)
 
 
 @pytest.mark.parametrize("group_size", [8, 4])
