@@ -66,6 +66,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--pass-only", choices=PASSES, default=None,
+                    help="only launch this pass, --steps times over the rotating buffer sets after --warmup "
+                         "launches, and print its kernel time (for per-pass rocprofv3 counter runs)")
+    ap.add_argument("--floor", action="store_true",
+                    help="only time plain device reads, writes and copies of the benchmark's byte counts "
+                         "(torch kernels over rotating buffers): the practical HBM floor at these sizes")
     return ap.parse_args()
 
 
@@ -356,6 +362,96 @@ def roofline_of(per, workload, dtype):
             "alg_bytes_per_launch": d["alg_bytes"], "flops_per_launch": d["flops"]}
 
 
+def run_pass_only(args, name, dtype):
+    """One pass of the workload, args.steps launches over rotating buffer sets (cold), after
+    args.warmup: the per-pass kernel time, and a clean dispatch list for counter runs."""
+    import torch
+    import block_sparse_matrix_amd as bs
+    import synth
+    P = synth.workload_problem(name, dtype)
+    m = bs.BlocksparseMatMul(P.layout, block_size=P.block, feature_axis=P.fa)
+    h, N, G = m.handle, P.N, len(P.xs)
+    dev = torch.device("cuda", 0)
+    p = args.pass_only
+    code = {"fprop": 0, "bprop": 1, "updat": 2}[p]
+    cost = pass_cost(P, dtype)
+    w0 = P.w.to(dev)
+    if p == "fprop":
+        ins, outs = [P.xs[0].to(dev)], torch.empty(m.o_shape(N), dtype=w0.dtype, device=dev)
+    elif p == "bprop":
+        ins, outs = [P.dys[0].to(dev)], torch.empty(m.i_shape(N), dtype=w0.dtype, device=dev)
+    else:
+        ins = [t.to(dev) for t in P.xs] + [t.to(dev) for t in P.dys]
+        outs = torch.empty(m.w_shape, dtype=torch.float32, device=dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in ins) + outs.numel() * outs.element_size() \
+        + (w0.numel() * w0.element_size() if p != "updat" else 0)
+    R = max(1, min(64, int(np.ceil(args.rotate_mib * 2**20 / cost[p][1])), (16 << 30) // set_bytes))
+    sets = [([t.clone() for t in ins], w0.clone() if p != "updat" else None, torch.empty_like(outs)) for _ in range(R)]
+    nb = bs.bsmm_workspace_size(h, code, N, w0.dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+    def launch(s):
+        i, w, o = s
+        if p == "fprop":
+            bs.bsmm_fprop(h, i[0], w, o, N, ws=ws)
+        elif p == "bprop":
+            bs.bsmm_bprop(h, i[0], w, o, N, ws=ws)
+        else:
+            bs.bsmm_updat(h, i[:G], i[G:], o, N, ws=ws)
+
+    for i in range(args.warmup):
+        launch(sets[i % R])
+    torch.cuda.synchronize()
+    bs.bsmm_profile_begin()
+    for i in range(args.steps):
+        launch(sets[i % R])
+    torch.cuda.synchronize()
+    tot, cnt = bs.bsmm_profile_end()[p]
+    us = tot / cnt * 1e3
+    flops, nbytes = cost[p]
+    bound, tstar = roof(flops, nbytes, dtype)
+    print(json.dumps({"workload": name, "dtype": dtype, "pass": p, "kernel": m.kernel_name(p, N, w0.dtype, G if p == "updat" else 1),
+                      "launches": args.steps, "warmup": args.warmup, "buffer_sets_rotated": R, "kernel_us": round(us, 3),
+                      "alg_bytes": int(nbytes), "flops": int(flops), "bound": bound,
+                      "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 4)}))
+
+
+def run_floor(args):
+    """Plain streaming kernels (torch) at the benchmark's sizes, cold over rotating buffers:
+    read (sum) of |W| bf16 and fp32, write (fill) of |dW| fp32, copy of |W| bf16."""
+    import torch
+    out = {}
+    for label, nbytes, op in (("read_17.8MB", 17807360, "sum"), ("read_35.6MB", 35614720, "sum"),
+                              ("write_33.5MB", 33554432, "fill"), ("copy_17.8MB", 17807360, "copy")):
+        n = nbytes // 4
+        R = max(2, (1 << 30) // nbytes)
+        bufs = [torch.ones(n, device="cuda") for _ in range(R)]
+        dst = [torch.empty(n, device="cuda") for _ in range(R)] if op == "copy" else None
+        acc = torch.empty((), device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+        def go(i):
+            if op == "sum":
+                torch.sum(bufs[i % R], 0, out=acc)
+            elif op == "fill":
+                bufs[i % R].fill_(2.0)
+            else:
+                dst[i % R].copy_(bufs[i % R])
+
+        for i in range(args.warmup):
+            go(i)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record()
+            go(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[len(ev) // 2]
+        out[label] = {"bytes": nbytes, "median_us_events": round(us, 3), "op": op}
+    print(json.dumps({"floor": out, "note": "torch kernels; the rocprofv3 kernel trace of this command gives "
+                                            "their GPU durations"}))
+
+
 def run_layer_norm(reps=20):
     """Kernel time of layer_norm and its gradient on the band workload's activation
     (N = 4096 vectors of C = 8192 bf16 features), both feature axes, over rotating buffer
@@ -536,6 +632,14 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.floor:
+        run_floor(args)
+        return
+    if args.pass_only:
+        import synth
+        wl = synth.WORKLOADS[args.workload]
+        run_pass_only(args, args.workload, args.dtype or wl.dtypes[0])
         return
     import torch
     import synth

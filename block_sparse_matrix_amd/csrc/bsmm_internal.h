@@ -54,7 +54,8 @@ struct HostLut {
     // 0, 0.  gptr holds groups+1 entry offsets.
     std::vector<int32_t> cgptr, cgent, rgptr, rgent;
     // Weight-gradient tiles (32x32 blocks only): utiles (r0, c0, blocks, first) per
-    // tile with at least kTileMin blocks, row-major tile order; utblk holds, per such
+    // tile with at least kTileMin blocks, in super-block order (kSuperRows x kSuperCols
+    // tiles, row-major within and between super-blocks); utblk holds, per such
     // tile from index first, the ids of its 8x8 positions row-major (-1 where absent);
     // the other blocks in urest row groups (first, count, row, 1), whose ids are
     // urids[first .. first+count-1].

@@ -7,6 +7,7 @@
 // are the row-major rank of a nonzero.
 #include <algorithm>
 #include <numeric>
+#include <tuple>
 
 #include "bsmm_internal.h"
 
@@ -167,6 +168,25 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
                     if (id >= 0) in_tile[id] = 1;
                 L.utblk.insert(L.utblk.end(), pos.begin(), pos.end());
             }
+        // Processing order of the tiles: super-blocks of kSuperRows tile rows x kSuperCols
+        // tile columns, row-major within and between super-blocks.  The weight-gradient
+        // kernel hands each XCD a contiguous range of this order, so the tiles an XCD runs
+        // at once form a compact block whose x rows and dy columns it reads from one L2
+        // (in plain row-major order they were one tile row x every tile column, and each
+        // dy column was fetched again for every tile row).
+        {
+            std::vector<int32_t> ord(L.utiles.size() / 4);
+            std::iota(ord.begin(), ord.end(), 0);
+            auto key = [&](int32_t i) {
+                const int64_t tr = L.utiles[4 * i] / kTileSide, tc = L.utiles[4 * i + 1] / kTileSide;
+                return std::make_tuple(tr / kSuperRows, tc / kSuperCols, tr, tc);
+            };
+            std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return key(x) < key(y); });
+            std::vector<int32_t> sorted;
+            sorted.reserve(L.utiles.size());
+            for (int32_t i : ord) sorted.insert(sorted.end(), L.utiles.begin() + 4 * i, L.utiles.begin() + 4 * i + 4);
+            L.utiles.swap(sorted);
+        }
         for (int64_t c = 0; c < R; c++) {
             int32_t n = 0;
             for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++) {

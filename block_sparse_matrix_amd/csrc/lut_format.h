@@ -18,5 +18,8 @@ constexpr int kGroupMaxSteps = 1024;   // longest group walk the group kernels t
 constexpr int kTileSide = 8;
 constexpr int kTileMin = 16;
 constexpr int kTileWaves = 8;   // a tile's blocks are split over 8 waves, in order
+// Tiles are processed in super-blocks of kSuperRows x kSuperCols tiles (layout.cpp).
+constexpr int kSuperRows = 4;
+constexpr int kSuperCols = 8;
 
 }  // namespace bsmm

@@ -77,7 +77,9 @@ typedef enum {
     BSMM_ERR_OOM = 5            /* host or device allocation failed */
 } bsmm_status;
 
-typedef enum { BSMM_F32 = 0, BSMM_BF16 = 1, BSMM_F16 = 2 } bsmm_dtype;
+/* BSMM_DTYPE_MAX_ENUM is not a dtype: it makes every int value a valid bsmm_dtype, so the
+ * calls can reject an unknown code with BSMM_ERR_INVALID_ARG. */
+typedef enum { BSMM_F32 = 0, BSMM_BF16 = 1, BSMM_F16 = 2, BSMM_DTYPE_MAX_ENUM = 0x7fffffff } bsmm_dtype;
 
 typedef enum {
     BSMM_PASS_FPROP = 0,
@@ -238,8 +240,9 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  *                     absent), 0, 0)
  *         14 rgptr    (block size 32 only: ceil(R/8)+1 offsets into rgent)
  *         15 rgent    (the same for groups of 8 block rows, walking k ascending)
- *         16 utiles   (block size 32 only: 4 per weight-gradient tile, row-major tile
- *                     order: first block row, first block column, block count, index
+ *         16 utiles   (block size 32 only: 4 per weight-gradient tile, in super-blocks
+ *                     of 4 x 8 tiles, row-major within and between super-blocks: first
+ *                     block row, first block column, block count, index
  *                     of its first entry in utblk; tiles are 8x8 blocks of the layout
  *                     holding at least 16 blocks)
  *         17 utblk    (64 per tile: the ids of its 8x8 positions, row-major, -1 where
