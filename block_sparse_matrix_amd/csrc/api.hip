@@ -109,11 +109,12 @@ bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out, bool m
                     "the layout tables are not on this device yet and this call allocates nothing: make one call "
                     "of an allocating entry point on this device first");
     const HostLut& L = h->lut;
-    constexpr int NP = 20;
+    constexpr int NP = 23;
     const std::vector<int32_t>* parts[NP] = {&L.coords,  &L.colptr,   &L.colent,   &L.rowptr,  &L.rowent,
                                              &L.colorder, &L.roworder, &L.colwork, &L.rowwork, &L.ugroups,
                                              &L.colrec,  &L.rowrec,   &L.cgptr,    &L.cgent,   &L.rgptr,
-                                             &L.rgent,   &L.utiles,   &L.utblk,    &L.urest,   &L.urids};
+                                             &L.rgent,   &L.utiles,   &L.utblk,    &L.urest,   &L.urids,
+                                             &L.stiles,  &L.stmask,   &L.stids};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -151,6 +152,10 @@ bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out, bool m
     d.utblk = (const int32_t*)(b + off[17]);
     d.urest = (const int32_t*)(b + off[18]);
     d.urids = (const int32_t*)(b + off[19]);
+    d.stiles = (const int32_t*)(b + off[20]);
+    d.stmask = (const int32_t*)(b + off[21]);
+    d.stids = (const int32_t*)(b + off[22]);
+    d.nstiles = (int32_t)(L.stiles.size() / 4);
     d.nutiles = (int32_t)(L.utiles.size() / 4);
     d.nurest = (int32_t)(L.urest.size() / 4);
     d.nugroups = (int32_t)(L.ugroups.size() / 4);
@@ -270,6 +275,7 @@ UpArgs up_args(const HostLut& L, int64_t N, int group) {
     a.ntiles = (int32_t)(L.utiles.size() / 4);
     a.nrest = (int32_t)(L.urest.size() / 4);
     a.ngroups = (int32_t)(L.ugroups.size() / 4);
+    a.nstiles = (int32_t)(L.stiles.size() / 4);
     a.N = N;
     a.C = (int32_t)(L.R * L.b);
     a.K = (int32_t)(L.S * L.b);
@@ -462,6 +468,9 @@ bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* 
     a.rest = d->urest;
     a.rids = d->urids;
     a.nrest = d->nurest;
+    a.stiles = d->stiles;
+    a.stmask = d->stmask;
+    a.stids = d->stids;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     a.force = h->force[BSMM_PASS_UPDAT];
     {   // a contraction split of the tiles needs the workspace; without it, no split
@@ -607,7 +616,10 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 17: v = &L.utblk; break;
     case 18: v = &L.urest; break;
     case 19: v = &L.urids; break;
-    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 19]");
+    case 20: v = &L.stiles; break;
+    case 21: v = &L.stmask; break;
+    case 22: v = &L.stids; break;
+    default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 22]");
     }
     *len = (int64_t)v->size();
     const int64_t n = cap < *len ? cap : *len;

@@ -60,6 +60,9 @@ struct HostLut {
     // the other blocks in urest row groups (first, count, row, 1), whose ids are
     // urids[first .. first+count-1].
     std::vector<int32_t> utiles, utblk, urest, urids;
+    // Small-block weight-gradient tiles (8x8 and 16x16 blocks; format in lut_format.h):
+    // stiles (4 per tile), stmask (16 per tile), stids (256 or 1024 per tile).
+    std::vector<int32_t> stiles, stmask, stids;
 };
 
 // Builds every table above.  Pure host code: never touches HIP.  Returns false with a
@@ -92,6 +95,10 @@ struct DeviceLut {
     const int32_t* urest = nullptr;
     const int32_t* urids = nullptr;
     int32_t nutiles = 0, nurest = 0;
+    const int32_t* stiles = nullptr;
+    const int32_t* stmask = nullptr;
+    const int32_t* stids = nullptr;
+    int32_t nstiles = 0;
 };
 
 }  // namespace bsmm

@@ -70,6 +70,11 @@ struct UpArgs {
     int32_t split;          // tiles: contraction split in this many parts (1: none)
     float* ws;              // tiles with split > 1: fp32 partial sums, split*ntiles*64 blocks
     int32_t acc;            // 1: add the sum to what dw holds (dW += ...); 0: overwrite
+    // 8x8 and 16x16 blocks: small-block tiles (lut_format.h)
+    const int32_t* stiles;
+    const int32_t* stmask;
+    const int32_t* stids;
+    int32_t nstiles;
 };
 
 // Contraction split of the weight-gradient tiles: enough parts to give ~256 workgroups,
@@ -84,7 +89,7 @@ inline int tile_split(int ntiles) {
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.
 enum MMKind { MM_N16 = 1, MM_N64, MM_MID, MM_STACK, MM_GROUPS, MM_V_W16, MM_V_STACK1, MM_V_STACK2, MM_N64_W8, MM_ROWS };
-enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES, UP_RUNS };
+enum UpKind { UP_D2B1 = 1, UP_D1B2, UP_ROWS, UP_D4B1, UP_D2B2, UP_D2B4, UP_D2B8, UP_D1B4, UP_TILES, UP_RUNS, UP_STILES };
 int mm_kind(const MMArgs& a, int dt, int b, int fa);
 const char* mm_kind_name(int kind);
 int updat_kind(const UpArgs& a, int dt, int b, int fa);

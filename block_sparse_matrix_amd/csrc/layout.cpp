@@ -6,6 +6,7 @@
 // ones and a block size of 8, 16 or 32; block_coord maps a block id to (c, k).  Ids
 // are the row-major rank of a nonzero.
 #include <algorithm>
+#include <array>
 #include <numeric>
 #include <tuple>
 
@@ -197,6 +198,51 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
                 L.urest[L.urest.size() - 3]++;
                 n = n == 7 ? 0 : n + 1;
             }
+        }
+    }
+    if (b == 8 || b == 16) {
+        // small-block weight-gradient tiles (lut_format.h), in super-block order
+        const int64_t TB = kSmallTileFeat / b;          // blocks per tile side
+        const int64_t QB = b == 8 ? 2 : 1;              // blocks per quad side
+        const int64_t TR = (R + TB - 1) / TB, TC = (S + TB - 1) / TB;
+        std::vector<std::array<int64_t, 2>> order;
+        for (int64_t tr = 0; tr < TR; tr++)
+            for (int64_t tc = 0; tc < TC; tc++) order.push_back({tr, tc});
+        std::stable_sort(order.begin(), order.end(), [](const std::array<int64_t, 2>& x, const std::array<int64_t, 2>& y) {
+            return std::make_tuple(x[0] / kSuperRows, x[1] / kSuperCols, x[0], x[1]) <
+                   std::make_tuple(y[0] / kSuperRows, y[1] / kSuperCols, y[0], y[1]);
+        });
+        // id of block (c, k), -1 if absent: rows are consecutive ids
+        auto block_id = [&](int64_t c, int64_t k) -> int32_t {
+            if (c >= R || k >= S) return -1;
+            const int32_t* beg = L.rowent.data() + 2 * L.rowptr[c];
+            int32_t lo = 0, hi = L.rowptr[c + 1] - L.rowptr[c];
+            while (lo < hi) {   // entries ascending in k
+                const int32_t mid = (lo + hi) / 2;
+                if (beg[2 * mid] < k) lo = mid + 1; else hi = mid;
+            }
+            return lo < L.rowptr[c + 1] - L.rowptr[c] && beg[2 * lo] == k ? beg[2 * lo + 1] : -1;
+        };
+        for (const auto& tcell : order) {
+            const int64_t tr = tcell[0], tc = tcell[1];
+            std::vector<int32_t> ids(kSmallQuads * kSmallQuads * QB * QB, -1), mask(kSmallQuads, 0);
+            int32_t n = 0;
+            for (int64_t qi = 0; qi < kSmallQuads; qi++)
+                for (int64_t qj = 0; qj < kSmallQuads; qj++)
+                    for (int64_t di = 0; di < QB; di++)
+                        for (int64_t dj = 0; dj < QB; dj++) {
+                            const int32_t id = block_id(tr * TB + qi * QB + di, tc * TB + qj * QB + dj);
+                            ids[((qi * kSmallQuads + qj) * QB + di) * QB + dj] = id;
+                            if (id >= 0) {
+                                mask[qi] |= 1 << qj;
+                                n++;
+                            }
+                        }
+            if (n == 0) continue;
+            L.stiles.insert(L.stiles.end(), {(int32_t)(tr * kSmallTileFeat), (int32_t)(tc * kSmallTileFeat),
+                                             (int32_t)L.stids.size(), 0});
+            L.stmask.insert(L.stmask.end(), mask.begin(), mask.end());
+            L.stids.insert(L.stids.end(), ids.begin(), ids.end());
         }
     }
     out = std::move(L);

@@ -22,4 +22,13 @@ constexpr int kTileWaves = 8;   // a tile's blocks are split over 8 waves, in or
 constexpr int kSuperRows = 4;
 constexpr int kSuperCols = 8;
 
+// Weight-gradient tiles of small blocks (8x8 and 16x16): 256 x 256 features of the
+// layout, cut into 16 x 16 quads of 16 x 16 features (one 16x16 block, or 2 x 2 blocks
+// of 8x8).  Per tile with any block: (first x feature, first dy feature, index of its
+// first id, 0); per tile 16 quad-row masks (bit j: quad column j holds a block); per
+// tile 256 quads x (1 or 4) ids, row-major quads, blocks within a quad row-major, -1
+// where absent.
+constexpr int kSmallTileFeat = 256;
+constexpr int kSmallQuads = 16;
+
 }  // namespace bsmm

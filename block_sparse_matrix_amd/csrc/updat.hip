@@ -1059,6 +1059,168 @@ static hipError_t launch_updat_runs(const UpArgs& a, hipStream_t st) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Small blocks (8x8, 16x16), features first (x, dy stored (features, N)), 16-bit, long
+// contractions.  A workgroup (16 waves) owns one tile of 256 x 256 features of the
+// layout; per step of 32 minibatch columns it stages the tile's 256 dy feature rows in
+// LDS once (16 KB, every thread one 16-byte load) and each wave loads the 16 x feature
+// rows of its quad row straight into a fragment (features first: the contraction index
+// is contiguous).  The wave then runs one 16x16x32 matrix-core step per present quad of
+// its row (a quad is one 16x16 block, or 2 x 2 blocks of 8x8), the dy fragment read from
+// LDS; the quad's fp32 sums stay in registers (slot = quad column) for the whole
+// contraction.  Loads run RD steps ahead in registers, the LDS stage is double
+// buffered: one barrier per step.  Each block has one writer; no atomics.
+template <int DT, int B, int RD, int QG>
+__global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
+    constexpr int TF = kSmallTileFeat, Q = kSmallQuads, KS = 32, IPQ = B == 8 ? 4 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t stg[2][TF * KS];
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // quad row
+    const int r16 = lane & 15, g = lane >> 4;
+    // tiles in super-block order, XCD x taking the x-th contiguous range
+    const int per = (a.nstiles + 7) / 8;
+    const int ti = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (ti >= a.nstiles) return;   // whole workgroup
+    const int4 tl = reinterpret_cast<const int4*>(a.stiles)[ti];
+    const int fx0 = tl.x, fy0 = tl.y, first = tl.z;
+    const int mask = __builtin_amdgcn_readfirstlane(a.stmask[ti * Q + w]);
+    const int N = (int)a.N;
+    const int spt = N / KS + (N % KS ? 1 : 0);
+    const int nsteps = a.G * spt;
+
+    // x fragment: feature fx0 + 16 w + r16, columns n0 + 8 g ..; dy stage: thread t ->
+    // feature fy0 + t / 4, columns n0 + 8 (t % 4) ..  (N % 8 == 0: an 8-column chunk is
+    // all in or all out)
+    const int fx = fx0 + 16 * w + r16, fy = fy0 + (t >> 2), cy = t & 3;
+    const uint32_t xo = fx < a.C ? (uint32_t)fx * N * 2u + 16u * g : kOffLane;
+    const uint32_t yo = fy < a.K ? (uint32_t)fy * N * 2u + 16u * cy : kOffLane;
+    const int ql = (t >> 2) * KS + ((cy ^ bswz(t >> 2)) << 3);   // stage slot of thread t
+    struct Slot {
+        u32x4 x, y;
+    };
+    auto issue = [&](Slot& sl, int s, auto& pick) {
+        const bool sv = s < nsteps;   // uniform
+        const int ss = sv ? s : 0;
+        const int tt = ss / spt, n0 = (ss % spt) * KS;
+        rsrc_t rx, ry;
+        pick(a, tt, rx, ry);
+        const uint32_t so = sv ? (uint32_t)n0 * 2u : kOffOff;
+        // a chunk past N is switched off with the top offset bit (no branch)
+        const uint32_t offx = ((uint32_t)(N - 1 - n0 - 8 * g) >> 31) << 31;
+        const uint32_t offy = ((uint32_t)(N - 1 - n0 - 8 * cy) >> 31) << 31;
+        sl.x = bload128(rx, xo | offx, so);
+        sl.y = bload128(ry, yo | offy, so);
+    };
+    // dy fragment of quad column j: rows 16 j + r16 of the stage, columns 8 g ..
+    int boff[Q];
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        const int r = 16 * j + r16;
+        boff[j] = r * KS + ((g ^ bswz(r)) << 3);
+    }
+    f32x4 acc[Q];
+#pragma unroll
+    for (int j = 0; j < Q; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto run = [&](auto&& pick) {
+        Slot ring[RD];
+#pragma unroll
+        for (int i = 0; i < RD; i++) {
+            issue(ring[i], i, pick);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_store16((BSMM_LDS uint16_t*)stg[0] + ql, ring[0].y);
+        __syncthreads();
+        for (int s0 = 0; s0 < nsteps; s0 += RD) {
+#pragma unroll
+            for (int i = 0; i < RD; i++) {
+                const int s = s0 + i;
+                const BSMM_LDS uint16_t* cur = (const BSMM_LDS uint16_t*)stg[s & 1];
+                if (s < nsteps) {
+                    // quad columns in groups of QG: the group's LDS reads are issued
+                    // together, so one wait covers them
+#pragma unroll
+                    for (int j0 = 0; j0 < Q; j0 += QG) {
+                        u32x4 bf[QG];
+#pragma unroll
+                        for (int jj = 0; jj < QG; jj++)
+                            if ((mask >> (j0 + jj)) & 1) bf[jj] = *reinterpret_cast<const BSMM_LDS u32x4*>(cur + boff[j0 + jj]);
+#pragma unroll
+                        for (int jj = 0; jj < QG; jj++)
+                            if ((mask >> (j0 + jj)) & 1) mma<DT>(acc[j0 + jj], ring[i].x, bf[jj]);   // D[x f][dy f]
+                    }
+                }
+                // stage step s + 1 (loaded RD - 1 steps ago), then refill this slot
+                BSMM_LDS uint16_t* nxt = (BSMM_LDS uint16_t*)stg[(s + 1) & 1];
+                lds_store16(nxt + ql, ring[(i + 1) % RD].y);
+                issue(ring[i], s + RD, pick);
+                __syncthreads();
+            }
+        }
+    };
+    if (a.G == 1) {
+        PickOne p1 = pick_one(a);
+        run(p1);
+    } else {
+        PickMany pm;
+        run(pm);
+    }
+
+    // lane holds D[4 g + v][r16] of each present quad: x feature 4 g + v, dy feature r16
+    const int* ids = a.stids + first + w * Q * IPQ;
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        if (!((mask >> j) & 1)) continue;   // uniform
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int p = 4 * g + v, q = r16;
+            int id;
+            int64_t e;
+            if constexpr (B == 16) {
+                id = ids[j];
+                e = p * 16 + q;
+            } else {
+                id = ids[j * 4 + (p >> 3) * 2 + (q >> 3)];
+                e = (p & 7) * 8 + (q & 7);
+            }
+            if (id >= 0) {
+                const int64_t idx = (int64_t)id * B * B + e;
+                if (a.acc) {
+                    float o;
+                    if (a.dwdt == BSMM_F32) o = ((const float*)a.dw)[idx];
+                    else {
+                        const uint32_t h = ((const uint16_t*)a.dw)[idx];
+                        o = a.dwdt == BSMM_BF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+                    }
+                    store_elt(a.dw, idx, acc[j][v] + o, a.dwdt);
+                } else {
+                    store_elt(a.dw, idx, acc[j][v], a.dwdt);
+                }
+            }
+        }
+    }
+}
+
+template <int DT, int B>
+static hipError_t launch_updat_small_tiles(const UpArgs& a, hipStream_t st) {
+    if constexpr (DT == BSMM_F32 || (B != 8 && B != 16)) {
+        return hipErrorInvalidValue;
+    } else {
+        const int grid = ((a.nstiles + 7) / 8) * 8;
+        if (grid == 0) return hipSuccess;
+        static const int qg = [] {
+            const char* e = getenv("BSMM_STILES_QG");   // A/B measurements: quad columns per LDS batch
+            return e ? atoi(e) : 1;
+        }();
+        switch (qg) {
+        case 1: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 1>, dim3((unsigned)grid), dim3(1024), st, a);
+        case 2: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 2>, dim3((unsigned)grid), dim3(1024), st, a);
+        case 8: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 8>, dim3((unsigned)grid), dim3(1024), st, a);
+        default: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 4>, dim3((unsigned)grid), dim3(1024), st, a);
+        }
+    }
+}
+
 template <int DT, int B, int FA>
 static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
     switch (kind) {
@@ -1074,6 +1236,9 @@ static hipError_t launch_updat_t(const UpArgs& a, int kind, hipStream_t st) {
     case UP_RUNS:
         if constexpr (B == 32 && FA == 1) return launch_updat_runs<DT>(a, st);
         break;
+    case UP_STILES:
+        if constexpr (B < 32 && FA == 0) return launch_updat_small_tiles<DT, B>(a, st);
+        break;
     }
     return hipErrorInvalidValue;
 }
@@ -1088,9 +1253,13 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
     const bool tiles_wide = a.ntiles * a.split >= 128;
     // one step group of at most 64 rows, 32x32 blocks, features last: row runs
     const bool runs_ok = b == 32 && fa == 1 && a.G == 1 && a.N > 0 && a.N <= 64 && a.ngroups > 0;
+    // small blocks, features first, 16-bit, whole 8-column chunks, >= 8 steps of 32
+    const bool stiles_ok = b < 32 && fa == 0 && dt != BSMM_F32 && a.nstiles > 0 && a.N % 8 == 0 &&
+                           (int64_t)a.G * ((a.N + 31) / 32) >= 8;
     if (a.force > 0) {
         if (a.force == UP_TILES && !tiles_ok) return -1;
         if (a.force == UP_RUNS && !runs_ok) return -1;
+        if (a.force == UP_STILES && !stiles_ok) return -1;
         return a.force;
     }
     switch (updat_variant()) {
@@ -1109,6 +1278,7 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
     }
     if (tiles_ok && tiles_wide) return UP_TILES;
     if (runs_ok) return UP_RUNS;
+    if (stiles_ok) return UP_STILES;
     const int KS = dt == BSMM_F32 ? 16 : 32;
     const int64_t steps = (int64_t)a.G * ((a.N + KS - 1) / KS);
     // Long contractions: row groups, 4 waves per block group.
@@ -1121,7 +1291,7 @@ int updat_kind(const UpArgs& a, int dt, int b, int fa) {
 }
 
 int updat_kind_of_name(const char* name) {
-    for (int k = UP_D2B1; k <= UP_RUNS; k++)
+    for (int k = UP_D2B1; k <= UP_STILES; k++)
         if (std::strcmp(name, updat_kind_name(k)) == 0) return k;
     return 0;
 }
@@ -1138,6 +1308,7 @@ const char* updat_kind_name(int kind) {
     case UP_D1B4: return "blocks_4perwave_noring";
     case UP_TILES: return "dense_tiles";
     case UP_RUNS: return "row_runs";
+    case UP_STILES: return "small_tiles";
     }
     return "none";
 }

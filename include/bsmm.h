@@ -251,6 +251,13 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  *                     row then k, at most 8 per group: index of its first id in
  *                     urids, count, row, 1)
  *         19 urids    (the ids of those groups)
+ *         20 stiles   (block size 8 or 16 only: 4 per weight-gradient tile of 256 x 256
+ *                     features holding a block, in super-blocks of 4 x 8 tiles: first x
+ *                     feature, first dy feature, index of its first entry in stids, 0)
+ *         21 stmask   (16 per such tile: per row of 16-feature quads, bit j set when
+ *                     quad column j holds a block)
+ *         22 stids    (per such tile, 256 quads row-major x the quad's blocks (1 for
+ *                     16x16 blocks, 2 x 2 row-major for 8x8): block id or -1)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full
  * length into *len. */
 BSMM_API bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, int64_t* len);

@@ -212,7 +212,9 @@ def test_kernel_choice_names():
     assert big.kernel_name("updat", 64, torch.bfloat16) == "row_runs"
     assert big.kernel_name("updat", 64, torch.bfloat16, group=2) == "blocks_2perwave"
     assert big.kernel_name("updat", 65, torch.float32) == "blocks_2perwave"
-    assert m8.kernel_name("updat", 4096, torch.bfloat16) == "row_groups"
+    assert m8.kernel_name("updat", 4096, torch.bfloat16) == "small_tiles"
+    assert m8.kernel_name("updat", 4100, torch.bfloat16) == "row_groups"   # not whole 8-column chunks
+    assert m8.kernel_name("updat", 4096, torch.float32) == "row_groups"
     assert m32.kernel_name("identity", 0, torch.bfloat16) == "identity"
     # 256x256 layouts at N = 4096: the output groups take sparse layouts once there
     # are >= 512 workgroups and the groups are >= 17 % full

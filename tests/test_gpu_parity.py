@@ -411,6 +411,40 @@ def test_updat_row_runs(N, dtype, dw_dtype):
     assert torch.equal(dw, dw2)
 
 
+@pytest.mark.parametrize("b,R,S,density", [(8, 40, 36, 0.1), (16, 20, 18, 0.3), (8, 64, 64, 1.0)])
+@pytest.mark.parametrize("N,G,dtype,dw_dtype", [(256, 1, "bf16", "f32"), (264, 3, "f16", "f32"),
+                                                (512, 1, "f16", "bf16"), (1024, 1, "bf16", "f32")])
+def test_updat_small_tiles(b, R, S, density, N, G, dtype, dw_dtype):
+    """The small-block weight-gradient tiles (8x8 / 16x16 blocks, features first): tiles
+    of 256 x 256 features with partial edge tiles, an empty tile row, grouped steps,
+    ragged last step, a full layout; every block against the oracle; then the
+    accumulating form; bit-reproducible."""
+    print(f"case small_tiles b={b} R={R} S={S} p={density} N={N} G={G} {dtype} dw={dw_dtype}", flush=True)
+    rng = np.random.default_rng(b * 7 + N + G)
+    L = (rng.random((R, S)) < density).astype(np.uint8)
+    if density < 1.0:
+        L[: 256 // b, S - 1] = 0   # a column that is empty in the first tile row
+        L[0, 0] = 1
+    P = synth.random_problem(rng, L, b, N, 0, dtype, G=G, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=0)
+    assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == "small_tiles"
+    xs, dys = [dev(t) for t in P.xs], [dev(t) for t in P.dys]
+    dw = m.updat(xs, dys, dw_dtype=TORCH_DT[dw_dtype])
+    dw2 = m.updat(xs, dys, dw_dtype=TORCH_DT[dw_dtype])
+    torch.cuda.synchronize()
+    bits = synth.to_bits
+    ref = oracle.updat(L, b, 0, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype)
+    assert_close(dw, ref, "f32" if dw_dtype == "f32" else "bf16", "updat small_tiles")
+    assert torch.equal(dw, dw2)
+    dw0 = (torch.randn(m.w_shape) * 3.0).to(TORCH_DT[dw_dtype])
+    out = dev(dw0)
+    m.updat(xs, dys, out=out, accumulate=True)
+    torch.cuda.synchronize()
+    refa = oracle.updat_accumulate(L, b, 0, bits(dw0), dw_dtype, [bits(t) for t in P.xs], [bits(t) for t in P.dys],
+                                   N, dtype)
+    assert_close(out, refa, "bf16", "updat small_tiles accumulate")
+
+
 @pytest.mark.parametrize("group_size", [8, 4])
 def test_group_param_grads_longer_than_a_group(group_size):
     """11 steps sharing one weight: the first group's launch writes the gradient, the

@@ -204,3 +204,49 @@ def test_weight_gradient_tiles_and_rest_cover_every_block_once():
         assert np.all(seen == 1)
     m8 = bs.BlocksparseMatMul(np.ones((16, 16), np.uint8), block_size=16)
     assert all(len(bs.bsmm_debug_lut(m8.handle, w)) == 0 for w in (16, 17, 18, 19))
+
+
+def test_small_block_gradient_tiles_cover_every_block_once():
+    """8x8 and 16x16 blocks: the 256 x 256-feature weight-gradient tiles list every
+    block exactly once at its own quad, with quad-row masks that match, tiles without
+    blocks left out, tiles in super-blocks of 4 x 8 tiles."""
+    rng = np.random.default_rng(11)
+    for b in (8, 16):
+        TB = 256 // b
+        QB = 2 if b == 8 else 1
+        for R, S, p in [(40, 70, 0.1), (TB, TB, 1.0), (3, 5, 0.5), (2 * TB + 3, 9 * TB + 1, 0.004), (4, 4, 0.0)]:
+            L = (rng.random((R, S)) < p).astype(np.uint8)
+            m = bs.BlocksparseMatMul(L, block_size=b)
+            coords = bs.bsmm_debug_lut(m.handle, 0).reshape(-1, 2)
+            tiles = bs.bsmm_debug_lut(m.handle, 20).reshape(-1, 4)
+            masks = bs.bsmm_debug_lut(m.handle, 21).reshape(-1, 16)
+            ids = bs.bsmm_debug_lut(m.handle, 22).reshape(-1, 16, 16, QB, QB)
+            assert len(tiles) == len(masks) == len(ids)
+            seen = np.zeros(int(L.sum()), dtype=int)
+            cells = []
+            for t, (f0, g0, first, zero) in enumerate(tiles):
+                assert f0 % 256 == 0 and g0 % 256 == 0 and zero == 0
+                assert first == t * 256 * QB * QB
+                tr, tc = f0 // 256, g0 // 256
+                cells.append((tr, tc))
+                n = 0
+                for qi in range(16):
+                    for qj in range(16):
+                        blk = ids[t, qi, qj]
+                        for di in range(QB):
+                            for dj in range(QB):
+                                r, c = tr * TB + qi * QB + di, tc * TB + qj * QB + dj
+                                if r < R and c < S and L[r, c]:
+                                    bid = blk[di, dj]
+                                    assert bid >= 0 and tuple(coords[bid]) == (r, c)
+                                    seen[bid] += 1
+                                    n += 1
+                                else:
+                                    assert blk[di, dj] == -1
+                        assert bool((masks[t, qi] >> qj) & 1) == bool(np.any(blk >= 0))
+                assert n > 0
+            assert np.all(seen == 1)
+            key = [(tr // 4, tc // 8, tr, tc) for tr, tc in cells]
+            assert key == sorted(key)
+    m = bs.BlocksparseMatMul(np.ones((3, 3), np.uint8), block_size=32)
+    assert all(len(bs.bsmm_debug_lut(m.handle, w)) == 0 for w in (20, 21, 22))
