@@ -114,7 +114,7 @@ bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out, bool m
                                              &L.colorder, &L.roworder, &L.colwork, &L.rowwork, &L.ugroups,
                                              &L.colrec,  &L.rowrec,   &L.cgptr,    &L.cgent,   &L.rgptr,
                                              &L.rgent,   &L.utiles,   &L.utblk,    &L.urest,   &L.urids,
-                                             &L.stiles,  &L.stmask,   &L.stids};
+                                             &L.stiles,  &L.stplan,   &L.stids};
     size_t off[NP], total = 0;
     for (int i = 0; i < NP; i++) {
         off[i] = total;
@@ -153,7 +153,7 @@ bsmm_status device_lut(bsmm_plan* h, void* stream, const DeviceLut** out, bool m
     d.urest = (const int32_t*)(b + off[18]);
     d.urids = (const int32_t*)(b + off[19]);
     d.stiles = (const int32_t*)(b + off[20]);
-    d.stmask = (const int32_t*)(b + off[21]);
+    d.stplan = (const int32_t*)(b + off[21]);
     d.stids = (const int32_t*)(b + off[22]);
     d.nstiles = (int32_t)(L.stiles.size() / 4);
     d.nutiles = (int32_t)(L.utiles.size() / 4);
@@ -469,7 +469,7 @@ bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* 
     a.rids = d->urids;
     a.nrest = d->nurest;
     a.stiles = d->stiles;
-    a.stmask = d->stmask;
+    a.stplan = d->stplan;
     a.stids = d->stids;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     a.force = h->force[BSMM_PASS_UPDAT];
@@ -617,7 +617,7 @@ bsmm_status bsmm_debug_lut(bsmm_handle h, int which, int64_t* out, int64_t cap, 
     case 18: v = &L.urest; break;
     case 19: v = &L.urids; break;
     case 20: v = &L.stiles; break;
-    case 21: v = &L.stmask; break;
+    case 21: v = &L.stplan; break;
     case 22: v = &L.stids; break;
     default: return fail(BSMM_ERR_INVALID_ARG, "which must be in [0, 22]");
     }

@@ -61,8 +61,8 @@ struct HostLut {
     // urids[first .. first+count-1].
     std::vector<int32_t> utiles, utblk, urest, urids;
     // Small-block weight-gradient tiles (8x8 and 16x16 blocks; format in lut_format.h):
-    // stiles (4 per tile), stmask (16 per tile), stids (256 or 1024 per tile).
-    std::vector<int32_t> stiles, stmask, stids;
+    // stiles (4 per tile), stplan (16 x 8 per tile), stids (256 or 1024 per tile).
+    std::vector<int32_t> stiles, stplan, stids;
 };
 
 // Builds every table above.  Pure host code: never touches HIP.  Returns false with a
@@ -96,7 +96,7 @@ struct DeviceLut {
     const int32_t* urids = nullptr;
     int32_t nutiles = 0, nurest = 0;
     const int32_t* stiles = nullptr;
-    const int32_t* stmask = nullptr;
+    const int32_t* stplan = nullptr;
     const int32_t* stids = nullptr;
     int32_t nstiles = 0;
 };

@@ -72,7 +72,7 @@ struct UpArgs {
     int32_t acc;            // 1: add the sum to what dw holds (dW += ...); 0: overwrite
     // 8x8 and 16x16 blocks: small-block tiles (lut_format.h)
     const int32_t* stiles;
-    const int32_t* stmask;
+    const int32_t* stplan;
     const int32_t* stids;
     int32_t nstiles;
 };

@@ -241,7 +241,36 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
             if (n == 0) continue;
             L.stiles.insert(L.stiles.end(), {(int32_t)(tr * kSmallTileFeat), (int32_t)(tc * kSmallTileFeat),
                                              (int32_t)L.stids.size(), 0});
-            L.stmask.insert(L.stmask.end(), mask.begin(), mask.end());
+            // quad rows to waves: wave w runs on SIMD w % 4 of its compute unit, so the
+            // rows go to the four SIMDs (four rows each) fullest first, each to the SIMD
+            // with the fewest quads so far, so that no SIMD's matrix core carries much
+            // more than a quarter of the tile
+            std::vector<int32_t> cnt(kSmallQuads, 0), order(kSmallQuads);
+            for (int64_t qi = 0; qi < kSmallQuads; qi++) cnt[qi] = __builtin_popcount((uint32_t)mask[qi]);
+            std::iota(order.begin(), order.end(), 0);
+            std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cnt[x] > cnt[y]; });
+            int32_t load[4] = {0, 0, 0, 0}, taken[4] = {0, 0, 0, 0}, rowof[kSmallQuads];
+            for (int32_t r : order) {
+                int best = -1;
+                for (int sm = 0; sm < 4; sm++)
+                    if (taken[sm] < kSmallQuads / 4 && (best < 0 || load[sm] < load[best])) best = sm;
+                rowof[best + 4 * taken[best]] = r;
+                taken[best]++;
+                load[best] += cnt[r];
+            }
+            for (int wv = 0; wv < kSmallQuads; wv++) {
+                const int32_t qi = rowof[wv];
+                std::vector<int32_t> plan(kSmallPlanInts, 0);
+                int32_t c = 0;
+                for (int qj = 0; qj < kSmallQuads; qj++)
+                    if ((mask[qi] >> qj) & 1) {
+                        plan[1 + c / 4] |= (int32_t)((uint32_t)qj << (8 * (c % 4)));
+                        c++;
+                    }
+                plan[0] = c;
+                plan[5] = qi;
+                L.stplan.insert(L.stplan.end(), plan.begin(), plan.end());
+            }
             L.stids.insert(L.stids.end(), ids.begin(), ids.end());
         }
     }

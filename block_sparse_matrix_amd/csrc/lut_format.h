@@ -25,10 +25,14 @@ constexpr int kSuperCols = 8;
 // Weight-gradient tiles of small blocks (8x8 and 16x16): 256 x 256 features of the
 // layout, cut into 16 x 16 quads of 16 x 16 features (one 16x16 block, or 2 x 2 blocks
 // of 8x8).  Per tile with any block: (first x feature, first dy feature, index of its
-// first id, 0); per tile 16 quad-row masks (bit j: quad column j holds a block); per
-// tile 256 quads x (1 or 4) ids, row-major quads, blocks within a quad row-major, -1
-// where absent.
+// first id, 0); per tile and wave (16 waves) kSmallPlanInts ints: the number of quads
+// of the wave's quad row that hold a block, their quad columns in ascending order (one
+// byte each, four to an int from the low byte, zero past the end), the quad row, then
+// zeros (rows are dealt to waves so that waves w, w + 4, w + 8, w + 12 together hold
+// about a quarter of the tile's quads); per tile 256 quads x (1 or 4) ids, row-major
+// quads, blocks within a quad row-major, -1 where absent.
 constexpr int kSmallTileFeat = 256;
 constexpr int kSmallQuads = 16;
+constexpr int kSmallPlanInts = 8;
 
 }  // namespace bsmm

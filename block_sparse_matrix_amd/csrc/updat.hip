@@ -1067,10 +1067,16 @@ static hipError_t launch_updat_runs(const UpArgs& a, hipStream_t st) {
 // rows of its quad row straight into a fragment (features first: the contraction index
 // is contiguous).  The wave then runs one 16x16x32 matrix-core step per present quad of
 // its row (a quad is one 16x16 block, or 2 x 2 blocks of 8x8), the dy fragment read from
-// LDS; the quad's fp32 sums stay in registers (slot = quad column) for the whole
-// contraction.  Loads run RD steps ahead in registers, the LDS stage is double
-// buffered: one barrier per step.  Each block has one writer; no atomics.
-template <int DT, int B, int RD, int QG>
+// LDS.  The row's present quads come as a list (layout compiler), walked four entries
+// at a time: the group's fragment reads are issued together, so the waves meeting at
+// the step's barrier each wait for about one LDS round trip per four quads, not one per
+// quad.  The layout compiler also picks which quad row each wave takes, so that the
+// four SIMDs of the compute unit (wave w runs on SIMD w % 4) get about the same number
+// of quads: their matrix cores, not the waves, set the pace of a step.  The quads'
+// fp32 sums stay in registers (slot = list position) for the whole contraction.  Loads run RD steps ahead in registers, the LDS
+// stage is double buffered: one barrier per step.  Each block has one writer; no
+// atomics.
+template <int DT, int B, int RD>
 __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
     constexpr int TF = kSmallTileFeat, Q = kSmallQuads, KS = 32, IPQ = B == 8 ? 4 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t stg[2][TF * KS];
@@ -1083,18 +1089,29 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
     if (ti >= a.nstiles) return;   // whole workgroup
     const int4 tl = reinterpret_cast<const int4*>(a.stiles)[ti];
     const int fx0 = tl.x, fy0 = tl.y, first = tl.z;
-    const int mask = __builtin_amdgcn_readfirstlane(a.stmask[ti * Q + w]);
+    // the wave's quad row and its list: length, then the row's quad columns, one byte
+    // each, four to an int
+    const int* pl = a.stplan + (ti * Q + w) * kSmallPlanInts;
+    const int cnt = __builtin_amdgcn_readfirstlane(pl[0]);
+    const int qr = __builtin_amdgcn_readfirstlane(pl[5]);
+    uint32_t ent[Q / 4];
+#pragma unroll
+    for (int k = 0; k < Q / 4; k++) ent[k] = (uint32_t)__builtin_amdgcn_readfirstlane(pl[1 + k]);
+    const int ngr = (cnt + 3) >> 2;
     const int N = (int)a.N;
     const int spt = N / KS + (N % KS ? 1 : 0);
     const int nsteps = a.G * spt;
 
-    // x fragment: feature fx0 + 16 w + r16, columns n0 + 8 g ..; dy stage: thread t ->
-    // feature fy0 + t / 4, columns n0 + 8 (t % 4) ..  (N % 8 == 0: an 8-column chunk is
-    // all in or all out)
-    const int fx = fx0 + 16 * w + r16, fy = fy0 + (t >> 2), cy = t & 3;
+    // x fragment: feature fx0 + 16 w + r16, columns n0 + 8 g ..; wave w stages the dy
+    // fragment of quad column w the same way: feature fy0 + 16 w + r16, columns n0 + 8 g
+    // .. (N % 8 == 0: an 8-column chunk is all in or all out).  The stage holds each quad
+    // column's fragment as the 64 lanes' 16-byte pieces in lane order (1 KB), so that
+    // both the stage writes and the fragment reads are plain consecutive 16-byte
+    // accesses, which the LDS serves at full rate.
+    const int fx = fx0 + 16 * qr + r16, fy = fy0 + 16 * w + r16;
     const uint32_t xo = fx < a.C ? (uint32_t)fx * N * 2u + 16u * g : kOffLane;
-    const uint32_t yo = fy < a.K ? (uint32_t)fy * N * 2u + 16u * cy : kOffLane;
-    const int ql = (t >> 2) * KS + ((cy ^ bswz(t >> 2)) << 3);   // stage slot of thread t
+    const uint32_t yo = fy < a.K ? (uint32_t)fy * N * 2u + 16u * g : kOffLane;
+    const int ql = w * 512 + lane * 8;   // stage slot of thread t
     struct Slot {
         u32x4 x, y;
     };
@@ -1106,18 +1123,13 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
         pick(a, tt, rx, ry);
         const uint32_t so = sv ? (uint32_t)n0 * 2u : kOffOff;
         // a chunk past N is switched off with the top offset bit (no branch)
-        const uint32_t offx = ((uint32_t)(N - 1 - n0 - 8 * g) >> 31) << 31;
-        const uint32_t offy = ((uint32_t)(N - 1 - n0 - 8 * cy) >> 31) << 31;
-        sl.x = bload128(rx, xo | offx, so);
-        sl.y = bload128(ry, yo | offy, so);
+        const uint32_t off = ((uint32_t)(N - 1 - n0 - 8 * g) >> 31) << 31;
+        sl.x = bload128(rx, xo | off, so);
+        sl.y = bload128(ry, yo | off, so);
     };
-    // dy fragment of quad column j: rows 16 j + r16 of the stage, columns 8 g ..
-    int boff[Q];
-#pragma unroll
-    for (int j = 0; j < Q; j++) {
-        const int r = 16 * j + r16;
-        boff[j] = r * KS + ((g ^ bswz(r)) << 3);
-    }
+    // dy fragment of quad column j: its 1 KB of the stage (j * 512 elements), this
+    // lane's 16 bytes
+    const int boff = lane * 8;
     f32x4 acc[Q];
 #pragma unroll
     for (int j = 0; j < Q; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1135,19 +1147,24 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
 #pragma unroll
             for (int i = 0; i < RD; i++) {
                 const int s = s0 + i;
-                const BSMM_LDS uint16_t* cur = (const BSMM_LDS uint16_t*)stg[s & 1];
+                const BSMM_LDS uint16_t* cur = (const BSMM_LDS uint16_t*)stg[s & 1] + boff;
                 if (s < nsteps) {
-                    // quad columns in groups of QG: the group's LDS reads are issued
-                    // together, so one wait covers them
 #pragma unroll
-                    for (int j0 = 0; j0 < Q; j0 += QG) {
-                        u32x4 bf[QG];
+                    for (int k = 0; k < Q / 4; k++) {
+                        if (k < ngr) {   // uniform
+                            // the group's columns are decoded again every step (a few
+                            // scalar instructions) rather than held across the loop
+                            uint32_t ek = ent[k];
+                            asm volatile("" : "+s"(ek));
+                            u32x4 bf[4];
 #pragma unroll
-                        for (int jj = 0; jj < QG; jj++)
-                            if ((mask >> (j0 + jj)) & 1) bf[jj] = *reinterpret_cast<const BSMM_LDS u32x4*>(cur + boff[j0 + jj]);
+                            for (int q = 0; q < 4; q++)
+                                if (4 * k + q < cnt) bf[q] = *reinterpret_cast<const BSMM_LDS u32x4*>(cur + ((ek >> (8 * q)) & 15u) * 512);
+                            __builtin_amdgcn_sched_barrier(0);   // the group's reads in flight first
 #pragma unroll
-                        for (int jj = 0; jj < QG; jj++)
-                            if ((mask >> (j0 + jj)) & 1) mma<DT>(acc[j0 + jj], ring[i].x, bf[jj]);   // D[x f][dy f]
+                            for (int q = 0; q < 4; q++)
+                                if (4 * k + q < cnt) mma<DT>(acc[4 * k + q], ring[i].x, bf[q]);   // D[x f][dy f]
+                        }
                     }
                 }
                 // stage step s + 1 (loaded RD - 1 steps ago), then refill this slot
@@ -1166,37 +1183,41 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
         run(pm);
     }
 
-    // lane holds D[4 g + v][r16] of each present quad: x feature 4 g + v, dy feature r16
-    const int* ids = a.stids + first + w * Q * IPQ;
+    // lane holds D[4 g + v][r16] of each listed quad: x feature 4 g + v, dy feature r16.
+    // Those four elements lie in one block (8x8 blocks: block row g / 2, column r16 / 8
+    // of the quad), so a lane needs one id per quad; all of them are loaded together
+    // (entries past the list's end load quad column 0's and are not used) before any
+    // store, one memory round trip rather than one per quad.
+    const int* ids = a.stids + first + qr * Q * IPQ;
+    const int sub = B == 16 ? 0 : (g >> 1) * 2 + (r16 >> 3);
+    int idv[Q];
 #pragma unroll
-    for (int j = 0; j < Q; j++) {
-        if (!((mask >> j) & 1)) continue;   // uniform
+    for (int jj = 0; jj < Q; jj++) {
+        const int j = (int)((ent[jj >> 2] >> (8 * (jj & 3))) & 15u);   // quad column
+        idv[jj] = ids[j * IPQ + sub];
+    }
+    const int64_t e0 = B == 16 ? (int64_t)(4 * g) * 16 + r16 : (int64_t)((4 * g) & 7) * 8 + (r16 & 7);
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int p = 4 * g + v, q = r16;
-            int id;
-            int64_t e;
-            if constexpr (B == 16) {
-                id = ids[j];
-                e = p * 16 + q;
-            } else {
-                id = ids[j * 4 + (p >> 3) * 2 + (q >> 3)];
-                e = (p & 7) * 8 + (q & 7);
-            }
-            if (id >= 0) {
-                const int64_t idx = (int64_t)id * B * B + e;
-                if (a.acc) {
-                    float o;
-                    if (a.dwdt == BSMM_F32) o = ((const float*)a.dw)[idx];
-                    else {
-                        const uint32_t h = ((const uint16_t*)a.dw)[idx];
-                        o = a.dwdt == BSMM_BF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-                    }
-                    store_elt(a.dw, idx, acc[j][v] + o, a.dwdt);
-                } else {
-                    store_elt(a.dw, idx, acc[j][v], a.dwdt);
+    for (int jj = 0; jj < Q; jj++) {
+        if (jj >= cnt) continue;   // uniform (no break: the loop unrolls, acc stays in registers)
+        if (idv[jj] < 0) continue;
+        const int64_t base = (int64_t)idv[jj] * B * B + e0;   // element (4 g, r16); v adds v rows
+        if (a.acc) {
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int64_t idx = base + v * B;
+                if (a.dwdt == BSMM_F32) o[v] = ((const float*)a.dw)[idx];
+                else {
+                    const uint32_t h = ((const uint16_t*)a.dw)[idx];
+                    o[v] = a.dwdt == BSMM_BF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
                 }
             }
+#pragma unroll
+            for (int v = 0; v < 4; v++) store_elt(a.dw, base + v * B, acc[jj][v] + o[v], a.dwdt);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; v++) store_elt(a.dw, base + v * B, acc[jj][v], a.dwdt);
         }
     }
 }
@@ -1208,16 +1229,7 @@ static hipError_t launch_updat_small_tiles(const UpArgs& a, hipStream_t st) {
     } else {
         const int grid = ((a.nstiles + 7) / 8) * 8;
         if (grid == 0) return hipSuccess;
-        static const int qg = [] {
-            const char* e = getenv("BSMM_STILES_QG");   // A/B measurements: quad columns per LDS batch
-            return e ? atoi(e) : 1;
-        }();
-        switch (qg) {
-        case 1: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 1>, dim3((unsigned)grid), dim3(1024), st, a);
-        case 2: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 2>, dim3((unsigned)grid), dim3(1024), st, a);
-        case 8: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 8>, dim3((unsigned)grid), dim3(1024), st, a);
-        default: return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3, 4>, dim3((unsigned)grid), dim3(1024), st, a);
-        }
+        return launch(BSMM_PASS_UPDAT, upds_kernel<DT, B, 3>, dim3((unsigned)grid), dim3(1024), st, a);
     }
 }
 

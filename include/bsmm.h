@@ -254,8 +254,11 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  *         20 stiles   (block size 8 or 16 only: 4 per weight-gradient tile of 256 x 256
  *                     features holding a block, in super-blocks of 4 x 8 tiles: first x
  *                     feature, first dy feature, index of its first entry in stids, 0)
- *         21 stmask   (16 per such tile: per row of 16-feature quads, bit j set when
- *                     quad column j holds a block)
+ *         21 stplan   (8 per such tile and wave, 16 waves: the number of 16-feature
+ *                     quads holding a block in the wave's quad row, their quad columns
+ *                     ascending, one byte each, four per value from the low byte, zero
+ *                     past the end, then the quad row, then 2 zeros; each row taken by
+ *                     one wave, waves w, w+4, w+8, w+12 sharing one SIMD)
  *         22 stids    (per such tile, 256 quads row-major x the quad's blocks (1 for
  *                     16x16 blocks, 2 x 2 row-major for 8x8): block id or -1)
  * Copies min(cap, length) values into out (may be NULL when cap = 0) and the full

@@ -208,8 +208,9 @@ def test_weight_gradient_tiles_and_rest_cover_every_block_once():
 
 def test_small_block_gradient_tiles_cover_every_block_once():
     """8x8 and 16x16 blocks: the 256 x 256-feature weight-gradient tiles list every
-    block exactly once at its own quad, with quad-row masks that match, tiles without
-    blocks left out, tiles in super-blocks of 4 x 8 tiles."""
+    block exactly once at its own quad, with per-quad-row lists of exactly the quads
+    that hold a block (ascending), tiles without blocks left out, tiles in
+    super-blocks of 4 x 8 tiles."""
     rng = np.random.default_rng(11)
     for b in (8, 16):
         TB = 256 // b
@@ -219,9 +220,9 @@ def test_small_block_gradient_tiles_cover_every_block_once():
             m = bs.BlocksparseMatMul(L, block_size=b)
             coords = bs.bsmm_debug_lut(m.handle, 0).reshape(-1, 2)
             tiles = bs.bsmm_debug_lut(m.handle, 20).reshape(-1, 4)
-            masks = bs.bsmm_debug_lut(m.handle, 21).reshape(-1, 16)
+            plans = bs.bsmm_debug_lut(m.handle, 21).reshape(-1, 16, 8)
             ids = bs.bsmm_debug_lut(m.handle, 22).reshape(-1, 16, 16, QB, QB)
-            assert len(tiles) == len(masks) == len(ids)
+            assert len(tiles) == len(plans) == len(ids)
             seen = np.zeros(int(L.sum()), dtype=int)
             cells = []
             for t, (f0, g0, first, zero) in enumerate(tiles):
@@ -243,7 +244,19 @@ def test_small_block_gradient_tiles_cover_every_block_once():
                                     n += 1
                                 else:
                                     assert blk[di, dj] == -1
-                        assert bool((masks[t, qi] >> qj) & 1) == bool(np.any(blk >= 0))
+                counts = [sum(np.any(ids[t, qi, qj] >= 0) for qj in range(16)) for qi in range(16)]
+                assert sorted(int(r) for r in plans[t, :, 5]) == list(range(16))   # every row once
+                for wv in range(16):
+                    qi = int(plans[t, wv, 5])
+                    present = [qj for qj in range(16) if np.any(ids[t, qi, qj] >= 0)]
+                    cnt = int(plans[t, wv, 0])
+                    cols = plans[t, wv, 1:5].astype(np.uint32).view(np.uint8)   # little-endian bytes
+                    assert cnt == len(present) and list(cols[:cnt]) == present
+                    assert np.all(cols[cnt:] == 0) and np.all(plans[t, wv, 6:] == 0)
+                # waves w, w+4, w+8, w+12 share a SIMD: dealt fullest row first to the
+                # least-loaded SIMD, no SIMD ends more than one row's count above another
+                simd = [sum(counts[int(plans[t, wv, 5])] for wv in range(sm, 16, 4)) for sm in range(4)]
+                assert max(simd) - min(simd) <= max(counts)
                 assert n > 0
             assert np.all(seen == 1)
             key = [(tr // 4, tc // 8, tr, tc) for tr, tc in cells]
