@@ -100,8 +100,8 @@ def roof(flops, nbytes, dtype):
 # argument set-up and layout tables).  A stored counter reading is used only while the
 # hash of these files matches the one recorded with it.
 KERNEL_SOURCES = {
-    "fprop": ["mm.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
-    "bprop": ["mm.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
+    "fprop": ["mm.hip", "mmt.hip", "rows.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
+    "bprop": ["mm.hip", "mmt.hip", "rows.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
     "updat": ["updat.hip", "common.h", "kernels.h", "lut_format.h", "api.hip", "layout.cpp"],
 }
 
