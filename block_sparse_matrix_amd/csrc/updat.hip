@@ -761,22 +761,22 @@ static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int 
     return launch_ev(updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, e0, e1, a, groups, ngroups);
 }
 
-// Sum of the split parts of every tile block, in part order (deterministic), to dW.
+// Sum of the split parts of every tile block, in part order (deterministic), to dW: one
+// workgroup per (tile, block position), so all the blocks' part reads are in flight at
+// once (absent positions leave at once).
 template <int B>
 __global__ __launch_bounds__(256) void updt_reduce(UpArgs a) {
-    const int ti = blockIdx.x;
-    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
     constexpr int TT = kTileSide * kTileSide;
-    for (int pos = 0; pos < TT; pos++) {
-        const int id = a.tblk[tl.w + pos];
-        if (id < 0) continue;   // workgroup-uniform
-        for (int e = 4 * threadIdx.x; e < B * B; e += 4 * 256) {
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int p = 0; p < a.split; p++)
-                s += *reinterpret_cast<const f32x4*>(a.ws + (((int64_t)p * a.ntiles + ti) * TT + pos) * B * B + e);
-            const int64_t idx = (int64_t)id * B * B + e;
-            store_dw4(a, idx, s);
-        }
+    const int ti = blockIdx.x / TT, pos = blockIdx.x % TT;
+    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
+    const int id = a.tblk[tl.w + pos];
+    if (id < 0) return;   // whole workgroup
+    for (int e = 4 * threadIdx.x; e < B * B; e += 4 * 256) {
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < a.split; p++)
+            s += *reinterpret_cast<const f32x4*>(a.ws + (((int64_t)p * a.ntiles + ti) * TT + pos) * B * B + e);
+        const int64_t idx = (int64_t)id * B * B + e;
+        store_dw4(a, idx, s);
     }
 }
 
@@ -794,10 +794,29 @@ static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
         hipError_t e = launch_ev(updt_kernel<DT, FA, 2>, dim3((unsigned)grid), dim3(512), st, e0, more ? nullptr : e1, a);
         if (e != hipSuccess) return e;
         if (a.split > 1) {
-            e = launch_ev(updt_reduce<B>, dim3((unsigned)a.ntiles), dim3(256), st, nullptr, a.nrest > 0 ? nullptr : e1, a);
+            e = launch_ev(updt_reduce<B>, dim3((unsigned)(a.ntiles * kTileSide * kTileSide)), dim3(256), st, nullptr,
+                          a.nrest > 0 ? nullptr : e1, a);
             if (e != hipSuccess) return e;
         }
         if (a.nrest == 0) return hipSuccess;
+        if (a.G > 1 && a.dwdt == BSMM_F32) {
+            // Remaining blocks of several step groups, fp32 dW: one launch per group, each
+            // adding its group to dW (the first overwrites unless the call accumulates).
+            // A launch then reads one group's activations only, which stay in the
+            // memory-side cache while every row group reads the dy slabs of its blocks;
+            // one launch over all groups streams them all at once and misses it.
+            for (int t = 0; t < a.G; t++) {
+                UpArgs at = a;
+                at.G = 1;
+                at.xs[0] = a.xs[t];
+                at.dys[0] = a.dys[t];
+                at.acc = a.acc || t > 0;
+                e = launch_updat_grouped<DT, B, FA>(at, (const int4*)a.rest, a.nrest, st, nullptr,
+                                                    t == a.G - 1 ? e1 : nullptr, false);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
         return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.rest, a.nrest, st, nullptr, e1, false);
     }
 }
