@@ -188,15 +188,18 @@ bool compile_layout(const uint8_t* layout, int64_t R, int64_t S, int b, int fa, 
             for (int32_t i : ord) sorted.insert(sorted.end(), L.utiles.begin() + 4 * i, L.utiles.begin() + 4 * i + 4);
             L.utiles.swap(sorted);
         }
+        // the rest: per row, its blocks outside the tiles in groups of at most
+        // kRestGroup, as even as possible (the slowest group sets the launch's time)
         for (int64_t c = 0; c < R; c++) {
-            int32_t n = 0;
-            for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++) {
-                const int32_t id = L.rowent[2 * e + 1];
-                if (in_tile[id]) continue;
-                if (n == 0) L.urest.insert(L.urest.end(), {(int32_t)L.urids.size(), 0, (int32_t)c, 1});
-                L.urids.push_back(id);
-                L.urest[L.urest.size() - 3]++;
-                n = n == 7 ? 0 : n + 1;
+            std::vector<int32_t> ids;
+            for (int32_t e = L.rowptr[c]; e < L.rowptr[c + 1]; e++)
+                if (!in_tile[L.rowent[2 * e + 1]]) ids.push_back(L.rowent[2 * e + 1]);
+            const int32_t n = (int32_t)ids.size(), ng = (n + kRestGroup - 1) / kRestGroup;
+            for (int32_t gi = 0, at = 0; gi < ng; gi++) {
+                const int32_t cnt = n / ng + (gi < n % ng ? 1 : 0);
+                L.urest.insert(L.urest.end(), {(int32_t)L.urids.size(), cnt, (int32_t)c, 1});
+                L.urids.insert(L.urids.end(), ids.begin() + at, ids.begin() + at + cnt);
+                at += cnt;
             }
         }
     }

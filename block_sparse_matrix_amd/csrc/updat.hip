@@ -750,10 +750,9 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
     }
 }
 
-template <int DT, int B, int FA>
+template <int DT, int B, int FA, int GM = 8>
 static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int ngroups, hipStream_t st,
                                        void* e0 = nullptr, void* e1 = nullptr, bool own_events = true) {
-    constexpr int GM = 8;
     const int grid = ((ngroups + 7) / 8) * 8;
     if (own_events)
         return launch(BSMM_PASS_UPDAT, updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, a, groups,
@@ -811,13 +810,13 @@ static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
                 at.xs[0] = a.xs[t];
                 at.dys[0] = a.dys[t];
                 at.acc = a.acc || t > 0;
-                e = launch_updat_grouped<DT, B, FA>(at, (const int4*)a.rest, a.nrest, st, nullptr,
-                                                    t == a.G - 1 ? e1 : nullptr, false);
+                e = launch_updat_grouped<DT, B, FA, kRestGroup>(at, (const int4*)a.rest, a.nrest, st, nullptr,
+                                                                t == a.G - 1 ? e1 : nullptr, false);
                 if (e != hipSuccess) return e;
             }
             return hipSuccess;
         }
-        return launch_updat_grouped<DT, B, FA>(a, (const int4*)a.rest, a.nrest, st, nullptr, e1, false);
+        return launch_updat_grouped<DT, B, FA, kRestGroup>(a, (const int4*)a.rest, a.nrest, st, nullptr, e1, false);
     }
 }
 

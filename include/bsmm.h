@@ -248,7 +248,8 @@ BSMM_API bsmm_status bsmm_force_kernel(bsmm_handle h, int pass, const char* name
  *         17 utblk    (64 per tile: the ids of its 8x8 positions, row-major, -1 where
  *                     the layout is 0)
  *         18 urest    (4 per row group of the blocks outside those tiles, ascending
- *                     row then k, at most 8 per group: index of its first id in
+ *                     row then k; a row's blocks split into the fewest groups of at
+ *                     most 4, sizes differing by at most 1: index of its first id in
  *                     urids, count, row, 1)
  *         19 urids    (the ids of those groups)
  *         20 stiles   (block size 8 or 16 only: 4 per weight-gradient tile of 256 x 256
