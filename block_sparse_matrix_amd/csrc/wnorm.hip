@@ -9,8 +9,10 @@
 //   dW    = g[o]/n[o] * dOut - [sum of squares > epsilon] * g[o]*s[o]/n[o]^3 * W,
 //   dg[o] = s[o] / n[o].
 // A workgroup owns one block column and walks its block list (the fprop column list
-// of the layout tables) twice in 16-byte vectors: the column sums (fp32, a fixed
-// order: deterministic), then the elementwise pass, whose re-read hits L2.
+// of the layout tables) in 16-byte vectors: the column sums (fp32: a butterfly inside
+// each wave, then the waves in order — deterministic), then the elementwise pass.  The
+// first round of blocks stays in registers between the two passes; only longer
+// columns read the rest again (from L2).
 // Bound: HBM (|W| read, |out| written; |dOut| + |W| read, |dW| written).
 #include "common.h"
 
@@ -18,39 +20,7 @@ namespace bsmm {
 
 constexpr int kWnThreads = 1024;   // 16 waves: a block column's loads all in flight
 
-// VW consecutive values of storage dtype DT at element idx (VW = 4 or 8; 8- or 16-byte
-// aligned), widened to float
-template <int DT, int VW> __device__ __forceinline__ void wn_loadv(const void* base, int64_t idx, float* v) {
-    if constexpr (DT == BSMM_F32) {
-#pragma unroll
-        for (int h = 0; h < VW; h += 4) {
-            const f32x4 q = *reinterpret_cast<const f32x4*>((const float*)base + idx + h);
-            v[h] = q.x;
-            v[h + 1] = q.y;
-            v[h + 2] = q.z;
-            v[h + 3] = q.w;
-        }
-    } else {
-        uint32_t w[VW / 2];
-        if constexpr (VW == 8) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>((const uint16_t*)base + idx);
-            w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
-        } else {
-            const u32x2 q = *reinterpret_cast<const u32x2*>((const uint16_t*)base + idx);
-            w[0] = q.x; w[1] = q.y;
-        }
-#pragma unroll
-        for (int i = 0; i < VW / 2; i++) {
-            if constexpr (DT == BSMM_BF16) {
-                v[2 * i] = __uint_as_float(w[i] << 16);
-                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-            } else {
-                v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
-                v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
-            }
-        }
-    }
-}
+// VW floats stored as dtype DT at element idx (round to nearest even for 16-bit)
 template <int DT, int VW> __device__ __forceinline__ void wn_storev(void* base, int64_t idx, const float* v) {
     if constexpr (DT == BSMM_F32) {
 #pragma unroll
@@ -67,74 +37,142 @@ template <int DT, int VW> __device__ __forceinline__ void wn_storev(void* base, 
     }
 }
 
+// Raw storage of VW values of dtype DT (8, 16 or 32 bytes), kept in registers between
+// the two passes.
+template <int DT, int VW> struct WnRaw {
+    static constexpr int NB = VW * (DT == BSMM_F32 ? 4 : 2);
+    uint32_t w[NB / 4];
+};
+template <int DT, int VW> __device__ __forceinline__ void wn_rawload(WnRaw<DT, VW>& r, const void* base, int64_t idx) {
+    const char* p = (const char*)base + idx * (DT == BSMM_F32 ? 4 : 2);
+    if constexpr (WnRaw<DT, VW>::NB == 8) {
+        const u32x2 q = *reinterpret_cast<const u32x2*>(p);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < WnRaw<DT, VW>::NB / 16; h++) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(p + 16 * h);
+            r.w[4 * h] = q.x;
+            r.w[4 * h + 1] = q.y;
+            r.w[4 * h + 2] = q.z;
+            r.w[4 * h + 3] = q.w;
+        }
+    }
+}
+template <int DT, int VW> __device__ __forceinline__ void wn_rawcvt(const WnRaw<DT, VW>& r, float* v) {
+    if constexpr (DT == BSMM_F32) {
+#pragma unroll
+        for (int i = 0; i < VW; i++) v[i] = __uint_as_float(r.w[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VW / 2; i++) {
+            if constexpr (DT == BSMM_BF16) {
+                v[2 * i] = __uint_as_float(r.w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+            } else {
+                v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.w[i] & 0xffffu));
+                v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.w[i] >> 16));
+            }
+        }
+    }
+}
+
 // Work map: a thread owns one 16-byte vector of the weights' storage (VW values of one
 // block row) per block; the workgroup covers P blocks of the list side by side, walked
 // U at a time so that U loads per thread are in flight.  Thread t: block slot t / VB,
-// row (t % VB) / VR, columns (t % VR)*VW .. +VW-1.
+// row (t % VB) / VR, columns (t % VR)*VW .. +VW-1.  The first IT rounds of U blocks
+// stay in registers from the sums to the elementwise pass (a column of up to IT*P*U
+// blocks is read once); longer columns read the rest again.
 template <int B, int DTI> struct WnMap {
     static constexpr int VW = DTI == BSMM_F32 ? 4 : 8;
     static constexpr int VR = B / VW;                 // vectors per block row (>= 1)
     static constexpr int VB = B * VR;                 // vectors per block
     static constexpr int P = kWnThreads / VB;         // blocks side by side (>= 1)
     static constexpr int U = 8;
+    static constexpr int IT = 1;    // rounds kept (the gradient keeps one round of two tensors)
     static_assert(B % VW == 0 && kWnThreads % VB == 0, "work map");
 };
 
 // Column sums of two per-thread VW-vectors over the threads of the same column vector
-// (threads t, t + VR, t + 2 VR, ...): a halving tree over the thread index (fixed
-// order: deterministic); thread t < B gets column t's sums.
-template <int B, int VW, int VR>
+// (threads t = cv mod VR): a butterfly over the lane bits above VR inside each wave,
+// then the 16 waves' sums added in wave order (fixed order: deterministic); thread
+// t < B gets column t's sums.
+template <int B, int VW, int VR, bool TWO>
 __device__ __forceinline__ void wn_colsum(const float* a, const float* b, float* ra, float* rb, float& oa, float& ob) {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    float x[VW], y[VW];
 #pragma unroll
     for (int k = 0; k < VW; k++) {
-        ra[t * VW + k] = a[k];
-        rb[t * VW + k] = b[k];
+        x[k] = a[k];
+        y[k] = TWO ? b[k] : 0.f;
     }
+#pragma unroll
+    for (int o = VR; o < 64; o <<= 1)
+#pragma unroll
+        for (int k = 0; k < VW; k++) {
+            x[k] += __shfl_xor(x[k], o);
+            if constexpr (TWO) y[k] += __shfl_xor(y[k], o);
+        }
+    if (lane < VR)   // lane = column vector cv: columns cv*VW .. +VW-1
+#pragma unroll
+        for (int k = 0; k < VW; k++) {
+            ra[wv * B + lane * VW + k] = x[k];
+            if constexpr (TWO) rb[wv * B + lane * VW + k] = y[k];
+        }
     __syncthreads();
-#pragma unroll
-    for (int half = kWnThreads / 2; half >= VR; half >>= 1) {
-        if (t < half)
-#pragma unroll
-            for (int k = 0; k < VW; k++) {
-                ra[t * VW + k] += ra[(t + half) * VW + k];
-                rb[t * VW + k] += rb[(t + half) * VW + k];
-            }
-        __syncthreads();
-    }
     oa = ob = 0.f;
     if (t < B) {
-        oa = ra[t];   // thread cv = t / VW's value k = t % VW: index cv*VW + k = t
-        ob = rb[t];
+        for (int w = 0; w < kWnThreads / 64; w++) {
+            oa += ra[w * B + t];
+            if constexpr (TWO) ob += rb[w * B + t];
+        }
     }
 }
 
 template <int B, int DTI, int DTO>
 __global__ __launch_bounds__(kWnThreads) void wn_fwd(WnArgs a) {
     using Map = WnMap<B, DTI>;
-    constexpr int VW = Map::VW, VR = Map::VR, VB = Map::VB, P = Map::P, U = Map::U;
-    __shared__ float ra[kWnThreads * VW], rb[kWnThreads * VW], scale[B];
+    constexpr int VW = Map::VW, VR = Map::VR, VB = Map::VB, P = Map::P, U = Map::U, IT = Map::IT;
+    __shared__ float ra[kWnThreads / 64 * B], rb[kWnThreads / 64 * B], scale[B];
     const int k = blockIdx.x, t = threadIdx.x;
     const int beg = a.colptr[k], end = a.colptr[k + 1];
     const int slot = t / VB, e0 = (t % VB) * VW;   // element offset inside a block
-    float ss[VW], zero[VW];
+    float ss[VW];
 #pragma unroll
-    for (int i = 0; i < VW; i++) ss[i] = zero[i] = 0.f;
-    for (int q0 = beg + slot; q0 < end; q0 += P * U) {
-        float v[U][VW];
+    for (int i = 0; i < VW; i++) ss[i] = 0.f;
+    // block q of the list -> its element offset; blocks past the end read the list's first
+    auto off = [&](int q) { return (int64_t)a.colent[2 * (q < end ? q : beg) + 1] * B * B + e0; };
+    WnRaw<DTI, VW> keep[IT][U];
 #pragma unroll
-        for (int uu = 0; uu < U; uu++) {   // loads first; blocks past the end read block q0
-            const int q = q0 + P * uu;
-            wn_loadv<DTI, VW>(a.w, (int64_t)a.colent[2 * (q < end ? q : q0) + 1] * B * B + e0, v[uu]);
-        }
+    for (int it = 0; it < IT; it++) {
+        const int q0 = beg + slot + it * P * U;
+#pragma unroll
+        for (int uu = 0; uu < U; uu++) wn_rawload<DTI, VW>(keep[it][uu], a.w, off(q0 + P * uu));
 #pragma unroll
         for (int uu = 0; uu < U; uu++)
-            if (q0 + P * uu < end)
+            if (q0 + P * uu < end) {
+                float v[VW];
+                wn_rawcvt<DTI, VW>(keep[it][uu], v);
 #pragma unroll
-                for (int i = 0; i < VW; i++) ss[i] += v[uu][i] * v[uu][i];
+                for (int i = 0; i < VW; i++) ss[i] += v[i] * v[i];
+            }
+    }
+    for (int q0 = beg + slot + IT * P * U; q0 < end; q0 += P * U) {
+        WnRaw<DTI, VW> r[U];
+#pragma unroll
+        for (int uu = 0; uu < U; uu++) wn_rawload<DTI, VW>(r[uu], a.w, off(q0 + P * uu));
+#pragma unroll
+        for (int uu = 0; uu < U; uu++)
+            if (q0 + P * uu < end) {
+                float v[VW];
+                wn_rawcvt<DTI, VW>(r[uu], v);
+#pragma unroll
+                for (int i = 0; i < VW; i++) ss[i] += v[i] * v[i];
+            }
     }
     float s, unused;
-    wn_colsum<B, VW, VR>(ss, zero, ra, rb, s, unused);
+    wn_colsum<B, VW, VR, false>(ss, ss, ra, rb, s, unused);
     if (t < B) {
         const int o = k * B + t;
         const float n = sqrtf(fmaxf(s, a.eps));
@@ -145,56 +183,83 @@ __global__ __launch_bounds__(kWnThreads) void wn_fwd(WnArgs a) {
     float sc[VW];
 #pragma unroll
     for (int i = 0; i < VW; i++) sc[i] = scale[(e0 + i) % B];
-    for (int q0 = beg + slot; q0 < end; q0 += P * U) {   // U loads in flight, then U stores
-        float v[U][VW];
-        int64_t idx[U];
+    auto put = [&](const WnRaw<DTI, VW>& r, int q) {
+        float v[VW];
+        wn_rawcvt<DTI, VW>(r, v);
+#pragma unroll
+        for (int i = 0; i < VW; i++) v[i] *= sc[i];
+        wn_storev<DTO, VW>(a.out, off(q), v);
+    };
+#pragma unroll
+    for (int it = 0; it < IT; it++)
 #pragma unroll
         for (int uu = 0; uu < U; uu++) {
-            const int q = q0 + P * uu;
-            idx[uu] = (int64_t)a.colent[2 * (q < end ? q : q0) + 1] * B * B + e0;
-            wn_loadv<DTI, VW>(a.w, idx[uu], v[uu]);
+            const int q = beg + slot + it * P * U + P * uu;
+            if (q < end) put(keep[it][uu], q);
         }
+    for (int q0 = beg + slot + IT * P * U; q0 < end; q0 += P * U) {   // U loads in flight, then U stores
+        WnRaw<DTI, VW> r[U];
+#pragma unroll
+        for (int uu = 0; uu < U; uu++) wn_rawload<DTI, VW>(r[uu], a.w, off(q0 + P * uu));
 #pragma unroll
         for (int uu = 0; uu < U; uu++)
-            if (q0 + P * uu < end) {
-#pragma unroll
-                for (int i = 0; i < VW; i++) v[uu][i] *= sc[i];
-                wn_storev<DTO, VW>(a.out, idx[uu], v[uu]);
-            }
+            if (q0 + P * uu < end) put(r[uu], q0 + P * uu);
     }
 }
 
 template <int B, int DTI, int DTD>
 __global__ __launch_bounds__(kWnThreads) void wn_bwd(WnArgs a) {
     using Map = WnMap<B, DTI>;
-    constexpr int VW = Map::VW, VR = Map::VR, VB = Map::VB, P = Map::P, U = Map::U;
-    __shared__ float ra[kWnThreads * VW], rb[kWnThreads * VW], ca[B], cb[B];
+    constexpr int VW = Map::VW, VR = Map::VR, VB = Map::VB, P = Map::P, U2 = Map::U / 2, IT = 1;
+    __shared__ float ra[kWnThreads / 64 * B], rb[kWnThreads / 64 * B], ca[B], cb[B];
     const int k = blockIdx.x, t = threadIdx.x;
     const int beg = a.colptr[k], end = a.colptr[k + 1];
     const int slot = t / VB, e0 = (t % VB) * VW;
     float ss[VW], sd[VW];
 #pragma unroll
     for (int i = 0; i < VW; i++) ss[i] = sd[i] = 0.f;
-    for (int q0 = beg + slot; q0 < end; q0 += P * (U / 2)) {   // two tensors: U/2 blocks
-        float w[U / 2][VW], d[U / 2][VW];
+    auto off = [&](int q) { return (int64_t)a.colent[2 * (q < end ? q : beg) + 1] * B * B + e0; };
+    // two tensors: U/2 blocks per round
+    WnRaw<DTI, VW> kw[IT][U2];
+    WnRaw<DTD, VW> kd[IT][U2];
+    auto sums = [&](const WnRaw<DTI, VW>& rw, const WnRaw<DTD, VW>& rd) {
+        float w[VW], d[VW];
+        wn_rawcvt<DTI, VW>(rw, w);
+        wn_rawcvt<DTD, VW>(rd, d);
 #pragma unroll
-        for (int uu = 0; uu < U / 2; uu++) {
-            const int q = q0 + P * uu;
-            const int64_t idx = (int64_t)a.colent[2 * (q < end ? q : q0) + 1] * B * B + e0;
-            wn_loadv<DTI, VW>(a.w, idx, w[uu]);
-            wn_loadv<DTD, VW>(a.dy, idx, d[uu]);
+        for (int i = 0; i < VW; i++) {
+            ss[i] += w[i] * w[i];
+            sd[i] += d[i] * w[i];
+        }
+    };
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int q0 = beg + slot + it * P * U2;
+#pragma unroll
+        for (int uu = 0; uu < U2; uu++) {
+            const int64_t idx = off(q0 + P * uu);
+            wn_rawload<DTI, VW>(kw[it][uu], a.w, idx);
+            wn_rawload<DTD, VW>(kd[it][uu], a.dy, idx);
         }
 #pragma unroll
-        for (int uu = 0; uu < U / 2; uu++)
-            if (q0 + P * uu < end)
+        for (int uu = 0; uu < U2; uu++)
+            if (q0 + P * uu < end) sums(kw[it][uu], kd[it][uu]);
+    }
+    for (int q0 = beg + slot + IT * P * U2; q0 < end; q0 += P * U2) {
+        WnRaw<DTI, VW> rw[U2];
+        WnRaw<DTD, VW> rd[U2];
 #pragma unroll
-                for (int i = 0; i < VW; i++) {
-                    ss[i] += w[uu][i] * w[uu][i];
-                    sd[i] += d[uu][i] * w[uu][i];
-                }
+        for (int uu = 0; uu < U2; uu++) {
+            const int64_t idx = off(q0 + P * uu);
+            wn_rawload<DTI, VW>(rw[uu], a.w, idx);
+            wn_rawload<DTD, VW>(rd[uu], a.dy, idx);
+        }
+#pragma unroll
+        for (int uu = 0; uu < U2; uu++)
+            if (q0 + P * uu < end) sums(rw[uu], rd[uu]);
     }
     float s2, s1;
-    wn_colsum<B, VW, VR>(ss, sd, ra, rb, s2, s1);
+    wn_colsum<B, VW, VR, true>(ss, sd, ra, rb, s2, s1);
     if (t < B) {
         const int o = k * B + t;
         const float n = sqrtf(fmaxf(s2, a.eps));
@@ -210,25 +275,33 @@ __global__ __launch_bounds__(kWnThreads) void wn_bwd(WnArgs a) {
         c1[i] = ca[(e0 + i) % B];
         c2[i] = cb[(e0 + i) % B];
     }
-    constexpr int U2 = U / 2;
-    for (int q0 = beg + slot; q0 < end; q0 += P * U2) {
-        float w[U2][VW], d[U2][VW];
-        int64_t idx[U2];
+    auto put = [&](const WnRaw<DTI, VW>& rw, const WnRaw<DTD, VW>& rd, int q) {
+        float w[VW], d[VW], r[VW];
+        wn_rawcvt<DTI, VW>(rw, w);
+        wn_rawcvt<DTD, VW>(rd, d);
+#pragma unroll
+        for (int i = 0; i < VW; i++) r[i] = c1[i] * d[i] - c2[i] * w[i];
+        wn_storev<BSMM_F32, VW>(a.out, off(q), r);
+    };
+#pragma unroll
+    for (int it = 0; it < IT; it++)
 #pragma unroll
         for (int uu = 0; uu < U2; uu++) {
-            const int q = q0 + P * uu;
-            idx[uu] = (int64_t)a.colent[2 * (q < end ? q : q0) + 1] * B * B + e0;
-            wn_loadv<DTI, VW>(a.w, idx[uu], w[uu]);
-            wn_loadv<DTD, VW>(a.dy, idx[uu], d[uu]);
+            const int q = beg + slot + it * P * U2 + P * uu;
+            if (q < end) put(kw[it][uu], kd[it][uu], q);
+        }
+    for (int q0 = beg + slot + IT * P * U2; q0 < end; q0 += P * U2) {
+        WnRaw<DTI, VW> rw[U2];
+        WnRaw<DTD, VW> rd[U2];
+#pragma unroll
+        for (int uu = 0; uu < U2; uu++) {
+            const int64_t idx = off(q0 + P * uu);
+            wn_rawload<DTI, VW>(rw[uu], a.w, idx);
+            wn_rawload<DTD, VW>(rd[uu], a.dy, idx);
         }
 #pragma unroll
         for (int uu = 0; uu < U2; uu++)
-            if (q0 + P * uu < end) {
-                float r[VW];
-#pragma unroll
-                for (int i = 0; i < VW; i++) r[i] = c1[i] * d[uu][i] - c2[i] * w[uu][i];
-                wn_storev<BSMM_F32, VW>(a.out, idx[uu], r);
-            }
+            if (q0 + P * uu < end) put(rw[uu], rd[uu], q0 + P * uu);
     }
 }
 
