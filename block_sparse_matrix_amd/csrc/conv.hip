@@ -508,6 +508,182 @@ __global__ __launch_bounds__(512) void conv_mfma_updat_kernel(ConvArgs a) {
     }
 }
 
+// Filter gradient, row form (2-D / 1-D, stride 1, dilation 1, 16-bit; Bc and Bk of 16,
+// 32 or 64; input and output widths multiples of 8; column shifts s - pad of at most 3
+// either way).  One workgroup (8 waves) per (block, filter row r, part) owns
+// dF[b, :, (r, s), :] for every column tap s: each step of SP output positions (whole
+// 8-position pieces of output rows, flattened row-major) stages the dO values once and
+// the input row pieces once per shift s (aligned 16-byte loads of the three 8-element
+// chunks around each piece, shifted in registers: conv_shifted), so the step's dO
+// fragment feeds all S taps.  Against one workgroup per tap this reads each input and
+// dO value once per filter row instead of once per tap, with 16-byte loads instead of
+// per-element gathers.  Waves take 16x16 (j, i) tiles; with fewer than 8 tiles the
+// waves of a tile split the step's 32-deep chunks and their partial tiles are added in
+// wave order at the end.  One writer per output, fixed summation order.
+template <int DT, int SP, int TPW>
+__global__ __launch_bounds__(512) void conv_updat_rows_kernel(ConvArgs a) {
+    constexpr int XP = SP + 8, NTH = 512, NCH = SP / 8, KK = SP / 32;
+    constexpr int MI = (64 * NCH + NTH - 1) / NTH;   // staging items per thread (<= 64 channels)
+    constexpr int SMAX = 7;
+    extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
+    const int S = a.S, R = a.R, RS = R * S;
+    const int part = blockIdx.x % a.nparts, br = blockIdx.x / a.nparts;
+    const int b = br / R, r = br % R;
+    const int Bc = a.Bc, Bk = a.Bk;
+    const int H = a.H, W = a.W, P = a.P, Q = a.Q;
+    const int64_t PQ = (int64_t)P * Q, HW = (int64_t)H * W;
+    const int64_t nsteps_img = (PQ + SP - 1) / SP, nsteps = a.N * nsteps_img;
+    const int64_t st0 = nsteps * part / a.nparts, st1 = nsteps * (part + 1) / a.nparts;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int ph = a.pad[1], pw = a.pad[2];
+    const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
+    const uint16_t* dO = (const uint16_t*)a.b;
+    __shared__ int sch[128];   // the block's input channels, then its output channels
+    if (t < Bc) sch[t] = a.cidx[b * Bc + t];
+    if (t < Bk) sch[64 + t] = a.kidx[b * Bk + t];
+    __syncthreads();
+
+    u32x4 vin[MI][3], vd[MI];
+    auto load = [&](int64_t st) {
+        const bool sv = st < nsteps;
+        const int64_t n = sv ? st / nsteps_img : 0;
+        const int p0 = sv ? (int)(st % nsteps_img) * SP : 0;
+#pragma unroll
+        for (int u = 0; u < MI; u++) {
+            const int item = t + NTH * u, c = item / NCH, ch = item % NCH;
+            const int p = p0 + 8 * ch;
+            const int y = p / Q, x0 = p % Q, yi = y + r - ph;
+            const bool ok = sv && c < Bc && p < PQ && yi >= 0 && yi < H;
+            const int64_t row = ok ? ((n * a.C + sch[c]) * HW + (int64_t)yi * W) : 0;
+            auto chunk = [&](int xx) {   // an aligned 8-element chunk, wholly inside or outside the row
+                return bload128(rin, ok && xx >= 0 && xx < W ? (uint32_t)((row + xx) * 2) : kOffLane, 0);
+            };
+            vin[u][0] = chunk(x0 - 8);
+            vin[u][1] = chunk(x0);
+            vin[u][2] = chunk(x0 + 8);
+            const int k = item / NCH;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (sv && k < Bk && p < PQ) v = *reinterpret_cast<const u32x4*>(dO + (n * a.K + sch[64 + k]) * PQ + p);
+            vd[u] = v;
+        }
+    };
+    BSMM_LDS uint16_t* smi = (BSMM_LDS uint16_t*)dsm;          // [buf][s][c][XP]
+    BSMM_LDS uint16_t* smd = smi + 2 * S * Bc * XP;             // [buf][k][XP]
+    auto stage = [&](int buf) {
+        BSMM_LDS uint16_t* li = smi + buf * S * Bc * XP;
+        BSMM_LDS uint16_t* ld = smd + buf * Bk * XP;
+#pragma unroll
+        for (int u = 0; u < MI; u++) {
+            const int item = t + NTH * u, c = item / NCH, ch = item % NCH;
+            if (c < Bc) {
+                const uint32_t w12[12] = {vin[u][0].x, vin[u][0].y, vin[u][0].z, vin[u][0].w, vin[u][1].x, vin[u][1].y,
+                                          vin[u][1].z, vin[u][1].w, vin[u][2].x, vin[u][2].y, vin[u][2].z, vin[u][2].w};
+                for (int sh = 0; sh < S; sh++) {
+                    u32x4 v;
+                    switch (sh - pw) {
+                    case -3: v = conv_shifted<-3>(w12); break;
+                    case -2: v = conv_shifted<-2>(w12); break;
+                    case -1: v = conv_shifted<-1>(w12); break;
+                    case 0: v = conv_shifted<0>(w12); break;
+                    case 1: v = conv_shifted<1>(w12); break;
+                    case 2: v = conv_shifted<2>(w12); break;
+                    default: v = conv_shifted<3>(w12); break;
+                    }
+                    lds_store16(li + (sh * Bc + c) * XP + 8 * ch, v);
+                }
+            }
+            if (item / NCH < Bk) lds_store16(ld + (item / NCH) * XP + 8 * ch, vd[u]);
+        }
+    };
+    // tiles of the (Bk/16) x (Bc/16) grid: wave w takes tiles w, w+8 (TPW of them) over the
+    // whole step, or, with fewer than 8 tiles, tile w % ntile and part w / ntile of the
+    // step's 32-deep chunks
+    const int tj = Bk / 16, ntile = tj * (Bc / 16);
+    const int nh = ntile >= 8 ? 1 : 8 / ntile, half = ntile >= 8 ? 0 : wave / ntile;
+    const int kk0 = half * KK / nh, kk1 = (half + 1) * KK / nh;
+    f32x4 acc[TPW][SMAX];
+#pragma unroll
+    for (int u = 0; u < TPW; u++)
+#pragma unroll
+        for (int sh = 0; sh < SMAX; sh++) acc[u][sh] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(st0);
+    for (int64_t st = st0; st < st1; st++) {
+        const int buf = (int)((st - st0) & 1);
+        stage(buf);
+        __syncthreads();
+        load(st + 1);   // in flight during this step's products
+        const BSMM_LDS uint16_t* li = smi + buf * S * Bc * XP;
+        const BSMM_LDS uint16_t* ld = smd + buf * Bk * XP;
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int tile = ntile >= 8 ? wave + 8 * u : wave % ntile;
+            const int jt = tile % tj, it = tile / tj;
+            for (int kk = kk0; kk < kk1; kk++) {
+                const u32x4 fb = *reinterpret_cast<const BSMM_LDS u32x4*>(ld + (jt * 16 + m16) * XP + kk * 32 + 8 * g4);
+#pragma unroll
+                for (int sh = 0; sh < SMAX; sh++)
+                    if (sh < S) {
+                        const u32x4 fa = *reinterpret_cast<const BSMM_LDS u32x4*>(
+                            li + (sh * Bc + it * 16 + m16) * XP + kk * 32 + 8 * g4);
+                        mma<DT>(acc[u][sh], fb, fa);   // D[j][i]: lane holds j = 4*g4 + v, i = m16
+                    }
+            }
+        }
+        // the other buffer is rewritten next step, after the barrier that follows its stage
+    }
+    // partial tiles of a tile's waves (ntile < 8), added in wave order
+    f32x4* red = reinterpret_cast<f32x4*>(dsm);   // [wave][tap][lane]
+    if (nh > 1) {
+        __syncthreads();   // the step buffers are no longer read
+        if (half > 0)
+#pragma unroll
+            for (int sh = 0; sh < SMAX; sh++)
+                if (sh < S) red[(wave * SMAX + sh) * 64 + lane] = acc[0][sh];
+        __syncthreads();
+        if (half == 0)
+            for (int hh = 1; hh < nh; hh++)
+#pragma unroll
+                for (int sh = 0; sh < SMAX; sh++)
+                    if (sh < S) acc[0][sh] += red[((wave + hh * ntile) * SMAX + sh) * 64 + lane];
+    }
+    if (half > 0) return;
+#pragma unroll
+    for (int u = 0; u < TPW; u++) {
+        const int tile = ntile >= 8 ? wave + 8 * u : wave % ntile;
+        if (tile >= ntile) continue;
+        const int jt = tile % tj, it = tile / tj;
+        const int i = it * 16 + m16;
+#pragma unroll
+        for (int sh = 0; sh < SMAX; sh++) {
+            if (sh >= S) continue;
+            const int tap = r * S + sh;
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int j = jt * 16 + 4 * g4 + v;
+                const int64_t e = (((int64_t)b * Bc + i) * RS + tap) * Bk + j;
+                if (a.nparts > 1)
+                    a.ws[(int64_t)part * a.nb * Bc * RS * Bk + e] = acc[u][sh][v];
+                else
+                    ((float*)a.out)[e] = acc[u][sh][v];
+            }
+        }
+    }
+}
+
+// Positions per step of the row-form filter gradient (its LDS: two buffers of S input
+// copies and the dO values), or 0 when the shape does not fit it.
+static int conv_updat_rows_sp(const ConvArgs& a) {
+    if (!conv_mfma_updat_ok(a)) return 0;
+    if ((a.Bc != 16 && a.Bc != 32 && a.Bc != 64) || (a.Bk != 16 && a.Bk != 32 && a.Bk != 64)) return 0;
+    if (a.W % 8 != 0 || a.Q % 8 != 0 || a.S > 7 || a.pad[2] > 3 || a.S - 1 - a.pad[2] > 3) return 0;
+    for (int sp : {256, 128}) {
+        const int64_t lds = 2LL * (a.S * a.Bc + a.Bk) * (sp + 8) * 2;
+        if (lds <= 160 * 1024) return sp;
+    }
+    return 0;
+}
+
 // Sum of the filter gradient's parts in part order (deterministic).
 __global__ __launch_bounds__(256) void conv_updat_reduce(ConvArgs a, int64_t E) {
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < E; e += (int64_t)gridDim.x * 256) {
@@ -518,7 +694,7 @@ __global__ __launch_bounds__(256) void conv_updat_reduce(ConvArgs a, int64_t E) 
 }
 
 int conv_updat_parts(const ConvArgs& a) {
-    const int64_t wgs = (int64_t)a.nb * a.R * a.S;
+    const int64_t wgs = (int64_t)a.nb * a.R * (conv_updat_rows_sp(a) ? 1 : a.S);
     const int64_t steps = a.N * (((int64_t)a.P * a.Q + 255) / 256);
     int64_t p = wgs > 0 ? (4096 + wgs - 1) / wgs : 1;   // ~16 workgroups per compute unit
     if (p > 16) p = 16;
@@ -603,6 +779,29 @@ static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
     if constexpr (DT != BSMM_F32) {
         if (a.mfma && pass == 0) return launch_conv_mfma<DT, false>(a, st);
         if (a.mfma && pass == 1) return launch_conv_mfma<DT, true>(a, st);
+    }
+    if (pass == 2 && DT != BSMM_F32 && conv_updat_rows_sp(a)) {
+        const int sp = conv_updat_rows_sp(a);
+        const int64_t wgs = (int64_t)a.nb * a.R * a.nparts;
+        if (wgs == 0) return hipSuccess;
+        if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
+        const int ntile = (a.Bc / 16) * (a.Bk / 16);
+        const int64_t lds = std::max<int64_t>(2LL * (a.S * a.Bc + a.Bk) * (sp + 8) * 2, 8LL * 7 * 64 * 16);
+        void *e0 = nullptr, *e1 = nullptr;
+        prof_events(BSMM_PASS_CONV_UPDAT, &e0, &e1);
+        auto kern = sp == 256 ? (ntile > 8 ? conv_updat_rows_kernel<DT, 256, 2> : conv_updat_rows_kernel<DT, 256, 1>)
+                              : (ntile > 8 ? conv_updat_rows_kernel<DT, 128, 2> : conv_updat_rows_kernel<DT, 128, 1>);
+        if (e0 || e1)
+            hipExtLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(512), (uint32_t)lds, st, (hipEvent_t)e0,
+                                  (hipEvent_t)(a.nparts == 1 ? e1 : nullptr), 0, a);
+        else
+            hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(512), (uint32_t)lds, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.nparts == 1) return e;
+        const int64_t E = (int64_t)a.nb * a.Bc * a.R * a.S * a.Bk;
+        int64_t rg = (E + 255) / 256;
+        if (rg > 4096) rg = 4096;
+        return launch_ev(conv_updat_reduce, dim3((unsigned)rg), dim3(256), st, nullptr, e1, a, E);
     }
     if (pass == 2 && DT != BSMM_F32 && conv_mfma_updat_ok(a)) {
         const int64_t wgs = (int64_t)a.nb * a.R * a.S * a.nparts;
