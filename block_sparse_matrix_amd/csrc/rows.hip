@@ -28,7 +28,11 @@
 //      transposing LDS read.
 //   fp32 uses four 16x16x4 steps per 16 contraction values: lane group g's four values
 //   in step u are contraction indices 16 u + 4 g .. 16 u + 4 g + 3, the same map for
-//   both operands.
+//   both operands.  fp32 bprop loads the dy rows and the weight rows in row order,
+//   four consecutive lanes covering one row's 64 bytes, which the memory path serves
+//   several times faster than the fragment order (consecutive lanes on different rows);
+//   a lane permutation in registers (ds_bpermute) then forms the fragments (bprop
+//   11 % faster; fprop, with its 8-byte weight loads, gained nothing from it).
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -41,6 +45,14 @@ __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+// 16 rows x 64 bytes loaded in row order (lane l: row l / 4, 16-byte chunk l % 4) to the
+// fragment order (lane l: row l % 16, chunk l / 16): lane l takes lane 4 (l % 16) + l / 16.
+__device__ __forceinline__ u32x4 rows_to_frag(const u32x4& v, int lane) {
+    const int src = (4 * (lane & 15) + (lane >> 4)) * 4;
+    return u32x4{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x), (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.y),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.z), (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.w)};
+}
+
 template <int DT, bool TW> struct RowsCfgT {
     static constexpr bool F32 = DT == BSMM_F32;
     static constexpr int S = F32 ? 4 : 2;
@@ -49,6 +61,7 @@ template <int DT, bool TW> struct RowsCfgT {
     static constexpr int U = F32 ? 2 : 1;        // activation loads per tile and block
     static constexpr int WR = F32 ? (TW ? 4 : 8) : 2;
     static constexpr int WPITCH = 40;            // staged weight row pitch, 16-bit elements
+    static constexpr bool XROW = F32 && TW;      // fp32 bprop: rows loaded in row order
     // output feature (within the block) of lane row r in output tile t
     static __device__ __forceinline__ int qmap(int t, int r) { return W8 ? 2 * r + t : 16 * t + r; }
 };
@@ -67,6 +80,17 @@ __device__ __forceinline__ void rows_compute(f32x4 (&acc)[MT][2], const RowsSlot
                                               BSMM_LDS uint16_t* wt, int lane) {
     using C = RowsCfgT<DT, TW>;
     if constexpr (C::F32) {
+        u32x4 xf[MT * 2];   // activation fragments
+#pragma unroll
+        for (int i = 0; i < MT * 2; i++) xf[i] = C::XROW ? rows_to_frag(sl.x[i], lane) : sl.x[i];
+        typename std::conditional<C::W8, u32x2, u32x4>::type wf[C::WR];
+#pragma unroll
+        for (int i = 0; i < C::WR; i++) {
+            if constexpr (C::W8)
+                wf[i] = sl.w[i];
+            else
+                wf[i] = rows_to_frag(sl.w[i], lane);   // bprop weight rows, loaded in row order
+        }
 #pragma unroll
         for (int u = 0; u < 2; u++)
 #pragma unroll
@@ -75,12 +99,12 @@ __device__ __forceinline__ void rows_compute(f32x4 (&acc)[MT][2], const RowsSlot
                 for (int mt = 0; mt < MT; mt++)
 #pragma unroll
                     for (int t = 0; t < 2; t++) {
-                        const uint32_t av = sl.x[mt * 2 + u][v];
+                        const uint32_t av = xf[mt * 2 + u][v];
                         uint32_t bv;
                         if constexpr (C::W8)
-                            bv = sl.w[u * 4 + v][t];
+                            bv = wf[u * 4 + v][t];
                         else
-                            bv = sl.w[t * 2 + u][v];
+                            bv = wf[t * 2 + u][v];
                         acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av), __uint_as_float(bv),
                                                                           acc[mt][t], 0, 0, 0);
                     }
@@ -145,7 +169,10 @@ __global__ __launch_bounds__(64 * WAVES) void rows_kernel(MMArgs a) {
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int n = n0 + 16 * mt + r16, k0 = C::F32 ? 16 * u + 4 * g : 8 * g;
+            // fp32 bprop: row order (lane l: row l / 4, values 16 u + 4 (l % 4) ..); else
+            // fragment order (lane l: row l % 16, values 16 u + 4 (l / 16) .. or 8 (l / 16) ..)
+            const int n = n0 + 16 * mt + (C::XROW ? lane >> 2 : r16);
+            const int k0 = C::F32 ? 16 * u + 4 * (C::XROW ? lane & 3 : g) : 8 * g;
             xo[mt * U + u] = n < N ? ((uint32_t)n * (uint32_t)a.fin + k0) * S : kOffLane;
         }
     uint32_t wo[WR];
@@ -153,8 +180,8 @@ __global__ __launch_bounds__(64 * WAVES) void rows_kernel(MMArgs a) {
     for (int i = 0; i < WR; i++) {
         if constexpr (C::W8)
             wo[i] = (uint32_t)(((16 * (i / 4) + 4 * g + i % 4) * B + 2 * r16) * S);
-        else if constexpr (C::F32)
-            wo[i] = (uint32_t)(((16 * (i / 2) + r16) * B + 16 * (i % 2) + 4 * g) * S);
+        else if constexpr (C::F32)   // row order, as the activations
+            wo[i] = (uint32_t)(((16 * (i / 2) + (lane >> 2)) * B + 16 * (i % 2) + 4 * (lane & 3)) * S);
         else if constexpr (C::WTR)
             wo[i] = (uint32_t)((((lane + 64 * i) >> 2) * B + 8 * ((lane + 64 * i) & 3)) * S);
         else

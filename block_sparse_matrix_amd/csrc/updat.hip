@@ -1097,7 +1097,9 @@ static hipError_t launch_updat_runs(const UpArgs& a, hipStream_t st) {
 template <int DT, int B, int RD>
 __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
     constexpr int TF = kSmallTileFeat, Q = kSmallQuads, KS = 32, IPQ = B == 8 ? 4 : 1;
-    __shared__ __attribute__((aligned(16))) uint16_t stg[2][TF * KS];
+    constexpr int PITCH = KS + 8;   // staged row: 32 values + 16 bytes (fragment reads hit every bank once)
+    __shared__ __attribute__((aligned(16))) uint16_t stg[2][TF * PITCH];          // dy rows of the tile
+    __shared__ __attribute__((aligned(16))) uint16_t xst[2][16 * 16 * PITCH];     // x rows, 16 per wave
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // quad row
     const int r16 = lane & 15, g = lane >> 4;
@@ -1120,16 +1122,19 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
     const int spt = N / KS + (N % KS ? 1 : 0);
     const int nsteps = a.G * spt;
 
-    // x fragment: feature fx0 + 16 w + r16, columns n0 + 8 g ..; wave w stages the dy
-    // fragment of quad column w the same way: feature fy0 + 16 w + r16, columns n0 + 8 g
-    // .. (N % 8 == 0: an 8-column chunk is all in or all out).  The stage holds each quad
-    // column's fragment as the 64 lanes' 16-byte pieces in lane order (1 KB), so that
-    // both the stage writes and the fragment reads are plain consecutive 16-byte
-    // accesses, which the LDS serves at full rate.
-    const int fx = fx0 + 16 * qr + r16, fy = fy0 + 16 * w + r16;
-    const uint32_t xo = fx < a.C ? (uint32_t)fx * N * 2u + 16u * g : kOffLane;
-    const uint32_t yo = fy < a.K ? (uint32_t)fy * N * 2u + 16u * g : kOffLane;
-    const int ql = w * 512 + lane * 8;   // stage slot of thread t
+    // Loads go row by row: lane l takes row l / 4 of the wave's 16 feature rows, columns
+    // n0 + 8 (l % 4) .. (four consecutive lanes read one row's 64 bytes, which the memory
+    // path serves several times faster than the matrix-core fragment order, where
+    // consecutive lanes hold different rows).  Wave w loads the 16 x rows of its quad
+    // row (features fx0 + 16 qr ..) and the 16 dy rows of quad column w (fy0 + 16 w ..);
+    // both go to LDS as rows, and the fragments are read back from there.  (N % 8 == 0:
+    // an 8-column chunk is all in or all out.)
+    const int lr = lane >> 2, lc = lane & 3;
+    const int fx = fx0 + 16 * qr + lr, fy = fy0 + 16 * w + lr;
+    const uint32_t xo = fx < a.C ? (uint32_t)fx * N * 2u + 16u * lc : kOffLane;
+    const uint32_t yo = fy < a.K ? (uint32_t)fy * N * 2u + 16u * lc : kOffLane;
+    const int ql = (16 * w + lr) * PITCH + 8 * lc;   // this lane's stage slot (dy row 16 w + l / 4)
+    const int xl = w * 16 * PITCH + lr * PITCH + 8 * lc;   // and its x slot
     struct Slot {
         u32x4 x, y;
     };
@@ -1141,13 +1146,14 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
         pick(a, tt, rx, ry);
         const uint32_t so = sv ? (uint32_t)n0 * 2u : kOffOff;
         // a chunk past N is switched off with the top offset bit (no branch)
-        const uint32_t off = ((uint32_t)(N - 1 - n0 - 8 * g) >> 31) << 31;
+        const uint32_t off = ((uint32_t)(N - 1 - n0 - 8 * lc) >> 31) << 31;
         sl.x = bload128(rx, xo | off, so);
         sl.y = bload128(ry, yo | off, so);
     };
-    // dy fragment of quad column j: its 1 KB of the stage (j * 512 elements), this
-    // lane's 16 bytes
-    const int boff = lane * 8;
+    // fragments: lane l holds row l % 16, columns 8 (l / 16) ..; dy of quad column j at
+    // stage row 16 j + l % 16, x at this wave's row l % 16
+    const int boff = r16 * PITCH + 8 * g;
+    const int xf = w * 16 * PITCH + r16 * PITCH + 8 * g;
     f32x4 acc[Q];
 #pragma unroll
     for (int j = 0; j < Q; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1160,6 +1166,7 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_store16((BSMM_LDS uint16_t*)stg[0] + ql, ring[0].y);
+        lds_store16((BSMM_LDS uint16_t*)xst[0] + xl, ring[0].x);
         __syncthreads();
         for (int s0 = 0; s0 < nsteps; s0 += RD) {
 #pragma unroll
@@ -1167,6 +1174,7 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
                 const int s = s0 + i;
                 const BSMM_LDS uint16_t* cur = (const BSMM_LDS uint16_t*)stg[s & 1] + boff;
                 if (s < nsteps) {
+                    const u32x4 xfr = *reinterpret_cast<const BSMM_LDS u32x4*>((const BSMM_LDS uint16_t*)xst[s & 1] + xf);
 #pragma unroll
                     for (int k = 0; k < Q / 4; k++) {
                         if (k < ngr) {   // uniform
@@ -1177,17 +1185,18 @@ __global__ __launch_bounds__(1024) void upds_kernel(UpArgs a) {
                             u32x4 bf[4];
 #pragma unroll
                             for (int q = 0; q < 4; q++)
-                                if (4 * k + q < cnt) bf[q] = *reinterpret_cast<const BSMM_LDS u32x4*>(cur + ((ek >> (8 * q)) & 15u) * 512);
+                                if (4 * k + q < cnt) bf[q] = *reinterpret_cast<const BSMM_LDS u32x4*>(cur + ((ek >> (8 * q)) & 15u) * 16 * PITCH);
                             __builtin_amdgcn_sched_barrier(0);   // the group's reads in flight first
 #pragma unroll
                             for (int q = 0; q < 4; q++)
-                                if (4 * k + q < cnt) mma<DT>(acc[4 * k + q], ring[i].x, bf[q]);   // D[x f][dy f]
+                                if (4 * k + q < cnt) mma<DT>(acc[4 * k + q], xfr, bf[q]);   // D[x f][dy f]
                         }
                     }
                 }
                 // stage step s + 1 (loaded RD - 1 steps ago), then refill this slot
                 BSMM_LDS uint16_t* nxt = (BSMM_LDS uint16_t*)stg[(s + 1) & 1];
                 lds_store16(nxt + ql, ring[(i + 1) % RD].y);
+                lds_store16((BSMM_LDS uint16_t*)xst[(s + 1) & 1] + xl, ring[(i + 1) % RD].x);
                 issue(ring[i], s + RD, pick);
                 __syncthreads();
             }
