@@ -1054,17 +1054,17 @@ static hipError_t launch_updat_runs_t(const UpArgs& a, hipStream_t st) {
     return launch(BSMM_PASS_UPDAT, updr_kernel<DT, 2, RL>, dim3((unsigned)grid), dim3(256), st, a);
 }
 
-// Blocks per wave: 1 for fp32 (the contraction is the work: more waves hide more
-// latency), 2 for 16-bit storage (measured on the 4096-wide N = 64 workload among 1, 2,
-// 4 and 8: fp32 20.4 / 21.2 / 27.4 / 30.2 us, bf16 10.6 / 10.1 / 10.8 / 10.9 us).
+// Blocks per wave: 1 (more waves hide more latency; measured on the 4096-wide N = 64
+// workload among 1, 2, 4 and 8: fp32 20.4 / 21.2 / 27.4 / 30.2 us; bf16 in alternating
+// runs on one box 9.3-9.9 us with 1 against 10.1-10.6 with 2, 10.3-10.4 with 4).
 // BSMM_UPDAT_RUN=<1|2|4|8> (read once) overrides it for A/B measurements.
-static int updat_run_len(int dt) {
+static int updat_run_len(int) {
     static const int forced = [] {
         const char* e = getenv("BSMM_UPDAT_RUN");
         return e ? atoi(e) : 0;
     }();
     if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
-    return dt == BSMM_F32 ? 1 : 2;
+    return 1;
 }
 
 template <int DT>
