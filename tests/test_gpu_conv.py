@@ -93,6 +93,7 @@ MFMA_CASES = [
     (2, 64, 64, 32, 32, 4, (2, 2), (8, 8), "SAME"),     # even filter: the odd pad after
     (4, 32, 32, 32, 32, 1, (7,), (48,), "SAME"),        # 1-D, width a multiple of 8: shifts -3 .. 3
     (2, 64, 64, 32, 32, 3, (1, 5), (8, 24), "SAME"),    # width a multiple of 8: shifts -2 .. 2
+    (2, 64, 32, 32, 16, 4, (3, 3), (8, 16), "SAME"),    # row-form filter gradient, 2 tiles of 16x16
 ]
 
 
@@ -187,3 +188,30 @@ def test_bench_configuration_sampled_images():
     sub = (bck[0][blocks], bck[1][blocks])
     ref = oc.updat(sub, _f64(P.I), _f64(P.dO), g).reshape((len(blocks),) + tuple(dF.shape[1:]))
     assert_close(dF[blocks], ref, "bf16", "updat")
+
+
+@pytest.mark.parametrize("Bc,Bk,TRS,DHW,pad", [
+    (16, 16, (3, 3), (8, 16), "SAME"),    # one 16x16 tile: 8 waves split each step
+    (16, 32, (2, 1), (6, 8), "VALID"),    # two tiles, an even filter height
+    (64, 16, (3, 3), (9, 8), 1),          # four tiles, explicit padding
+    (64, 64, (1, 3), (4, 24), "SAME"),    # sixteen tiles: two per wave
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_conv_filter_gradient_rows(Bc, Bk, TRS, DHW, pad, dtype):
+    """The row-form matrix-core filter gradient (one workgroup per block and filter row,
+    every column tap of the row) for every tile count a wave split can take, against the
+    oracle; deterministic."""
+    print(f"case conv rows Bc={Bc} Bk={Bk} {TRS} {DHW} {pad} {dtype}", flush=True)
+    N, C, K = 3, 2 * Bc, 2 * Bk
+    g = oc.geometry(TRS, DHW, padding=pad)
+    MPQ = g[2][3 - len(DHW):]
+    rng = np.random.default_rng(Bc * 7 + Bk + len(TRS))
+    P = synth.conv_problem(rng, N, C, K, Bc, Bk, 3, TRS, DHW, MPQ, dtype, contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, padding=pad)
+    assert conv.kernel_name("updat", synth.DTYPES[dtype]) == "matrix_core"
+    I, dO = dev(P.I), dev(P.dO)
+    dF = conv.updat(I, dO)
+    torch.cuda.synchronize()
+    ref = oc.updat(oc.split_bck(P.BCK), _f64(P.I), _f64(P.dO), g).reshape(dF.shape)
+    assert_close(dF, ref, dtype, "row-form filter gradient")
+    assert torch.equal(dF, conv.updat(I, dO))
