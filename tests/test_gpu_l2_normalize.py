@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 def _layout(rng, R, S, p):
     L = (rng.random((R, S)) < p).astype(np.uint8)
     L[:, 1] = 0   # an empty block column
+    L[:, -1] = 0  # and an empty last one (its list starts past the last entry)
     return L
 
 
@@ -89,3 +90,36 @@ def test_l2_normalize_autograd_and_benchmark_layout():
                                      "bf16", "bf16")
     assert_close(w.grad, rdw, "bf16", "dw")   # dw returned in w's dtype
     assert rel_err(g.grad, rdg) <= 1e-5
+
+
+@pytest.mark.parametrize("b,dtype", [(8, "bf16"), (8, "f32"), (16, "f16"), (32, "f32"), (32, "bf16")])
+def test_l2_normalize_long_columns(b, dtype):
+    """Columns longer than the blocks one round of loads holds (they read the rest
+    again) and longer than the 1024 entries a list record keeps inline (the rest come
+    from the column list), beside short and empty columns."""
+    print(f"case l2_normalize long columns b={b} dtype={dtype}", flush=True)
+    rng = np.random.default_rng(700 + b)
+    R = 1100
+    L = np.zeros((R, 4), np.uint8)
+    L[:, 0] = 1                               # 1100 blocks
+    L[:, 2] = rng.random(R) < 0.1             # ~110 blocks
+    L[rng.choice(R, 3, replace=False), 3] = 1  # 3 blocks; column 1 stays empty
+    m = bs.BlocksparseMatMul(L, block_size=b)
+    P = synth.random_problem(rng, L, b, 1, 1, dtype, w_std=0.5)
+    w = dev(P.w)
+    g = torch.from_numpy((rng.random(m.K) + 0.5).astype(np.float32))
+    out = torch.empty(w.shape, dtype=TORCH_DT[dtype], device="cuda")
+    norms = torch.empty(m.K, device="cuda")
+    bs.bsmm_l2_normalize(m.handle, w, dev(g), out, norms, 1e-6)
+    dy = synth._draw(rng, tuple(w.shape), 1.0, dtype)
+    dw = torch.empty(w.shape, device="cuda")
+    dg = torch.empty(m.K, device="cuda")
+    bs.bsmm_l2_normalize_grad(m.handle, dev(dy), w, dev(g), dw, dg, 1e-6)
+    torch.cuda.synchronize()
+    wb = synth.to_bits(P.w)
+    rout, rn = ol2.l2_normalize(L, wb, b, g.numpy(), 1e-6, dtype)
+    assert_close(out, rout, dtype, "l2_normalize out")
+    assert rel_err(norms, rn) <= 1e-5
+    rdw, rdg = ol2.l2_normalize_grad(L, synth.to_bits(dy), wb, b, g.numpy(), 1e-6, dtype, dtype)
+    assert rel_err(dw, rdw) <= 1e-5, ("dw", rel_err(dw, rdw))
+    assert rel_err(dg, rdg) <= 1e-5, ("dgain", rel_err(dg, rdg))
