@@ -542,25 +542,28 @@ def run_sparse_proj(reps=20):
     return out
 
 
-def run_conv(reps=3):
+def run_conv(reps=3, dt="bf16", strides=(1, 1)):
     """Kernel time of BlocksparseConv (fprop, input gradient, filter gradient) on a 2-D
     workload: 256 input and output channels in blocks of 32 x 32 channels (half of the
     8 x 8 block grid present, consecutive channels), 3 x 3 filter, 32 x 32 images,
-    N = 32, SAME, stride 1, bf16.  FLOPs per pass 2 * N * M*P*Q * nblocks * Bc * Bk * T*R*S;
-    algorithmic bytes |I| + |O| + |F| (fprop, bprop), |I| + |dO| + |dF| (float32 dF)."""
+    N = 32, SAME, stride 1 and bf16 unless given.  FLOPs per pass 2 * N * M*P*Q *
+    nblocks * Bc * Bk * T*R*S; algorithmic bytes |I| + |O| + |F| (fprop, bprop), |I| +
+    |dO| + |dF| (float32 dF)."""
     import numpy as np
     import torch
     import block_sparse_matrix_amd as bs
     import synth
-    N, C, B, TRS, DHW, dt = 32, 256, 32, (3, 3), (32, 32), "bf16"
+    N, C, B, TRS, DHW = 32, 256, 32, (3, 3), (32, 32)
     nb = (C // B) * (C // B) // 2
-    P = synth.conv_problem(np.random.default_rng(23), N, C, C, B, B, nb, TRS, DHW, DHW, dt,
+    MPQ = tuple((d + s - 1) // s for d, s in zip(DHW, strides))   # SAME
+    P = synth.conv_problem(np.random.default_rng(23), N, C, C, B, B, nb, TRS, DHW, MPQ, dt,
                            contiguous_blocks=True)
-    conv = bs.BlocksparseConv(P.BCK, TRS, DHW)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, strides=strides)
     F, I, dO = P.F.cuda(), P.I.cuda(), P.dO.cuda()
     O, dI = torch.empty_like(dO), torch.empty_like(I)
     dF = torch.empty(conv.f_shape(), dtype=torch.float32, device="cuda")
     h = conv.handle
+    tdt = synth.DTYPES[dt]
 
     def launch():
         bs.bsmm_conv_fprop(h, F, I, O, N)
@@ -574,17 +577,20 @@ def run_conv(reps=3):
         launch()
     torch.cuda.synchronize()
     pr = bs.bsmm_profile_end()
-    flops = 2.0 * N * DHW[0] * DHW[1] * nb * B * B * TRS[0] * TRS[1]
-    act, fb = N * C * DHW[0] * DHW[1] * 2, nb * B * B * TRS[0] * TRS[1]
-    nbytes = {"conv_fprop": 2 * act + 2 * fb, "conv_bprop": 2 * act + 2 * fb, "conv_updat": 2 * act + 4 * fb}
+    es = 4 if dt == "f32" else 2
+    flops = 2.0 * N * MPQ[0] * MPQ[1] * nb * B * B * TRS[0] * TRS[1]
+    iact, oact, fb = N * C * DHW[0] * DHW[1] * es, N * C * MPQ[0] * MPQ[1] * es, nb * B * B * TRS[0] * TRS[1]
+    nbytes = {"conv_fprop": iact + oact + es * fb, "conv_bprop": iact + oact + es * fb,
+              "conv_updat": iact + oact + 4 * fb}
     out = {"workload": f"BlocksparseConv 2-D, C = K = {C} in {B}x{B}-channel blocks ({nb} of 64), 3x3 filter, "
-                       f"32x32 images, N = {N}, SAME, bf16"}
+                       f"32x32 images, N = {N}, SAME, strides {tuple(strides)}, {dt}"}
     for key, nbt in nbytes.items():
         us = pr[key][0] / pr[key][1] * 1e3
         bound, tstar = roof(flops, nbt, dt)
         out[key[5:]] = {"kernel_us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 3),
                         "alg_bytes": int(nbt), "flops": int(flops), "bound": bound,
-                        "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 5)}
+                        "roofline_us": round(tstar * 1e6, 3), "frac": round(tstar / (us * 1e-6), 5),
+                        "kernels": conv.kernel_name(key[5:], tdt)}
     return out
 
 
@@ -684,6 +690,8 @@ def main():
         out["l2_normalize"] = run_l2_normalize(P)
         out["sparse_proj"] = run_sparse_proj()
         out["conv"] = run_conv()
+        out["conv_f32"] = run_conv(dt="f32")
+        out["conv_strided"] = run_conv(strides=(2, 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P, dtype, args.cpu_seconds)
     else:

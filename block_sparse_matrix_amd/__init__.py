@@ -910,7 +910,8 @@ class BlocksparseConv:
             self.handle = None
 
     def kernel_name(self, pass_: str, dtype=torch.bfloat16) -> str:
-        """Kernel family a pass ("fprop", "bprop", "updat") launches: "matrix_core" or "direct"."""
+        """Kernel family a pass ("fprop", "bprop", "updat") launches: "matrix_core",
+        "matrix_core_gather" or "direct"."""
         name = ctypes.c_char_p()
         _check(lib().bsmm_conv_kernel_name(self.handle, {"fprop": 0, "bprop": 1, "updat": 2}[pass_],
                                            DTYPE_CODE[dtype], ctypes.byref(name)), "bsmm_conv_kernel_name")

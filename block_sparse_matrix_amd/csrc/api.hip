@@ -1034,8 +1034,8 @@ size_t conv_ws_bytes(const bsmm_conv_plan* h, int64_t N, int dt) {
     if (N <= 0 || h->nb == 0) return 0;
     ConvArgs x = conv_args(h, dt);
     x.N = N;
-    x.a_bytes = 1;
-    if (!conv_mfma_updat_ok(x)) return 0;
+    x.a_bytes = x.b_bytes = 1;
+    if (!conv_mfma_updat_ok(x) && !conv_gather_updat_ok(x)) return 0;
     const int p = conv_updat_parts(x);
     if (p <= 1) return 0;
     return (size_t)p * h->nb * h->Bc * h->TRS[0] * h->TRS[1] * h->TRS[2] * h->Bk * sizeof(float);
@@ -1066,6 +1066,10 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
         const uint64_t es = dt == BSMM_F32 ? 4 : 2;
         const uint64_t ab = (uint64_t)N * es * (pass == 1 ? (uint64_t)h->K * sp_out : (uint64_t)h->C * sp_in);
         x.a_bytes = ab <= kMaxTensorBytes ? (uint32_t)ab : 0u;
+        if (pass == 2) {   // b is dO
+            const uint64_t bb = (uint64_t)N * es * (uint64_t)h->K * sp_out;
+            x.b_bytes = bb <= kMaxTensorBytes ? (uint32_t)bb : 0u;
+        }
     }
     x.a = a;
     x.b = b;
@@ -1083,8 +1087,13 @@ bsmm_status conv_call(bsmm_conv_handle h, int pass, const void* a, const void* b
             x.ws = (float*)ws;
         }
     }
-    if (pass < 2 && h->gok[pass] && h->gptr[pass].size() > 1 && conv_mfma_plan(x, pass)) {
-        x.mfma = 1;
+    if (pass < 2 && h->gok[pass] && h->gptr[pass].size() > 1) {
+        if (conv_mfma_plan(x, pass))
+            x.mfma = 1;
+        else if (conv_gather_ok(x, pass) && (N == 0 || h->nb == 0 || aligned16(b)))
+            x.mfma = 2;
+    }
+    if (x.mfma) {
         x.gptr = d + off[pass == 0 ? 6 : 9];
         x.gblk = d + off[pass == 0 ? 7 : 10];
         x.zch = d + off[pass == 0 ? 8 : 11];
@@ -1249,10 +1258,14 @@ bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, c
     if (!h || !name || pass < 0 || pass > 2) return fail(BSMM_ERR_INVALID_ARG, "bad argument");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     ConvArgs x = conv_args(h, dt);
-    x.a_bytes = 1;   // the choice assuming the pass's input is below 2 GiB
-    const bool mc = pass < 2 ? h->gok[pass] && h->gptr[pass].size() > 1 && conv_mfma_plan(x, pass)
-                             : conv_mfma_updat_ok(x);
-    *name = mc ? "matrix_core" : "direct";
+    x.a_bytes = x.b_bytes = 1;   // the choice assuming the pass's inputs are below 2 GiB
+    const bool grouped = pass < 2 && h->gok[pass] && h->gptr[pass].size() > 1;
+    if (pass == 2)
+        *name = conv_mfma_updat_ok(x) ? "matrix_core" : conv_gather_updat_ok(x) ? "matrix_core_gather" : "direct";
+    else if (grouped && conv_mfma_plan(x, pass))
+        *name = "matrix_core";
+    else
+        *name = grouped && conv_gather_ok(x, pass) ? "matrix_core_gather" : "direct";
     return BSMM_OK;
 }
 

@@ -693,9 +693,17 @@ __global__ __launch_bounds__(256) void conv_updat_reduce(ConvArgs a, int64_t E) 
     }
 }
 
+bool conv_gather_updat_ok(const ConvArgs& a) {
+    if (conv_mfma_updat_ok(a) || a.a_bytes == 0 || a.b_bytes == 0) return false;
+    return (a.Bc == 16 || a.Bc == 32 || a.Bc == 64) && (a.Bk == 16 || a.Bk == 32 || a.Bk == 64);
+}
+
 int conv_updat_parts(const ConvArgs& a) {
-    const int64_t wgs = (int64_t)a.nb * a.R * (conv_updat_rows_sp(a) ? 1 : a.S);
-    const int64_t steps = a.N * (((int64_t)a.P * a.Q + 255) / 256);
+    const bool gather = conv_gather_updat_ok(a);
+    const int64_t wgs = gather ? (int64_t)a.nb * a.T * a.R * a.S
+                               : (int64_t)a.nb * a.R * (conv_updat_rows_sp(a) ? 1 : a.S);
+    const int64_t mpq = (int64_t)a.M * a.P * a.Q, np = gather ? 128 : 256;
+    const int64_t steps = a.N * ((mpq + np - 1) / np);
     int64_t p = wgs > 0 ? (4096 + wgs - 1) / wgs : 1;   // ~16 workgroups per compute unit
     if (p > 16) p = 16;
     if (p > steps / 4) p = steps / 4;
@@ -707,6 +715,316 @@ bool conv_mfma_updat_ok(const ConvArgs& a) {
     for (int i = 0; i < 3; i++)
         if (a.st[i] != 1 || a.dl[i] != 1) return false;
     return a.Bc % 16 == 0 && a.Bk % 16 == 0 && a.Bc <= 64 && a.Bk <= 64;
+}
+
+// ---------------------------------------------------------------------------------
+// Gathering matrix-core path (fprop and bprop for any geometry: 1-, 2- or 3-D images,
+// strides, dilations, every padding; fp32 and 16-bit storage).  It is the implicit
+// product of each filter tap with the input values that tap reads:
+//
+//   out[n, o, pos] = sum over the group's blocks b, taps tau, contraction channels c of
+//                    Wop[b, tau][o][c] * In[n, in(b, c), src(pos, tau)]
+//
+// fprop: src = pos*stride - pad + tau*dilation per dimension (zero outside the image),
+// Wop[o][c] = F[b, c, tau, o].  bprop (the input gradient): src = (pos + pad -
+// tau*dilation) / stride where that divides exactly and lands inside dO, else zero,
+// Wop[o][c] = F[b, o, tau, c]; this is the transposed convolution with no flipped
+// filter copy.  A workgroup (4 waves) owns one block group (blocks sharing one output
+// channel list, CO = 16*OT channels), one image and 256 consecutive output positions,
+// one per thread.  Per step (block, tap, KC contraction channels) each thread gathers
+// its position's KC input values (one buffer load per channel: the channel offset is
+// scalar, the position offset per lane, out-of-image positions read zero) and writes
+// them as one LDS row [position][channel]; the filter tile is staged as [output
+// channel][channel].  Both operand fragments are then plain 16-byte LDS reads (lane l:
+// row l % 16, channels 16 bytes' worth from (l / 16)); wave w runs position tiles 4w ..
+// 4w+3 against every output tile.  The next step's loads are in flight during the
+// current step's products (double-buffered LDS, one barrier per step); the sum runs in
+// a fixed order (blocks, taps, channels): deterministic.
+template <int DT, int OT, bool TR>
+__global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
+    constexpr bool F32 = DT == BSMM_F32;
+    constexpr int ES = F32 ? 4 : 2;          // bytes per value
+    constexpr int VEC = 16 / ES;             // values per 16 bytes
+    constexpr int KC = 4 * VEC;              // contraction channels per step
+    constexpr int CO = 16 * OT;
+    constexpr int NP = 256;                  // output positions per workgroup
+    constexpr int PITCH = 80;                // LDS row: KC values (64 bytes) + 16
+    constexpr int WCH = KC * CO / VEC;       // 16-byte filter chunks per step (<= 256)
+    __shared__ __attribute__((aligned(16))) char gsm[2][NP * PITCH];
+    __shared__ __attribute__((aligned(16))) char wsm[2][CO * PITCH];
+
+    const int CI = TR ? a.Bk : a.Bc;
+    const int32_t* in_idx = TR ? a.kidx : a.cidx;
+    const int32_t* out_idx = TR ? a.cidx : a.kidx;
+    const int Di = TR ? a.M : a.D, Hi = TR ? a.P : a.H, Wi = TR ? a.Q : a.W;   // gathered tensor
+    const int Ho = TR ? a.H : a.P, Wo = TR ? a.W : a.Q;                         // this pass's output
+    const int64_t HWi = (int64_t)Di * Hi * Wi;
+    const int64_t HWo = (int64_t)(TR ? a.D : a.M) * Ho * Wo;
+    const int64_t Cin = TR ? a.K : a.C, Cout = TR ? a.C : a.K;
+    const int TRS = a.T * a.R * a.S;
+    const int nch = (CI + KC - 1) / KC;
+
+    const int64_t npt = (HWo + NP - 1) / NP;
+    const int64_t pt = blockIdx.x % npt, rest = blockIdx.x / npt;
+    const int64_t n = rest % a.N;
+    const int g = (int)(rest / a.N);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int gb = a.gptr[g], ge = a.gptr[g + 1];
+    const int nsteps = (ge - gb) * TRS * nch;
+    const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
+
+    // this thread's output position
+    const int64_t pos = pt * NP + t;
+    const bool pok = pos < HWo;
+    const int ow = (int)(pos % Wo), oh = (int)((pos / Wo) % Ho), od = (int)(pos / ((int64_t)Wo * Ho));
+
+    // per-lane element offset of the gathered value for tap (tt, r, s), or -1
+    auto src_of = [&](int tt, int r, int s) -> int64_t {
+        int c3[3];
+        const int o3[3] = {od, oh, ow}, t3[3] = {tt, r, s}, n3[3] = {Di, Hi, Wi};
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            if constexpr (TR) {
+                const int u = o3[d] + a.pad[d] - t3[d] * a.dl[d];
+                if (u < 0 || u % a.st[d] != 0) return -1;
+                c3[d] = u / a.st[d];
+            } else {
+                c3[d] = o3[d] * a.st[d] - a.pad[d] + t3[d] * a.dl[d];
+            }
+            if (c3[d] < 0 || c3[d] >= n3[d]) return -1;
+        }
+        return ((int64_t)c3[0] * Hi + c3[1]) * Wi + c3[2];
+    };
+
+    uint32_t gv[KC];   // the next step's gathered values (16-bit: low half)
+    u32x4 wv;          // and one 16-byte filter chunk (threads < WCH)
+    const int wc = t / (CO / VEC), wp = t % (CO / VEC);   // fprop chunk: channel, output part
+    const int bo = t / (KC / VEC), bq = t % (KC / VEC);   // bprop chunk: output, channel part
+    auto issue = [&](int step) {
+        const int chunk = step % nch, tap = (step / nch) % TRS, e = step / (nch * TRS);
+        const int b = __builtin_amdgcn_readfirstlane(a.gblk[gb + e]);
+        const int s = tap % a.S, r = (tap / a.S) % a.R, tt = tap / (a.S * a.R);
+        const int64_t so = pok ? src_of(tt, r, s) : -1;
+        const uint32_t voff = so >= 0 ? (uint32_t)(so * ES) : kOffLane;
+        const int c0 = chunk * KC;
+#pragma unroll
+        for (int c = 0; c < KC; c++) {
+            const bool cv = c0 + c < CI;   // uniform
+            const int ch = cv ? in_idx[b * CI + c0 + c] : 0;
+            const uint32_t soff = cv ? (uint32_t)(((n * Cin + ch) * HWi) * ES) : kOffOff;
+            gv[c] = F32 ? bload32(rin, voff, soff) : bload16(rin, voff, soff);
+        }
+        const void* fp = kZero16;
+        if constexpr (TR) {
+            if (t < WCH && c0 + bq * VEC < CI)
+                fp = (const char*)a.b + ((((int64_t)b * a.Bc + bo) * TRS + tap) * a.Bk + c0 + bq * VEC) * ES;
+        } else {
+            if (t < WCH && c0 + wc < CI)
+                fp = (const char*)a.b + ((((int64_t)b * a.Bc + c0 + wc) * TRS + tap) * a.Bk + wp * VEC) * ES;
+        }
+        wv = *reinterpret_cast<const u32x4*>(fp);
+    };
+    auto stage = [&](int buf) {
+        char* grow = gsm[buf] + t * PITCH;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            u32x4 v;
+            if constexpr (F32) {
+                v = u32x4{gv[4 * j], gv[4 * j + 1], gv[4 * j + 2], gv[4 * j + 3]};
+            } else {
+                v = u32x4{gv[8 * j] | (gv[8 * j + 1] << 16), gv[8 * j + 2] | (gv[8 * j + 3] << 16),
+                          gv[8 * j + 4] | (gv[8 * j + 5] << 16), gv[8 * j + 6] | (gv[8 * j + 7] << 16)};
+            }
+            *reinterpret_cast<u32x4*>(grow + 16 * j) = v;
+        }
+        if (t < WCH) {
+            if constexpr (TR) {
+                *reinterpret_cast<u32x4*>(wsm[buf] + bo * PITCH + bq * 16) = wv;
+            } else {
+                const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int h = 0; h < VEC; h++) {
+                    char* dst = wsm[buf] + (wp * VEC + h) * PITCH + wc * ES;
+                    if constexpr (F32)
+                        *reinterpret_cast<uint32_t*>(dst) = w[h];
+                    else
+                        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(h & 1 ? w[h >> 1] >> 16 : w[h >> 1]);
+                }
+            }
+        }
+    };
+
+    f32x4 acc[4][OT];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int o = 0; o < OT; o++) acc[u][o] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int m16 = lane & 15, q16 = (lane >> 4) * 16;
+    if (nsteps > 0) {
+        issue(0);
+        stage(0);
+    }
+    __syncthreads();
+    for (int step = 0; step < nsteps; step++) {
+        const int buf = step & 1;
+        if (step + 1 < nsteps) issue(step + 1);
+        u32x4 bf[OT];
+#pragma unroll
+        for (int o = 0; o < OT; o++) bf[o] = *reinterpret_cast<const u32x4*>(wsm[buf] + (o * 16 + m16) * PITCH + q16);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const u32x4 af = *reinterpret_cast<const u32x4*>(gsm[buf] + ((wave * 4 + u) * 16 + m16) * PITCH + q16);
+#pragma unroll
+            for (int o = 0; o < OT; o++) mma<DT>(acc[u][o], af, bf[o]);
+        }
+        if (step + 1 < nsteps) stage(buf ^ 1);
+        __syncthreads();
+    }
+    // lane: positions 4*(lane/16) .. +3 of each of its tiles, output channel o*16 + lane%16
+    const int b0 = a.gblk[gb];
+    const bool vec = HWo % 4 == 0;
+#pragma unroll
+    for (int o = 0; o < OT; o++) {
+        const int64_t ch = out_idx[b0 * CO + o * 16 + m16];
+        const int64_t base = (n * Cout + ch) * HWo;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t p0 = pt * NP + (wave * 4 + u) * 16 + 4 * (lane >> 4);
+            if (vec && p0 + 4 <= HWo) {
+                store4<DT>(a.out, base + p0, acc[u][o]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    if (p0 + v < HWo) store_elt(a.out, base + p0 + v, acc[u][o][v], DT);
+            }
+        }
+    }
+}
+
+// Gathering matrix-core filter gradient (any geometry and dtype; Bc and Bk of 16, 32 or
+// 64): dF[b, :, tau, :] = G^T . dO over the (image, position) pairs, where G[p][c] =
+// In[n, C_b[c], src(p, tau)] (the fprop gather, zero outside the image).  One workgroup
+// per (block, tap, part) walks its part of the (image, 128-position tile) steps: two
+// threads per position load half of its Bc gathered input values and half of its Bk dO
+// values (channel offsets scalar, position offsets per lane) into registers during the
+// previous step's products, then write them as [channel][position] rows; each wave
+// contracts 32 of the step's positions for every (16 x 16) tile of dF (both fragments
+// plain 16-byte LDS reads).  The waves' partial tiles are added in wave order, and parts
+// (with a workspace) are summed in part order by conv_updat_reduce: deterministic.
+template <int DT, int BCT, int BKT>
+__global__ __launch_bounds__(256) void conv_gather_updat_kernel(ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
+    constexpr bool F32 = DT == BSMM_F32;
+    constexpr int ES = F32 ? 4 : 2;
+    constexpr int BC = 16 * BCT, BK = 16 * BKT, HC = BC / 2, HK = BK / 2;
+    constexpr int NP = 128;                   // positions per step
+    constexpr int PP = NP * ES + 16;          // LDS row pitch, bytes
+    char* gs = reinterpret_cast<char*>(dsm);  // [BC][PP]
+    char* ds = gs + BC * PP;                  // [BK][PP]
+
+    const int TRS = a.T * a.R * a.S;
+    const int part = blockIdx.x % a.nparts;
+    const int bt = blockIdx.x / a.nparts;
+    const int tap = bt % TRS, b = bt / TRS;
+    const int s = tap % a.S, r = (tap / a.S) % a.R, tt = tap / (a.S * a.R);
+    const int64_t MPQ = (int64_t)a.M * a.P * a.Q, DHW = (int64_t)a.D * a.H * a.W;
+    const int64_t npt = (MPQ + NP - 1) / NP, nst = a.N * npt;
+    const int64_t s0 = nst * part / a.nparts, s1 = nst * (part + 1) / a.nparts;
+    const rsrc_t rin = make_rsrc(a.a, a.a_bytes), rdo = make_rsrc(a.b, a.b_bytes);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int p = t % NP, hh = t / NP;
+
+    uint32_t gv[HC], dv[HK];
+    auto issue = [&](int64_t step) {
+        const int64_t n = step / npt, pos = (step % npt) * NP + p;
+        uint32_t vi = kOffLane, vo = kOffLane;
+        if (pos < MPQ) {
+            vo = (uint32_t)(pos * ES);
+            const int ow = (int)(pos % a.Q), oh = (int)((pos / a.Q) % a.P), od = (int)(pos / ((int64_t)a.Q * a.P));
+            const int id = od * a.st[0] - a.pad[0] + tt * a.dl[0];
+            const int ih = oh * a.st[1] - a.pad[1] + r * a.dl[1];
+            const int iw = ow * a.st[2] - a.pad[2] + s * a.dl[2];
+            if (id >= 0 && id < a.D && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W)
+                vi = (uint32_t)((((int64_t)id * a.H + ih) * a.W + iw) * ES);
+        }
+#pragma unroll
+        for (int c = 0; c < HC; c++) {
+            const int ch = a.cidx[b * BC + hh * HC + c];
+            const uint32_t so = (uint32_t)((n * a.C + ch) * DHW * ES);
+            gv[c] = F32 ? bload32(rin, vi, so) : bload16(rin, vi, so);
+        }
+#pragma unroll
+        for (int j = 0; j < HK; j++) {
+            const int kc = a.kidx[b * BK + hh * HK + j];
+            const uint32_t so = (uint32_t)((n * a.K + kc) * MPQ * ES);
+            dv[j] = F32 ? bload32(rdo, vo, so) : bload16(rdo, vo, so);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int c = 0; c < HC; c++) {
+            char* dst = gs + (hh * HC + c) * PP + p * ES;
+            if constexpr (F32)
+                *reinterpret_cast<uint32_t*>(dst) = gv[c];
+            else
+                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)gv[c];
+        }
+#pragma unroll
+        for (int j = 0; j < HK; j++) {
+            char* dst = ds + (hh * HK + j) * PP + p * ES;
+            if constexpr (F32)
+                *reinterpret_cast<uint32_t*>(dst) = dv[j];
+            else
+                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)dv[j];
+        }
+    };
+
+    f32x4 acc[BCT][BKT];
+#pragma unroll
+    for (int i = 0; i < BCT; i++)
+#pragma unroll
+        for (int j = 0; j < BKT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int m16 = lane & 15, g4 = lane >> 4;
+    if (s0 < s1) issue(s0);
+    for (int64_t step = s0; step < s1; step++) {
+        __syncthreads();   // the previous step's fragments are read
+        stage();
+        __syncthreads();
+        if (step + 1 < s1) issue(step + 1);
+        // wave w: positions 32w .. 32w+31 of the step (16-bit: one 32-deep fragment; fp32:
+        // two of 16)
+#pragma unroll
+        for (int f = 0; f < (F32 ? 2 : 1); f++) {
+            const int off = (F32 ? (32 * wave + 16 * f + 4 * g4) : (32 * wave + 8 * g4)) * ES;
+            u32x4 bf[BKT];
+#pragma unroll
+            for (int j = 0; j < BKT; j++) bf[j] = *reinterpret_cast<const u32x4*>(ds + (16 * j + m16) * PP + off);
+#pragma unroll
+            for (int i = 0; i < BCT; i++) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(gs + (16 * i + m16) * PP + off);
+#pragma unroll
+                for (int j = 0; j < BKT; j++) mma<DT>(acc[i][j], af, bf[j]);
+            }
+        }
+    }
+    // the four waves' partial tiles, added in wave order
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(dsm);   // [wave][tile][lane]
+    constexpr int NT = BCT * BKT;
+#pragma unroll
+    for (int i = 0; i < BCT; i++)
+#pragma unroll
+        for (int j = 0; j < BKT; j++) red[(wave * NT + i * BKT + j) * 64 + lane] = acc[i][j];
+    __syncthreads();
+    float* out = a.nparts > 1 ? a.ws + (int64_t)part * a.nb * BC * TRS * BK : (float*)a.out;
+    for (int q = t; q < NT * 64; q += 256) {
+        const int tile = q / 64, l = q % 64;
+        const f32x4 v = ((red[tile * 64 + l] + red[(NT + tile) * 64 + l]) + red[(2 * NT + tile) * 64 + l]) +
+                        red[(3 * NT + tile) * 64 + l];
+        const int i0 = (tile / BKT) * 16 + 4 * (l >> 4), j = (tile % BKT) * 16 + (l & 15);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; v4++) out[(((int64_t)b * BC + i0 + v4) * TRS + tap) * BK + j] = v[v4];
+    }
 }
 
 // Output channels that no block writes: zero.
@@ -764,6 +1082,45 @@ static hipError_t launch_conv_mfma_t(const ConvArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+bool conv_gather_ok(const ConvArgs& a, int pass) {
+    if (pass > 1 || a.a_bytes == 0) return false;
+    const int CO = pass == 1 ? a.Bc : a.Bk;
+    if (CO != 16 && CO != 32 && CO != 64) return false;
+    const int vec = a.dt == BSMM_F32 ? 4 : 8;
+    return pass == 0 || a.Bk % vec == 0;   // bprop reads 16-byte runs of the contraction
+}
+
+// The channels no group writes are zeroed first; one timing record spans both launches.
+template <int DT, int OT, bool TR>
+static hipError_t launch_conv_gather_t(const ConvArgs& a, hipStream_t st) {
+    const int64_t HWo = TR ? (int64_t)a.D * a.H * a.W : (int64_t)a.M * a.P * a.Q;
+    const int64_t grid = (int64_t)a.ngroups * a.N * ((HWo + 255) / 256);
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int pass = TR ? BSMM_PASS_CONV_BPROP : BSMM_PASS_CONV_FPROP;
+    void *e0 = nullptr, *e1 = nullptr;
+    prof_events(pass, &e0, &e1);
+    if (a.nz > 0) {
+        const int64_t Cout = TR ? a.C : a.K;
+        int64_t zg = (a.N * a.nz * HWo + 255) / 256;
+        if (zg > (1 << 20)) zg = 1 << 20;
+        hipError_t e = launch_ev(conv_zero_kernel<DT>, dim3((unsigned)zg), dim3(256), st, e0, nullptr, a, Cout, HWo);
+        if (e != hipSuccess) return e;
+        e0 = nullptr;
+    }
+    if (grid == 0) return hipSuccess;
+    return launch_ev(conv_gather_kernel<DT, OT, TR>, dim3((unsigned)grid), dim3(256), st, e0, e1, a);
+}
+
+template <int DT, bool TR>
+static hipError_t launch_conv_gather(const ConvArgs& a, hipStream_t st) {
+    switch (TR ? a.Bc : a.Bk) {
+    case 16: return launch_conv_gather_t<DT, 1, TR>(a, st);
+    case 32: return launch_conv_gather_t<DT, 2, TR>(a, st);
+    case 64: return launch_conv_gather_t<DT, 4, TR>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DT, bool TR>
 static hipError_t launch_conv_mfma(const ConvArgs& a, hipStream_t st) {
     switch (TR ? a.Bc : a.Bk) {
@@ -774,12 +1131,58 @@ static hipError_t launch_conv_mfma(const ConvArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int DT, int BCT, int BKT>
+static hipError_t launch_conv_gather_updat_t(const ConvArgs& a, hipStream_t st) {
+    const int64_t wgs = (int64_t)a.nb * a.T * a.R * a.S * a.nparts;
+    if (wgs == 0) return hipSuccess;
+    if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
+    constexpr int ES = DT == BSMM_F32 ? 4 : 2;
+    const int stage = 16 * (BCT + BKT) * (128 * ES + 16), red = 4 * BCT * BKT * 64 * 16;
+    const int lds = stage > red ? stage : red;
+    void *e0 = nullptr, *e1 = nullptr;   // one timing record spans the parts and their sum
+    prof_events(BSMM_PASS_CONV_UPDAT, &e0, &e1);
+    auto kern = conv_gather_updat_kernel<DT, BCT, BKT>;
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(256), lds, st, (hipEvent_t)e0,
+                              (hipEvent_t)(a.nparts == 1 ? e1 : nullptr), 0, a);
+    else
+        hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(256), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nparts == 1) return e;
+    const int64_t E = (int64_t)a.nb * a.Bc * a.T * a.R * a.S * a.Bk;
+    int64_t rg = (E + 255) / 256;
+    if (rg > 4096) rg = 4096;
+    return launch_ev(conv_updat_reduce, dim3((unsigned)rg), dim3(256), st, nullptr, e1, a, E);
+}
+
+template <int DT, int BCT>
+static hipError_t launch_conv_gather_updat_c(const ConvArgs& a, hipStream_t st) {
+    switch (a.Bk) {
+    case 16: return launch_conv_gather_updat_t<DT, BCT, 1>(a, st);
+    case 32: return launch_conv_gather_updat_t<DT, BCT, 2>(a, st);
+    case 64: return launch_conv_gather_updat_t<DT, BCT, 4>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DT>
+static hipError_t launch_conv_gather_updat(const ConvArgs& a, hipStream_t st) {
+    switch (a.Bc) {
+    case 16: return launch_conv_gather_updat_c<DT, 1>(a, st);
+    case 32: return launch_conv_gather_updat_c<DT, 2>(a, st);
+    case 64: return launch_conv_gather_updat_c<DT, 4>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DT>
 static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
     if constexpr (DT != BSMM_F32) {
-        if (a.mfma && pass == 0) return launch_conv_mfma<DT, false>(a, st);
-        if (a.mfma && pass == 1) return launch_conv_mfma<DT, true>(a, st);
+        if (a.mfma == 1 && pass == 0) return launch_conv_mfma<DT, false>(a, st);
+        if (a.mfma == 1 && pass == 1) return launch_conv_mfma<DT, true>(a, st);
     }
+    if (a.mfma == 2 && pass == 0) return launch_conv_gather<DT, false>(a, st);
+    if (a.mfma == 2 && pass == 1) return launch_conv_gather<DT, true>(a, st);
     if (pass == 2 && DT != BSMM_F32 && conv_updat_rows_sp(a)) {
         const int sp = conv_updat_rows_sp(a);
         const int64_t wgs = (int64_t)a.nb * a.R * a.nparts;
@@ -824,6 +1227,7 @@ static hipError_t launch_conv_dt(const ConvArgs& a, int pass, hipStream_t st) {
         if (rg > 4096) rg = 4096;
         return launch_ev(conv_updat_reduce, dim3((unsigned)rg), dim3(256), st, nullptr, e1, a, E);
     }
+    if (pass == 2 && conv_gather_updat_ok(a)) return launch_conv_gather_updat<DT>(a, st);
     if (pass == 2) {
         const int64_t rows = (int64_t)a.nb * a.Bc * a.T * a.R * a.S;
         if (rows == 0) return hipSuccess;

@@ -190,7 +190,7 @@ struct ConvArgs {
     // Matrix-core path (2-D, stride 1, dilation 1, 16-bit; fprop, and bprop as the
     // transposed convolution): blocks grouped by their output channel list (the
     // pass's output role), the groups' lists disjoint.
-    int mfma;             // 1: take the matrix-core kernel
+    int mfma;             // 1: the matrix-core kernel; 2: the gathering matrix-core kernel
     const int32_t* gptr;  // ngroups+1 offsets into gblk
     const int32_t* gblk;  // block ids of each group, ascending
     int ngroups;
@@ -200,18 +200,26 @@ struct ConvArgs {
     int cpitch;           // LDS elements per staged channel
     int lds_bytes;
     uint32_t a_bytes;     // size of `a` in bytes when below 2^31 (32-bit buffer offsets), else 0
+    uint32_t b_bytes;     // the same for `b` (set for the filter gradient, where it is dO)
     // matrix-core filter gradient: contraction split in nparts parts (fp32 partials in
     // ws, nparts * nblocks*Bc*T*R*S*Bk floats, then their sum in part order); 1: none
     int nparts;
     float* ws;
 };
-// Parts of the matrix-core filter gradient's contraction for N images (enough
-// workgroups to fill the chip twice, at least 4 steps of 256 positions each, at most 16).
+// Parts of the matrix-core filter gradient's contraction for N images (about 16
+// workgroups per compute unit, at least 4 steps each, at most 16).
 int conv_updat_parts(const ConvArgs& a);
 hipError_t launch_conv(const ConvArgs& a, int pass, void* stream);   // pass: 0 fprop, 1 bprop, 2 updat
 // LDS layout of the matrix-core conv kernel: fills a.TH, a.cpitch, a.lds_bytes; false
 // when the shape does not fit it (the direct kernels run instead).
 bool conv_mfma_plan(ConvArgs& a, int pass);
+// The gathering matrix-core fprop / bprop applies (any geometry and dtype; output
+// channels per block 16, 32 or 64; bprop: Bk a multiple of 16 bytes' worth of values;
+// the pass's input below 2 GiB); it needs the block groups and a 16-byte aligned filter.
+bool conv_gather_ok(const ConvArgs& a, int pass);
+// The gathering matrix-core filter gradient applies: every shape the matrix-core filter
+// gradient above does not take, with Bc and Bk of 16, 32 or 64 and I and dO below 2 GiB.
+bool conv_gather_updat_ok(const ConvArgs& a);
 // The filter gradient's matrix-core kernel applies (2-D / 1-D, stride 1, dilation 1,
 // 16-bit, Bc and Bk multiples of 16 up to 64); no grouping needed.
 bool conv_mfma_updat_ok(const ConvArgs& a);

@@ -406,13 +406,20 @@ BSMM_API void bsmm_conv_destroy(bsmm_conv_handle h);
 /* Output image size (M, P, Q) and the leading pads of each dim. */
 BSMM_API bsmm_status bsmm_conv_geometry(bsmm_conv_handle h, int64_t MPQ[3], int64_t pads[3]);
 /* Which kernel family a conv pass (0 fprop, 1 bprop, 2 updat) launches for dtype dt
- * (host only): "matrix_core" or "direct".  All matrix-core kernels need 2-D or 1-D
- * images, stride and dilation 1 and 16-bit storage.  fprop / bprop also need the pass's
- * contraction channels per block (Bc / Bk) a multiple of 32, its output channels per
- * block (Bk / Bc) 16, 32 or 64, blocks with the same output channel list forming groups
- * that share no channel, and (bprop) pads below the filter size; updat needs Bc and Bk
- * multiples of 16 up to 64.  A call whose input activation exceeds 2 GiB takes the
- * direct kernels (the matrix-core kernels address it with 32-bit offsets). */
+ * (host only): "matrix_core", "matrix_core_gather" or "direct".  Every matrix-core
+ * fprop / bprop needs blocks with the same output channel list to form groups that
+ * share no channel, the pass's output channels per block (Bk for fprop, Bc for bprop)
+ * 16, 32 or 64, and the pass's input activation below 2 GiB (32-bit offsets).
+ * "matrix_core" (the staged kernel) further needs 2-D or 1-D images, stride and
+ * dilation 1, 16-bit storage, the contraction channels per block (Bc / Bk) a multiple
+ * of 32 and (bprop) pads below the filter size.  "matrix_core_gather" takes every other
+ * geometry (1-, 2- or 3-D, strides, dilations, any padding) and dtype, fp32 included;
+ * its bprop needs Bk a multiple of 16 bytes' worth of values (4 fp32, 8 16-bit), and a
+ * call whose filter is not 16-byte aligned takes the direct kernels.  updat:
+ * "matrix_core" for 2-D or 1-D images, stride and dilation 1, 16-bit storage and Bc
+ * and Bk multiples of 16 up to 64; "matrix_core_gather" for every other geometry and
+ * dtype with Bc and Bk of 16, 32 or 64, and I and dO below 2 GiB.  Anything else takes
+ * the direct kernels. */
 BSMM_API bsmm_status bsmm_conv_kernel_name(bsmm_conv_handle h, int pass, bsmm_dtype dt, const char** name);
 /* O = fprop(F, I). */
 BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const void* I, void* O, int64_t N,
@@ -421,8 +428,8 @@ BSMM_API bsmm_status bsmm_conv_fprop(bsmm_conv_handle h, const void* F, const vo
 BSMM_API bsmm_status bsmm_conv_bprop(bsmm_conv_handle h, const void* F, const void* dO, void* dI, int64_t N,
                                      bsmm_dtype dt, void* stream);
 /* Device workspace bytes bsmm_conv_updat can use for N images (0: it uses none).  With
- * it the matrix-core filter gradient splits its contraction over the images into parts
- * whose fp32 partial sums live in the workspace, then adds them in part order. */
+ * it either matrix-core filter gradient splits its contraction over the images into
+ * parts whose fp32 partial sums live in the workspace, then adds them in part order. */
 BSMM_API bsmm_status bsmm_conv_workspace_size(bsmm_conv_handle h, int64_t N, bsmm_dtype dt, size_t* bytes);
 /* dF = updat(I, dO), float32.  ws, ws_bytes: device workspace of at least
  * bsmm_conv_workspace_size bytes, 16-byte aligned, or NULL / smaller (then unsplit:

@@ -55,7 +55,10 @@ def test_call_validation_before_gpu():
     n = ctypes.c_size_t(7)
     assert L.bsmm_conv_workspace_size(h, 64, 1, ctypes.byref(n)) == 0 and n.value == 0   # 2-channel blocks: direct
     c16 = bs.BlocksparseConv([(tuple(range(16)), tuple(range(16)))], (3, 3), (8, 8))
-    assert L.bsmm_conv_workspace_size(c16.handle, 64, 0, ctypes.byref(n)) == 0 and n.value == 0   # fp32: direct
+    # fp32: the gathering filter gradient, 16 parts (64 images of one 128-position step, at
+    # least 4 steps per part) of 16 x 9 x 16 fp32 partials
+    assert L.bsmm_conv_workspace_size(c16.handle, 64, 0, ctypes.byref(n)) == 0 and n.value == 16 * 16 * 9 * 16 * 4
+    assert L.bsmm_conv_workspace_size(c16.handle, 8, 0, ctypes.byref(n)) == 0 and n.value == 2 * 16 * 9 * 16 * 4
     assert L.bsmm_conv_workspace_size(c16.handle, 64, 1, ctypes.byref(n)) == 0
     assert n.value == 16 * 16 * 16 * 9 * 4                      # 16 parts of 16 x 9 x 16 fp32 partials
     assert L.bsmm_conv_fprop(h, None, None, None, 0, 0, None) == 0

@@ -112,7 +112,7 @@ def test_conv_matrix_core(case, dtype):
     assert conv.kernel_name("fprop", tdt) == "matrix_core"
     pads = g[5]
     want_b = Bk % 32 == 0 and Bc in (16, 32, 64) and pads[1] <= g[0][1] - 1 and pads[2] <= g[0][2] - 1
-    assert conv.kernel_name("bprop", tdt) == ("matrix_core" if want_b else "direct")
+    assert conv.kernel_name("bprop", tdt) == ("matrix_core" if want_b else "matrix_core_gather")
     bck = oc.split_bck(P.BCK)
     F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
     assert conv.kernel_name("updat", tdt) == ("matrix_core" if Bc % 16 == 0 and Bk % 16 == 0 else "direct")
@@ -214,4 +214,77 @@ def test_conv_filter_gradient_rows(Bc, Bk, TRS, DHW, pad, dtype):
     torch.cuda.synchronize()
     ref = oc.updat(oc.split_bck(P.BCK), _f64(P.I), _f64(P.dO), g).reshape(dF.shape)
     assert_close(dF, ref, dtype, "row-form filter gradient")
+    assert torch.equal(dF, conv.updat(I, dO))
+
+
+GATHER_CASES = [
+    # N, C, K, Bc, Bk, nblocks, TRS, DHW, strides, dilates, padding
+    (2, 64, 64, 32, 32, 3, (3, 3), (12, 11), (2, 2), (1, 1), "SAME"),            # strided
+    (2, 64, 32, 32, 16, 3, (3, 3), (10, 10), (1, 1), (2, 2), "SAME"),            # dilated, Bk 16
+    (2, 32, 64, 16, 32, 4, (2, 3, 3), (4, 6, 5), (1, 1, 1), (1, 1, 1), "SAME"),  # 3-D
+    (1, 32, 32, 16, 16, 3, (3, 2, 3), (7, 6, 9), (2, 1, 2), (1, 2, 1), "VALID"),  # 3-D strided + dilated
+    (3, 64, 128, 64, 64, 2, (5,), (40,), (3,), (1,), 2),                          # 1-D, stride 3, pads 2
+    (2, 64, 64, 32, 32, 4, (3, 3), (9, 9), (1, 1), (1, 1), "SAME"),              # stride 1 (fp32 takes it)
+    (1, 32, 32, 32, 32, 1, (3, 3), (19, 17), (1, 1), (2, 1), "SAME"),            # 323 positions: ragged tile
+    (2, 96, 32, 48, 16, 3, (3, 3), (8, 8), (2, 1), (1, 1), "SAME"),              # 48 contraction channels
+    (2, 32, 16, 16, 8, 2, (3, 3), (6, 6), (1, 2), (1, 1), "SAME"),               # bprop over 8 channels
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES,
+                         ids=[f"{len(c[7])}d-st{c[8]}-dl{c[9]}-{c[10]}-B{c[3]}x{c[4]}" for c in GATHER_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_conv_gather(case, dtype):
+    """The gathering matrix-core fprop / input gradient (any geometry and dtype) against
+    the oracle, for the passes whose output channels per block are 16, 32 or 64, and the
+    gathering filter gradient (Bc and Bk of 16, 32 or 64) split over a workspace and
+    unsplit; deterministic."""
+    import ctypes
+    N, C, K, Bc, Bk, nb, TRS, DHW, st, dl, pad = case
+    print(f"case conv gather {case} {dtype}", flush=True)
+    g = oc.geometry(TRS, DHW, st, dl, pad)
+    MPQ = g[2][3 - len(DHW):]
+    rng = np.random.default_rng(C + 3 * K + nb + 5 * len(DHW) + Bk)
+    P = synth.conv_problem(rng, N, C, K, Bc, Bk, nb, TRS, DHW, MPQ, dtype, contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, strides=st, dilates=dl, padding=pad)
+    tdt = synth.DTYPES[dtype]
+    vec = 4 if dtype == "f32" else 8
+    plain = dtype != "f32" and all(v == 1 for v in st) and all(v == 1 for v in dl) and len(DHW) < 3
+    for name, co, ok in (("fprop", Bk, True), ("bprop", Bc, Bk % vec == 0)):
+        got = conv.kernel_name(name, tdt)
+        if co in (16, 32, 64) and ok:
+            assert got == "matrix_core_gather" or (plain and got == "matrix_core"), (name, got)
+        else:
+            assert got == "direct", (name, got)
+    if not plain:
+        assert "matrix_core_gather" in (conv.kernel_name("fprop", tdt), conv.kernel_name("bprop", tdt))
+    bck = oc.split_bck(P.BCK)
+    F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    O = conv.fprop(F, I)
+    dI = conv.bprop(F, dO)
+    torch.cuda.synchronize()
+    Fr, Ir, dOr = _f64(P.F), _f64(P.I), _f64(P.dO)
+    assert_close(O, oc.fprop(bck, Fr, Ir, conv.K, g).reshape(O.shape), dtype, "conv fprop (gather)")
+    assert_close(dI, oc.bprop(bck, Fr, dOr, conv.C, g).reshape(dI.shape), dtype, "conv bprop (gather)")
+    O2 = conv.fprop(F, I)
+    dI2 = conv.bprop(F, dO)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(dI, dI2)
+    # filter gradient
+    got = conv.kernel_name("updat", tdt)
+    if Bc in (16, 32, 64) and Bk in (16, 32, 64):
+        assert got == "matrix_core_gather" or (plain and got == "matrix_core"), ("updat", got)
+    else:
+        assert got == "direct", ("updat", got)
+    dF = conv.updat(I, dO)   # with the workspace the library asks for
+    dF1 = torch.empty_like(dF)
+    code = {"f32": 0, "bf16": 1, "f16": 2}[dtype]
+    assert bs.lib().bsmm_conv_updat(conv.handle, ctypes.c_void_p(I.data_ptr()), ctypes.c_void_p(dO.data_ptr()),
+                                    ctypes.c_void_p(dF1.data_ptr()), N, code, None, 0,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    ref = oc.updat(bck, Ir, dOr, g).reshape(dF.shape)
+    tol = "f32" if dtype == "f32" else dtype
+    assert_close(dF, ref, tol, "conv updat (gather, split)")
+    assert_close(dF1, ref, tol, "conv updat (gather, one part)")
     assert torch.equal(dF, conv.updat(I, dO))
