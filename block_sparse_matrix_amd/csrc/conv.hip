@@ -740,6 +740,12 @@ bool conv_mfma_updat_ok(const ConvArgs& a) {
 // 4w+3 against every output tile.  The next step's loads are in flight during the
 // current step's products (double-buffered LDS, one barrier per step); the sum runs in
 // a fixed order (blocks, taps, channels): deterministic.
+// Positions of the largest residue class (residue 0 in every dimension) of a D x H x W
+// image under strides st.
+__host__ __device__ inline int64_t conv_class_max(int D, int H, int W, const int* st) {
+    return (int64_t)((D + st[0] - 1) / st[0]) * ((H + st[1] - 1) / st[1]) * ((W + st[2] - 1) / st[2]);
+}
+
 template <int DT, int OT, bool TR>
 __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
     constexpr bool F32 = DT == BSMM_F32;
@@ -764,19 +770,69 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
     const int TRS = a.T * a.R * a.S;
     const int nch = (CI + KC - 1) / KC;
 
-    const int64_t npt = (HWo + NP - 1) / NP;
-    const int64_t pt = blockIdx.x % npt, rest = blockIdx.x / npt;
+    // The input gradient with a stride above 1 takes its output positions one residue
+    // class (position mod stride in every dimension) at a time: inside a class the taps
+    // that divide exactly are the same for every position, so the others are skipped
+    // whole.  Otherwise one class holds every position.  Class positions: x_d = cr[d] +
+    // k*cs[d], k < cn[d].
+    const bool cls = TR && (a.st[0] > 1 || a.st[1] > 1 || a.st[2] > 1);
+    const int Do = TR ? a.D : a.M;
+    int cr[3] = {0, 0, 0}, cs[3] = {1, 1, 1}, cn[3] = {Do, Ho, Wo};
+    int64_t tile, rest;
+    if (cls) {
+        const int nclass = a.st[0] * a.st[1] * a.st[2];
+        const int64_t tpc = (conv_class_max(Do, Ho, Wo, a.st) + NP - 1) / NP;
+        const int64_t ct = blockIdx.x % (nclass * tpc);
+        rest = blockIdx.x / (nclass * tpc);
+        const int cl = (int)(ct / tpc);
+        tile = ct % tpc;
+        cr[2] = cl % a.st[2];
+        cr[1] = (cl / a.st[2]) % a.st[1];
+        cr[0] = cl / (a.st[2] * a.st[1]);
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            cs[d] = a.st[d];
+            cn[d] = cr[d] < cn[d] ? (cn[d] - cr[d] + a.st[d] - 1) / a.st[d] : 0;
+        }
+    } else {
+        const int64_t tpc = (HWo + NP - 1) / NP;
+        tile = blockIdx.x % tpc;
+        rest = blockIdx.x / tpc;
+    }
+    const int64_t ccount = (int64_t)cn[0] * cn[1] * cn[2];
     const int64_t n = rest % a.N;
     const int g = (int)(rest / a.N);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int gb = a.gptr[g], ge = a.gptr[g + 1];
-    const int nsteps = (ge - gb) * TRS * nch;
+    const int nsteps = ccount > 0 ? (ge - gb) * TRS * nch : 0;   // an empty class writes nothing
     const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
+    // position i of the class -> its element offset in the output image
+    auto coords = [&](int64_t i, int& x0, int& x1, int& x2) {
+        x2 = cr[2] + (int)(i % cn[2]) * cs[2];
+        x1 = cr[1] + (int)((i / cn[2]) % cn[1]) * cs[1];
+        x0 = cr[0] + (int)(i / ((int64_t)cn[2] * cn[1])) * cs[0];
+    };
 
     // this thread's output position
-    const int64_t pos = pt * NP + t;
-    const bool pok = pos < HWo;
-    const int ow = (int)(pos % Wo), oh = (int)((pos / Wo) % Ho), od = (int)(pos / ((int64_t)Wo * Ho));
+    const int64_t pidx = tile * NP + t;
+    const bool pok = pidx < ccount;
+    int od = 0, oh = 0, ow = 0;
+    if (pok) coords(pidx, od, oh, ow);
+    // steps whose tap has no exactly dividing position in this class are skipped
+    auto tap_ok = [&](int tap) -> bool {
+        if (!cls) return true;
+        const int t3[3] = {tap / (a.S * a.R), (tap / a.S) % a.R, tap % a.S};
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+            const int u = cr[d] + a.pad[d] - t3[d] * a.dl[d];
+            if (((u % a.st[d]) + a.st[d]) % a.st[d] != 0) return false;
+        }
+        return true;
+    };
+    auto next_step = [&](int st) {
+        while (st < nsteps && !tap_ok((st / nch) % TRS)) st++;
+        return st;
+    };
 
     // per-lane element offset of the gathered value for tap (tt, r, s), or -1
     auto src_of = [&](int tt, int r, int s) -> int64_t {
@@ -860,14 +916,15 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
 #pragma unroll
         for (int o = 0; o < OT; o++) acc[u][o] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int m16 = lane & 15, q16 = (lane >> 4) * 16;
-    if (nsteps > 0) {
-        issue(0);
+    int step = next_step(0), buf = 0;
+    if (step < nsteps) {
+        issue(step);
         stage(0);
     }
     __syncthreads();
-    for (int step = 0; step < nsteps; step++) {
-        const int buf = step & 1;
-        if (step + 1 < nsteps) issue(step + 1);
+    while (step < nsteps) {
+        const int nxt = next_step(step + 1);
+        if (nxt < nsteps) issue(nxt);
         u32x4 bf[OT];
 #pragma unroll
         for (int o = 0; o < OT; o++) bf[o] = *reinterpret_cast<const u32x4*>(wsm[buf] + (o * 16 + m16) * PITCH + q16);
@@ -877,25 +934,32 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
 #pragma unroll
             for (int o = 0; o < OT; o++) mma<DT>(acc[u][o], af, bf[o]);
         }
-        if (step + 1 < nsteps) stage(buf ^ 1);
+        if (nxt < nsteps) stage(buf ^ 1);
         __syncthreads();
+        buf ^= 1;
+        step = nxt;
     }
-    // lane: positions 4*(lane/16) .. +3 of each of its tiles, output channel o*16 + lane%16
+    // lane: class positions 4*(lane/16) .. +3 of each of its tiles, output channel
+    // o*16 + lane%16 (consecutive in memory unless positions go by residue class)
     const int b0 = a.gblk[gb];
-    const bool vec = HWo % 4 == 0;
+    const bool vec = !cls && HWo % 4 == 0;
 #pragma unroll
     for (int o = 0; o < OT; o++) {
         const int64_t ch = out_idx[b0 * CO + o * 16 + m16];
         const int64_t base = (n * Cout + ch) * HWo;
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            const int64_t p0 = pt * NP + (wave * 4 + u) * 16 + 4 * (lane >> 4);
+            const int64_t p0 = tile * NP + (wave * 4 + u) * 16 + 4 * (lane >> 4);
             if (vec && p0 + 4 <= HWo) {
                 store4<DT>(a.out, base + p0, acc[u][o]);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; v++)
-                    if (p0 + v < HWo) store_elt(a.out, base + p0 + v, acc[u][o][v], DT);
+                    if (p0 + v < ccount) {
+                        int x0, x1, x2;
+                        coords(p0 + v, x0, x1, x2);
+                        store_elt(a.out, base + ((int64_t)x0 * Ho + x1) * Wo + x2, acc[u][o][v], DT);
+                    }
             }
         }
     }
@@ -1094,7 +1158,10 @@ bool conv_gather_ok(const ConvArgs& a, int pass) {
 template <int DT, int OT, bool TR>
 static hipError_t launch_conv_gather_t(const ConvArgs& a, hipStream_t st) {
     const int64_t HWo = TR ? (int64_t)a.D * a.H * a.W : (int64_t)a.M * a.P * a.Q;
-    const int64_t grid = (int64_t)a.ngroups * a.N * ((HWo + 255) / 256);
+    const bool cls = TR && (a.st[0] > 1 || a.st[1] > 1 || a.st[2] > 1);   // residue classes
+    const int64_t tiles = cls ? (int64_t)a.st[0] * a.st[1] * a.st[2] * ((conv_class_max(a.D, a.H, a.W, a.st) + 255) / 256)
+                              : (HWo + 255) / 256;
+    const int64_t grid = (int64_t)a.ngroups * a.N * tiles;
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
     const int pass = TR ? BSMM_PASS_CONV_BPROP : BSMM_PASS_CONV_FPROP;
     void *e0 = nullptr, *e1 = nullptr;
