@@ -660,7 +660,13 @@ static hipError_t launch_mm_t(const MMArgs& a, int kind, hipStream_t st, int pas
     switch (kind) {
     case MM_N16: return launch_cfg<DT, B, FA, TW, 1, 1, 4, DS>(a, st, pass);
     case MM_N64: return launch_cfg<DT, B, FA, TW, 2, 1, 4, DS>(a, st, pass);
-    case MM_MID: return launch_cfg<DT, B, FA, TW, 2, 4, 1, DM>(a, st, pass);
+    case MM_MID:
+        // 8x8 blocks, 16-bit, features first: 2 waves x 64 rows, so each activation row
+        // piece is a whole 128-byte line (4 waves x 32 rows read half lines): b = 8,
+        // N = 1024 fprop 156.6 -> 139-140 us, bprop 141.6 -> 121.6 us; 16x16 blocks
+        // run slower that way (hidden 4096, N = 512 fprop 32.2 -> 35.3 us)
+        if constexpr (B == 8 && FA == 0 && DT != BSMM_F32) return launch_cfg<DT, B, FA, TW, 4, 2, 1, DM>(a, st, pass);
+        return launch_cfg<DT, B, FA, TW, 2, 4, 1, DM>(a, st, pass);
     case MM_STACK: return launch_large<DT, B, FA, TW, 4, DS>(a, st, pass);
     case MM_V_W16: return launch_cfg<DT, B, FA, TW, 2, 1, 16, DS>(a, st, pass);
     case MM_N64_W8: return launch_cfg<DT, B, FA, TW, 2, 1, 8, DS>(a, st, pass);
