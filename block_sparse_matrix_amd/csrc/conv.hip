@@ -746,14 +746,16 @@ __host__ __device__ inline int64_t conv_class_max(int D, int H, int W, const int
     return (int64_t)((D + st[0] - 1) / st[0]) * ((H + st[1] - 1) / st[1]) * ((W + st[2] - 1) / st[2]);
 }
 
-template <int DT, int OT, bool TR>
+template <int DT, int OT, bool TR, int NP>
 __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
     constexpr bool F32 = DT == BSMM_F32;
     constexpr int ES = F32 ? 4 : 2;          // bytes per value
     constexpr int VEC = 16 / ES;             // values per 16 bytes
     constexpr int KC = 4 * VEC;              // contraction channels per step
     constexpr int CO = 16 * OT;
-    constexpr int NP = 256;                  // output positions per workgroup
+    // NP output positions per workgroup (256 or 64): TPP threads per position, each
+    // gathering CPT of the step's channels; TPW 16-position tiles per wave
+    constexpr int TPP = 256 / NP, CPT = KC / TPP, TPW = NP / 64;
     constexpr int PITCH = 80;                // LDS row: KC values (64 bytes) + 16
     constexpr int WCH = KC * CO / VEC;       // 16-byte filter chunks per step (<= 256)
     __shared__ __attribute__((aligned(16))) char gsm[2][NP * PITCH];
@@ -803,6 +805,8 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
     const int64_t n = rest % a.N;
     const int g = (int)(rest / a.N);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    // this thread's position and channel part (the part is the wave's: a scalar)
+    const int tp = t % NP, cq = TPP == 1 ? 0 : __builtin_amdgcn_readfirstlane(t / NP);
     const int gb = a.gptr[g], ge = a.gptr[g + 1];
     const int nsteps = ccount > 0 ? (ge - gb) * TRS * nch : 0;   // an empty class writes nothing
     const rsrc_t rin = make_rsrc(a.a, a.a_bytes);
@@ -814,7 +818,7 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
     };
 
     // this thread's output position
-    const int64_t pidx = tile * NP + t;
+    const int64_t pidx = tile * NP + tp;
     const bool pok = pidx < ccount;
     int od = 0, oh = 0, ow = 0;
     if (pok) coords(pidx, od, oh, ow);
@@ -852,7 +856,7 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
         return ((int64_t)c3[0] * Hi + c3[1]) * Wi + c3[2];
     };
 
-    uint32_t gv[KC];   // the next step's gathered values (16-bit: low half)
+    uint32_t gv[CPT];   // the next step's gathered values (16-bit: low half)
     u32x4 wv;          // and one 16-byte filter chunk (threads < WCH)
     const int wc = t / (CO / VEC), wp = t % (CO / VEC);   // fprop chunk: channel, output part
     const int bo = t / (KC / VEC), bq = t % (KC / VEC);   // bprop chunk: output, channel part
@@ -862,11 +866,11 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
         const int s = tap % a.S, r = (tap / a.S) % a.R, tt = tap / (a.S * a.R);
         const int64_t so = pok ? src_of(tt, r, s) : -1;
         const uint32_t voff = so >= 0 ? (uint32_t)(so * ES) : kOffLane;
-        const int c0 = chunk * KC;
+        const int c0 = chunk * KC, cc0 = c0 + cq * CPT;
 #pragma unroll
-        for (int c = 0; c < KC; c++) {
-            const bool cv = c0 + c < CI;   // uniform
-            const int ch = cv ? in_idx[b * CI + c0 + c] : 0;
+        for (int c = 0; c < CPT; c++) {
+            const bool cv = cc0 + c < CI;   // uniform per wave
+            const int ch = cv ? in_idx[b * CI + cc0 + c] : 0;
             const uint32_t soff = cv ? (uint32_t)(((n * Cin + ch) * HWi) * ES) : kOffOff;
             gv[c] = F32 ? bload32(rin, voff, soff) : bload16(rin, voff, soff);
         }
@@ -881,9 +885,9 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
         wv = *reinterpret_cast<const u32x4*>(fp);
     };
     auto stage = [&](int buf) {
-        char* grow = gsm[buf] + t * PITCH;
+        char* grow = gsm[buf] + tp * PITCH + cq * (64 / TPP);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < CPT / VEC; j++) {
             u32x4 v;
             if constexpr (F32) {
                 v = u32x4{gv[4 * j], gv[4 * j + 1], gv[4 * j + 2], gv[4 * j + 3]};
@@ -910,9 +914,9 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
         }
     };
 
-    f32x4 acc[4][OT];
+    f32x4 acc[TPW][OT];
 #pragma unroll
-    for (int u = 0; u < 4; u++)
+    for (int u = 0; u < TPW; u++)
 #pragma unroll
         for (int o = 0; o < OT; o++) acc[u][o] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int m16 = lane & 15, q16 = (lane >> 4) * 16;
@@ -929,8 +933,8 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
 #pragma unroll
         for (int o = 0; o < OT; o++) bf[o] = *reinterpret_cast<const u32x4*>(wsm[buf] + (o * 16 + m16) * PITCH + q16);
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const u32x4 af = *reinterpret_cast<const u32x4*>(gsm[buf] + ((wave * 4 + u) * 16 + m16) * PITCH + q16);
+        for (int u = 0; u < TPW; u++) {
+            const u32x4 af = *reinterpret_cast<const u32x4*>(gsm[buf] + ((wave * TPW + u) * 16 + m16) * PITCH + q16);
 #pragma unroll
             for (int o = 0; o < OT; o++) mma<DT>(acc[u][o], af, bf[o]);
         }
@@ -948,8 +952,8 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(ConvArgs a) {
         const int64_t ch = out_idx[b0 * CO + o * 16 + m16];
         const int64_t base = (n * Cout + ch) * HWo;
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int64_t p0 = tile * NP + (wave * 4 + u) * 16 + 4 * (lane >> 4);
+        for (int u = 0; u < TPW; u++) {
+            const int64_t p0 = tile * NP + (wave * TPW + u) * 16 + 4 * (lane >> 4);
             if (vec && p0 + 4 <= HWo) {
                 store4<DT>(a.out, base + p0, acc[u][o]);
             } else {
@@ -1159,9 +1163,13 @@ template <int DT, int OT, bool TR>
 static hipError_t launch_conv_gather_t(const ConvArgs& a, hipStream_t st) {
     const int64_t HWo = TR ? (int64_t)a.D * a.H * a.W : (int64_t)a.M * a.P * a.Q;
     const bool cls = TR && (a.st[0] > 1 || a.st[1] > 1 || a.st[2] > 1);   // residue classes
-    const int64_t tiles = cls ? (int64_t)a.st[0] * a.st[1] * a.st[2] * ((conv_class_max(a.D, a.H, a.W, a.st) + 255) / 256)
-                              : (HWo + 255) / 256;
-    const int64_t grid = (int64_t)a.ngroups * a.N * tiles;
+    auto tiles = [&](int np) {
+        return cls ? (int64_t)a.st[0] * a.st[1] * a.st[2] * ((conv_class_max(a.D, a.H, a.W, a.st) + np - 1) / np)
+                   : (HWo + np - 1) / np;
+    };
+    // 256-position tiles while they give at least two workgroups per CU, else 64
+    const bool big = (int64_t)a.ngroups * a.N * tiles(256) >= 512;
+    const int64_t grid = (int64_t)a.ngroups * a.N * tiles(big ? 256 : 64);
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
     const int pass = TR ? BSMM_PASS_CONV_BPROP : BSMM_PASS_CONV_FPROP;
     void *e0 = nullptr, *e1 = nullptr;
@@ -1175,7 +1183,8 @@ static hipError_t launch_conv_gather_t(const ConvArgs& a, hipStream_t st) {
         e0 = nullptr;
     }
     if (grid == 0) return hipSuccess;
-    return launch_ev(conv_gather_kernel<DT, OT, TR>, dim3((unsigned)grid), dim3(256), st, e0, e1, a);
+    if (big) return launch_ev(conv_gather_kernel<DT, OT, TR, 256>, dim3((unsigned)grid), dim3(256), st, e0, e1, a);
+    return launch_ev(conv_gather_kernel<DT, OT, TR, 64>, dim3((unsigned)grid), dim3(256), st, e0, e1, a);
 }
 
 template <int DT, bool TR>

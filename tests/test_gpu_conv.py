@@ -288,3 +288,30 @@ def test_conv_gather(case, dtype):
     assert_close(dF, ref, tol, "conv updat (gather, split)")
     assert_close(dF1, ref, tol, "conv updat (gather, one part)")
     assert torch.equal(dF, conv.updat(I, dO))
+
+
+@pytest.mark.parametrize("dtype,st", [("f32", (1, 1)), ("bf16", (2, 2))])
+def test_conv_gather_large_grid(dtype, st):
+    """The gathering kernels at a grid of 512 or more workgroups, where they take
+    256-position tiles (smaller grids take 64): 64 images of 32 x 32, checked against
+    the oracle on the first and last image (each image's outputs depend on that image
+    only)."""
+    N, C, B, TRS, DHW = 64, 64, 32, (3, 3), (32, 32)
+    print(f"case conv gather large grid {dtype} strides={st}", flush=True)
+    g = oc.geometry(TRS, DHW, st)
+    MPQ = g[2][1:]
+    P = synth.conv_problem(np.random.default_rng(91), N, C, C, B, B, 4, TRS, DHW, MPQ, dtype,
+                           contiguous_blocks=True)
+    conv = bs.BlocksparseConv(P.BCK, TRS, DHW, strides=st)
+    tdt = synth.DTYPES[dtype]
+    assert conv.kernel_name("bprop", tdt) == "matrix_core_gather"
+    F, I, dO = dev(P.F), dev(P.I), dev(P.dO)
+    O = conv.fprop(F, I)
+    dI = conv.bprop(F, dO)
+    torch.cuda.synchronize()
+    bck = oc.split_bck(P.BCK)
+    Fr = _f64(P.F)
+    for n in (0, N - 1):
+        Irn, dOn = _f64(P.I[n:n + 1]), _f64(P.dO[n:n + 1])
+        assert_close(O[n:n + 1], oc.fprop(bck, Fr, Irn, conv.K, g).reshape(1, conv.K, *MPQ), dtype, "fprop")
+        assert_close(dI[n:n + 1], oc.bprop(bck, Fr, dOn, conv.C, g).reshape(1, conv.C, *DHW), dtype, "bprop")
