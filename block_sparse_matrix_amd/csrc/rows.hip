@@ -28,11 +28,11 @@
 //      transposing LDS read.
 //   fp32 uses four 16x16x4 steps per 16 contraction values: lane group g's four values
 //   in step u are contraction indices 16 u + 4 g .. 16 u + 4 g + 3, the same map for
-//   both operands.  fp32 bprop loads the dy rows and the weight rows in row order,
-//   four consecutive lanes covering one row's 64 bytes, which the memory path serves
-//   several times faster than the fragment order (consecutive lanes on different rows);
-//   a lane permutation in registers (ds_bpermute) then forms the fragments (bprop
-//   11 % faster; fprop, with its 8-byte weight loads, gained nothing from it).
+//   both operands.  bprop (every dtype) loads the dy rows and the weight rows in row
+//   order, four consecutive lanes covering one row's 64 bytes, which the memory path
+//   serves several times faster than the fragment order (consecutive lanes on different
+//   rows); a lane permutation in registers (ds_bpermute) then forms the fragments (fp32
+//   bprop 11 % faster, 16-bit bprop ~5 %; fprop gained nothing from it).
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -61,7 +61,8 @@ template <int DT, bool TW> struct RowsCfgT {
     static constexpr int U = F32 ? 2 : 1;        // activation loads per tile and block
     static constexpr int WR = F32 ? (TW ? 4 : 8) : 2;
     static constexpr int WPITCH = 40;            // staged weight row pitch, 16-bit elements
-    static constexpr bool XROW = F32 && TW;      // fp32 bprop: rows loaded in row order
+    static constexpr bool XROW = TW;             // bprop: activation rows loaded in row order
+    static constexpr bool WROW = !F32 && TW;             // 16-bit bprop weight rows too
     // output feature (within the block) of lane row r in output tile t
     static __device__ __forceinline__ int qmap(int t, int r) { return W8 ? 2 * r + t : 16 * t + r; }
 };
@@ -121,13 +122,16 @@ __device__ __forceinline__ void rows_compute(f32x4 (&acc)[MT][2], const RowsSlot
             wf[1] = frag_tr16(wt, C::WPITCH, 16, lane);
             wave_lds_order();
         } else {
-            wf[0] = sl.w[0];
-            wf[1] = sl.w[1];
+            wf[0] = C::WROW ? rows_to_frag(sl.w[0], lane) : sl.w[0];
+            wf[1] = C::WROW ? rows_to_frag(sl.w[1], lane) : sl.w[1];
         }
+        u32x4 xf[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) xf[mt] = C::XROW ? rows_to_frag(sl.x[mt], lane) : sl.x[mt];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-            for (int t = 0; t < 2; t++) mma<DT>(acc[mt][t], sl.x[mt], wf[t]);
+            for (int t = 0; t < 2; t++) mma<DT>(acc[mt][t], xf[mt], wf[t]);
     }
 }
 
@@ -169,10 +173,10 @@ __global__ __launch_bounds__(64 * WAVES) void rows_kernel(MMArgs a) {
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            // fp32 bprop: row order (lane l: row l / 4, values 16 u + 4 (l % 4) ..); else
-            // fragment order (lane l: row l % 16, values 16 u + 4 (l / 16) .. or 8 (l / 16) ..)
+            // bprop: row order (lane l: row l / 4, values 16 u + 4 (l % 4) .. or 8 (l % 4) ..);
+            // else fragment order (lane l: row l % 16, values 16 u + 4 (l / 16) .. or 8 (l / 16) ..)
             const int n = n0 + 16 * mt + (C::XROW ? lane >> 2 : r16);
-            const int k0 = C::F32 ? 16 * u + 4 * (C::XROW ? lane & 3 : g) : 8 * g;
+            const int k0 = C::F32 ? 16 * u + 4 * (C::XROW ? lane & 3 : g) : 8 * (C::XROW ? lane & 3 : g);
             xo[mt * U + u] = n < N ? ((uint32_t)n * (uint32_t)a.fin + k0) * S : kOffLane;
         }
     uint32_t wo[WR];
@@ -184,6 +188,8 @@ __global__ __launch_bounds__(64 * WAVES) void rows_kernel(MMArgs a) {
             wo[i] = (uint32_t)(((16 * (i / 2) + (lane >> 2)) * B + 16 * (i % 2) + 4 * (lane & 3)) * S);
         else if constexpr (C::WTR)
             wo[i] = (uint32_t)((((lane + 64 * i) >> 2) * B + 8 * ((lane + 64 * i) & 3)) * S);
+        else if constexpr (C::WROW)
+            wo[i] = (uint32_t)(((16 * i + (lane >> 2)) * B + 8 * (lane & 3)) * S);
         else
             wo[i] = (uint32_t)(((16 * i + r16) * B + 8 * g) * S);
     }
