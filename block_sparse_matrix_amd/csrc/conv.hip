@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void conv_updat_kernel(ConvArgs a) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < a.Bk) {
+    if ((int)threadIdx.x < a.Bk) {
         const int j = threadIdx.x;
         const float v = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
         ((float*)a.out)[(int64_t)row * a.Bk + j] = v;

@@ -878,7 +878,6 @@ template <int DT, int D, int RL>
 __global__ __launch_bounds__(256) void updr_kernel(UpArgs a) {
     constexpr int B = 32;
     constexpr bool F32 = DT == BSMM_F32;
-    constexpr int S = F32 ? 4 : 2;
     // fp32: 4 chunks of 16 rows, 4 matrix-core steps of 4 rows each; 16-bit: 2 chunks
     // of 32 rows, one step each
     constexpr int NCH = F32 ? 4 : 2;
