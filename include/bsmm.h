@@ -39,8 +39,9 @@
  *     dtype with round-to-nearest-even.
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Kernels are
  *     enqueued asynchronously; no call synchronizes the device.
- *   - Every activation and weight tensor must be smaller than 2 GiB (the kernels use
- *     32-bit offsets); larger ones are rejected with BSMM_ERR_UNSUPPORTED.
+ *   - Every input activation and weight tensor must be at most 2 GiB - 64 KiB
+ *     (2,147,418,112 bytes: the kernels read them with 32-bit offsets); larger ones are
+ *     rejected with BSMM_ERR_UNSUPPORTED.  Outputs are written with 64-bit offsets.
  *   - N = 0: fprop and bprop do nothing and return BSMM_OK; updat writes dW = 0 (the
  *     empty sum).  Activation pointers may be NULL only when N = 0.
  *   - A handle is immutable after bsmm_create; it may be used from several host

@@ -98,6 +98,11 @@ def test_call_validation_before_gpu():
         assert L.bsmm_bprop(h, good, odd, good, 4, 2, None, 0, None) == ALIGN
         assert L.bsmm_fprop(None, good, good, good, 4, 0, None, 0, None) == INVALID
         assert L.bsmm_fprop(h, good, good, good, 1 << 40, 0, None, 0, None) == UNSUPPORTED
+        # one row past the largest input activation the kernels address (2 GiB - 64 KiB):
+        # x has 16 bf16 features per row (67 106 817 rows are 2 147 418 144 bytes), dy 24
+        # (44 737 878 rows)
+        assert L.bsmm_fprop(h, good, good, good, 67106817, 1, None, 0, None) == UNSUPPORTED
+        assert L.bsmm_bprop(h, good, good, good, 44737878, 1, None, 0, None) == UNSUPPORTED
         # N = 0 is a no-op for fprop / bprop, even with NULL pointers
         assert L.bsmm_fprop(h, None, None, None, 0, 0, None, 0, None) == 0
         assert L.bsmm_bprop(h, None, None, None, 0, 1, None, 0, None) == 0
