@@ -52,9 +52,13 @@ struct MMCfg {
     static constexpr int TILE_BYTES = WAVES * (WTILE + XTILE) * 2;
     static constexpr int RED_BYTES = WK > 1 ? WAVES * MT * QT * 64 * 16 : 0;   // partial tiles
     static constexpr int SMEM = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+    // List entries staged in LDS at a time.  16-bit 8x8 blocks with features first and
+    // whole-list waves stage 128: their lists are short (about 100 entries at 10 %
+    // density over 1024 block rows) and the smaller stage lets 6 instead of 4 waves per
+    // SIMD fit (hidden 8192, N = 1024: fprop and bprop about 11 % faster).  Elsewhere
+    // 1024 (16x16 fp16 with features first measured slower with 256).
+    static constexpr int LCAP = (B == 8 && FA == 0 && S16 && WK == 1) ? 128 : 1024;
 };
-
-constexpr int LCAP = 1024;   // list entries staged in LDS at a time
 
 template <int WR, int XR> struct Slot {
     u32x4 w[WR];
@@ -74,9 +78,10 @@ __global__ __launch_bounds__(64 * WM * WK) void mm_kernel(MMArgs a) {
     constexpr int EPS = UNI ? 1 : KS / B;   // entries per step
     // wave-private transpose tiles during the walk; the WK partial tiles afterwards
     __shared__ __attribute__((aligned(16))) char smem[Cfg::SMEM > 0 ? Cfg::SMEM : 16];
-    // The list is staged in LDS (chunks of LCAP entries): the ring's loads then depend
+    // The list is staged in LDS (chunks of Cfg::LCAP entries): the ring's loads then depend
     // on LDS reads only, never on another global load, which would make the wave wait
     // for every load in flight.
+    constexpr int LCAP = Cfg::LCAP;
     __shared__ int2 lst[LCAP];
 
     const int lane = threadIdx.x & 63;

@@ -245,12 +245,14 @@ def test_long_minibatch(b, fa, dtype, N):
     assert_close(dw, rdw, dtype, "updat")
 
 
-@pytest.mark.parametrize("N", [64, 2048])
-@pytest.mark.parametrize("b,fa,dtype", [(8, 1, "f32"), (8, 0, "bf16"), (16, 1, "bf16"), (32, 0, "f16")])
+@pytest.mark.parametrize("N", [64, 1000, 2048])
+@pytest.mark.parametrize("b,fa,dtype", [(8, 1, "f32"), (8, 0, "bf16"), (8, 0, "f16"), (16, 1, "bf16"), (32, 0, "f16")])
 def test_lists_longer_than_one_chunk(b, fa, dtype, N):
     """Block lists longer than one staged chunk: 1030 entries at N = 64 (the record
-    holds the first 1024); at N = 2048 lists longer than the LDS weight stack holds
-    (at most 187 entries of 8x8 blocks, 18 of 32x32)."""
+    holds the first 1024); at N = 1000, 300 entries (16-bit 8x8 blocks with features
+    first stage 128 at a time, so the list walk takes three chunks, the last partial);
+    at N = 2048 lists longer than the LDS weight stack holds (at most 187 entries of 8x8
+    blocks, 18 of 32x32)."""
     R = 1030 if N == 64 else (300 if b < 32 else 40)
     print(f"case longlist b={b} fa={fa} dtype={dtype} N={N} R={R}", flush=True)
     rng = np.random.default_rng(11 * b + N)
@@ -259,6 +261,10 @@ def test_lists_longer_than_one_chunk(b, fa, dtype, N):
     L[2, :] = 1                       # one input block feeding R outputs
     L[np.arange(R), np.arange(R)] = 1
     P = synth.random_problem(rng, L, b, N, fa, dtype, w_std=0.05)
+    if N == 1000 and b == 8 and fa == 0:
+        m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=fa)
+        for p in ("fprop", "bprop"):
+            assert m.kernel_name(p, N, TORCH_DT[dtype]) == "list_rows128"
     y, dx, dw = _run_all(P, dtype)
     ry, rdx, rdw = _oracle_all(P, dtype)
     assert_close(y, ry, dtype, "fprop")
