@@ -269,9 +269,23 @@ bsmm_status mm_pass(bsmm_handle h, const void* in, const void* w, void* out, int
     return e == hipSuccess ? BSMM_OK : dev_fail(e, transw ? "bprop launch" : "fprop launch");
 }
 
+// Workspace of the dense-tile weight gradient (32x32 blocks, 16-bit activations): the
+// tiles' split partial sums, then the split partial sums of the blocks outside them.
+void updat_ws_parts(const HostLut& L, int64_t N, bsmm_dtype dt, size_t* tiles, size_t* rest) {
+    *tiles = *rest = 0;
+    if (N <= 0 || dt == BSMM_F32 || L.b != 32) return;
+    const int nt = (int)(L.utiles.size() / 4);
+    const int p = tile_split(nt);
+    if (p > 1) *tiles = (size_t)p * nt * kTileSide * kTileSide * 32 * 32 * sizeof(float);
+    if (nt * p >= 128)   // the tile kernel can be chosen (enough tiles x parts)
+        *rest = (size_t)kRestSplit * L.urids.size() * 32 * 32 * sizeof(float);
+}
+
 UpArgs up_args(const HostLut& L, int64_t N, int group) {
     UpArgs a{};
     a.split = 1;
+    a.rsplit = 1;
+    a.nrids = (int32_t)L.urids.size();
     a.ntiles = (int32_t)(L.utiles.size() / 4);
     a.nrest = (int32_t)(L.urest.size() / 4);
     a.ngroups = (int32_t)(L.ugroups.size() / 4);
@@ -368,10 +382,10 @@ bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype d
     if (N < 0) return fail(BSMM_ERR_INVALID_ARG, "N must be >= 0");
     if (!valid_dt(dt)) return fail(BSMM_ERR_INVALID_ARG, "bad dtype");
     *bytes = 0;
-    if (pass == BSMM_PASS_UPDAT && N > 0 && dt != BSMM_F32 && h->lut.b == 32) {
-        const int nt = (int)(h->lut.utiles.size() / 4);
-        const int p = tile_split(nt);
-        if (p > 1) *bytes = (size_t)p * nt * kTileSide * kTileSide * 32 * 32 * sizeof(float);
+    if (pass == BSMM_PASS_UPDAT) {
+        size_t tb = 0, rb = 0;
+        updat_ws_parts(h->lut, N, dt, &tb, &rb);
+        *bytes = tb + rb;
     }
     return BSMM_OK;
 }
@@ -406,9 +420,9 @@ bsmm_status bsmm_kernel_name(bsmm_handle h, int pass, int64_t N, int group, bsmm
     } else if (pass == BSMM_PASS_UPDAT) {
         UpArgs a = up_args(L, N, group);
         a.force = h->force[BSMM_PASS_UPDAT];
-        size_t need = 0;
-        (void)bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need);
-        if (need > 0) a.split = tile_split(a.ntiles);   // as when the workspace is given
+        size_t tb = 0, rb = 0;
+        updat_ws_parts(L, N, dt, &tb, &rb);
+        if (tb > 0) a.split = tile_split(a.ntiles);   // as when the workspace is given
         if (L.nnz > 0) *name = updat_kind_name(updat_kind(a, dt, L.b, L.fa));
     } else if (pass == BSMM_PASS_IDENTITY) {
         if (L.nnz > 0) *name = "identity";
@@ -473,11 +487,17 @@ bsmm_status updat_call(bsmm_handle h, const void* const* xs, const void* const* 
     a.stids = d->stids;
     a.dy_bytes = (uint32_t)((uint64_t)N * a.K * es);
     a.force = h->force[BSMM_PASS_UPDAT];
-    {   // a contraction split of the tiles needs the workspace; without it, no split
-        size_t need = 0;
-        (void)bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need);
-        a.split = need > 0 && ws && ws_bytes >= need && ((uintptr_t)ws & 15u) == 0 ? tile_split(a.ntiles) : 1;
+    {   // a contraction split needs the workspace: the tiles' when it holds their parts,
+        // the other blocks' when it holds both; without it, no split
+        size_t tb = 0, rb = 0;
+        updat_ws_parts(L, N, dt, &tb, &rb);
+        const bool ok = ws && ((uintptr_t)ws & 15u) == 0;
+        a.split = ok && tb > 0 && ws_bytes >= tb ? tile_split(a.ntiles) : 1;
         a.ws = (float*)ws;
+        if (ok && rb > 0 && a.nrest > 0 && ws_bytes >= tb + rb) {
+            a.rsplit = kRestSplit;
+            a.rws = (float*)((char*)ws + tb);
+        }
     }
     if (updat_kind(a, dt, L.b, L.fa) < 0)
         return fail(BSMM_ERR_UNSUPPORTED, "the forced kernel does not apply to these arguments");
@@ -540,12 +560,15 @@ bsmm_status bsmm_updat_noalloc(bsmm_handle h, const void* const* xs, const void*
                                int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* stream) {
     bsmm_status s = check_call(h, N, dt);
     if (s != BSMM_OK) return s;
-    size_t need = 0;
-    if ((s = bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need)) != BSMM_OK) return s;
-    if (need > kScratchBytes)
-        return fail(BSMM_ERR_UNSUPPORTED, "this weight gradient needs " + std::to_string(need) +
+    // The tiles' partial sums must fit the scratch; the other blocks' split is used when
+    // both fit, else those blocks are written unsplit.
+    size_t tb = 0, rb = 0;
+    updat_ws_parts(h->lut, N, dt, &tb, &rb);
+    if (tb > kScratchBytes)
+        return fail(BSMM_ERR_UNSUPPORTED, "this weight gradient needs " + std::to_string(tb) +
                                               " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
                                               "-byte scratch of the allocation-free entry point");
+    const size_t need = tb + rb <= kScratchBytes ? tb + rb : tb;
     void* ws = nullptr;
     if (need > 0 && (s = scratch_address(&ws)) != BSMM_OK) return s;
     return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, need, stream, false, true);

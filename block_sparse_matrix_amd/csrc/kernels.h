@@ -69,6 +69,9 @@ struct UpArgs {
     int32_t force;          // UpKind to use (0: automatic)
     int32_t split;          // tiles: contraction split in this many parts (1: none)
     float* ws;              // tiles with split > 1: fp32 partial sums, split*ntiles*64 blocks
+    int32_t nrids;          // blocks outside the tiles (entries of rids)
+    int32_t rsplit;         // those blocks' contraction split (1: none, written to dw directly)
+    float* rws;             // rsplit > 1: fp32 partial sums, rsplit*nrids blocks, part-major
     int32_t acc;            // 1: add the sum to what dw holds (dW += ...); 0: overwrite
     // 8x8 and 16x16 blocks: small-block tiles (lut_format.h)
     const int32_t* stiles;
@@ -85,6 +88,10 @@ inline int tile_split(int ntiles) {
     const int p = 256 / ntiles;
     return p < 1 ? 1 : p > kMaxSplit ? kMaxSplit : p;
 }
+// Contraction split of the blocks outside the tiles (their row groups are few, about one
+// workgroup per CU): four parts, each summed over the step groups in order, then the
+// parts in order.  Needs kRestSplit*nrids*b*b*4 more bytes of workspace.
+constexpr int kRestSplit = 4;
 
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.

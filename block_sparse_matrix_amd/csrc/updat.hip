@@ -312,6 +312,11 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
 // steps; their partial tiles are added in wave order through LDS and each block is
 // written once.  Groups are dealt to XCDs in contiguous row ranges, so neighbouring
 // rows (which share columns, e.g. in a banded layout) reuse dy slabs from one L2.
+// With nparts > 1 the contraction is also cut into nparts consecutive step ranges, one
+// workgroup each (parts of one XCD's groups follow each other), and part p of the
+// group's j-th block goes to pws[(p * nrids + first + j) * b * b ...] instead of dw:
+// written when addp is 0, added to what is there otherwise (one writer per element,
+// launches in stream order).
 template <int DT, int B, int FA, int GM, int D>
 struct UGCfg {
     static constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;
@@ -328,7 +333,8 @@ struct UGCfg {
 };
 
 template <int DT, int B, int FA, int GM, int D>
-__global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restrict__ groups, int ngroups) {
+__global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restrict__ groups, int ngroups,
+                                                   int nparts, float* __restrict__ pws, int addp) {
     using Cfg = UGCfg<DT, B, FA, GM, D>;
     using T = typename Elt<DT>::T;
     constexpr int S = (int)sizeof(T);
@@ -342,8 +348,9 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
     const int r16 = lane & 15, g = lane >> 4;
     // group index: XCD x takes the x-th contiguous range of groups (rows)
     const int gpx = (ngroups + 7) / 8;
-    const int gi = (blockIdx.x & 7) * gpx + (blockIdx.x >> 3);
-    if (gi >= ngroups) return;   // whole workgroup
+    const int slot = blockIdx.x >> 3, part = slot / gpx;
+    const int gi = (blockIdx.x & 7) * gpx + slot % gpx;
+    if (gi >= ngroups || part >= nparts) return;   // whole workgroup
     const int4 gr = groups[gi];   // (first, count, row, 0: ids first.. / 1: ids rids[first..])
     const int id0 = gr.x, cnt = gr.y, c = gr.z;
     const bool listed = gr.w != 0;
@@ -418,8 +425,11 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         }
     };
 
-    auto load_slot = [&](Slot& sl, int st0, auto& pick) {
-        const bool sv = st0 < nsb;   // wave-uniform
+    // this part's steps [sbeg, send)
+    const int sbeg = (int)((int64_t)nsb * part / nparts), send = (int)((int64_t)nsb * (part + 1) / nparts);
+    auto load_slot = [&](Slot& sl, int sr, auto& pick) {   // sr: step within the part
+        const int st0 = sbeg + sr;
+        const bool sv = st0 < send;   // wave-uniform
         const int st = sv ? st0 : 0;
         const int t = st / spt;
         const int nb = (st % spt) * KS;
@@ -476,7 +486,8 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
                     for (int pt = 0; pt < PT; pt++) mma<DT>(acc[j][qt][pt], fr[1 + j][qt], fr[0][pt]);   // D[q][p]
     };
 
-    const int mysteps = nsb > wk ? (nsb - wk + 3) / 4 : 0;
+    const int nps = send - sbeg;
+    const int mysteps = nps > wk ? (nps - wk + 3) / 4 : 0;
     auto run = [&](auto&& pick) {
         Slot ring[D];
 #pragma unroll
@@ -518,8 +529,14 @@ __global__ __launch_bounds__(256) void updg_kernel(UpArgs a, const int4* __restr
         const int qt = rem / (PT * 64), pt = (rem / 64) % PT, l = rem % 64;
         const int p = pt * 16 + (l & 15), q = qt * 16 + 4 * (l >> 4);
         if (p < B && q < B) {
-            const int64_t idx = (int64_t)(listed ? a.rids[id0 + j] : id0 + j) * B * B + p * B + q;
-            store_dw4(a, idx, sum);
+            if (pws) {   // listed groups only: id0 + j is the block's entry of rids
+                f32x4* dst = reinterpret_cast<f32x4*>(pws + ((int64_t)part * a.nrids + id0 + j) * B * B + p * B + q);
+                if (addp) sum += *dst;
+                *dst = sum;
+            } else {
+                const int64_t idx = (int64_t)(listed ? a.rids[id0 + j] : id0 + j) * B * B + p * B + q;
+                store_dw4(a, idx, sum);
+            }
         }
     }
 }
@@ -752,12 +769,28 @@ __global__ __launch_bounds__(512) void updt_kernel(UpArgs a) {
 
 template <int DT, int B, int FA, int GM = 8>
 static hipError_t launch_updat_grouped(const UpArgs& a, const int4* groups, int ngroups, hipStream_t st,
-                                       void* e0 = nullptr, void* e1 = nullptr, bool own_events = true) {
-    const int grid = ((ngroups + 7) / 8) * 8;
+                                       void* e0 = nullptr, void* e1 = nullptr, bool own_events = true,
+                                       int nparts = 1, float* pws = nullptr, int addp = 0) {
+    const int grid = ((ngroups + 7) / 8) * 8 * nparts;
     if (own_events)
         return launch(BSMM_PASS_UPDAT, updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, a, groups,
-                      ngroups);
-    return launch_ev(updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, e0, e1, a, groups, ngroups);
+                      ngroups, nparts, pws, addp);
+    return launch_ev(updg_kernel<DT, B, FA, GM, 2>, dim3((unsigned)grid), dim3(256), st, e0, e1, a, groups, ngroups,
+                     nparts, pws, addp);
+}
+
+// Sum of the contraction parts of every block outside the tiles, in part order, to dW:
+// one workgroup per block.
+template <int B>
+__global__ __launch_bounds__(256) void updg_reduce(UpArgs a) {
+    const int r = blockIdx.x;
+    const int id = a.rids[r];
+    for (int e = 4 * threadIdx.x; e < B * B; e += 4 * 256) {
+        f32x4 s = *reinterpret_cast<const f32x4*>(a.rws + (int64_t)r * B * B + e);
+        for (int p = 1; p < a.rsplit; p++)
+            s += *reinterpret_cast<const f32x4*>(a.rws + ((int64_t)p * a.nrids + r) * B * B + e);
+        store_dw4(a, (int64_t)id * B * B + e, s);
+    }
 }
 
 // Sum of the split parts of every tile block, in part order (deterministic), to dW: one
@@ -798,6 +831,21 @@ static hipError_t launch_updat_tiles(const UpArgs& a, hipStream_t st) {
             if (e != hipSuccess) return e;
         }
         if (a.nrest == 0) return hipSuccess;
+        if (a.rsplit > 1) {
+            // Remaining blocks with a contraction split: fp32 parts in rws (one launch per
+            // step group, each adding its group to the parts, so a launch reads one group's
+            // activations only), then the parts' sum to dW.
+            for (int t = 0; t < a.G; t++) {
+                UpArgs at = a;
+                at.G = 1;
+                at.xs[0] = a.xs[t];
+                at.dys[0] = a.dys[t];
+                e = launch_updat_grouped<DT, B, FA, kRestGroup>(at, (const int4*)a.rest, a.nrest, st, nullptr, nullptr,
+                                                                false, a.rsplit, a.rws, t > 0);
+                if (e != hipSuccess) return e;
+            }
+            return launch_ev(updg_reduce<B>, dim3((unsigned)a.nrids), dim3(256), st, nullptr, e1, a);
+        }
         if (a.G > 1 && a.dwdt == BSMM_F32) {
             // Remaining blocks of several step groups, fp32 dW: one launch per group, each
             // adding its group to dW (the first overwrites unless the call accumulates).

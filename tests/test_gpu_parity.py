@@ -341,13 +341,71 @@ def test_updat_dense_tiles_unsplit(fa):
     P = synth.random_problem(rng, L, 32, N, fa, "bf16", w_std=0.1)
     m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
     assert len(bs.bsmm_debug_lut(m.handle, 16)) // 4 >= 128
-    assert bs.bsmm_workspace_size(m.handle, 2, N, torch.bfloat16) == 0
+    # no tile partials; the blocks outside the tiles take their split parts
+    nrest = len(bs.bsmm_debug_lut(m.handle, 19))
+    assert nrest > 0
+    assert bs.bsmm_workspace_size(m.handle, 2, N, torch.bfloat16) == 4 * nrest * 32 * 32 * 4
     assert m.kernel_name("updat", N, torch.bfloat16) == "dense_tiles"
     dw = m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys])
     torch.cuda.synchronize()
     bits = synth.to_bits
     rdw = oracle.updat(P.layout, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, "bf16")
     assert_close(dw, rdw, "bf16", "updat")
+
+
+def _tiles_and_rest(rng):
+    """20 dense 8x8-block tiles (Bernoulli(0.45) over 32 x 40 blocks) and a sparse last
+    tile column (Bernoulli(0.1)), whose blocks stay outside the tiles."""
+    L = np.zeros((32, 48), dtype=np.uint8)
+    L[:, :40] = rng.random((32, 40)) < 0.45
+    L[:, 40:] = rng.random((32, 8)) < 0.1
+    return L
+
+
+@pytest.mark.parametrize("fa,dtype,N,G,dw_dtype,acc", [
+    (1, "bf16", 520, 3, "f32", False),   # per-step-group launches adding to the parts
+    (1, "bf16", 1000, 1, "f32", False),  # one launch
+    (0, "f16", 512, 2, "f32", False),
+    (0, "bf16", 520, 1, "bf16", False),  # 16-bit gradient from the parts' fp32 sum
+    (1, "f16", 512, 2, "f32", True),     # accumulating: the parts' sum added to dW
+])
+def test_updat_tiles_with_split_rest(fa, dtype, N, G, dw_dtype, acc):
+    """Dense tiles with enough tiles for the split tile path, and blocks outside the tiles
+    whose contraction is cut into four parts (fp32 parts in the workspace after the
+    tiles' partials, each part summed over the step groups, then the parts in order)."""
+    if fa == 0 and N % 8:
+        pytest.skip("features-first activations take the tile kernel only for N % 8 == 0")
+    print(f"case tiles+rest fa={fa} {dtype} N={N} G={G} dw={dw_dtype} acc={acc}", flush=True)
+    rng = np.random.default_rng(900 + N + G + fa)
+    L = _tiles_and_rest(rng)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=fa)
+    nt = len(bs.bsmm_debug_lut(m.handle, 16)) // 4
+    nrest = len(bs.bsmm_debug_lut(m.handle, 19))
+    assert nt >= 16 and nrest > 0
+    split = min(8, 256 // nt)
+    assert bs.bsmm_workspace_size(m.handle, 2, N, TORCH_DT[dtype]) == (split * nt * 64 + 4 * nrest) * 32 * 32 * 4
+    assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == "dense_tiles"
+    P = synth.random_problem(rng, L, 32, N, fa, dtype, G=G, w_std=0.1)
+    xs, dys = [dev(t) for t in P.xs], [dev(t) for t in P.dys]
+    def run():
+        if acc:
+            out = dev(dw0)
+        else:
+            out = torch.full(m.w_shape, float("nan"), device="cuda").to(TORCH_DT[dw_dtype])
+        bs.bsmm_updat(m.handle, xs, dys, out, N, accumulate=acc)
+        torch.cuda.synchronize()
+        return out
+
+    bits = synth.to_bits
+    if acc:
+        dw0 = (torch.randn(m.w_shape, generator=torch.Generator().manual_seed(5)) * 3.0).to(TORCH_DT[dw_dtype])
+        ref = oracle.updat_accumulate(L, 32, fa, bits(dw0), dw_dtype, [bits(t) for t in P.xs],
+                                      [bits(t) for t in P.dys], N, dtype)
+    else:
+        ref = oracle.updat(L, 32, fa, [bits(t) for t in P.xs], [bits(t) for t in P.dys], N, dtype)
+    dw = run()
+    assert_close(dw, ref, dtype, "updat")
+    assert torch.equal(dw, run())   # deterministic: a second call gives the same bits
 
 
 @pytest.mark.parametrize("dw_dtype", ["f32", "bf16", "f16"])

@@ -21,11 +21,26 @@ def _band(R, width):
     return (np.abs(c[:, None] - c[None, :]) <= width).astype(np.uint8)
 
 
+def _tiles_and_rest(rng):
+    """20 dense 8x8-block tiles and a sparse last tile column outside them: the blocks
+    outside the tiles take the split path too (their parts after the tiles' in the
+    scratch)."""
+    L = np.zeros((32, 48), dtype=np.uint8)
+    L[:, :40] = rng.random((32, 40)) < 0.45
+    L[:, 40:] = rng.random((32, 8)) < 0.1
+    return L
+
+
 @pytest.mark.parametrize("b,fa,dtype,layout", [(32, 1, "bf16", "band"), (32, 0, "f16", "band"),
-                                                (16, 0, "f16", "random")])
+                                                (32, 1, "bf16", "tiles_rest"), (16, 0, "f16", "random")])
 def test_noalloc_matches_updat(b, fa, dtype, layout):
     rng = np.random.default_rng(77 + b + fa)
-    L = _band(64, 2) if layout == "band" else (rng.random((24, 20)) < 0.3).astype(np.uint8)
+    if layout == "band":
+        L = _band(64, 2)
+    elif layout == "tiles_rest":
+        L = _tiles_and_rest(rng)
+    else:
+        L = (rng.random((24, 20)) < 0.3).astype(np.uint8)
     m = bs.BlocksparseMatMul(L, block_size=b, feature_axis=fa)
     h = m.handle
     for call, (N, G) in enumerate([(512, 2), (256, 2)]):   # second call: a smaller input
@@ -34,8 +49,8 @@ def test_noalloc_matches_updat(b, fa, dtype, layout):
         xs = [dev(t) for t in P.xs]
         dys = [dev(t) for t in P.dys]
         need = bs.bsmm_workspace_size(h, 2, N, xs[0].dtype)
-        if layout == "band":
-            assert need > 0, "the band layout must take the split tile path"
+        if layout != "random":
+            assert need > 0, "this layout must take the split tile path"
         ref = torch.empty(m.w_shape, dtype=torch.float32, device="cuda")
         bs.bsmm_updat(h, xs, dys, ref, N)                  # also uploads the layout tables
         got = torch.full(m.w_shape, float("nan"), device="cuda")
