@@ -527,7 +527,7 @@ bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs, const vo
 // copy per GPU, held until the process ends, shared by every call on that GPU.  Host
 // code never passes `scratch` itself (on the host the name is only a stand-in); it
 // passes the device address hipGetSymbolAddress reports for the current device.
-constexpr size_t kScratchBytes = 64ull << 20;
+constexpr size_t kScratchBytes = 128ull << 20;
 static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 namespace {
@@ -560,15 +560,12 @@ bsmm_status bsmm_updat_noalloc(bsmm_handle h, const void* const* xs, const void*
                                int64_t N, bsmm_dtype dt, bsmm_dtype dw_dt, void* stream) {
     bsmm_status s = check_call(h, N, dt);
     if (s != BSMM_OK) return s;
-    // The tiles' partial sums must fit the scratch; the other blocks' split is used when
-    // both fit, else those blocks are written unsplit.
-    size_t tb = 0, rb = 0;
-    updat_ws_parts(h->lut, N, dt, &tb, &rb);
-    if (tb > kScratchBytes)
-        return fail(BSMM_ERR_UNSUPPORTED, "this weight gradient needs " + std::to_string(tb) +
+    size_t need = 0;
+    if ((s = bsmm_workspace_size(h, BSMM_PASS_UPDAT, N, dt, &need)) != BSMM_OK) return s;
+    if (need > kScratchBytes)
+        return fail(BSMM_ERR_UNSUPPORTED, "this weight gradient needs " + std::to_string(need) +
                                               " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
                                               "-byte scratch of the allocation-free entry point");
-    const size_t need = tb + rb <= kScratchBytes ? tb + rb : tb;
     void* ws = nullptr;
     if (need > 0 && (s = scratch_address(&ws)) != BSMM_OK) return s;
     return updat_call(h, xs, dys, group, dw, N, dt, dw_dt, ws, need, stream, false, true);

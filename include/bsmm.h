@@ -132,10 +132,14 @@ BSMM_API bsmm_status bsmm_block_coord(bsmm_handle h, int64_t block, int64_t* c, 
 BSMM_API bsmm_status bsmm_plan_info(bsmm_handle h, int64_t out[5]);
 
 /* Bytes of device workspace a pass needs for minibatch N and dtype.  Non-zero only for
- * updat with 32x32 blocks and 16-bit activations when the layout has few dense 8x8-block
- * tiles: the tiles' contraction is then split in parts whose fp32 partial sums live in
- * the workspace (parts x tiles x 64 x 4 KiB).  updat called with a smaller or NULL
- * workspace runs unsplit (correct, slower).  pass is a bsmm_pass value. */
+ * updat with 32x32 blocks and 16-bit activations on layouts with dense 8x8-block tiles:
+ * when the tiles are few, their contraction is split in parts whose fp32 partial sums
+ * live in the workspace (parts x tiles x 64 x 4 KiB), and when there are enough tiles
+ * for the tile kernel, the blocks outside the tiles have their contraction cut in four
+ * parts, also summed in fp32 in the workspace after the tiles' (4 x those blocks x
+ * 4 KiB).  updat called with a smaller workspace splits only what it holds (the tiles'
+ * parts first), and with a NULL one runs unsplit (correct, slower; the summation order,
+ * and so the rounding, differs).  pass is a bsmm_pass value. */
 BSMM_API bsmm_status bsmm_workspace_size(bsmm_handle h, int pass, int64_t N, bsmm_dtype dt, size_t* bytes);
 
 /* fprop: y = x . W~.
@@ -180,11 +184,11 @@ BSMM_API bsmm_status bsmm_updat_accumulate(bsmm_handle h, const void* const* xs,
 /* updat for callers that cannot allocate device memory (code under HIP-graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same result as bsmm_updat
  * (same kernels, bit for bit), with the split weight-gradient kernels' fp32 partial sums
- * in a fixed 64 MiB device array of the library instead of a caller workspace.  The
+ * in a fixed 128 MiB device array of the library instead of a caller workspace.  The
  * call makes no hipMalloc / hipFree and calls no allocating routine.
  *   Arguments as bsmm_updat without ws / ws_bytes.
  *   Errors as bsmm_updat, and BSMM_ERR_UNSUPPORTED when bsmm_workspace_size(h,
- *   BSMM_PASS_UPDAT, N, dt) exceeds 64 MiB, or when the handle's layout tables are not
+ *   BSMM_PASS_UPDAT, N, dt) exceeds 128 MiB, or when the handle's layout tables are not
  *   on the current device yet (they are uploaded by the first call of any other entry
  *   point on that device).
  * The array is one per GPU, held until the process ends, and shared by every call on

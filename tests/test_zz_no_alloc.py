@@ -76,3 +76,31 @@ def test_noalloc_needs_tables_on_the_device():
     assert "allocating entry point" in str(ei.value)
     torch.cuda.synchronize()
     assert torch.all(dw == 3.0)
+
+
+def test_noalloc_band_workload_size():
+    """The band workload's weight gradient at its full size (hidden 8192, 32x32 blocks,
+    N = 4096, 8 step groups): 32 tiles split 8 ways (64 MiB of parts) and 869 blocks
+    outside them split 4 ways (14 MiB) fit the scratch; bit-identical to bsmm_updat with
+    a caller workspace, on two calls in a row (the second with 2 step groups and N = 1024)."""
+    wl = synth.WORKLOADS["hidden8192_b32_n4096_g8"]
+    rng = np.random.default_rng(wl.seed)
+    R = wl.hidden // wl.block
+    L = synth.make_layout(wl.layout_kind, R, R, rng)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    h = m.handle
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for call, (N, G) in enumerate([(4096, 8), (1024, 2)]):
+        print(f"case noalloc band workload call={call} N={N} G={G}", flush=True)
+        xs = [(torch.randn(N, wl.hidden, device="cuda", generator=gen)).to(torch.bfloat16) for _ in range(G)]
+        dys = [(torch.randn(N, wl.hidden, device="cuda", generator=gen)).to(torch.bfloat16) for _ in range(G)]
+        need = bs.bsmm_workspace_size(h, 2, N, torch.bfloat16)
+        assert 64 << 20 < need <= 128 << 20 if call == 0 else need > 0
+        assert m.kernel_name("updat", N, torch.bfloat16, G) == "dense_tiles"
+        ref = torch.empty(m.w_shape, dtype=torch.float32, device="cuda")
+        bs.bsmm_updat(h, xs, dys, ref, N)
+        got = torch.full(m.w_shape, float("nan"), device="cuda")
+        bs.bsmm_updat_noalloc(h, xs, dys, got, N)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "the allocation-free call differs from bsmm_updat"
+        del xs, dys
