@@ -88,10 +88,10 @@ inline int tile_split(int ntiles) {
     const int p = 256 / ntiles;
     return p < 1 ? 1 : p > kMaxSplit ? kMaxSplit : p;
 }
-// Contraction split of the blocks outside the tiles (their row groups are few, about one
-// workgroup per CU): four parts, each summed over the step groups in order, then the
-// parts in order.  Needs kRestSplit*nrids*b*b*4 more bytes of workspace.
-constexpr int kRestSplit = 4;
+// Contraction split of the blocks outside the tiles (their row groups are few, a few
+// hundred 4-wave workgroups): eight parts, each summed over the step groups in order,
+// then the parts in order.  Needs kRestSplit*nrids*b*b*4 more bytes of workspace.
+constexpr int kRestSplit = 8;
 
 // Kernel choice of a pass for its arguments (the launchers use the same choice).  A
 // forced kind that cannot serve the arguments gives -1.

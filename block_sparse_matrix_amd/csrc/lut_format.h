@@ -20,7 +20,7 @@ constexpr int kTileMin = 16;
 constexpr int kTileWaves = 8;   // a tile's blocks are split over 8 waves, in order
 // Tiles are processed in super-blocks of kSuperRows x kSuperCols tiles (layout.cpp).
 // Blocks outside the dense tiles: row groups of at most this many ids.
-constexpr int kRestGroup = 4;
+constexpr int kRestGroup = 2;
 constexpr int kSuperRows = 4;
 constexpr int kSuperCols = 8;
 

@@ -313,10 +313,10 @@ __global__ __launch_bounds__(256) void updat_kernel(UpArgs a) {
 // written once.  Groups are dealt to XCDs in contiguous row ranges, so neighbouring
 // rows (which share columns, e.g. in a banded layout) reuse dy slabs from one L2.
 // With nparts > 1 the contraction is also cut into nparts consecutive step ranges, one
-// workgroup each (parts of one XCD's groups follow each other), and part p of the
-// group's j-th block goes to pws[(p * nrids + first + j) * b * b ...] instead of dw:
-// written when addp is 0, added to what is there otherwise (one writer per element,
-// launches in stream order).
+// workgroup each (an XCD runs part 0 of each of its groups, then part 1, ...), and part
+// p of the group's j-th block goes to pws[(p * nrids + first + j) * b * b ...] instead
+// of dw: written when addp is 0, added to what is there otherwise (one writer per
+// element, launches in stream order).  Only listed groups (ids in rids) take parts.
 template <int DT, int B, int FA, int GM, int D>
 struct UGCfg {
     static constexpr int VEC = Elt<DT>::VEC, KS = 4 * VEC;

@@ -135,8 +135,8 @@ BSMM_API bsmm_status bsmm_plan_info(bsmm_handle h, int64_t out[5]);
  * updat with 32x32 blocks and 16-bit activations on layouts with dense 8x8-block tiles:
  * when the tiles are few, their contraction is split in parts whose fp32 partial sums
  * live in the workspace (parts x tiles x 64 x 4 KiB), and when there are enough tiles
- * for the tile kernel, the blocks outside the tiles have their contraction cut in four
- * parts, also summed in fp32 in the workspace after the tiles' (4 x those blocks x
+ * for the tile kernel, the blocks outside the tiles have their contraction cut in eight
+ * parts, also summed in fp32 in the workspace after the tiles' (8 x those blocks x
  * 4 KiB).  updat called with a smaller workspace splits only what it holds (the tiles'
  * parts first), and with a NULL one runs unsplit (correct, slower; the summation order,
  * and so the rounding, differs).  pass is a bsmm_pass value. */

@@ -344,7 +344,7 @@ def test_updat_dense_tiles_unsplit(fa):
     # no tile partials; the blocks outside the tiles take their split parts
     nrest = len(bs.bsmm_debug_lut(m.handle, 19))
     assert nrest > 0
-    assert bs.bsmm_workspace_size(m.handle, 2, N, torch.bfloat16) == 4 * nrest * 32 * 32 * 4
+    assert bs.bsmm_workspace_size(m.handle, 2, N, torch.bfloat16) == 8 * nrest * 32 * 32 * 4
     assert m.kernel_name("updat", N, torch.bfloat16) == "dense_tiles"
     dw = m.updat([dev(t) for t in P.xs], [dev(t) for t in P.dys])
     torch.cuda.synchronize()
@@ -371,7 +371,7 @@ def _tiles_and_rest(rng):
 ])
 def test_updat_tiles_with_split_rest(fa, dtype, N, G, dw_dtype, acc):
     """Dense tiles with enough tiles for the split tile path, and blocks outside the tiles
-    whose contraction is cut into four parts (fp32 parts in the workspace after the
+    whose contraction is cut into eight parts (fp32 parts in the workspace after the
     tiles' partials, each part summed over the step groups, then the parts in order)."""
     if fa == 0 and N % 8:
         pytest.skip("features-first activations take the tile kernel only for N % 8 == 0")
@@ -383,7 +383,7 @@ def test_updat_tiles_with_split_rest(fa, dtype, N, G, dw_dtype, acc):
     nrest = len(bs.bsmm_debug_lut(m.handle, 19))
     assert nt >= 16 and nrest > 0
     split = min(8, 256 // nt)
-    assert bs.bsmm_workspace_size(m.handle, 2, N, TORCH_DT[dtype]) == (split * nt * 64 + 4 * nrest) * 32 * 32 * 4
+    assert bs.bsmm_workspace_size(m.handle, 2, N, TORCH_DT[dtype]) == (split * nt * 64 + 8 * nrest) * 32 * 32 * 4
     assert m.kernel_name("updat", N, TORCH_DT[dtype], G) == "dense_tiles"
     P = synth.random_problem(rng, L, 32, N, fa, dtype, G=G, w_std=0.1)
     xs, dys = [dev(t) for t in P.xs], [dev(t) for t in P.dys]

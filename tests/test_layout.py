@@ -198,14 +198,14 @@ def test_weight_gradient_tiles_and_rest_cover_every_block_once():
                         assert bid == -1
         sizes = {}
         for first, n, c, flag in rest:
-            assert flag == 1 and 1 <= n <= 4
+            assert flag == 1 and 1 <= n <= 2
             ids = rids[first:first + n]
             assert np.all(coords[ids, 0] == c) and np.all(np.diff(coords[ids, 1]) > 0)
             seen[ids] += 1
             sizes.setdefault(int(c), []).append(int(n))
         assert np.all(seen == 1)
-        for c, sz in sizes.items():   # fewest groups of <= 4, sizes within 1 of each other
-            assert len(sz) == (sum(sz) + 3) // 4 and max(sz) - min(sz) <= 1
+        for c, sz in sizes.items():   # fewest groups of <= 2, sizes within 1 of each other
+            assert len(sz) == (sum(sz) + 1) // 2 and max(sz) - min(sz) <= 1
     m8 = bs.BlocksparseMatMul(np.ones((16, 16), np.uint8), block_size=16)
     assert all(len(bs.bsmm_debug_lut(m8.handle, w)) == 0 for w in (16, 17, 18, 19))
 

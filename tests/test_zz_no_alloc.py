@@ -81,7 +81,7 @@ def test_noalloc_needs_tables_on_the_device():
 def test_noalloc_band_workload_size():
     """The band workload's weight gradient at its full size (hidden 8192, 32x32 blocks,
     N = 4096, 8 step groups): 32 tiles split 8 ways (64 MiB of parts) and 869 blocks
-    outside them split 4 ways (14 MiB) fit the scratch; bit-identical to bsmm_updat with
+    outside them split 8 ways (27 MiB) fit the scratch; bit-identical to bsmm_updat with
     a caller workspace, on two calls in a row (the second with 2 step groups and N = 1024)."""
     wl = synth.WORKLOADS["hidden8192_b32_n4096_g8"]
     rng = np.random.default_rng(wl.seed)
