@@ -57,3 +57,42 @@ def test_capture_after_first_call(b, fa, dtype):
         torch.cuda.synchronize()
         for got, r in zip((y, dx, dw), ref):
             assert torch.equal(got, r), f"replay {rep} differs from the eager result"
+
+
+@pytest.mark.parametrize("G,acc", [(3, False), (2, True)])
+def test_capture_split_weight_gradient(G, acc):
+    """The dense-tile weight gradient with both splits (tile parts, and the blocks outside
+    the tiles in contraction parts that later launches add to) captured with a fixed
+    workspace: every replay, with eager work between, gives the eager result bit for bit
+    (accumulating: the eager result of the same starting dW)."""
+    print(f"case graph capture split updat G={G} acc={acc}", flush=True)
+    rng = np.random.default_rng(17 + G)
+    L = np.zeros((32, 48), dtype=np.uint8)
+    L[:, :40] = rng.random((32, 40)) < 0.45   # 20 dense tiles: the tile kernel, split
+    L[:, 40:] = rng.random((32, 8)) < 0.1     # blocks outside the tiles
+    N = 512
+    P = synth.random_problem(rng, L, 32, N, 1, "bf16", G=G, w_std=0.1)
+    m = bs.BlocksparseMatMul(L, block_size=32, feature_axis=1)
+    h = m.handle
+    assert m.kernel_name("updat", N, torch.bfloat16, G) == "dense_tiles"
+    assert len(bs.bsmm_debug_lut(h, 19)) > 0
+    xs, dys = [dev(t) for t in P.xs], [dev(t) for t in P.dys]
+    nb = bs.bsmm_workspace_size(h, 2, N, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dw0 = torch.randn(m.w_shape, generator=torch.Generator().manual_seed(2)).cuda()
+    dw = dw0.clone()
+    bs.bsmm_updat(h, xs, dys, dw, N, accumulate=acc, ws=ws)   # eager (also uploads the tables)
+    torch.cuda.synchronize()
+    ref = dw.clone()
+    dw.copy_(dw0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bs.bsmm_updat(h, xs, dys, dw, N, accumulate=acc, ws=ws)
+    for rep in range(3):
+        dw.copy_(dw0)                    # eager work between replays
+        ws.fill_(0xFF)                   # the parts are written before they are read
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw, ref), f"replay {rep} differs from the eager result"
