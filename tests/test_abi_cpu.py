@@ -232,6 +232,47 @@ def test_kernel_choice_names():
         m32.kernel_name("updat", 64, torch.bfloat16, group=9)
 
 
+def test_weight_gradient_workspace_size():
+    """The dense-tile weight gradient's workspace, from the layout alone: the tiles'
+    split partials (parts = clamp(256 / tiles, 1, 8), 64 blocks of 4 KiB each per tile
+    and part), then 8 parts of every block outside the tiles -- the latter only when
+    the tiles can take the tile kernel (tiles x parts >= 128); 16-bit activations of
+    32x32 blocks only, and none for N = 0."""
+    import torch
+    rng = np.random.default_rng(4)
+
+    def ws(L, N=512, dt=torch.bfloat16):
+        return bs.bsmm_workspace_size(bs.BlocksparseMatMul(L, block_size=32).handle, 2, N, dt)
+
+    def counts(L):
+        m = bs.BlocksparseMatMul(L, block_size=32)
+        return len(bs.bsmm_debug_lut(m.handle, 16)) // 4, len(bs.bsmm_debug_lut(m.handle, 19))
+
+    L = np.zeros((32, 48), dtype=np.uint8)   # 20 dense tiles and a sparse tile column
+    L[:, :40] = rng.random((32, 40)) < 0.45
+    L[:, 40:] = rng.random((32, 8)) < 0.1
+    nt, nr = counts(L)
+    assert nt >= 16 and nr > 0
+    p = min(8, 256 // nt)
+    assert ws(L) == (p * nt * 64 + 8 * nr) * 4096
+    assert ws(L, dt=torch.float16) == ws(L)
+    assert ws(L, dt=torch.float32) == 0 and ws(L, N=0) == 0
+    few = np.zeros((16, 16), dtype=np.uint8)   # 4 dense tiles: tiles x parts = 32 < 128
+    few[:, :] = rng.random((16, 16)) < 0.5
+    few[:8, 8:] = 0
+    few[0, 15] = 1                             # one block outside the tiles
+    nt, nr = counts(few)
+    assert 0 < nt < 16 and nr > 0
+    assert ws(few) == 8 * nt * 64 * 4096       # the tiles' parts only
+    many = (rng.random((128, 128)) < 0.5).astype(np.uint8)
+    nt, nr = counts(many)
+    assert nt >= 256                           # unsplit tiles: the rest's parts only
+    assert ws(many) == 8 * nr * 4096
+    empty_rest = np.ones((16, 16), dtype=np.uint8)
+    assert counts(empty_rest)[1] == 0 and ws(empty_rest) == 8 * 4 * 64 * 4096
+    assert ws(np.zeros((8, 8), dtype=np.uint8)) == 0
+
+
 def test_force_kernel():
     import torch
     rng = np.random.default_rng(1)
